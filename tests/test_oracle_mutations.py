@@ -1,0 +1,183 @@
+"""Planted mistakes in the oracle (CPU only): every mutant must trip at least one pin.
+
+Each mutant replaces one oracle function by a plausible wrong version (wrong head
+grouping, missing scale, swapped operands, no max subtraction, off-by-one slot
+offset, LIFO reuse, copy-on-write that forgets the refcount) and reruns pin
+tests, which must then fail.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import allocator as al
+from oracle import attention as oa
+from oracle import cache as oc
+
+import test_oracle_allocator as t_alloc
+import test_oracle_attention as t_attn
+import test_oracle_cache as t_cache
+
+_true_attention = oa.attention_contiguous
+
+
+def _mut_head_mapping(q, k, v, scale):
+    Hq, d = q.shape
+    n, Hkv, _ = k.shape
+    out = np.empty((Hq, d))
+    for h in range(Hq):
+        g = h % Hkv  # wrong: interleaved instead of contiguous groups
+        s = scale * (k[:, g, :] @ q[h])
+        w = np.exp(s - s.max())
+        out[h] = (w @ v[:, g, :]) / w.sum()
+    return out
+
+
+def _mut_no_scale(q, k, v, scale):
+    return _true_attention(q, k, v, 1.0)
+
+
+def _mut_swap_kv(q, k, v, scale):
+    return _true_attention(q, v, k, scale)
+
+
+def _mut_no_max(q, k, v, scale):
+    Hq, d = q.shape
+    n, Hkv, _ = k.shape
+    G = Hq // Hkv
+    out = np.empty((Hq, d))
+    with np.errstate(over="ignore", invalid="ignore"):
+        for h in range(Hq):
+            g = h // G
+            w = np.exp(scale * (k[:, g, :] @ q[h]))
+            out[h] = (w @ v[:, g, :]) / w.sum()
+    return out
+
+
+def _mut_drop_last_token(q, k, v, scale):
+    return _true_attention(q, k[:-1] if len(k) > 1 else k, v[:-1] if len(v) > 1 else v, scale)
+
+
+ATTENTION_PINS = [
+    lambda: t_attn.test_matches_torch_sdpa(8, 2, 1, 16),
+    lambda: t_attn.test_matches_torch_sdpa(64, 8, 300, 128),
+    t_attn.test_gqa_equals_mha_with_repeated_kv,
+    t_attn.test_single_token_returns_value_exactly,
+    t_attn.test_dominant_key_selects_its_value,
+    lambda: test_large_scores_stay_finite(),
+]
+
+
+def test_large_scores_stay_finite():
+    # a pin in its own right: scores around 1e3 must not overflow (max subtraction)
+    rng = np.random.default_rng(0)
+    q = np.zeros((1, 4))
+    q[0, 0] = 1.0
+    k = rng.standard_normal((10, 1, 4))
+    k[:, 0, 0] = 1000.0 + np.arange(10)
+    v = rng.standard_normal((10, 1, 4))
+    out = oa.attention_contiguous(q, k, v, 1.0)
+    w = np.exp(np.arange(10) - 9.0)
+    assert np.allclose(out[0], (w @ v[:, 0]) / w.sum(), atol=1e-13, rtol=0)
+
+
+def _fails_some(pins):
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("mutant", [_mut_head_mapping, _mut_no_scale, _mut_swap_kv, _mut_no_max,
+                                    _mut_drop_last_token])
+def test_attention_mutants_are_caught(monkeypatch, mutant):
+    assert not _fails_some(ATTENTION_PINS)  # the true oracle passes
+    monkeypatch.setattr(oa, "attention_contiguous", mutant)
+    assert _fails_some(ATTENTION_PINS)
+
+
+def test_gather_off_by_one_is_caught(monkeypatch):
+    true_gather = oc.gather
+
+    def bad_gather(k_cache, v_cache, table, n):
+        nb, H, npieces, B, X = k_cache.shape
+        t = np.arange(n)
+        blk = np.asarray(table)[t // B]
+        off = (t + 1) % B
+        return k_cache[blk, :, :, off, :].reshape(n, H, npieces * X), v_cache[blk, :, off, :]
+
+    pins = [t_cache.test_gather_reassembles_logical_order, t_cache.test_scatter_gather_against_slot_dictionary]
+    assert not _fails_some(pins)
+    monkeypatch.setattr(oc, "gather", bad_gather)
+    assert _fails_some(pins)
+    monkeypatch.setattr(oc, "gather", true_gather)
+
+
+def test_key_piece_order_is_caught(monkeypatch):
+    def bad_scatter(k_cache, v_cache, k_new, v_new, slots):
+        nb, H, npieces, B, X = k_cache.shape
+        s = np.asarray(slots, dtype=np.int64)
+        keep = s >= 0
+        s = s[keep]
+        # wrong: pieces reversed
+        k_cache[s // B, :, :, s % B, :] = np.asarray(k_new)[keep].reshape(len(s), H, npieces, X)[:, :, ::-1, :]
+        v_cache[s // B, :, s % B, :] = np.asarray(v_new)[keep]
+
+    monkeypatch.setattr(oc, "scatter", bad_scatter)
+    assert _fails_some([lambda: t_cache.test_layout_offsets("bf16", 128)])
+
+
+def test_lifo_reuse_is_caught(monkeypatch):
+    def lifo_free(self, sid):
+        s = self._get(sid)
+        for b in s.table:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.free.appendleft(b)
+        del self.seqs[sid]
+
+    monkeypatch.setattr(al.BlockPool, "free_seq", lifo_free)
+    assert _fails_some([t_alloc.test_fifo_slots_by_hand, t_alloc.test_free_order_after_fork_free])
+
+
+def test_cow_without_decrement_is_caught(monkeypatch):
+    def bad_append_one(self, sid, count, slots, pairs):
+        B = self.block_size
+        s = self._get(sid)
+        if count == 0:
+            return
+        if s.length % B != 0 and self.refcount[s.table[-1]] > 1:
+            new = self._pop()
+            pairs.append((s.table[-1], new))
+            s.table[-1] = new  # wrong: old block keeps its count
+        for p in range(s.length, s.length + count):
+            if p % B == 0:
+                s.table.append(self._pop())
+            slots.append(s.table[p // B] * B + p % B)
+        s.length += count
+
+    monkeypatch.setattr(al.BlockPool, "_append_one", bad_append_one)
+    assert _fails_some([t_alloc.test_fork_and_copy_on_write_by_hand, t_alloc.test_beam_sharing_closed_form])
+
+
+def test_cow_on_full_blocks_is_caught(monkeypatch):
+    def bad_append_one(self, sid, count, slots, pairs):
+        B = self.block_size
+        s = self._get(sid)
+        if count == 0:
+            return
+        if s.table and self.refcount[s.table[-1]] > 1:  # wrong: copies full blocks too
+            last = s.table[-1]
+            new = self._pop()
+            pairs.append((last, new))
+            self.refcount[last] -= 1
+            s.table[-1] = new
+        for p in range(s.length, s.length + count):
+            if p % B == 0:
+                s.table.append(self._pop())
+            slots.append(s.table[p // B] * B + p % B)
+        s.length += count
+
+    monkeypatch.setattr(al.BlockPool, "_append_one", bad_append_one)
+    assert _fails_some([t_alloc.test_fork_and_copy_on_write_by_hand])
