@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode-attention step on one MI355X.
+
+A step is one pass of the decode hot path over a synthetic batch already
+resident in HBM: write each sequence's new K/V token into its slot
+(reshape_and_cache), then paged decode attention over every context (the
+partition kernel plus, when a context spans several partitions, the
+log-sum-exp reduce).  The block pool, tables and the rest of the context are
+built once before timing by the library's own allocator and kernels.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+METRIC = "decode-attention KV GB/s (% of HBM peak) and seq-steps/sec at 1 MI355X"
+HEADLINE = "llama7b_bf16"
+EXTRA = ["gqa_bf16_b16", "gqa_bf16_b32", "long_bf16", "beam_cow_bf16"]
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_physical_amd", "csrc", "kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def describe(w) -> dict:
+    s = w.spec
+    d = {"workload": s.name, "num_seqs": w.num_seqs, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+         "head_dim": s.head_dim, "block_size": s.block_size, "kv_dtype": s.kv_dtype,
+         "partition_size": s.partition_size, "total_context_tokens": w.total_tokens,
+         "max_context_len": w.max_context_len, "pool_blocks": w.num_blocks, "seed": s.seed,
+         "kv_bytes_per_step": w.kv_bytes}
+    if s.kind == "beam":
+        d["lengths"] = f"{s.prefix_len} shared + uniform{list(s.tail_range)}"
+    elif s.lens is not None:
+        d["lengths"] = list(s.lens)
+    else:
+        d["lengths"] = str(s.len_dist)
+    return d
+
+
+def time_launches(fn, n, stream):
+    """Average duration (ms) of n launches of fn, each bracketed by HIP events on `stream`."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(t.mean()), float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+def measure(w, steps, warmup, stream):
+    import torch
+    from paged_kv_cache_physical_amd.runner import GpuBatch
+
+    t0 = time.perf_counter()
+    gb = GpuBatch(w)
+    log(f"[bench] {w.spec.name}: built batch ({w.total_tokens} tokens, {w.kv_bytes / 1e9:.3f} GB KV) "
+        f"in {time.perf_counter() - t0:.1f}s")
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            gb.step(stream=stream)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(steps):
+            gb.step(stream=stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms_step = start.elapsed_time(end) / steps
+        n_k = max(steps, 20)
+        part = time_launches(lambda: gb.attention_partitions(stream=stream), n_k, stream)
+        red = time_launches(lambda: gb.attention_reduce(stream=stream), n_k, stream)
+        rc = time_launches(lambda: gb.write_decode_token(stream=stream), n_k, stream)
+        attn = time_launches(lambda: gb.attention(stream=stream), n_k, stream)
+    res = {
+        "ms_per_step": ms_step,
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "kv_gbps_step": w.kv_bytes / (ms_step * 1e-3) / 1e9,
+        "seq_steps_per_s": w.num_seqs / (ms_step * 1e-3),
+        "partition_kernel_us": {"mean": 1e3 * part[0], "median": 1e3 * part[1], "p10": 1e3 * part[2],
+                                "p90": 1e3 * part[3]},
+        "reduce_kernel_us": 1e3 * red[0],
+        "reshape_and_cache_us": 1e3 * rc[0],
+        "attention_us": 1e3 * attn[0],
+        "kv_gbps_partition_kernel": w.kv_bytes / (part[0] * 1e-3) / 1e9,
+        "kv_gbps_attention": w.kv_bytes / (attn[0] * 1e-3) / 1e9,
+    }
+    del gb
+    torch.cuda.empty_cache()
+    return res
+
+
+def hbm_read_ceiling(stream):
+    """Practical read bandwidth: torch's sum over a 2 GiB fp32 tensor (context only)."""
+    import torch
+    x = torch.ones(512 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            x.sum()
+        ms = time_launches(lambda: x.sum(), 20, stream)[1]
+    del x
+    torch.cuda.empty_cache()
+    return 2 ** 31 / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The float64 oracle, as it stands, on the host cores: paged attention over the batch."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oa
+    from oracle import run as orun
+
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    t0 = time.perf_counter()
+    rp = orun.replay(w)
+    log(f"[bench] oracle replay built in {time.perf_counter() - t0:.1f}s")
+    s = w.spec
+    order = np.random.default_rng(0).permutation(w.num_seqs)
+    done, tokens, elapsed, passes = 0, 0, 0.0, 0
+    with threadpool_limits(limits=cores):
+        while elapsed < budget_s:
+            for i in order:
+                t = time.perf_counter()
+                oa.paged_attention(w.q, rp.k_cache, rp.v_cache, rp.tables, rp.context_lens, w.scale, s.kv_dtype,
+                                   seqs=[int(i)])
+                elapsed += time.perf_counter() - t
+                done += 1
+                tokens += int(w.context_lens[i])
+                if elapsed >= budget_s:
+                    break
+            passes += 1
+    kv = tokens * w.kv_bytes_per_token
+    return {"value": kv / elapsed / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "seq_steps_per_s": done / elapsed,
+            "sample": f"{done} sequence-steps over {passes} pass(es) of the {w.num_seqs}-sequence {s.name} batch "
+                      f"({tokens} context tokens), float64 NumPy "
+                      f"oracle (gather through the block table, then softmax(qK^T*scale)V), BLAS threads={cores}, "
+                      f"{elapsed:.1f}s"}
+
+
+def traffic_from_profiles(workload: str):
+    path = os.path.join(ROOT, "profiles", f"paged_decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other decode batches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    from paged_kv_cache_physical_amd import _lib
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    _lib.lib()  # fail loudly if the HIP library is not built
+    stream = torch.cuda.Stream()  # default priority
+
+    w = wl.named(args.workload, seed=0)
+    head = measure(w, args.steps, args.warmup, stream)
+    log(f"[bench] {w.spec.name}: {json.dumps(head)}")
+    extra = {}
+    if not args.no_extra:
+        for name in EXTRA:
+            if name == args.workload:
+                continue
+            r = measure(wl.named(name, seed=0), 20, 5, stream)
+            r["pct_hbm_peak_partition_kernel"] = 100 * r["kv_gbps_partition_kernel"] / HBM_PEAK_GBPS
+            extra[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+            log(f"[bench] {name}: {json.dumps(extra[name])}")
+    ceiling = hbm_read_ceiling(stream)
+    log(f"[bench] torch sum read ceiling {ceiling:.0f} GB/s")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    if cpu:
+        log(f"[bench] cpu baseline {json.dumps(cpu)}")
+
+    achieved = head["kv_gbps_partition_kernel"]
+    line = {
+        "metric": METRIC,
+        "value": round(head["kv_gbps_step"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.spec.kv_dtype,
+        "data": "synthetic",
+        "config": describe(w),
+        "seq_steps_per_s": round(head["seq_steps_per_s"], 1),
+        "pct_hbm_peak_step": round(100 * head["kv_gbps_step"] / HBM_PEAK_GBPS, 2),
+        "kernels_us": {"paged_decode_partitions": round(head["partition_kernel_us"]["mean"], 2),
+                       "lse_reduce": round(head["reduce_kernel_us"], 2),
+                       "reshape_and_cache": round(head["reshape_and_cache_us"], 2),
+                       "attention_call": round(head["attention_us"], 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles(w.spec.name),
+                     "kernel": "paged_decode_kernel (partition pass)",
+                     "bytes_per_launch": w.kv_bytes},
+        "hbm_read_ceiling_gbps": round(ceiling, 1),
+        "cpu_baseline": cpu,
+        "other_workloads": extra,
+        "kernel_source_sha": kernel_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,265 @@
+/*
+ * pkv.h — C interface of libpkv, a paged KV-cache decode-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (four web pages about the PagedAttention paper,
+ * "Efficient Memory Management for Large Language Model Serving with
+ * PagedAttention"):
+ *   [P1] lain42.top reading note (abstract; summary "core method" bullets).
+ *   [P2] aiplusplus.yigather.com explainer (sections "core idea" and
+ *        "key technical points" 1-4).
+ *   [P3] auturnal.com analytical guide "paged-attention-serving" (sections
+ *        1-6, "Equations and derivations" Eq. (1)-(3), "Verification protocol").
+ *   [P4] cayang0802.github.io blog "paged-attention" (KV block and block
+ *        table figure, beam-search sharing, preemption).
+ *
+ * Two halves:
+ *   - a host block pool (pkv_pool_*, pkv_seq_*, pkv_append_tokens,
+ *     pkv_block_tables): fixed-size blocks, per-sequence block tables,
+ *     on-demand allocation, refcounted sharing and copy-on-write.  Host
+ *     memory only; no GPU is touched, so these calls also work on a machine
+ *     without one.
+ *   - device calls (pkv_reshape_and_cache, pkv_copy_blocks,
+ *     pkv_paged_attention_decode): HIP kernels enqueued on the caller's
+ *     stream.  Every pointer they take is caller-owned device memory; they
+ *     allocate nothing, never synchronise, validate arguments on the host and
+ *     return the error synchronously; a failed launch returns PKV_ERR_HIP.
+ *
+ * Status codes: 0 on success, negative on error.  On any error from the
+ * pool, the pool's state is unchanged.
+ *
+ * Physical cache layout (one key cache and one value cache per layer):
+ *   value cache  V[num_blocks][H_kv][B][d]
+ *   key cache    K[num_blocks][H_kv][d / X][B][X],   X = 64 / bytes_per_scalar
+ * Each (block, KV head) owns one contiguous tile of B * d scalars.  In a key
+ * tile, a token's d values are split into 64-byte pieces and piece j of all B
+ * tokens is stored together.  Token position t of a sequence whose table is
+ * bt lives in block bt[t / B] at offset t % B; its slot is
+ * bt[t / B] * B + t % B.  Scalars are fp32 or bf16 (PKV_F32 / PKV_BF16).
+ *
+ * Supported shapes: head_dim d in {64, 128}; block size B in {16, 32};
+ * H_q / H_kv in {1, 2, 4, 8}; fp32 or bf16 scalars.  Others give
+ * PKV_ERR_UNSUPPORTED.
+ *
+ * Threading: a pool is not thread-safe; the caller serialises calls on one
+ * pool.  Device calls are safe to issue from any thread.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,   /* bad pointer, size, id or shape */
+  PKV_ERR_OUT_OF_BLOCKS = -2, /* the pool cannot hold the whole batch */
+  PKV_ERR_NO_SUCH_SEQ = -3,   /* sequence id unknown or already freed */
+  PKV_ERR_REFCOUNT = -4,      /* pkv_pool_validate found a broken invariant */
+  PKV_ERR_UNSUPPORTED = -5,   /* shape or dtype outside the supported set */
+  PKV_ERR_HIP = -6,           /* a kernel launch failed */
+  PKV_ERR_WORKSPACE = -7      /* attention workspace missing or too small */
+};
+
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+typedef struct pkv_pool pkv_pool; /* opaque; owns host metadata only */
+
+typedef struct pkv_stats {
+  int64_t num_blocks;      /* pool capacity */
+  int64_t free_blocks;     /* blocks in the free queue */
+  int64_t used_blocks;     /* physical blocks with refcount > 0 */
+  int64_t sum_refcount;    /* equals logical_blocks while the pool is sound */
+  int64_t num_seqs;        /* live sequences */
+  int64_t logical_tokens;  /* sum of live sequence lengths */
+  int64_t logical_blocks;  /* sum of live block-table lengths */
+  int64_t allocated_slots; /* used_blocks * B: Eq. (2)'s A_B summed, [P3] */
+  int64_t table_bytes;     /* 4 * logical_blocks */
+} pkv_stats;
+
+/* Human-readable name of a status code (static string). */
+const char* pkv_status_string(pkv_status status);
+
+/* Interface version; bumped whenever a signature or the cache layout changes. */
+int32_t pkv_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Host block pool
+ * ------------------------------------------------------------------------- */
+
+/* Create a pool of num_blocks blocks of block_size token slots.
+ * [P2] core idea items 1 and 4: fixed-size blocks, allocated on demand.
+ * free_order: a permutation of [0, num_blocks) giving the initial order of the
+ *   free queue (host array, read only, copied), or NULL for 0, 1, 2, ...
+ *   Blocks are taken from the head of the queue and freed blocks join its tail
+ *   (FIFO), so a freed block is reused as late as possible.
+ * out: receives the pool; destroy it with pkv_pool_destroy.
+ * Errors: INVALID_ARG (non-positive sizes, free_order not a permutation). */
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                           pkv_pool** out);
+
+/* Destroy a pool and every sequence in it.  NULL is ignored. */
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* Create an empty sequence (0 tokens, 0 blocks).  Ids are 0, 1, 2, ... in
+ * creation order (forks included) and are never reused. */
+pkv_status pkv_seq_create(pkv_pool* pool, int32_t* out_seq);
+
+/* Create a child that shares every block of parent: the child's table is a copy
+ * of the parent's and each block's refcount rises by one.  [P4] beam-search
+ * sharing; [P3] section 3 (sharing needs identical tokens and positions, which
+ * a fork guarantees).  Errors: NO_SUCH_SEQ. */
+pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* out_child);
+
+/* Release a sequence (finish, cancel or time-out, [P2] key technical point 2,
+ * [P3] section 3): refcounts drop in logical order and blocks that reach zero
+ * join the tail of the free queue.  Errors: NO_SUCH_SEQ. */
+pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
+
+/* Append counts[i] tokens to seqs[i] for i < n, in that order, all or nothing.
+ * [P1]/[P2]: a sequence takes a new block only when it grows onto one.
+ * [P3] section 3: a branch writing into a shared block that is not full copies
+ * it first.  Per sequence with current length L and count c > 0:
+ *   1. if L % B != 0 and the last block's refcount > 1: pop a fresh block,
+ *      record the pair (old, new), decrement old, point the table at new;
+ *   2. for each position p in [L, L + c): if p % B == 0 pop a fresh block;
+ *      emit slot table[p / B] * B + p % B.
+ * out_slots: host int64[slots_cap] receiving sum(counts) slots, sequence-major
+ *   and in position order.
+ * out_cow_pairs: host int32[2 * cow_cap] receiving (src, dst) block pairs; the
+ *   caller must run pkv_copy_blocks on them before writing the new tokens.
+ *   At most one pair per sequence, so cow_cap >= n always suffices.
+ * out_n_cow: receives the number of pairs.
+ * Errors (pool unchanged): INVALID_ARG (n < 0, NULL arrays, negative count,
+ *   a sequence listed twice, slots_cap < sum(counts), cow_cap too small; in
+ *   the last case *out_n_cow holds the number needed), NO_SUCH_SEQ,
+ *   OUT_OF_BLOCKS (the batch needs more blocks than are free). */
+pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t* counts, int32_t n,
+                             int64_t* out_slots, int64_t slots_cap, int32_t* out_cow_pairs,
+                             int32_t cow_cap, int32_t* out_n_cow);
+
+/* Dense block tables for seqs[0..n): host int32 out_tables[n][max_blocks],
+ * row i = the physical blocks of seqs[i] in logical order, padded with -1;
+ * out_context_lens[i] = its length in tokens ([P2] key technical point 1).
+ * Errors: INVALID_ARG (a table longer than max_blocks, NULL arrays),
+ * NO_SUCH_SEQ. */
+pkv_status pkv_block_tables(const pkv_pool* pool, const int32_t* seqs, int32_t n, int32_t max_blocks,
+                            int32_t* out_tables, int32_t* out_context_lens);
+
+/* Length in tokens and number of blocks of one sequence.  Errors: NO_SUCH_SEQ. */
+pkv_status pkv_seq_info(const pkv_pool* pool, int32_t seq, int32_t* out_len, int32_t* out_num_blocks);
+
+/* Pool counters ([P3] Eq. (2)-(3) and section 6's accounting categories). */
+pkv_status pkv_pool_stats(const pkv_pool* pool, pkv_stats* out);
+
+/* Refcount of one physical block, or -1 for an id out of range. */
+int32_t pkv_block_refcount(const pkv_pool* pool, int32_t block);
+
+/* Copy the free queue, head first, into host out[cap]; *out_n = its length.
+ * Errors: INVALID_ARG if cap < the queue length. */
+pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* out_n);
+
+/* Check the pool's invariants: each block's refcount equals the number of live
+ * tables holding it; a free block has refcount 0 and appears once; free plus
+ * used equals capacity; each table has ceil(length / B) entries.  [P3] section
+ * 3 asks tests to check refcounts and reuse.  Errors: REFCOUNT. */
+pkv_status pkv_pool_validate(const pkv_pool* pool);
+
+/* ---------------------------------------------------------------------------
+ * Device calls (HIP, gfx950).  All pointers are device memory owned by the
+ * caller, 16-byte aligned; `stream` may be NULL (the default stream).
+ * ------------------------------------------------------------------------- */
+
+/* Write token i's key and value (k_new, v_new: [num_tokens][H_kv][d], the
+ * cache's scalar type) into slot slots[i] of the caches, in the layout above.
+ * Decoding computes only the new token's K/V and reads the rest from the cache
+ * ([P4] KV-cache introduction; [P2] core idea item 3).
+ * slots: device int64[num_tokens]; a slot of -1 is skipped, a slot at or past
+ * num_blocks * B is skipped as well.  Slots must be distinct within a call
+ * (two writers of one slot race).
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t kv_dtype, hipStream_t stream);
+
+/* Copy whole blocks (every head and slot of both caches) src -> dst for each
+ * pair: the device half of copy-on-write ([P3] section 3).
+ * pairs: device int32[n_pairs][2] as returned by pkv_append_tokens.  The dst
+ * blocks must be distinct and no dst may be another pair's src (the pool never
+ * produces either).  Pairs with an id out of [0, num_blocks) are skipped.
+ * block_bytes: bytes of one block in one cache, H_kv * B * d * scalar size.
+ * Errors: INVALID_ARG (block_bytes not a positive multiple of 16), HIP. */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
+                           int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
+
+/* Bytes of workspace pkv_paged_attention_decode needs for these sizes (0 when
+ * no sequence can span more than one partition). */
+size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t max_context_len,
+                                     int32_t partition_size);
+
+/* Decode attention, one query token per sequence, reading K/V through block
+ * tables ([P2] key technical point 1; [P1] "custom kernel fusing table lookup,
+ * block fetch and attention"; [P3] section 1: paging changes storage, not the
+ * result).  For sequence s, query head h and g = h / (H_q / H_kv):
+ *   out[s][h] = sum_{t < n_s} softmax_t(scale * q[s][h] . K_s[t][g]) V_s[t][g]
+ * where K_s[t] is the key of token position t read through block_tables[s].
+ *   out: fp32 [num_seqs][H_q][d].
+ *   q: [num_seqs][H_q][d] in the cache's scalar type.
+ *   block_tables: device int32 [num_seqs][max_blocks] (entries past the
+ *     sequence's last block are not read).
+ *   context_lens: device int32 [num_seqs]; n_s counts the token just written.
+ *     n_s == 0 gives an all-zero output row; n_s < 0, n_s > max_context_len,
+ *     n_s > max_blocks * B, or a block id outside [0, num_blocks) gives NaN.
+ *   partition_size: tokens per context partition (a multiple of B), or 0 for
+ *     one partition per sequence.  Sequences longer than one partition are
+ *     computed as independent partitions combined by a log-sum-exp reduction
+ *     (split context); that needs `workspace` (device, workspace_bytes >=
+ *     pkv_attention_workspace_bytes(...)).
+ * Arithmetic: fp32 accumulation; bf16 inputs are multiplied exactly and summed
+ * in fp32.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks, int32_t max_context_len, float scale,
+                                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                      int32_t kv_dtype, hipStream_t stream);
+
+/* The two stages of pkv_paged_attention_decode, for callers that schedule or
+ * time them separately.  Same arguments and errors; issue `partitions` then
+ * `reduce` on one stream.
+ * pkv_paged_attention_partitions: one pass over every (sequence, KV head,
+ *   partition); writes the final rows of sequences that fit one partition and
+ *   the per-partition (acc, max, sum) of the others into the workspace.
+ * pkv_paged_attention_reduce: combines the partitions of every sequence that
+ *   has more than one (log-sum-exp weights); a no-op when none has. */
+pkv_status pkv_paged_attention_partitions(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_tables, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                          int32_t max_blocks, int32_t max_context_len, float scale,
+                                          int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                          int32_t kv_dtype, hipStream_t stream);
+pkv_status pkv_paged_attention_reduce(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks, int32_t max_blocks,
+                                      int32_t max_context_len, float scale, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes, int32_t kv_dtype,
+                                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,312 @@
+"""paged_kv_cache_physical_amd — Python binding of libpkv, the paged KV-cache decode
+path for AMD MI355X (gfx950).
+
+Argument marshalling only: every call below forwards to the C function of the
+same name in ``libpkv.so`` (declared in ``include/pkv.h``); host arrays are
+NumPy, device buffers are torch tensors (PyTorch provides device memory and
+streams, nothing else).  The library must have been built first
+(``python -m paged_kv_cache_physical_amd.build``); otherwise every call raises.
+
+Cache tensors use the interface's physical layout:
+  key cache    [num_blocks][H_kv][d / X][B][X],  X = 64 / bytes_per_scalar
+  value cache  [num_blocks][H_kv][B][d]
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from ._lib import (PKV_BF16, PKV_F32, InvalidArg, NoSuchSeq, OutOfBlocks, PkvError, Stats, check,  # noqa: F401
+                   header_symbols, lib)
+
+__all__ = [
+    "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_create", "pkv_seq_fork", "pkv_seq_free", "pkv_append_tokens",
+    "pkv_block_tables", "pkv_seq_info", "pkv_pool_stats", "pkv_block_refcount", "pkv_pool_free_list",
+    "pkv_pool_validate", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_attention_workspace_bytes",
+    "pkv_paged_attention_decode", "pkv_paged_attention_partitions", "pkv_paged_attention_reduce", "pkv_abi_version", "Pool", "cache_shapes", "empty_caches", "PkvError",
+    "OutOfBlocks", "NoSuchSeq", "InvalidArg",
+]
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None and a.size else None
+
+
+def pkv_abi_version() -> int:
+    return int(lib().pkv_abi_version())
+
+
+# ---------------------------------------------------------------------------
+# Host block pool
+# ---------------------------------------------------------------------------
+
+
+def pkv_pool_create(num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None) -> ctypes.c_void_p:
+    order = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+    if order is not None and order.size != num_blocks:
+        raise InvalidArg(-1, "pkv_pool_create", "free_order length differs from num_blocks")
+    out = ctypes.c_void_p()
+    check(lib().pkv_pool_create(num_blocks, block_size, _ptr(order), ctypes.byref(out)), "pkv_pool_create")
+    return out
+
+
+def pkv_pool_destroy(pool) -> None:
+    lib().pkv_pool_destroy(pool)
+
+
+def pkv_seq_create(pool) -> int:
+    sid = ctypes.c_int32()
+    check(lib().pkv_seq_create(pool, ctypes.byref(sid)), "pkv_seq_create")
+    return sid.value
+
+
+def pkv_seq_fork(pool, parent: int) -> int:
+    sid = ctypes.c_int32()
+    check(lib().pkv_seq_fork(pool, parent, ctypes.byref(sid)), "pkv_seq_fork")
+    return sid.value
+
+
+def pkv_seq_free(pool, seq: int) -> None:
+    check(lib().pkv_seq_free(pool, seq), "pkv_seq_free")
+
+
+def pkv_append_tokens(pool, seqs: Sequence[int], counts: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """Returns (slots int64[sum counts], copy-on-write pairs int32[k][2])."""
+    seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    if seqs.shape != counts.shape or seqs.ndim != 1:
+        raise InvalidArg(-1, "pkv_append_tokens", "seqs and counts must be 1-D and equal in length")
+    total = int(counts[counts > 0].sum()) if counts.size else 0
+    slots = np.empty(max(total, 0), dtype=np.int64)
+    pairs = np.empty((max(len(seqs), 1), 2), dtype=np.int32)
+    n_cow = ctypes.c_int32()
+    check(lib().pkv_append_tokens(pool, _ptr(seqs), _ptr(counts), len(seqs), _ptr(slots), slots.size,
+                                  _ptr(pairs), pairs.shape[0], ctypes.byref(n_cow)), "pkv_append_tokens")
+    return slots, pairs[:n_cow.value].copy()
+
+
+def pkv_block_tables(pool, seqs: Sequence[int], max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+    seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+    tables = np.empty((len(seqs), max_blocks), dtype=np.int32)
+    lens = np.empty(len(seqs), dtype=np.int32)
+    check(lib().pkv_block_tables(pool, _ptr(seqs), len(seqs), max_blocks, _ptr(tables), _ptr(lens)),
+          "pkv_block_tables")
+    return tables, lens
+
+
+def pkv_seq_info(pool, seq: int) -> Tuple[int, int]:
+    n, nb = ctypes.c_int32(), ctypes.c_int32()
+    check(lib().pkv_seq_info(pool, seq, ctypes.byref(n), ctypes.byref(nb)), "pkv_seq_info")
+    return n.value, nb.value
+
+
+def pkv_pool_stats(pool) -> dict:
+    st = Stats()
+    check(lib().pkv_pool_stats(pool, ctypes.byref(st)), "pkv_pool_stats")
+    return st.as_dict()
+
+
+def pkv_block_refcount(pool, block: int) -> int:
+    return int(lib().pkv_block_refcount(pool, block))
+
+
+def pkv_pool_free_list(pool) -> np.ndarray:
+    n = ctypes.c_int32()
+    lib().pkv_pool_free_list(pool, None, 0, ctypes.byref(n))
+    out = np.empty(n.value, dtype=np.int32)
+    check(lib().pkv_pool_free_list(pool, _ptr(out), out.size, ctypes.byref(n)), "pkv_pool_free_list")
+    return out
+
+
+def pkv_pool_validate(pool) -> None:
+    check(lib().pkv_pool_validate(pool), "pkv_pool_validate")
+
+
+class Pool:
+    """Owning wrapper around a pkv_pool handle; methods map 1:1 onto the C calls."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self.handle = pkv_pool_create(num_blocks, block_size, free_order)
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self.handle is not None:
+            pkv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def create(self) -> int:
+        return pkv_seq_create(self.handle)
+
+    def fork(self, parent: int) -> int:
+        return pkv_seq_fork(self.handle, parent)
+
+    def free_seq(self, seq: int) -> None:
+        pkv_seq_free(self.handle, seq)
+
+    def append(self, seqs, counts):
+        return pkv_append_tokens(self.handle, seqs, counts)
+
+    def block_tables(self, seqs, max_blocks):
+        return pkv_block_tables(self.handle, seqs, max_blocks)
+
+    def info(self, seq):
+        return pkv_seq_info(self.handle, seq)
+
+    def stats(self) -> dict:
+        return pkv_pool_stats(self.handle)
+
+    def refcount(self, block: int) -> int:
+        return pkv_block_refcount(self.handle, block)
+
+    def free_list(self) -> np.ndarray:
+        return pkv_pool_free_list(self.handle)
+
+    def validate(self) -> None:
+        pkv_pool_validate(self.handle)
+
+
+# ---------------------------------------------------------------------------
+# Device calls (torch tensors on the GPU)
+# ---------------------------------------------------------------------------
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise InvalidArg(-1, "dtype", f"unsupported tensor dtype {t.dtype}")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise InvalidArg(-1, name, "tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise InvalidArg(-1, name, "tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def cache_shapes(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, kv_dtype: str):
+    X = 64 // (4 if kv_dtype == "f32" else 2)
+    return ((num_blocks, num_kv_heads, head_dim // X, block_size, X), (num_blocks, num_kv_heads, block_size, head_dim))
+
+
+def empty_caches(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype: str, device="cuda", poison=True):
+    """Key/value cache tensors in the interface layout, optionally filled with NaN."""
+    torch = _torch()
+    dt = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+    ks, vs = cache_shapes(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype)
+    k = torch.empty(ks, dtype=dt, device=device)
+    v = torch.empty(vs, dtype=dt, device=device)
+    if poison:
+        if kv_dtype == "f32":
+            k.view(torch.int32).fill_(0x7FC00000)
+            v.view(torch.int32).fill_(0x7FC00000)
+        else:
+            k.view(torch.int16).fill_(0x7FC0)
+            v.view(torch.int16).fill_(0x7FC0)
+    return k, v
+
+
+def pkv_reshape_and_cache(k_new, v_new, k_cache, v_cache, slots, block_size: int, stream=None) -> None:
+    """k_new, v_new: [T][H_kv][d]; slots: int64[T] on the GPU."""
+    if k_new.dim() != 3 or k_new.shape != v_new.shape:
+        raise InvalidArg(-1, "pkv_reshape_and_cache", "k_new and v_new must be [T][H_kv][d] and equal")
+    T, H, d = k_new.shape
+    torch = _torch()
+    if slots.dtype != torch.int64 or slots.numel() != T:
+        raise InvalidArg(-1, "pkv_reshape_and_cache", "slots must be int64[T]")
+    for t in (v_new, k_cache, v_cache):
+        if t.dtype != k_new.dtype:
+            raise InvalidArg(-1, "pkv_reshape_and_cache", "dtype mismatch")
+    nb = v_cache.shape[0]
+    if tuple(v_cache.shape) != (nb, H, block_size, d) or k_cache.numel() != v_cache.numel():
+        raise InvalidArg(-1, "pkv_reshape_and_cache", "cache shape does not match k_new / block_size")
+    check(lib().pkv_reshape_and_cache(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
+                                      _dev(v_cache, "v_cache"), _dev(slots, "slots"), T, H, d, block_size, nb,
+                                      _dtype_code(k_new), _stream(stream)), "pkv_reshape_and_cache")
+
+
+def pkv_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """pairs: int32[n][2] (src, dst) on the GPU."""
+    torch = _torch()
+    if pairs.dtype != torch.int32 or (pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2)):
+        raise InvalidArg(-1, "pkv_copy_blocks", "pairs must be int32[n][2]")
+    n = pairs.shape[0] if pairs.numel() else 0
+    if n == 0:
+        return
+    nb = v_cache.shape[0]
+    block_bytes = v_cache[0].numel() * v_cache.element_size()
+    check(lib().pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(pairs, "pairs"), n, nb,
+                                block_bytes, _stream(stream)), "pkv_copy_blocks")
+
+
+def pkv_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size, max_context_len,
+                                  partition_size) -> int:
+    return int(lib().pkv_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size, max_context_len,
+                                                   partition_size))
+
+
+def _attention(fn: str, out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int, scale: float,
+               partition_size: int = 0, workspace=None, stream=None) -> None:
+    torch = _torch()
+    S, Hq, d = q.shape
+    nb, Hkv, B, d2 = v_cache.shape
+    if d2 != d or out.shape != q.shape or out.dtype != torch.float32:
+        raise InvalidArg(-1, fn, "shape mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise InvalidArg(-1, fn, "tables and lengths must be int32")
+    if block_tables.shape[0] != S or context_lens.numel() != S or q.dtype != k_cache.dtype:
+        raise InvalidArg(-1, fn, "shape or dtype mismatch")
+    max_blocks = block_tables.shape[1]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    check(getattr(lib(), fn)(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                             _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq, Hkv, d,
+                             B, nb, max_blocks, int(max_context_len), float(scale), int(partition_size), ws_ptr,
+                             ws_bytes, _dtype_code(q), _stream(stream)), fn)
+
+
+def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                               scale: float, partition_size: int = 0, workspace=None, stream=None) -> None:
+    """out: fp32 [S][H_q][d]; q: [S][H_q][d] (cache dtype); block_tables int32 [S][max_blocks];
+    context_lens int32 [S]; workspace: uint8 tensor of >= pkv_attention_workspace_bytes(...) bytes."""
+    _attention("pkv_paged_attention_decode", out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+               scale, partition_size, workspace, stream)
+
+
+def pkv_paged_attention_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                                   scale: float, partition_size: int = 0, workspace=None, stream=None) -> None:
+    """First stage of pkv_paged_attention_decode (same arguments)."""
+    _attention("pkv_paged_attention_partitions", out, q, k_cache, v_cache, block_tables, context_lens,
+               max_context_len, scale, partition_size, workspace, stream)
+
+
+def pkv_paged_attention_reduce(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                               scale: float, partition_size: int = 0, workspace=None, stream=None) -> None:
+    """Second stage of pkv_paged_attention_decode (same arguments)."""
+    _attention("pkv_paged_attention_reduce", out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+               scale, partition_size, workspace, stream)

@@ -16,3 +16,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="session")
+def libpkv():
+    """The built library (built in-tree first if nothing is built yet)."""
+    from paged_kv_cache_physical_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from paged_kv_cache_physical_amd import build
+        build.build()
+    return _lib.lib()

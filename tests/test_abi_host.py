@@ -1,0 +1,199 @@
+"""The C-ABI library loads without a GPU, exports every function pkv.h declares,
+and its host pool matches the oracle's pool model bit for bit (slots, copy pairs,
+tables, refcounts, free-queue order, counters)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_physical_amd as pk
+import workloads as wl
+from oracle import allocator as al
+from oracle import run as orun
+from paged_kv_cache_physical_amd import _lib
+
+
+def test_exports_every_declared_symbol(libpkv):
+    syms = _lib.header_symbols()
+    assert len(syms) >= 18
+    missing = [s for s in syms if not hasattr(libpkv, s)]
+    assert missing == []
+    assert pk.pkv_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert libpkv.pkv_status_string(code)
+
+
+def same_state(cpool: pk.Pool, opool: al.BlockPool):
+    assert list(cpool.free_list()) == opool.free_list()
+    assert [cpool.refcount(b) for b in range(opool.num_blocks)] == opool.refcount
+    st = cpool.stats()
+    assert st == {**opool.stats()}
+    for sid, s in opool.seqs.items():
+        n, nb = cpool.info(sid)
+        assert (n, nb) == (s.length, len(s.table))
+    if opool.seqs:
+        ids = sorted(opool.seqs)
+        mb = max(1, max(len(s.table) for s in opool.seqs.values()))
+        ct, cl = cpool.block_tables(ids, mb)
+        ot, ol = opool.block_tables(ids, mb)
+        assert np.array_equal(ct, ot) and np.array_equal(cl, ol)
+    cpool.validate()
+
+
+def test_worked_example(libpkv):
+    for B, blocks in ((16, 62), (32, 32)):
+        c = pk.Pool(128, B)
+        ids = [c.create() for _ in range(5)]
+        c.append(ids, [37, 91, 128, 201, 511])
+        st = c.stats()
+        assert st["logical_tokens"] == 968 and st["used_blocks"] == blocks and st["allocated_slots"] == blocks * B
+
+
+def test_random_operations_match_oracle(libpkv):
+    rng = np.random.default_rng(2024)
+    for trial in range(30):
+        nb = int(rng.integers(4, 60))
+        B = int(rng.choice([1, 2, 4, 16, 32]))
+        order = rng.permutation(nb)
+        c, o = pk.Pool(nb, B, order), al.BlockPool(nb, B, order)
+        live = []
+        for _ in range(80):
+            op = int(rng.integers(0, 5))
+            if op == 0 or not live:
+                a, b = c.create(), o.create()
+                assert a == b
+                live.append(a)
+            elif op == 1:
+                p = int(rng.choice(live))
+                a, b = c.fork(p), o.fork(p)
+                assert a == b
+                live.append(a)
+            elif op == 2:
+                sid = int(rng.choice(live))
+                c.free_seq(sid)
+                o.free_seq(sid)
+                live.remove(sid)
+            else:
+                k = int(rng.integers(1, len(live) + 1))
+                seqs = [int(x) for x in rng.choice(live, size=k, replace=False)]
+                counts = [int(x) for x in rng.integers(0, 3 * B + 2, size=k)]
+                try:
+                    so, po = o.append(seqs, counts)
+                except al.OutOfBlocks:
+                    with pytest.raises(pk.OutOfBlocks):
+                        c.append(seqs, counts)
+                else:
+                    sc, pc = c.append(seqs, counts)
+                    assert np.array_equal(sc, so)
+                    assert np.array_equal(pc, po)
+            same_state(c, o)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "llama7b_bf16", "gqa_bf16_b16", "gqa_bf16_b32", "beam_cow_bf16",
+                                  "long_bf16"])
+def test_workload_scripts_match_oracle(libpkv, name):
+    w = wl.named(name, seed=0)
+    rp = orun.replay(w, with_cache=False)
+    c = pk.Pool(w.num_blocks, w.spec.block_size, w.free_order)
+    k = 0
+    for op in w.script():
+        if isinstance(op, wl.Create):
+            for _ in range(op.count):
+                c.create()
+        elif isinstance(op, wl.Fork):
+            c.fork(op.parent)
+        else:
+            slots, pairs = c.append(op.seqs, op.counts)
+            assert np.array_equal(slots, rp.slots[k]) and np.array_equal(pairs, rp.pairs[k])
+            k += 1
+    same_state(c, rp.pool)
+
+
+def test_errors_leave_pool_unchanged(libpkv):
+    c = pk.Pool(5, 4)
+    a, b = c.create(), c.create()
+    c.append([a, b], [6, 3])
+    f = c.fork(a)
+    before = (list(c.free_list()), [c.refcount(i) for i in range(5)], c.block_tables([a, b, f], 4))
+    with pytest.raises(pk.OutOfBlocks):
+        c.append([f, b, a], [3, 2, 3])
+    with pytest.raises(pk.InvalidArg):
+        c.append([a, a], [1, 1])
+    with pytest.raises(pk.InvalidArg):
+        c.append([a], [-1])
+    with pytest.raises(pk.NoSuchSeq):
+        c.append([a, 99], [1, 1])
+    with pytest.raises(pk.NoSuchSeq):
+        c.free_seq(99)
+    with pytest.raises(pk.NoSuchSeq):
+        c.fork(99)
+    with pytest.raises(pk.InvalidArg):
+        c.block_tables([a], 1)
+    after = (list(c.free_list()), [c.refcount(i) for i in range(5)], c.block_tables([a, b, f], 4))
+    assert before[0] == after[0] and before[1] == after[1]
+    assert all(np.array_equal(x, y) for x, y in zip(before[2], after[2]))
+    c.validate()
+    c.free_seq(a)
+    with pytest.raises(pk.NoSuchSeq):
+        c.free_seq(a)  # double free
+    assert c.refcount(-1) == -1 and c.refcount(5) == -1
+
+
+def test_pool_create_rejects_bad_orders(libpkv):
+    with pytest.raises(pk.InvalidArg):
+        pk.Pool(3, 4, [0, 0, 1])
+    with pytest.raises(pk.InvalidArg):
+        pk.Pool(3, 4, [0, 1, 3])
+    with pytest.raises(pk.InvalidArg):
+        pk.Pool(0, 4)
+    with pytest.raises(pk.InvalidArg):
+        pk.Pool(4, 0)
+
+
+def test_cow_capacity_error_reports_need(libpkv):
+    L = libpkv
+    c = pk.Pool(8, 4)
+    p = c.create()
+    c.append([p], [2])
+    kids = [c.fork(p) for _ in range(2)]
+    seqs = np.array(kids, np.int32)
+    counts = np.ones(2, np.int32)
+    slots = np.empty(2, np.int64)
+    n = ctypes.c_int32()
+    st = L.pkv_append_tokens(c.handle, seqs.ctypes.data_as(ctypes.c_void_p), counts.ctypes.data_as(ctypes.c_void_p),
+                             2, slots.ctypes.data_as(ctypes.c_void_p), 2, None, 0, ctypes.byref(n))
+    assert st == _lib.PKV_ERR_INVALID_ARG and n.value == 2
+    c.validate()
+
+
+def test_workspace_size_and_device_arg_checks(libpkv):
+    # sizes are host arithmetic: 0 when one partition holds every sequence
+    assert pk.pkv_attention_workspace_bytes(8, 32, 128, 16, 32768, 0) == 0
+    assert pk.pkv_attention_workspace_bytes(8, 32, 128, 16, 512, 512) == 0
+    nbytes = pk.pkv_attention_workspace_bytes(8, 32, 128, 16, 32768, 512)
+    rows = 8 * 32 * 64
+    assert nbytes >= rows * (128 + 2) * 4
+    # argument errors are returned before anything touches a GPU
+    L = libpkv
+    vp = ctypes.c_void_p
+    assert L.pkv_paged_attention_decode(None, None, None, None, None, None, 1, 6, 4, 128, 16, 10, 4, 64, 1.0, 0,
+                                        None, 0, 1, None) == _lib.PKV_ERR_INVALID_ARG  # 6 % 4 != 0
+    assert L.pkv_paged_attention_decode(None, None, None, None, None, None, 1, 48, 4, 128, 16, 10, 4, 64, 1.0, 0,
+                                        None, 0, 1, None) == _lib.PKV_ERR_UNSUPPORTED  # G = 12
+    assert L.pkv_paged_attention_decode(None, None, None, None, None, None, 1, 8, 8, 96, 16, 10, 4, 64, 1.0, 0,
+                                        None, 0, 1, None) == _lib.PKV_ERR_UNSUPPORTED  # d = 96
+    assert L.pkv_paged_attention_decode(None, None, None, None, None, None, 1, 8, 8, 128, 16, 10, 4, 64, 1.0, 24,
+                                        None, 0, 1, None) == _lib.PKV_ERR_INVALID_ARG  # P % B != 0
+    assert L.pkv_paged_attention_decode(None, None, None, None, None, None, 1, 8, 8, 128, 16, 10, 4, 64, 1.0, 0,
+                                        None, 0, 7, None) == _lib.PKV_ERR_UNSUPPORTED  # dtype
+    assert L.pkv_paged_attention_decode(None, None, None, None, None, None, 0, 8, 8, 128, 16, 10, 4, 64, 1.0, 0,
+                                        None, 0, 1, None) == _lib.PKV_OK  # empty batch: no-op
+    assert L.pkv_paged_attention_decode(None, None, None, None, None, None, 2, 8, 8, 128, 16, 10, 4, 64, 1.0, 0,
+                                        None, 0, 1, None) == _lib.PKV_ERR_INVALID_ARG  # NULL buffers
+    assert L.pkv_reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 10, 1, None) == _lib.PKV_OK
+    assert L.pkv_reshape_and_cache(None, None, None, None, None, 3, 8, 128, 16, 10, 1, None) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_reshape_and_cache(None, None, None, None, None, 3, 8, 128, 24, 10, 1, None) == _lib.PKV_ERR_UNSUPPORTED
+    assert L.pkv_copy_blocks(None, None, None, 0, 10, 4096, None) == _lib.PKV_OK
+    assert L.pkv_copy_blocks(None, None, None, 2, 10, 4096, None) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_copy_blocks(vp(16), vp(16), vp(16), 2, 10, 4100, None) == _lib.PKV_ERR_INVALID_ARG

@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path (through the C-ABI) against the float64 oracle.
+
+Bars: block tables, slots and cache bytes bit-exact; fp32 caches max abs error
+<= 1e-5; bf16 caches max abs <= 1e-2 and relative L2 <= 2e-3.  Because a single
+dropped token can hide under the bf16 bar, every case also meets a tighter
+bound derived from fp32 accumulation (relative L2 <= 1e-4).
+"""
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import attention as oa
+from oracle import cache as oc
+from oracle import run as orun
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(libpkv):
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU is required for the gpu-marked tests")
+    yield
+    torch.cuda.synchronize()
+
+
+def runner():
+    from paged_kv_cache_physical_amd.runner import GpuBatch
+    return GpuBatch
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def host_bits(t):
+    """Device cache tensor -> host NumPy array with the oracle's storage dtype."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def same_bits(a, b):
+    """Bit-for-bit equality (NaN poison included)."""
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    return a.shape == b.shape and a.dtype == b.dtype and a.tobytes() == b.tobytes()
+
+
+def check_close(out, ref, kv_dtype, what=""):
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(out - ref)))
+    rl2 = float(np.linalg.norm(out - ref) / np.linalg.norm(ref))
+    say(f"  {what}: max_abs={err:.3e} rel_l2={rl2:.3e}")
+    if kv_dtype == "f32":
+        assert err <= 1e-5, (what, err)
+    else:
+        assert err <= 1e-2 and rl2 <= 2e-3, (what, err, rl2)
+    assert rl2 <= 1e-4, (what, rl2)
+
+
+def oracle_rows(w, seqs):
+    s = w.spec
+    ref = {}
+    for i in seqs:
+        k, v = w.token_kv(i)
+        ref[i] = oa.attention_contiguous(oc.to_f64(w.q[i], s.kv_dtype), oc.to_f64(k, s.kv_dtype),
+                                         oc.to_f64(v, s.kv_dtype), w.scale)
+    return ref
+
+
+def full_parity(w, partitions):
+    GpuBatch = runner()
+    s = w.spec
+    say(f"case {s.name}: S={w.num_seqs} Hq={s.num_q_heads} Hkv={s.num_kv_heads} d={s.head_dim} B={s.block_size} "
+        f"{s.kv_dtype} max_n={w.max_context_len}")
+    gb = GpuBatch(w)
+    rp = orun.replay(w)
+    assert np.array_equal(gb.tables_host[:, :rp.tables.shape[1]], rp.tables)
+    assert np.all(gb.tables_host[:, rp.tables.shape[1]:] == -1)
+    assert np.array_equal(gb.lens_host, rp.context_lens)
+    for a, b in zip(gb.slots, rp.slots):
+        assert np.array_equal(a, b)
+    assert same_bits(host_bits(gb.k_cache), rp.k_cache)
+    assert same_bits(host_bits(gb.v_cache), rp.v_cache)
+    ref = oa.paged_attention(w.q, rp.k_cache, rp.v_cache, rp.tables, rp.context_lens, w.scale, s.kv_dtype)
+    outs = {}
+    for P in partitions:
+        out = gb.attention(P).cpu().numpy()
+        torch.cuda.synchronize()
+        check_close(out, ref, s.kv_dtype, f"P={P}")
+        outs[P] = out
+    return gb, outs
+
+
+@pytest.mark.parametrize("P", [0, 16, 64, 512])
+def test_tiny_f32(P):
+    full_parity(wl.named("tiny_f32", seed=0), [P])
+
+
+GRID = [(dt, d, G, B) for dt in ("f32", "bf16") for d in (64, 128) for G in (1, 2, 4, 8) for B in (16, 32)]
+
+
+@pytest.mark.parametrize("dt,d,G,B", GRID)
+def test_small_grid(dt, d, G, B):
+    w = wl.small_decode(7, (1, 300), 2 * G, 2, d, B, dt, seed=G * 100 + d + B)
+    full_parity(w, [0, 2 * B, 160 if B == 16 else 192])
+
+
+@pytest.mark.parametrize("G,lens", [(8, (513, 2000)), (4, (1025, 1500)), (1, (4097, 5000)), (2, (1, 2100))])
+def test_multi_chunk_unsplit(G, lens):
+    # one partition longer than a chunk (4096 / G tokens): the chunked online-softmax kernel
+    w = wl.small_decode(3, lens, 2 * G, 2, 128, 16, "bf16", seed=7 + G)
+    full_parity(w, [0, 4096 // G + 16 * 3])
+
+
+def test_ragged_boundaries():
+    # lengths at block, partition and chunk edges
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025]
+    w = wl.small_decode(len(lens), (1, 1), 16, 2, 128, 16, "bf16", seed=3, lens=lens)
+    full_parity(w, [0, 64, 512])
+
+
+@pytest.mark.parametrize("name,nsample", [("llama7b_bf16", 12), ("gqa_bf16_b16", 12), ("gqa_bf16_b32", 12),
+                                          ("beam_cow_bf16", 16), ("long_bf16", 3)])
+def test_named_full_size(name, nsample):
+    GpuBatch = runner()
+    w = wl.named(name, seed=0)
+    s = w.spec
+    say(f"case {name}: S={w.num_seqs} tokens={w.total_tokens} pool={w.num_blocks}")
+    gb = GpuBatch(w)
+    rp = orun.replay(w, with_cache=False)
+    assert np.array_equal(gb.tables_host[:, :rp.tables.shape[1]], rp.tables)
+    assert np.array_equal(gb.lens_host, rp.context_lens)
+    rng = np.random.default_rng(1)
+    lens = w.context_lens
+    picks = set(rng.choice(w.num_seqs, size=min(nsample, w.num_seqs), replace=False).tolist())
+    picks |= {int(np.argmax(lens)), int(np.argmin(lens))}
+    picks = sorted(picks)
+    # cache bytes of the sampled sequences, read back through their tables
+    kc, vc = host_bits(gb.k_cache), host_bits(gb.v_cache)
+    for i in picks:
+        kg, vg = oc.gather(kc, vc, rp.tables[i], int(lens[i]))
+        kt, vt = w.token_kv(i)
+        assert same_bits(kg, kt) and same_bits(vg, vt), f"cache bytes of sequence {i}"
+    del kc, vc
+    ref = oracle_rows(w, picks)
+    for P in sorted({s.partition_size, 0}):
+        out = gb.attention(P).cpu().numpy()
+        check_close(np.stack([out[i] for i in picks]), np.stack([ref[i] for i in picks]), s.kv_dtype,
+                    f"{name} P={P}")
+    # the decode step (K/V write + attention) is idempotent
+    out1 = gb.step().cpu().numpy()
+    out2 = gb.step().cpu().numpy()
+    assert np.array_equal(out1, out2)
+
+
+def test_placement_invariance_bitwise():
+    GpuBatch = runner()
+    w1 = wl.small_decode(9, (1, 700), 16, 2, 128, 16, "bf16", seed=5)
+    w2 = wl.small_decode(9, (1, 700), 16, 2, 128, 16, "bf16", seed=5)
+    w2.free_order = np.random.default_rng(77).permutation(w2.num_blocks).astype(np.int32)
+    g1, g2 = GpuBatch(w1), GpuBatch(w2)
+    assert not np.array_equal(g1.tables_host, g2.tables_host)
+    for P in (0, 64):
+        a = g1.attention(P).cpu().numpy()
+        b = g2.attention(P).cpu().numpy()
+        assert np.array_equal(a, b), P
+
+
+def test_shared_prefix_equals_private_bitwise():
+    import paged_kv_cache_physical_amd as pk
+    GpuBatch = runner()
+    w = wl.named("beam_cow_bf16", seed=2, prompts=4, prefix_len=200, tail_range=(1, 40), num_blocks=256)
+    s = w.spec
+    shared = GpuBatch(w)
+    rp = orun.replay(w)
+    # copy-on-write and writes: the whole pool matches the oracle's bytes
+    assert same_bits(host_bits(shared.k_cache), rp.k_cache)
+    assert same_bits(host_bits(shared.v_cache), rp.v_cache)
+    assert sum(len(p) for p in shared.pairs) == s.prompts * (s.beams - 1)
+    # private copies of every beam in a second pool
+    pool = pk.Pool(w.num_blocks * 2, s.block_size)
+    kc, vc = pk.empty_caches(w.num_blocks * 2, s.num_kv_heads, s.block_size, s.head_dim, "bf16")
+    from paged_kv_cache_physical_amd.runner import _to_device
+    ids = []
+    for i in range(w.num_seqs):
+        sid = pool.create()
+        ids.append(sid)
+        slots, _ = pool.append([sid], [int(w.context_lens[i])])
+        k, v = w.token_kv(i)
+        pk.pkv_reshape_and_cache(_to_device(k, "bf16", "cuda"), _to_device(v, "bf16", "cuda"), kc, vc,
+                                 torch.from_numpy(slots).cuda(), s.block_size)
+    mb = shared.max_blocks
+    tables, lens = pool.block_tables(ids, mb)
+    out_p = torch.empty_like(shared.out)
+    for P in (0, 64):
+        pk.pkv_paged_attention_decode(out_p, shared.q, kc, vc, torch.from_numpy(tables).cuda(),
+                                      torch.from_numpy(lens).cuda(), shared.max_context_len, float(w.scale), P,
+                                      shared.workspace(P))
+        a = shared.attention(P).cpu().numpy()
+        assert np.array_equal(a, out_p.cpu().numpy()), P
+        ref = oa.paged_attention(w.q, rp.k_cache, rp.v_cache, rp.tables, rp.context_lens, w.scale, "bf16")
+        check_close(a, ref, "bf16", f"beam P={P}")
+
+
+def test_split_matches_unsplit():
+    GpuBatch = runner()
+    w = wl.small_decode(6, (200, 1500), 32, 8, 128, 16, "bf16", seed=9)
+    gb = GpuBatch(w)
+    a = gb.attention(0).cpu().numpy()
+    for P in (16, 48, 512):
+        b = gb.attention(P).cpu().numpy()
+        assert float(np.linalg.norm(a - b) / np.linalg.norm(a)) <= 1e-5
+
+
+def test_edge_lengths_and_bad_inputs():
+    GpuBatch = runner()
+    w = wl.small_decode(5, (40, 300), 8, 2, 128, 16, "bf16", seed=4)
+    gb = GpuBatch(w)
+    refs = {P: gb.attention(P).cpu().numpy().copy() for P in (0, 16, 64)}
+    lens = gb.context_lens.clone()
+    tables = gb.block_tables.clone()
+    # a zero-length sequence gives zeros; lengths past max_context_len or negative give NaN
+    gb.context_lens.copy_(torch.tensor([0, -3, gb.max_context_len + 1, int(lens[3]), int(lens[4])],
+                                       dtype=torch.int32, device="cuda"))
+    for P in (0, 64):
+        out = gb.attention(P).cpu().numpy()
+        assert np.all(out[0] == 0)
+        assert np.all(np.isnan(out[1])) and np.all(np.isnan(out[2]))
+        np.testing.assert_array_equal(out[3:], refs[P][3:])
+    gb.context_lens.copy_(lens)
+    # an out-of-range block id poisons only its own sequence
+    bad = tables.clone()
+    bad[2, 1] = w.num_blocks
+    gb.block_tables.copy_(bad)
+    for P in (0, 16):
+        out = gb.attention(P).cpu().numpy()
+        assert np.all(np.isnan(out[2]))
+        np.testing.assert_array_equal(np.delete(out, 2, axis=0), np.delete(refs[P], 2, axis=0))
+    gb.block_tables.copy_(tables)
+    np.testing.assert_array_equal(gb.attention(64).cpu().numpy(), refs[64])
+
+
+def test_reshape_skips_negative_and_out_of_range_slots():
+    import paged_kv_cache_physical_amd as pk
+    nb, H, B, d = 4, 2, 16, 128
+    kc, vc = pk.empty_caches(nb, H, B, d, "bf16")
+    kcn, vcn = oc.empty_caches(nb, H, B, d, "bf16")
+    rng = np.random.default_rng(0)
+    k = wl.draw_values(rng, (4, H, d), "bf16")
+    v = wl.draw_values(rng, (4, H, d), "bf16")
+    slots = np.array([5, -1, nb * B, 63], np.int64)
+    from paged_kv_cache_physical_amd.runner import _to_device
+    pk.pkv_reshape_and_cache(_to_device(k, "bf16", "cuda"), _to_device(v, "bf16", "cuda"), kc, vc,
+                             torch.from_numpy(slots).cuda(), B)
+    keep = np.array([0, 3])
+    oc.scatter(kcn, vcn, k[keep], v[keep], slots[keep])
+    assert same_bits(host_bits(kc), kcn)
+    assert same_bits(host_bits(vc), vcn)
+
+
+def test_copy_blocks_f32_exact():
+    import paged_kv_cache_physical_amd as pk
+    nb, H, B, d = 6, 4, 32, 64
+    kc, vc = pk.empty_caches(nb, H, B, d, "f32")
+    kc.copy_(torch.randn_like(kc))
+    vc.copy_(torch.randn_like(vc))
+    k0, v0 = kc.cpu().numpy(), vc.cpu().numpy()
+    pairs = np.array([[1, 4], [3, 0], [2, 9]], np.int32)  # the last pair is out of range: skipped
+    pk.pkv_copy_blocks(kc, vc, torch.from_numpy(pairs).cuda())
+    kn, vn = k0.copy(), v0.copy()
+    oc.copy_blocks(kn, vn, pairs[:2])
+    assert same_bits(kc.cpu().numpy(), kn) and same_bits(vc.cpu().numpy(), vn)
+
+
+def test_empty_batch_is_noop():
+    import paged_kv_cache_physical_amd as pk
+    kc, vc = pk.empty_caches(2, 1, 16, 64, "f32")
+    q = torch.empty((0, 1, 64), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    pk.pkv_paged_attention_decode(out, q, kc, vc, torch.empty((0, 1), dtype=torch.int32, device="cuda"),
+                                  torch.empty(0, dtype=torch.int32, device="cuda"), 0, 0.125, 0)
+    torch.cuda.synchronize()

@@ -37,6 +37,7 @@ STREAM_Q = 3
 STREAM_KV = 4
 STREAM_TAIL_LENS = 5
 STREAM_TAIL_KV = 6
+STREAM_NEW_KV = 7  # the decode step's new token of each sequence
 
 # Bit patterns used to poison never-written cache slots.  A read that is not
 # masked turns the attention output into NaN.
@@ -210,14 +211,22 @@ class Workload:
         return k, v
 
     def token_kv(self, seq: int) -> Tuple[np.ndarray, np.ndarray]:
-        """Logical (contiguous, position-ordered) K and V of sequence ``seq``: ``[n][H_kv][d]``."""
+        """Logical (contiguous, position-ordered) K and V of sequence ``seq``: ``[n][H_kv][d]``.
+
+        Positions before the last come from the sequence's context stream (the
+        shared prompt stream plus the beam's own tail stream for beam search);
+        the last position is the decode step's new token, drawn from its own
+        stream.
+        """
         s = self.spec
+        kn, vn = self._token_block((STREAM_NEW_KV, seq), 1)
         if s.kind == "decode":
-            return self._token_block((STREAM_KV, seq), int(self.context_lens[seq]))
+            kc, vc = self._token_block((STREAM_KV, seq), int(self.context_lens[seq]) - 1)
+            return np.concatenate([kc, kn]), np.concatenate([vc, vn])
         p, b = divmod(seq, s.beams)
         kp, vp = self._token_block((STREAM_KV, p), s.prefix_len)
-        kt, vt = self._token_block((STREAM_TAIL_KV, p, b), int(self.tail_lens[p, b]))
-        return np.concatenate([kp, kt]), np.concatenate([vp, vt])
+        kt, vt = self._token_block((STREAM_TAIL_KV, p, b), int(self.tail_lens[p, b]) - 1)
+        return np.concatenate([kp, kt, kn]), np.concatenate([vp, vt, vn])
 
     def _gather_tokens(self, pieces: Sequence[Tuple[Tuple[int, ...], int, int, int]]) -> Tuple[np.ndarray, np.ndarray]:
         """Concatenate token ranges ``(key, n_total, lo, hi)`` of several streams, drawn in parallel."""
@@ -237,7 +246,7 @@ class Workload:
             v_out[offs[i]:offs[i + 1]] = v[lo:hi]
 
         threads = min(16, os.cpu_count() or 1, max(1, len(pieces)))
-        if threads > 1 and total > 100_000:
+        if threads > 1 and total * s.num_kv_heads * s.head_dim > 1_000_000:
             with ThreadPoolExecutor(threads) as ex:
                 list(ex.map(work, range(len(pieces))))
         else:
@@ -255,8 +264,8 @@ class Workload:
             lens = self.context_lens.astype(np.int64)
             seqs = np.arange(S, dtype=np.int32)
             ops.append(Create(S))
-            pre = [((STREAM_KV, i), int(lens[i]), 0, int(lens[i]) - 1) for i in range(S)]
-            dec = [((STREAM_KV, i), int(lens[i]), int(lens[i]) - 1, int(lens[i])) for i in range(S)]
+            pre = [((STREAM_KV, i), int(lens[i]) - 1, 0, int(lens[i]) - 1) for i in range(S)]
+            dec = [((STREAM_NEW_KV, i), 1, 0, 1) for i in range(S)]
             ops.append(Append(seqs, (lens - 1).astype(np.int32), lambda pre=pre: self._gather_tokens(pre)))
             ops.append(Append(seqs, np.ones(S, np.int32), lambda dec=dec: self._gather_tokens(dec), decode=True))
             return ops
@@ -275,9 +284,8 @@ class Workload:
         pre, dec = [], []
         for i in range(S):
             p, b = divmod(i, s.beams)
-            key = (STREAM_TAIL_KV, p, b)
-            pre.append((key, int(tails[i]), 0, int(tails[i]) - 1))
-            dec.append((key, int(tails[i]), int(tails[i]) - 1, int(tails[i])))
+            pre.append(((STREAM_TAIL_KV, p, b), int(tails[i]) - 1, 0, int(tails[i]) - 1))
+            dec.append(((STREAM_NEW_KV, i), 1, 0, 1))
         ops.append(Append(seqs, (tails - 1).astype(np.int32), lambda pre=pre: self._gather_tokens(pre)))
         ops.append(Append(seqs, np.ones(S, np.int32), lambda dec=dec: self._gather_tokens(dec), decode=True))
         return ops
