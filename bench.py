@@ -31,7 +31,8 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 METRIC = "decode-attention KV GB/s (% of HBM peak) and seq-steps/sec at 1 MI355X"
 HEADLINE = "llama7b_bf16"
 EXTRA = ["gqa_bf16_b16", "gqa_bf16_b32", "long_bf16", "beam_cow_bf16"]
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_physical_amd", "csrc", "kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_physical_amd", "csrc", f)
+               for f in ("attention.hip", "device_common.h")]
 
 
 def log(*a):
@@ -39,8 +40,12 @@ def log(*a):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernel's sources (ties profile-derived numbers to the code they measured)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def describe(w) -> dict:
@@ -117,16 +122,18 @@ def measure(w, steps, warmup, stream):
 
 
 def hbm_read_ceiling(stream):
-    """Practical read bandwidth: torch's sum over a 2 GiB fp32 tensor (context only)."""
+    """Practical HBM read rate of a plain streaming kernel over 4 GiB (context for the roofline)."""
     import torch
-    x = torch.ones(512 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    from paged_kv_cache_physical_amd import pkv_hbm_read_probe
+    x = torch.ones(4 * 1024 ** 3 // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     with torch.cuda.stream(stream):
         for _ in range(3):
-            x.sum()
-        ms = time_launches(lambda: x.sum(), 20, stream)[1]
+            pkv_hbm_read_probe(x, sink, stream)
+        ms = time_launches(lambda: pkv_hbm_read_probe(x, sink, stream), 20, stream)[1]
     del x
     torch.cuda.empty_cache()
-    return 2 ** 31 / (ms * 1e-3) / 1e9
+    return 4 * 1024 ** 3 / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(w, budget_s=12.0):

@@ -30,10 +30,11 @@
  *
  * Physical cache layout (one key cache and one value cache per layer):
  *   value cache  V[num_blocks][H_kv][B][d]
- *   key cache    K[num_blocks][H_kv][d / X][B][X],   X = 64 / bytes_per_scalar
+ *   key cache    K[num_blocks][H_kv][d / X][B][X],   X = 128 / bytes_per_scalar
  * Each (block, KV head) owns one contiguous tile of B * d scalars.  In a key
- * tile, a token's d values are split into 64-byte pieces and piece j of all B
- * tokens is stored together.  Token position t of a sequence whose table is
+ * tile, a token's d values are split into 128-byte pieces and piece j of all B
+ * tokens is stored together (for d * bytes_per_scalar = 128 the key tile is
+ * plain rows, like the value tile).  Token position t of a sequence whose table is
  * bt lives in block bt[t / B] at offset t % B; its slot is
  * bt[t / B] * B + t % B.  Scalars are fp32 or bf16 (PKV_F32 / PKV_BF16).
  *
@@ -257,6 +258,13 @@ pkv_status pkv_paged_attention_reduce(float* out, const void* q, const void* k_c
                                       int32_t max_context_len, float scale, int32_t partition_size,
                                       void* workspace, size_t workspace_bytes, int32_t kv_dtype,
                                       hipStream_t stream);
+
+/* Calibration: read `bytes` (a multiple of 16) of device memory once with a
+ * plain streaming kernel (16-byte loads, 8 in flight per thread) and discard
+ * the data.  Used to measure the practical HBM read ceiling next to the
+ * attention kernel's KV read rate.  sink: device uint32[1], never written in
+ * practice.  Errors: INVALID_ARG, HIP. */
+pkv_status pkv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

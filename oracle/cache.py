@@ -8,10 +8,10 @@ layout open.  The layout used by the library's interface (and restated here
 from that interface's definition, not from its code) is, per cache:
 
   value cache  V[num_blocks][H_kv][B][d]                 (row-major)
-  key cache    K[num_blocks][H_kv][d / X][B][X],  X = 64 / bytes_per_scalar
+  key cache    K[num_blocks][H_kv][d / X][B][X],  X = 128 / bytes_per_scalar
 
 i.e. each (block, KV head) owns one contiguous tile; in the key tile a token's
-d values are stored as d / X pieces of 64 bytes, piece j of every token of the
+d values are stored as d / X pieces of 128 bytes, piece j of every token of the
 block lying together.  Token position t of a sequence with table ``bt`` is in
 block ``bt[t // B]`` at offset ``t % B``; slot = block * B + offset.
 
@@ -31,8 +31,8 @@ _ITEM = {"f32": 4, "bf16": 2}
 
 
 def key_piece(kv_dtype: str) -> int:
-    """X: scalars per 64-byte piece of a key row."""
-    return 64 // _ITEM[kv_dtype]
+    """X: scalars per 128-byte piece of a key row."""
+    return 128 // _ITEM[kv_dtype]
 
 
 def empty_caches(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, kv_dtype: str
@@ -40,7 +40,7 @@ def empty_caches(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: 
     """Key and value caches with every slot set to the NaN poison pattern."""
     X = key_piece(kv_dtype)
     if head_dim % X:
-        raise ValueError("head_dim * bytes_per_scalar must be a multiple of 64")
+        raise ValueError("head_dim * bytes_per_scalar must be a multiple of 128")
     k = np.empty((num_blocks, num_kv_heads, head_dim // X, block_size, X), dtype=_STORE[kv_dtype])
     v = np.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=_STORE[kv_dtype])
     pattern = POISON[kv_dtype]

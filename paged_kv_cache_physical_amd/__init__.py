@@ -8,7 +8,7 @@ streams, nothing else).  The library must have been built first
 (``python -m paged_kv_cache_physical_amd.build``); otherwise every call raises.
 
 Cache tensors use the interface's physical layout:
-  key cache    [num_blocks][H_kv][d / X][B][X],  X = 64 / bytes_per_scalar
+  key cache    [num_blocks][H_kv][d / X][B][X],  X = 128 / bytes_per_scalar
   value cache  [num_blocks][H_kv][B][d]
 """
 
@@ -26,7 +26,7 @@ __all__ = [
     "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_create", "pkv_seq_fork", "pkv_seq_free", "pkv_append_tokens",
     "pkv_block_tables", "pkv_seq_info", "pkv_pool_stats", "pkv_block_refcount", "pkv_pool_free_list",
     "pkv_pool_validate", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_attention_workspace_bytes",
-    "pkv_paged_attention_decode", "pkv_paged_attention_partitions", "pkv_paged_attention_reduce", "pkv_abi_version", "Pool", "cache_shapes", "empty_caches", "PkvError",
+    "pkv_paged_attention_decode", "pkv_paged_attention_partitions", "pkv_paged_attention_reduce", "pkv_abi_version", "pkv_hbm_read_probe", "Pool", "cache_shapes", "empty_caches", "PkvError",
     "OutOfBlocks", "NoSuchSeq", "InvalidArg",
 ]
 
@@ -209,7 +209,7 @@ def _dev(t, name):
 
 
 def cache_shapes(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, kv_dtype: str):
-    X = 64 // (4 if kv_dtype == "f32" else 2)
+    X = 128 // (4 if kv_dtype == "f32" else 2)
     return ((num_blocks, num_kv_heads, head_dim // X, block_size, X), (num_blocks, num_kv_heads, block_size, head_dim))
 
 
@@ -261,6 +261,13 @@ def pkv_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     block_bytes = v_cache[0].numel() * v_cache.element_size()
     check(lib().pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(pairs, "pairs"), n, nb,
                                 block_bytes, _stream(stream)), "pkv_copy_blocks")
+
+
+def pkv_hbm_read_probe(buf, sink, stream=None) -> None:
+    """Stream-read the whole of `buf` (a GPU tensor); `sink` is an int32/uint32 GPU tensor of >= 1 element."""
+    nbytes = buf.numel() * buf.element_size()
+    check(lib().pkv_hbm_read_probe(_dev(buf, "buf"), nbytes, _dev(sink, "sink"), _stream(stream)),
+          "pkv_hbm_read_probe")
 
 
 def pkv_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size, max_context_len,

@@ -1,0 +1,140 @@
+// Cache writes and copies for gfx950: the slot scatter of new tokens'
+// keys/values (reshape_and_cache), whole-block copies for copy-on-write, and a
+// plain streaming-read probe used to measure the HBM read ceiling.
+
+#include "device_common.h"
+
+namespace pkv {
+namespace {
+
+// One thread moves 16 bytes of K and 16 bytes of V of one (token, head).
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(const char* __restrict__ k_new,
+                                                                const char* __restrict__ v_new,
+                                                                char* __restrict__ k_cache, char* __restrict__ v_cache,
+                                                                const int64_t* __restrict__ slots, int32_t num_tokens,
+                                                                int32_t num_heads, int32_t block_size, int32_t row_bytes,
+                                                                int64_t num_slots) {
+  const int chunks = row_bytes / 16;
+  const int pieces = row_bytes / kKeyPiece;
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_heads * chunks;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int c = static_cast<int>(idx % chunks);
+    const int64_t th = idx / chunks;  // token * H + head
+    const int64_t t = th / num_heads;
+    const int h = static_cast<int>(th % num_heads);
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / block_size;
+    const int off = static_cast<int>(slot % block_size);
+    const uint4 kv = *reinterpret_cast<const uint4*>(k_new + th * row_bytes + c * 16);
+    const uint4 vv = *reinterpret_cast<const uint4*>(v_new + th * row_bytes + c * 16);
+    const int piece = (c * 16) / kKeyPiece;
+    const int within = (c * 16) % kKeyPiece;
+    const int64_t tile = blk * num_heads + h;
+    *reinterpret_cast<uint4*>(k_cache + ((tile * pieces + piece) * block_size + off) * kKeyPiece + within) = kv;
+    *reinterpret_cast<uint4*>(v_cache + (tile * block_size + off) * row_bytes + c * 16) = vv;
+  }
+}
+
+// grid = (pairs, 2 caches, splits): each workgroup copies a slice of one block.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* k_cache, char* v_cache, const int32_t* __restrict__ pairs,
+                                                          int32_t num_blocks, int64_t block_bytes) {
+  const int pair = blockIdx.x;
+  const int32_t src = pairs[2 * pair];
+  const int32_t dst = pairs[2 * pair + 1];
+  if (static_cast<unsigned>(src) >= static_cast<unsigned>(num_blocks) ||
+      static_cast<unsigned>(dst) >= static_cast<unsigned>(num_blocks))
+    return;
+  char* base = blockIdx.y ? v_cache : k_cache;
+  const uint4* s = reinterpret_cast<const uint4*>(base + src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>(base + dst * block_bytes);
+  const int64_t n16 = block_bytes / 16;
+  for (int64_t i = static_cast<int64_t>(blockIdx.z) * blockDim.x + threadIdx.x; i < n16;
+       i += static_cast<int64_t>(gridDim.z) * blockDim.x)
+    d[i] = s[i];
+}
+
+// Plain streaming read: each workgroup owns consecutive 256 KiB chunks and
+// its threads keep 16 non-temporal 16-byte loads in flight; the words are
+// xor-folded and stored only for an impossible value, which keeps the loads
+// live without writing anything.
+constexpr int64_t kProbeChunk16 = 256 * 1024 / 16;
+constexpr int kProbeUnroll = 16;
+
+__global__ __launch_bounds__(256) void hbm_read_probe_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                             uint32_t* __restrict__ sink) {
+  uint32_t x = 0;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kProbeChunk16; base < n16;
+       base += static_cast<int64_t>(gridDim.x) * kProbeChunk16) {
+    const int64_t end = base + kProbeChunk16 < n16 ? base + kProbeChunk16 : n16;
+    int64_t i = base + threadIdx.x;
+    for (; i + (kProbeUnroll - 1) * 256 < end; i += kProbeUnroll * 256) {
+      uint4 v[kProbeUnroll];
+#pragma unroll
+      for (int u = 0; u < kProbeUnroll; ++u) v[u] = load_nt(src + i + u * 256);
+#pragma unroll
+      for (int u = 0; u < kProbeUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < end; i += 256) {
+      const uint4 v = load_nt(src + i);
+      x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  if (x == 0x9e3779b9u && threadIdx.x == 0x3ff) sink[0] = x;  // never taken for blockDim <= 1023
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, int32_t kv_dtype, hipStream_t stream) {
+  const int item = item_size(kv_dtype);
+  if (item == 0) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slots) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_INVALID_ARG;
+  const int row_bytes = head_dim * item;
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (row_bytes / 16);
+  const int64_t want = ceil_div64(total, 256);
+  const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const char*>(k_new),
+                     static_cast<const char*>(v_new), static_cast<char*>(k_cache), static_cast<char*>(v_cache), slots,
+                     num_tokens, num_kv_heads, block_size, row_bytes,
+                     static_cast<int64_t>(num_blocks) * block_size);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs, int32_t num_blocks,
+                           int64_t block_bytes, hipStream_t stream) {
+  if (n_pairs < 0 || num_blocks <= 0 || block_bytes <= 0 || block_bytes % 16) return PKV_ERR_INVALID_ARG;
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !pairs || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
+  const int64_t n16 = block_bytes / 16;
+  const int64_t splits = ceil_div64(n16, 256);
+  const unsigned z = static_cast<unsigned>(splits < 16 ? splits : 16);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n_pairs, 2, z), dim3(256), 0, stream, static_cast<char*>(k_cache),
+                     static_cast<char*>(v_cache), pairs, num_blocks, block_bytes);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes < 0 || bytes % 16 || (bytes > 0 && (!buf || !sink || !aligned16(buf)))) return PKV_ERR_INVALID_ARG;
+  if (bytes == 0) return PKV_OK;
+  const int64_t n16 = bytes / 16;
+  const int64_t chunks = ceil_div64(n16, kProbeChunk16);
+  const unsigned grid = static_cast<unsigned>(chunks < 8192 ? chunks : 8192);
+  hipLaunchKernelGGL(hbm_read_probe_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint4*>(buf), n16,
+                     sink);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

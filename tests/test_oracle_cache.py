@@ -11,11 +11,11 @@ from oracle import cache as oc
 
 @pytest.mark.parametrize("kv_dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64), ("f32", 128)])
 def test_layout_offsets(kv_dtype, d):
-    # Interface definition: V[nb][H][B][d]; K[nb][H][d/X][B][X] with X = 64 bytes / scalar size.
+    # Interface definition: V[nb][H][B][d]; K[nb][H][d/X][B][X] with X = 128 bytes / scalar size.
     nb, H, B = 5, 3, 16
     k, v = oc.empty_caches(nb, H, B, d, kv_dtype)
     item = 4 if kv_dtype == "f32" else 2
-    X = 64 // item
+    X = 128 // item
     rng = np.random.default_rng(0)
     kt = wl.draw_values(rng, (1, H, d), kv_dtype)
     vt = wl.draw_values(rng, (1, H, d), kv_dtype)
