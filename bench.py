@@ -189,6 +189,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-extra", action="store_true", help="skip the other decode batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--partition", type=int, default=None, help="override the workload's partition size")
+    ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated extra workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
@@ -204,15 +206,16 @@ def main():
     _lib.lib()  # fail loudly if the HIP library is not built
     stream = torch.cuda.Stream()  # default priority
 
-    w = wl.named(args.workload, seed=0)
+    over = {} if args.partition is None else {"partition_size": args.partition}
+    w = wl.named(args.workload, seed=0, **over)
     head = measure(w, args.steps, args.warmup, stream)
     log(f"[bench] {w.spec.name}: {json.dumps(head)}")
     extra = {}
     if not args.no_extra:
-        for name in EXTRA:
+        for name in [x for x in args.extra.split(",") if x]:
             if name == args.workload:
                 continue
-            r = measure(wl.named(name, seed=0), 20, 5, stream)
+            r = measure(wl.named(name, seed=0, **over), 20, 5, stream)
             r["pct_hbm_peak_partition_kernel"] = 100 * r["kv_gbps_partition_kernel"] / HBM_PEAK_GBPS
             extra[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
             log(f"[bench] {name}: {json.dumps(extra[name])}")

@@ -2,31 +2,47 @@
 // values read through block tables, split-context partitions combined by a
 // log-sum-exp reduction.
 //
-// Work decomposition.  One workgroup (4 waves) per (sequence, KV head, context
-// partition).  Each wave is an independent flash-decoding worker over the
-// 16-token groups g = wave, wave + 4, ... of every chunk of its partition:
-//   1. block ids of its groups: one vector load, lane k holding group k's id,
-//      read back with readlane (the ids live in registers, not LDS);
-//   2. keys streamed through a register ring (KPF groups in flight): the G
-//      logits of each token (raw dot products) go to the wave's LDS region;
-//      per-head maxima tracked in registers;
-//   3. first value loads issued, maxima reduced across the wave, running state
-//      rescaled (several chunks only), logits turned into probabilities in
-//      place with one fma + exp2 each;
-//   4. values streamed through a ring (VPF groups), p * V accumulated in fp32.
-// The G query heads of a KV head share every key and value load (GQA).  Waves
-// meet once, at the end, to merge their (max, sum, acc) through LDS, and then
-// write the output rows (one partition) or the partition's partials.
+// Unit of work: an item = (sequence, KV head, context partition of at most P
+// tokens).  A workgroup of 4 waves handles an item; wave w takes the 16-token
+// groups g = w, w + 4, ... of the partition.  Per group a wave
+//   - loads the group's 16 key rows (nontemporal 16-byte loads, one register
+//     ring slot per group),
+//   - computes the G logits of each token (raw q.k), writes them to its own LDS
+//     region and tracks per-head maxima, then refills the slot with the group's
+//     values, so the value loads overlap the rest of the QK work;
+// then reduces the maxima across the wave, turns logits into probabilities in
+// place (one fma + exp2 each), and accumulates p * V in fp32 from the ring.
+// The G query heads of a KV head share every key and value load (GQA).  The
+// four waves merge their (max, sum, acc) once, through LDS, and write the
+// output rows (one partition) or the partition's partials.
+//
+// QK runs on the matrix cores (v_mfma_f32_16x16x32_bf16) for bf16 caches with
+// G >= 4, where each 16-token group is a real [16 x d] x [d x G] contraction;
+// on the vector ALUs (v_dot2_f32_bf16 or fp32 fma, 8-lane DPP sums) otherwise.
+// PV always runs on the vector ALUs in fp32: probabilities are never rounded.
+//
+// Two kernels share these building blocks:
+//   paged_decode_persistent  partitions of at most 512 tokens (one ring batch
+//       per wave) and at most 4096 sequences: a grid sized to fill the chip
+//       walks the item list (built per workgroup from an LDS prefix sum of the
+//       partition counts); while a wave accumulates p * V of one item it
+//       refills each consumed ring slot with the keys of its next item, so the
+//       memory pipe stays busy across item boundaries.
+//   paged_decode_items       any partition size: one workgroup per item, the
+//       partition streamed in batches of ring slots with an online rescale.
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;                 // waves per workgroup
-constexpr int kThreads = kWave * kWaves;  // 256
 constexpr int kGroup = 16;                // tokens of one group
-constexpr int kLogitFloats = 4096;        // LDS floats for logits, 1024 per wave
+constexpr int kMaxPersistentSeqs = 4096;  // sequences the persistent kernel's LDS item list holds
 
 struct AttnArgs {
   float* out;
@@ -46,11 +62,12 @@ struct AttnArgs {
   int32_t max_context_len;
   int32_t partition_size;  // tokens, multiple of block_size
   int32_t max_parts;
-  float c;             // |scale| * log2(e) (>= FLT_MIN): logits enter exp2 as fma(s, c, -m)
-  uint32_t q_sign;     // xor mask applied to q's bits: flips its sign when scale < 0
+  float c;          // |scale| * log2(e) (>= FLT_MIN): logits enter exp2 as fma(s, c, -m)
+  uint32_t q_sign;  // xor mask applied to q's bits: flips its sign when scale < 0
 };
 
-// Number of partitions of a sequence of n_raw tokens; sets *bad for invalid lengths.
+// Number of partitions of a sequence of n_raw tokens (1 for an empty or
+// invalid one); sets *bad for invalid lengths.
 __device__ __forceinline__ int seq_parts(const AttnArgs& a, int n_raw, bool* bad) {
   *bad = n_raw < 0 || n_raw > a.max_context_len ||
          static_cast<int64_t>(n_raw) > static_cast<int64_t>(a.max_blocks) * a.block_size;
@@ -62,29 +79,28 @@ __device__ __forceinline__ int seq_parts(const AttnArgs& a, int n_raw, bool* bad
 template <class DT, int D, int G>
 struct Geo {
   static constexpr int kItem = DT::kItem;
-  static constexpr int R = D * kItem;                // bytes of one token row
-  static constexpr int NP = R / kKeyPiece;           // key pieces per row
-  static constexpr int LR = R / 16;                  // lanes covering one value row
-  static constexpr int TPL = kWave / LR;             // value rows per wave load
-  static constexpr int NLV = kGroup / TPL;           // value loads per group
-  static constexpr int E = 16 / kItem;               // scalars per 16 bytes
-  static constexpr int WF = kLogitFloats / kWaves;   // floats of one wave's LDS region
-  static constexpr int CW = WF / G;                  // tokens one wave holds per chunk
-  static constexpr int C = CW * kWaves;              // tokens per chunk of the workgroup
-  // Key groups in flight per wave: 3, or 2 where the query registers are many.
-  static constexpr int KPF = (G * NP * 4 >= 64) ? 2 : 3;
-  static constexpr int VPF = 2;                      // value groups in flight per wave
+  static constexpr int R = D * kItem;           // bytes of one token row
+  static constexpr int NP = R / kKeyPiece;      // key pieces per row
+  static constexpr int LR = R / 16;             // lanes covering one value row
+  static constexpr int TPL = kWave / LR;        // value rows per wave load
+  static constexpr int E = 16 / kItem;          // scalars per 16 bytes
+  static constexpr int NB16 = R / 64;           // 16-byte registers per lane per group (K or V)
+  // Waves per workgroup and ring slots (groups in flight) per wave: the ring
+  // (NBUF * NB16 * 4 VGPRs), the accumulators (G * E) and two items' query
+  // registers must fit 256 VGPRs for two waves per SIMD, so wide rows and
+  // head groups trade ring depth for waves.  W * NBUF stays 32 groups.
+  static constexpr int W = (G * NB16 >= 16) ? 8 : 4;
+  static constexpr int NBUF = 32 / W;
+  static constexpr int P1 = W * NBUF * kGroup;  // 512: longest partition one ring batch covers
+  static constexpr int RF = (NBUF * kGroup * G > G * D) ? NBUF * kGroup * G : G * D;  // floats per wave region
+  static constexpr int kThreads = W * kWave;
+  static constexpr int kMinWaves = 2;  // occupancy the register budget targets (per SIMD)
   static_assert(R % kKeyPiece == 0 && kGroup % TPL == 0, "unsupported row size");
-  static_assert(G * D <= WF, "a wave's partial output must fit its LDS region");
-  static_assert(CW / kGroup <= kWave, "a wave's block ids must fit one register");
+  static_assert(2 * NP == NB16 && kGroup / TPL == NB16, "K and V groups must fill the same registers");
 };
 
-template <int G>
-struct AttnShared {
-  float region[kWaves][kLogitFloats / kWaves];  // wave-private: logits, probabilities, then partial output
-  float wm[kWaves][G];                          // per-wave maximum (scaled, exp2 domain)
-  float wl[kWaves][G];                          // per-wave sum of probabilities
-};
+template <class DT, int G>
+constexpr bool kUseMfmaQK = std::is_same<DT, BF16>::value && G >= 4;
 
 // Orders one wave's LDS writes before later LDS reads of other lanes of the
 // same wave (a wave's LDS ops execute in order; this stops the compiler from
@@ -114,269 +130,258 @@ __device__ __forceinline__ float sum_mod(float x) {
   return x;
 }
 
-template <class DT, int D, int G, bool MULTI>
-__global__ __launch_bounds__(kThreads) void paged_decode_kernel(AttnArgs a) {
+template <bool V>
+using Bool = std::integral_constant<bool, V>;
+
+// ---------------------------------------------------------------------------
+// Per-group building blocks.
+// ---------------------------------------------------------------------------
+template <class DT, int D, int G, bool QKM>
+struct Ops {
   using Gm = Geo<DT, D, G>;
-  constexpr int NP = Gm::NP, E = Gm::E, C = Gm::C, R = Gm::R, NLV = Gm::NLV, TPL = Gm::TPL, LR = Gm::LR;
-  constexpr int KPF = Gm::KPF, VPF = Gm::VPF;
-  __shared__ AttnShared<G> sh;
+  static constexpr int NP = Gm::NP, E = Gm::E, R = Gm::R, TPL = Gm::TPL, LR = Gm::LR, NB16 = Gm::NB16;
+  static constexpr int NQ = QKM ? NB16 : G * NP;  // 16-byte query registers per lane
+  static constexpr int NM = QKM ? 1 : G;          // per-lane running maxima during QK
 
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int Hkv = a.num_kv_heads;
-  const int Hq = Hkv * G;
-  const int kvh = blockIdx.x % Hkv;
-  const int rest = blockIdx.x / Hkv;
-  const int seq = rest % a.num_seqs;
-  const int part = rest / a.num_seqs;
-  const int B = a.block_size;
-
-  const int n_raw = a.context_lens[seq];
-  bool bad_len;
-  const int nparts = seq_parts(a, n_raw, &bad_len);
-  if (part >= nparts) return;
-  const bool direct = nparts == 1;
-  float* out_rows = a.out + (static_cast<size_t>(seq) * Hq + static_cast<size_t>(kvh) * G) * D;
-  if (bad_len || n_raw == 0) {
-    const float fill = bad_len ? __builtin_nanf("") : 0.0f;
-    for (int i = tid; i < G * D; i += kThreads) out_rows[i] = fill;
-    return;
-  }
-  const int tok_begin = part * a.partition_size;
-  const int tok_end = min(n_raw, tok_begin + a.partition_size);
-
-  // Lane roles.  Keys: lane (l8, j8) holds the 16-byte column j8 of every
-  // 128-byte piece of tokens l8 and l8 + 8 of a group.  Values: lane holds
-  // bytes [cv*16, cv*16+16) of row rv of each wave load.
-  const int l8 = lane >> 3;
-  const int j8 = lane & 7;
-  const int cv = lane % LR;
-  const int rv = lane / LR;
-  const int hm = lane % G;  // the head whose probabilities this lane sums
-  const float c = a.c;
-
-  const int32_t* bt = a.block_tables + static_cast<size_t>(seq) * a.max_blocks;
-  const char* kbase = static_cast<const char*>(a.k_cache) + static_cast<size_t>(kvh) * B * R;
-  const char* vbase = static_cast<const char*>(a.v_cache) + static_cast<size_t>(kvh) * B * R;
-  const char* qrow = static_cast<const char*>(a.q) + (static_cast<size_t>(seq) * Hq + static_cast<size_t>(kvh) * G) * R;
-  const size_t block_stride = static_cast<size_t>(Hkv) * B * R;  // bytes between consecutive blocks
-  float* reg = sh.region[wave];
-
-  float m_run[G];              // running maxima (scaled), uniform across the wave
-  float acc[G][E];
-  float l_mine = 0.0f;         // partial sum of probabilities of head hm
-  float m_mine_run = -INFINITY;
-  bool poisoned = false;
+  // Matrix path: lane l feeds token row l % 16 and head column l % 16 with
+  // bytes [64 st + 16 (l / 16), +16) of the row in step st, and receives the
+  // logits of tokens 4 (l / 16) + r, r < 4, for head l % 16 (columns >= G are
+  // zero).  Vector path: lane (l8, j8) holds the 16-byte column j8 of every
+  // 128-byte key piece of tokens l8 and l8 + 8.
+  __device__ __forceinline__ static void load_query(uint4 (&q)[NQ], const char* qrow, uint32_t sign, int lane) {
+    if constexpr (QKM) {
+      const int mi = lane & 15, mk = lane >> 4;
 #pragma unroll
-  for (int h = 0; h < G; ++h) m_run[h] = -INFINITY;
-
-  for (int c0 = tok_begin; c0 < tok_end; c0 += C) {
-    const bool first = c0 == tok_begin;
-    const int cn = min(C, tok_end - c0);
-    const int ngroups = (cn + kGroup - 1) / kGroup;
-    const int nk = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;  // this wave's groups
-
-    // 1. block ids of this wave's groups, one per lane
-    int idv = 0;
-    bool bad_lane = false;
-    if (lane < nk) {
-      const int g = wave + lane * kWaves;
-      idv = bt[c0 / B + (g * kGroup) / B];
-      if (static_cast<unsigned>(idv) >= static_cast<unsigned>(a.num_blocks)) {
-        bad_lane = true;
-        idv = 0;
+      for (int st = 0; st < NB16; ++st) {
+        // Columns >= G read row 0 and are zeroed: no load sits behind a branch.
+        const uint4 v = *reinterpret_cast<const uint4*>(qrow + (mi < G ? mi : 0) * R + st * 64 + mk * 16);
+        const uint32_t s = mi < G ? sign : 0u, z = mi < G ? ~0u : 0u;
+        q[st] = make_uint4((v.x ^ s) & z, (v.y ^ s) & z, (v.z ^ s) & z, (v.w ^ s) & z);
       }
-    }
-    poisoned |= __ballot(bad_lane) != 0;
-    auto group_row = [&](int k) { return ((wave + k * kWaves) * kGroup) % B; };
-    auto tile_off = [&](int k) { return static_cast<size_t>(__builtin_amdgcn_readlane(idv, k)) * block_stride; };
-    auto load_k = [&](uint4 (&kr)[2][NP], int k) {
-      const char* p = kbase + tile_off(k) + (group_row(k) + l8) * kKeyPiece + j8 * 16;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < NP; ++i)
-          kr[hh][i] = load_nt(p + static_cast<size_t>(i) * B * kKeyPiece + hh * 8 * kKeyPiece);
-    };
-    auto load_v = [&](uint4 (&vr)[NLV], int k) {
-      const char* p = vbase + tile_off(k) + static_cast<size_t>(group_row(k) + rv) * R + cv * 16;
-#pragma unroll
-      for (int j = 0; j < NLV; ++j) vr[j] = load_nt(p + static_cast<size_t>(j) * TPL * R);
-    };
-
-    // 2. logits (raw dot products)
-    float lmax[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) lmax[h] = -INFINITY;
-    {
-      uint4 qr[G][NP];
+    } else {
+      const int j8 = lane & 7;
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
-          uint4 v = *reinterpret_cast<const uint4*>(qrow + h * R + i * kKeyPiece + j8 * 16);
-          v.x ^= a.q_sign;
-          v.y ^= a.q_sign;
-          v.z ^= a.q_sign;
-          v.w ^= a.q_sign;
-          qr[h][i] = v;
+          const uint4 v = *reinterpret_cast<const uint4*>(qrow + h * R + i * kKeyPiece + j8 * 16);
+          q[h * NP + i] = make_uint4(v.x ^ sign, v.y ^ sign, v.z ^ sign, v.w ^ sign);
         }
-      uint4 kb[KPF][2][NP];
+    }
+  }
+
+  // The 16 key rows starting at row0 of the key tile at ktile.
+  __device__ __forceinline__ static void load_keys(uint4 (&kb)[NB16], const char* ktile, int row0, int B, int lane) {
+    if constexpr (QKM) {
+      const char* p = ktile + (row0 + (lane & 15)) * kKeyPiece + (lane >> 4) * 16;
 #pragma unroll
-      for (int j = 0; j < KPF; ++j)
-        if (j < nk) load_k(kb[j], j);
-      for (int k0 = 0; k0 < nk; k0 += KPF) {
+      for (int st = 0; st < NB16; ++st)
+        kb[st] = load_nt(p + static_cast<size_t>(st / 2) * B * kKeyPiece + (st % 2) * 64);
+    } else {
+      const char* p = ktile + (row0 + (lane >> 3)) * kKeyPiece + (lane & 7) * 16;
 #pragma unroll
-        for (int j = 0; j < KPF; ++j) {
-          const int k = k0 + j;
-          if (k < nk) {
-            float s[2][G];
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+        for (int i = 0; i < NP; ++i)
+          kb[hh * NP + i] = load_nt(p + static_cast<size_t>(i) * B * kKeyPiece + hh * 8 * kKeyPiece);
+    }
+  }
+
+  // The 16 value rows starting at row0 of the value tile at vtile: lane holds
+  // bytes [cv * 16, +16) of rows row0 + rv + TPL * jj.
+  __device__ __forceinline__ static void load_values(uint4 (&vb)[NB16], const char* vtile, int row0, int lane) {
+    const char* p = vtile + static_cast<size_t>(row0 + lane / LR) * R + (lane % LR) * 16;
 #pragma unroll
-              for (int h = 0; h < G; ++h) {
-                float x = 0.0f;
+    for (int jj = 0; jj < NB16; ++jj) vb[jj] = load_nt(p + static_cast<size_t>(jj) * TPL * R);
+  }
+
+  __device__ __forceinline__ static void max_init(float (&m)[NM]) {
 #pragma unroll
-                for (int i = 0; i < NP; ++i) x = dot16(DT{}, qr[h][i], kb[j][hh][i], x);
-                s[hh][h] = x;
-              }
-            if (k + KPF < nk) load_k(kb[j], k + KPF);
+    for (int h = 0; h < NM; ++h) m[h] = -INFINITY;
+  }
+
+  // Raw logits of one group into lg[t * G + h] (t < 16), -inf for tokens at
+  // or past tok_end; folds them into the running maxima m.
+  __device__ __forceinline__ static void qk_group(const uint4 (&q)[NQ], const uint4 (&kb)[NB16], float* lg, int t_first, int tok_end,
+                                  float (&m)[NM], int lane) {
+    if constexpr (QKM) {
+      const int mi = lane & 15, mk = lane >> 4;
+      f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+      for (int st = 0; st < NB16; ++st)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[st]), as_bf16x8(q[st]), sc, 0, 0, 0);
+      if (t_first + kGroup > tok_end) {
 #pragma unroll
-              for (int h = 0; h < G; ++h) s[hh][h] = sum8(s[hh][h]);
-            const int t_first = c0 + (wave + k * kWaves) * kGroup;
-            if (t_first + kGroup > tok_end) {  // the partition's last group: mask the tail
+        for (int r = 0; r < 4; ++r)
+          if (t_first + 4 * mk + r >= tok_end) sc[r] = -INFINITY;
+      }
+      m[0] = fmaxf(m[0], fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      if (mi < G) {
 #pragma unroll
-              for (int hh = 0; hh < 2; ++hh)
-                if (t_first + hh * 8 + l8 >= tok_end) {
+        for (int r = 0; r < 4; ++r) lg[(4 * mk + r) * G + mi] = sc[r];
+      }
+    } else {
+      const int l8 = lane >> 3, j8 = lane & 7;
+      float s[2][G];
 #pragma unroll
-                  for (int h = 0; h < G; ++h) s[hh][h] = -INFINITY;
-                }
-            }
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int h = 0; h < G; ++h) lmax[h] = fmaxf(lmax[h], fmaxf(s[0][h], s[1][h]));
-            if (j8 == 0) {
+        for (int h = 0; h < G; ++h) {
+          float x = 0.0f;
 #pragma unroll
-              for (int hh = 0; hh < 2; ++hh) {
-                float* dst = reg + (k * kGroup + hh * 8 + l8) * G;
+          for (int i = 0; i < NP; ++i) x = dot16(DT{}, q[h * NP + i], kb[hh * NP + i], x);
+          s[hh][h] = sum8(x);
+        }
+      if (t_first + kGroup > tok_end) {
 #pragma unroll
-                for (int h = 0; h < G; ++h) dst[h] = s[hh][h];
-              }
-            }
+        for (int hh = 0; hh < 2; ++hh)
+          if (t_first + hh * 8 + l8 >= tok_end) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) s[hh][h] = -INFINITY;
           }
-        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) m[h] = fmaxf(m[h], fmaxf(s[0][h], s[1][h]));
+      if (j8 == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int h = 0; h < G; ++h) lg[(hh * 8 + l8) * G + h] = s[hh][h];
       }
     }
+  }
 
-    // 3. first value loads, wave maxima, running-state rescale, probabilities
-    uint4 vb[VPF][NLV];
+  // Wave-uniform per-head maxima (raw logits) from the lane state.
+  __device__ __forceinline__ static void max_finish(const float (&m)[NM], float (&lmax)[G]) {
+    if constexpr (QKM) {
+      const float x = max_xor32(max_xor16(m[0]));  // lane l: maximum of head l % 16
 #pragma unroll
-    for (int j = 0; j < VPF; ++j)
-      if (j < nk) load_v(vb[j], j);
-    float m_new[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float m = fmaxf(lmax[h], ror<8>(lmax[h]));  // lanes of a half-row already agree
-      m = max_xor16(m);
-      m = max_xor32(m);
-      m_new[h] = fmaxf(m_run[h], m * c);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) sh.wm[wave][h] = m_new[h];
-    }
-    wave_lds_sync();
-    const float m_mine = sh.wm[wave][hm];
-    if (!MULTI || first) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
+      for (int h = 0; h < G; ++h) lmax[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), h));
     } else {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float alpha = m_run[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - m_new[h]);
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
-      }
-      l_mine *= m_mine_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_mine_run - m_mine);
+      for (int h = 0; h < G; ++h) lmax[h] = max_xor32(max_xor16(fmaxf(m[h], ror<8>(m[h]))));
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h) m_run[h] = m_new[h];
-    m_mine_run = m_mine;
-    const int nlog = nk * kGroup * G;
-    for (int e = lane; e < nlog; e += kWave) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(reg[e], c, -m_mine));
-      reg[e] = p;
-      l_mine += p;
-    }
-    wave_lds_sync();
+  }
 
-    // 4. p * V
-    for (int k0 = 0; k0 < nk; k0 += VPF) {
+  // acc[h][e] += p[t][h] * V[t][e] over the group's tokens before tok_end.
+  __device__ __forceinline__ static void pv_group(const uint4 (&vb)[NB16], const float* pg, int t_first, int tok_end,
+                                  float (&acc)[G][E], int lane) {
+    const int rv = lane / LR;
 #pragma unroll
-      for (int j = 0; j < VPF; ++j) {
-        const int k = k0 + j;
-        if (k < nk) {
-          const int t_first = c0 + (wave + k * kWaves) * kGroup;
+    for (int jj = 0; jj < NB16; ++jj) {
+      const int tl = jj * TPL + rv;  // token within the group
+      if (t_first + tl < tok_end) {
+        float v[E];
+        widen16(DT{}, vb[jj], v);
+        const float* pp = pg + tl * G;
 #pragma unroll
-          for (int jj = 0; jj < NLV; ++jj) {
-            const int tl = jj * TPL + rv;  // token within the group
-            if (t_first + tl < tok_end) {
-              float v[E];
-              widen16(DT{}, vb[j][jj], v);
-              const float* pp = reg + (k * kGroup + tl) * G;
+        for (int h = 0; h < G; ++h) {
+          const float p = pp[h];
 #pragma unroll
-              for (int h = 0; h < G; ++h) {
-                const float p = pp[h];
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
-              }
-            }
-          }
-          if (k + VPF < nk) load_v(vb[j], k + VPF);
+          for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
         }
       }
     }
-    wave_lds_sync();
   }
+};
 
-  // Merge: lanes first, then the four waves through LDS.
-  l_mine = sum_mod<G>(l_mine);
+// ---------------------------------------------------------------------------
+// Softmax of one batch and the workgroup merge, shared by both kernels.
+// ---------------------------------------------------------------------------
+
+// Folds a batch's maxima into the running state, rescales acc and l when an
+// earlier batch exists, and turns the batch's nlog logits in reg into
+// probabilities.  wm: this wave's slot of the per-wave maxima (LDS).
+template <int G, int E>
+__device__ __forceinline__ void softmax_batch(float* reg, int nlog, const float (&lmax)[G], float c, bool first,
+                                              float (&m_run)[G], float& m_mine_run, float& l_mine,
+                                              float (&acc)[G][E], float* wm, int lane) {
+  float m_new[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) m_new[h] = fmaxf(m_run[h], lmax[h] * c);
+  if (lane == 0) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[h][e] = sum_mod<LR>(acc[h][e]);
-  if (poisoned) {
-    l_mine = __builtin_nanf("");
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] = __builtin_nanf("");
+    for (int h = 0; h < G; ++h) wm[h] = m_new[h];
   }
-  if (lane < LR) {
+  wave_lds_sync();
+  const float m_mine = wm[lane % G];
+  if (first) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < E; ++e) reg[h * D + cv * E + e] = acc[h][e];
+      for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float alpha = m_run[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - m_new[h]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+    }
+    l_mine *= m_mine_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_mine_run - m_mine);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) m_run[h] = m_new[h];
+  m_mine_run = m_mine;
+  for (int e = lane; e < nlog; e += kWave) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(reg[e], c, -m_mine));
+    reg[e] = p;
+    l_mine += p;
+  }
+  wave_lds_sync();
+}
+
+template <int W, int RF, int G>
+struct MergeShared {
+  float region[W][RF];  // wave-private: logits, probabilities, then partial output
+  float wm[W][G];       // per-wave maximum (scaled, exp2 domain)
+  float wl[W][G];       // per-wave sum of probabilities
+};
+
+// Combine lanes, then waves; write the item's output rows (one partition) or
+// its partials.  Ends with a barrier so the regions can be reused.  An item
+// with fill set (an empty or invalid sequence) writes zeros, or NaN
+// when bad, instead.
+template <class DT, int D, int G, class SH>
+__device__ __forceinline__ void merge_item(const AttnArgs& a, SH& sh, float (&acc)[G][Geo<DT, D, G>::E], float l_mine,
+                                           bool poisoned, int seq, int kvh, int part, bool direct, bool fill = false,
+                                           bool bad = false) {
+  using Gm = Geo<DT, D, G>;
+  constexpr int E = Gm::E, LR = Gm::LR, W = Gm::W, kThreads = Gm::kThreads;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: keeps per-wave math scalar
+  l_mine = sum_mod<G>(l_mine);
+  if (poisoned) l_mine = __builtin_nanf("");
+  float* reg = sh.region[wave];
+  // One head at a time keeps the cross-lane temporaries few: the next item's
+  // keys already occupy the ring registers here.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float x = sum_mod<LR>(acc[h][e]);
+      if (lane < LR) reg[h * D + (lane % LR) * E + e] = poisoned ? __builtin_nanf("") : x;
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (lane < G) sh.wl[wave][lane] = l_mine;  // sh.wm[wave] already holds the final maxima
   __syncthreads();
+  const int Hq = a.num_kv_heads * G;
+  float* out_rows = a.out + (static_cast<size_t>(seq) * Hq + static_cast<size_t>(kvh) * G) * D;
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.wm[w][h]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sh.wm[w][h]);
     float sa = 0.0f, sl = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float wt = __builtin_amdgcn_exp2f(sh.wm[w][h] - M);  // 0 for a wave that saw no token
       sa = fmaf(wt, sh.region[w][i], sa);
       sl = fmaf(wt, sh.wl[w][h], sl);
     }
-    if (direct) {
+    if (fill) {
+      out_rows[i] = bad ? __builtin_nanf("") : 0.0f;
+    } else if (direct) {
       out_rows[i] = sa / sl;
     } else {
       const size_t row = (static_cast<size_t>(seq) * Hq + static_cast<size_t>(kvh) * G + h) * a.max_parts + part;
@@ -387,10 +392,300 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(AttnArgs a) {
       }
     }
   }
+  __syncthreads();
 }
 
+// Rows of an empty (zeros) or invalid (NaN) sequence.
+template <int D, int G, int kThreads>
+__device__ __forceinline__ void fill_rows(const AttnArgs& a, int seq, int kvh, bool bad) {
+  float* out_rows = a.out + (static_cast<size_t>(seq) * a.num_kv_heads * G + static_cast<size_t>(kvh) * G) * D;
+  const float fill = bad ? __builtin_nanf("") : 0.0f;
+  for (int i = threadIdx.x; i < G * D; i += kThreads) out_rows[i] = fill;
+}
+
+// Block ids of this wave's groups j < nk, counted from the table entry bt of
+// the first group of the batch: lane j holds group j's id, lanes >= nk the id
+// of the batch's first entry (a valid address for the unused ring slots).
+// Out-of-range ids become 0; one read by a lane < nk sets *poisoned
+// (wave-uniform).  The load is unconditional: a load behind a branch makes
+// the compiler wait for every earlier load at the join.
+template <int W>
+__device__ __forceinline__ int load_ids(const AttnArgs& a, const int32_t* bt, int nk, int wave, int lane,
+                                        bool* poisoned) {
+  const int tok = lane < nk ? (wave + lane * W) * kGroup : 0;
+  int id = bt[tok / a.block_size];
+  const bool oob = static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks);
+  *poisoned = __ballot(oob && lane < nk) != 0;
+  return oob ? 0 : id;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1: one workgroup per item, any partition size.
+// ---------------------------------------------------------------------------
+template <class DT, int D, int G, bool QKM>
+__global__ __launch_bounds__((Geo<DT, D, G>::kThreads)) __attribute__((amdgpu_waves_per_eu(Geo<DT, D, G>::kMinWaves)))
+void paged_decode_items(AttnArgs a) {
+  using Gm = Geo<DT, D, G>;
+  using O = Ops<DT, D, G, QKM>;
+  constexpr int E = Gm::E, R = Gm::R, NB16 = Gm::NB16, NBUF = Gm::NBUF, W = Gm::W;
+  __shared__ MergeShared<W, Gm::RF, G> sh;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: keeps per-wave math scalar
+  const int Hkv = a.num_kv_heads;
+  const int kvh = blockIdx.x % Hkv;
+  const int rest = blockIdx.x / Hkv;
+  const int seq = rest % a.num_seqs;
+  const int part = rest / a.num_seqs;
+  const int B = a.block_size;
+
+  const int n_raw = a.context_lens[seq];
+  bool bad_len;
+  const int nparts = seq_parts(a, n_raw, &bad_len);
+  if (part >= nparts) return;
+  if (bad_len || n_raw == 0) {
+    fill_rows<D, G, Gm::kThreads>(a, seq, kvh, bad_len);
+    return;
+  }
+  const int tok_begin = part * a.partition_size;
+  const int tok_end = min(n_raw, tok_begin + a.partition_size);
+  const int ngroups = (tok_end - tok_begin + kGroup - 1) / kGroup;
+  const int nk = wave < ngroups ? (ngroups - wave + W - 1) / W : 0;  // this wave's groups
+
+  const int32_t* bt = a.block_tables + static_cast<size_t>(seq) * a.max_blocks + tok_begin / B;
+  const char* kbase = static_cast<const char*>(a.k_cache) + static_cast<size_t>(kvh) * B * R;
+  const char* vbase = static_cast<const char*>(a.v_cache) + static_cast<size_t>(kvh) * B * R;
+  const char* qrow =
+      static_cast<const char*>(a.q) + (static_cast<size_t>(seq) * Hkv * G + static_cast<size_t>(kvh) * G) * R;
+  const size_t block_stride = static_cast<size_t>(Hkv) * B * R;
+  float* reg = sh.region[wave];
+
+  float m_run[G];
+  float acc[G][E];
+  float l_mine = 0.0f;
+  float m_mine_run = -INFINITY;
+  bool poisoned = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) m_run[h] = -INFINITY;
+
+  // Batches of NBUF groups; group b0 + j of this wave is partition group
+  // wave + (b0 + j) * W.  A wave without groups still runs one empty batch so
+  // that its state is defined.
+  for (int b0 = 0; b0 < nk || b0 == 0; b0 += NBUF) {
+    const int nb = min(NBUF, nk - b0);
+    bool pois;
+    const int idv = load_ids<W>(a, bt + (b0 * W * kGroup) / B, nb, wave, lane, &pois);
+    poisoned |= pois;
+    // Ring slot j >= nb repeats slot 0's addresses (the batch's first entry,
+    // row 0, when the wave has no group), so every load is issued on every
+    // path: a load behind a branch makes the compiler wait for all earlier
+    // loads where the paths join.
+    auto src = [&](int j) __attribute__((always_inline)) { return j < nb ? j : 0; };
+    auto row = [&](int j) __attribute__((always_inline)) {
+      return nb > 0 ? ((wave + (b0 + src(j)) * W) * kGroup) % B : 0;
+    };
+    auto t_first = [&](int j) __attribute__((always_inline)) { return tok_begin + (wave + (b0 + j) * W) * kGroup; };
+    auto tile = [&](int j) __attribute__((always_inline)) {
+      return static_cast<size_t>(__builtin_amdgcn_readlane(idv, src(j))) * block_stride;
+    };
+
+    // The query first: the load counter is in order, so the first group's
+    // logits wait only for it and that group's keys.
+    uint4 q[O::NQ];
+    O::load_query(q, qrow, a.q_sign, lane);
+    uint4 buf[NBUF][NB16];
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) O::load_keys(buf[j], kbase + tile(j), row(j), B, lane);
+    float mstate[O::NM];
+    O::max_init(mstate);
+    {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        if (j < nb) O::qk_group(q, buf[j], reg + j * kGroup * G, t_first(j), tok_end, mstate, lane);
+        O::load_values(buf[j], vbase + tile(j), row(j), lane);  // refill the consumed slot
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    float lmax[G];
+    O::max_finish(mstate, lmax);
+    softmax_batch<G, E>(reg, max(nb, 0) * kGroup * G, lmax, a.c, b0 == 0, m_run, m_mine_run, l_mine, acc,
+                        sh.wm[wave], lane);
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (j < nb) O::pv_group(buf[j], reg + j * kGroup * G, t_first(j), tok_end, acc, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wave_lds_sync();  // the next batch rewrites the region
+  }
+  merge_item<DT, D, G>(a, sh, acc, l_mine, poisoned, seq, kvh, part, nparts == 1);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: persistent workgroups over the item list, one ring batch per item.
+// ---------------------------------------------------------------------------
+template <int W, int RF, int G>
+struct PersistShared : MergeShared<W, RF, G> {
+  int32_t psum[kMaxPersistentSeqs + 1];  // prefix sums of partition counts
+};
+
+struct Item {
+  int seq, kvh, part, n, nparts, tok_begin, tok_end, nk;
+  bool special, bad;
+};
+
+template <class DT, int D, int G, bool QKM>
+__global__ __launch_bounds__((Geo<DT, D, G>::kThreads)) __attribute__((amdgpu_waves_per_eu(Geo<DT, D, G>::kMinWaves)))
+void paged_decode_persistent(AttnArgs a) {
+  using Gm = Geo<DT, D, G>;
+  using O = Ops<DT, D, G, QKM>;
+  constexpr int E = Gm::E, R = Gm::R, NB16 = Gm::NB16, NBUF = Gm::NBUF, W = Gm::W;
+  __shared__ PersistShared<W, Gm::RF, G> sh;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: keeps per-wave math scalar
+  const int S = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
+  const int B = a.block_size;
+  const size_t block_stride = static_cast<size_t>(Hkv) * B * R;
+
+  // Item list: prefix sums of the partition counts (wave 0 scans; S <= 4096).
+  for (int s = tid; s < S; s += Gm::kThreads) {
+    bool bad;
+    sh.psum[s + 1] = seq_parts(a, a.context_lens[s], &bad);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int chunk = (S + kWave - 1) / kWave;
+    const int lo = lane * chunk, hi = min(S, lo + chunk);
+    int run = 0;
+    for (int i = lo; i < hi; ++i) run += sh.psum[i + 1];
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    int base = incl - run;
+    for (int i = lo; i < hi; ++i) {
+      base += sh.psum[i + 1];
+      sh.psum[i + 1] = base;
+    }
+    if (lane == 0) sh.psum[0] = 0;
+  }
+  __syncthreads();
+  const int total = sh.psum[S] * Hkv;
+  int k = blockIdx.x;
+  if (k >= total) return;
+
+  auto decode = [&](int kk) __attribute__((always_inline)) {
+    Item it;
+    it.kvh = kk % Hkv;
+    const int pidx = kk / Hkv;
+    // LDS reads land in vector registers; readfirstlane marks them
+    // wave-uniform so that every branch on the item stays a scalar branch.
+    int lo = 0, hi = S;  // psum[lo] <= pidx < psum[lo + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(sh.psum[mid]) <= pidx)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    it.seq = lo;
+    it.part = pidx - __builtin_amdgcn_readfirstlane(sh.psum[lo]);
+    it.n = a.context_lens[lo];
+    it.nparts = seq_parts(a, it.n, &it.bad);
+    it.special = it.bad || it.n == 0;
+    it.tok_begin = it.part * a.partition_size;
+    it.tok_end = min(it.n, it.tok_begin + a.partition_size);
+    const int ngroups = it.special ? 0 : (it.tok_end - it.tok_begin + kGroup - 1) / kGroup;
+    it.nk = wave < ngroups ? (ngroups - wave + W - 1) / W : 0;
+    return it;
+  };
+  auto ktile = [&](const Item& it, int idv, int j) __attribute__((always_inline)) {
+    return static_cast<const char*>(a.k_cache) + static_cast<size_t>(it.kvh) * B * R +
+           static_cast<size_t>(__builtin_amdgcn_readlane(idv, j < it.nk ? j : 0)) * block_stride;
+  };
+  auto vtile = [&](const Item& it, int idv, int j) __attribute__((always_inline)) {
+    return static_cast<const char*>(a.v_cache) + static_cast<size_t>(it.kvh) * B * R +
+           static_cast<size_t>(__builtin_amdgcn_readlane(idv, j < it.nk ? j : 0)) * block_stride;
+  };
+  // Ring slot j >= nk repeats slot 0's addresses (the item's first entry,
+  // row 0, when the wave has no group): every load is issued on every path.
+  auto src = [&](const Item& it, int j) __attribute__((always_inline)) { return j < it.nk ? j : 0; };
+  auto row = [&](const Item& it, int j) __attribute__((always_inline)) {
+    return it.nk > 0 ? ((wave + src(it, j) * W) * kGroup) % B : 0;
+  };
+  auto t_first = [&](const Item& it, int j) __attribute__((always_inline)) { return it.tok_begin + (wave + j * W) * kGroup; };
+  auto table = [&](const Item& it) __attribute__((always_inline)) {
+    return a.block_tables + static_cast<size_t>(it.seq) * a.max_blocks + it.tok_begin / B;
+  };
+  auto qrow = [&](const Item& it) __attribute__((always_inline)) {
+    return static_cast<const char*>(a.q) +
+           (static_cast<size_t>(it.seq) * Hkv * G + static_cast<size_t>(it.kvh) * G) * R;
+  };
+  float* reg = sh.region[wave];
+
+  Item cur = decode(k);
+  bool pois_cur;
+  int idv_cur = load_ids<W>(a, table(cur), cur.nk, wave, lane, &pois_cur);
+  uint4 q_cur[O::NQ];
+  O::load_query(q_cur, qrow(cur), a.q_sign, lane);
+  uint4 buf[NBUF][NB16];
+#pragma unroll
+  for (int j = 0; j < NBUF; ++j) O::load_keys(buf[j], ktile(cur, idv_cur, j), row(cur, j), B, lane);
+
+  for (;;) {
+    // The next item: its ids and query are fetched now, its keys go into ring
+    // slots as the current item's values are consumed.  After the last item
+    // the current one stands in for it, so the loads stay unconditional.
+    const int kn = k + static_cast<int>(gridDim.x);
+    const bool has_next = kn < total;
+    Item nxt = cur;
+    if (has_next) nxt = decode(kn);
+    bool pois_next;
+    const int idv_next = load_ids<W>(a, table(nxt), nxt.nk, wave, lane, &pois_next);
+    uint4 q_next[O::NQ];
+    O::load_query(q_next, qrow(nxt), a.q_sign, lane);
+
+    // An empty or invalid item has no groups; it runs the same path and its
+    // merge writes zeros or NaN.
+    float mstate[O::NM];
+    O::max_init(mstate);
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (j < cur.nk) O::qk_group(q_cur, buf[j], reg + j * kGroup * G, t_first(cur, j), cur.tok_end, mstate, lane);
+      O::load_values(buf[j], vtile(cur, idv_cur, j), row(cur, j), lane);  // refill the consumed slot
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float lmax[G], m_run[G], acc[G][E];
+    float l_mine = 0.0f, m_mine_run = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_run[h] = -INFINITY;
+    O::max_finish(mstate, lmax);
+    softmax_batch<G, E>(reg, cur.nk * kGroup * G, lmax, a.c, true, m_run, m_mine_run, l_mine, acc, sh.wm[wave], lane);
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (j < cur.nk) O::pv_group(buf[j], reg + j * kGroup * G, t_first(cur, j), cur.tok_end, acc, lane);
+      O::load_keys(buf[j], ktile(nxt, idv_next, j), row(nxt, j), B, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    merge_item<DT, D, G>(a, sh, acc, l_mine, pois_cur, cur.seq, cur.kvh, cur.part, cur.nparts == 1, cur.special,
+                         cur.bad);
+    if (!has_next) break;
+    cur = nxt;
+    idv_cur = idv_next;
+    pois_cur = pois_next;
+#pragma unroll
+    for (int i = 0; i < O::NQ; ++i) q_cur[i] = q_next[i];
+    k = kn;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Log-sum-exp combination of the partitions of one (sequence, query head):
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kWave) void lse_reduce_kernel(AttnArgs a, int num_q_heads) {
   const int row = blockIdx.x;  // seq * H_q + h
@@ -419,6 +714,9 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(AttnArgs a, int num_q
   for (int e = 0; e < PER; ++e) out[lane + e * kWave] = o[e] / L;
 }
 
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
 struct Plan {
   int32_t P;          // effective partition size
   int32_t max_parts;  // partitions of the longest sequence
@@ -440,30 +738,56 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t 
   return p;
 }
 
-template <class DT, int D, int G>
-void launch_attention_m(const AttnArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.partition_size <= Geo<DT, D, G>::C)
-    hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, false>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, true>), grid, dim3(kThreads), 0, stream, a);
+// Workgroups of a kernel that fit the whole device at once, cached per
+// device and per instantiation (Tag makes each kernel its own cache).
+template <class Tag, class K>
+int resident_workgroups(K kernel, int threads) {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+    cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
+  }
+  return cache[dev];
 }
 
-template <class DT, int D>
-hipError_t launch_attention_g(const AttnArgs& a, int G, dim3 grid, hipStream_t stream) {
-  switch (G) {
-    case 1: launch_attention_m<DT, D, 1>(a, grid, stream); break;
-    case 2: launch_attention_m<DT, D, 2>(a, grid, stream); break;
-    case 4: launch_attention_m<DT, D, 4>(a, grid, stream); break;
-    case 8: launch_attention_m<DT, D, 8>(a, grid, stream); break;
-    default: return hipErrorInvalidValue;
+template <class DT, int D, int G>
+hipError_t launch_attention_g(const AttnArgs& a, int64_t items, hipStream_t stream) {
+  using Gm = Geo<DT, D, G>;
+  constexpr bool QKM = kUseMfmaQK<DT, G>;
+  if (a.partition_size <= Gm::P1 && a.num_seqs <= kMaxPersistentSeqs) {
+    auto kernel = paged_decode_persistent<DT, D, G, QKM>;
+    const int fill = resident_workgroups<Ops<DT, D, G, QKM>>(kernel, Gm::kThreads);
+    if (fill <= 0) return hipErrorInvalidValue;
+    const int64_t grid = items < fill ? items : fill;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(Gm::kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((paged_decode_items<DT, D, G, QKM>), dim3(static_cast<unsigned>(items)), dim3(Gm::kThreads),
+                       0, stream, a);
   }
   return hipGetLastError();
 }
 
+template <class DT, int D>
+hipError_t launch_attention_d(const AttnArgs& a, int G, int64_t items, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_attention_g<DT, D, 1>(a, items, stream);
+    case 2: return launch_attention_g<DT, D, 2>(a, items, stream);
+    case 4: return launch_attention_g<DT, D, 4>(a, items, stream);
+    case 8: return launch_attention_g<DT, D, 8>(a, items, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <class DT>
-hipError_t launch_attention_d(const AttnArgs& a, int D, int G, dim3 grid, hipStream_t stream) {
-  if (D == 64) return launch_attention_g<DT, 64>(a, G, grid, stream);
-  if (D == 128) return launch_attention_g<DT, 128>(a, G, grid, stream);
+hipError_t launch_attention(const AttnArgs& a, int D, int G, int64_t items, hipStream_t stream) {
+  if (D == 64) return launch_attention_d<DT, 64>(a, G, items, stream);
+  if (D == 128) return launch_attention_d<DT, 128>(a, G, items, stream);
   return hipErrorInvalidValue;
 }
 
@@ -491,8 +815,8 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
 
   const Plan plan = make_plan(num_seqs, num_q_heads, head_dim, block_size, max_context_len, partition_size);
-  const int64_t grid = static_cast<int64_t>(plan.max_parts) * num_seqs * num_kv_heads;
-  if (grid > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  const int64_t items = static_cast<int64_t>(plan.max_parts) * num_seqs * num_kv_heads;
+  if (items > INT32_MAX) return PKV_ERR_INVALID_ARG;
   AttnArgs a{};
   a.out = out;
   a.q = q;
@@ -524,9 +848,8 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
   a.q_sign = scale < 0.0f ? (kv_dtype == PKV_BF16 ? BF16::kSignMask : F32::kSignMask) : 0u;
 
   if (stages & kStagePartitions) {
-    const dim3 g(static_cast<unsigned>(grid));
-    const hipError_t err = kv_dtype == PKV_BF16 ? launch_attention_d<BF16>(a, head_dim, G, g, stream)
-                                                : launch_attention_d<F32>(a, head_dim, G, g, stream);
+    const hipError_t err = kv_dtype == PKV_BF16 ? launch_attention<BF16>(a, head_dim, G, items, stream)
+                                                : launch_attention<F32>(a, head_dim, G, items, stream);
     if (err != hipSuccess) return PKV_ERR_HIP;
   }
   if ((stages & kStageReduce) && plan.max_parts > 1) {

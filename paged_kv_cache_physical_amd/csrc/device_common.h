@@ -23,6 +23,8 @@ constexpr int kWave = 64;
 constexpr int kKeyPiece = 128;  // bytes of one key piece
 
 typedef short bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 struct F32 {
@@ -43,6 +45,10 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
 }
 
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  const u32x4_t u = {v.x, v.y, v.z, v.w};
+  return __builtin_bit_cast(bf16x8_t, u);
+}
 
 // Partial dot product of 16 bytes of q with 16 bytes of k, accumulated in fp32.
 __device__ __forceinline__ float dot16(BF16, const uint4& q, const uint4& k, float acc) {
