@@ -29,13 +29,13 @@
  * pool, the pool's state is unchanged.
  *
  * Physical cache layout (one key cache and one value cache per layer):
- *   value cache  V[num_blocks][H_kv][B][d]
- *   key cache    K[num_blocks][H_kv][d / X][B][X],   X = 128 / bytes_per_scalar
+ *   key cache    K[num_blocks][H_kv][d / X][B][X],   X = 16 / bytes_per_scalar
+ *   value cache  V[num_blocks][H_kv][d][B]
  * Each (block, KV head) owns one contiguous tile of B * d scalars.  In a key
- * tile, a token's d values are split into 128-byte pieces and piece j of all B
- * tokens is stored together (for d * bytes_per_scalar = 128 the key tile is
- * plain rows, like the value tile).  Token position t of a sequence whose table is
- * bt lives in block bt[t / B] at offset t % B; its slot is
+ * tile, a token's d values are split into 16-byte pieces and piece j of all B
+ * tokens is stored together; a value tile is stored transposed, one row of B
+ * token values per head dimension.  Token position t of a sequence whose
+ * table is bt lives in block bt[t / B] at offset t % B; its slot is
  * bt[t / B] * B + t % B.  Scalars are fp32 or bf16 (PKV_F32 / PKV_BF16).
  *
  * Supported shapes: head_dim d in {64, 128}; block size B in {16, 32};

@@ -7,12 +7,13 @@ reads a sequence's scattered blocks through that table ([P2] core idea items
 layout open.  The layout used by the library's interface (and restated here
 from that interface's definition, not from its code) is, per cache:
 
-  value cache  V[num_blocks][H_kv][B][d]                 (row-major)
-  key cache    K[num_blocks][H_kv][d / X][B][X],  X = 128 / bytes_per_scalar
+  key cache    K[num_blocks][H_kv][d / X][B][X],  X = 16 / bytes_per_scalar
+  value cache  V[num_blocks][H_kv][d][B]
 
 i.e. each (block, KV head) owns one contiguous tile; in the key tile a token's
-d values are stored as d / X pieces of 128 bytes, piece j of every token of the
-block lying together.  Token position t of a sequence with table ``bt`` is in
+d values are stored as d / X pieces of 16 bytes, piece j of every token of the
+block lying together; the value tile is transposed, one row of B token values
+per head dimension.  Token position t of a sequence with table ``bt`` is in
 block ``bt[t // B]`` at offset ``t % B``; slot = block * B + offset.
 
 Arrays are NumPy arrays of the storage dtype (float32, or uint16 holding
@@ -31,8 +32,8 @@ _ITEM = {"f32": 4, "bf16": 2}
 
 
 def key_piece(kv_dtype: str) -> int:
-    """X: scalars per 128-byte piece of a key row."""
-    return 128 // _ITEM[kv_dtype]
+    """X: scalars per 16-byte piece of a key row."""
+    return 16 // _ITEM[kv_dtype]
 
 
 def empty_caches(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, kv_dtype: str
@@ -40,9 +41,9 @@ def empty_caches(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: 
     """Key and value caches with every slot set to the NaN poison pattern."""
     X = key_piece(kv_dtype)
     if head_dim % X:
-        raise ValueError("head_dim * bytes_per_scalar must be a multiple of 128")
+        raise ValueError("head_dim * bytes_per_scalar must be a multiple of 16")
     k = np.empty((num_blocks, num_kv_heads, head_dim // X, block_size, X), dtype=_STORE[kv_dtype])
-    v = np.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=_STORE[kv_dtype])
+    v = np.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=_STORE[kv_dtype])
     pattern = POISON[kv_dtype]
     k.view(pattern.dtype)[...] = pattern
     v.view(pattern.dtype)[...] = pattern
@@ -69,7 +70,7 @@ def scatter(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new: 
     kn = np.asarray(k_new)[keep]
     vn = np.asarray(v_new)[keep]
     k_cache[blk, :, :, off, :] = kn.reshape(len(s), H, npieces, X)
-    v_cache[blk, :, off, :] = vn
+    v_cache[blk, :, :, off] = vn
 
 
 def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs: np.ndarray) -> None:
@@ -93,7 +94,7 @@ def gather(k_cache: np.ndarray, v_cache: np.ndarray, table, n: int) -> Tuple[np.
         raise ValueError("block table entry out of range")
     off = t % B
     k = k_cache[blk, :, :, off, :].reshape(n, H, npieces * X)
-    v = v_cache[blk, :, off, :]
+    v = v_cache[blk, :, :, off]
     return k, v
 
 

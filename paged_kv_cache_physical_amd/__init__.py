@@ -185,6 +185,10 @@ def _torch():
     return torch
 
 
+def _dtype_name(t) -> str:
+    return "f32" if _dtype_code(t) == PKV_F32 else "bf16"
+
+
 def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.float32:
@@ -209,8 +213,8 @@ def _dev(t, name):
 
 
 def cache_shapes(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, kv_dtype: str):
-    X = 128 // (4 if kv_dtype == "f32" else 2)
-    return ((num_blocks, num_kv_heads, head_dim // X, block_size, X), (num_blocks, num_kv_heads, block_size, head_dim))
+    X = 16 // (4 if kv_dtype == "f32" else 2)
+    return ((num_blocks, num_kv_heads, head_dim // X, block_size, X), (num_blocks, num_kv_heads, head_dim, block_size))
 
 
 def empty_caches(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype: str, device="cuda", poison=True):
@@ -242,7 +246,8 @@ def pkv_reshape_and_cache(k_new, v_new, k_cache, v_cache, slots, block_size: int
         if t.dtype != k_new.dtype:
             raise InvalidArg(-1, "pkv_reshape_and_cache", "dtype mismatch")
     nb = v_cache.shape[0]
-    if tuple(v_cache.shape) != (nb, H, block_size, d) or k_cache.numel() != v_cache.numel():
+    ks, vs = cache_shapes(nb, H, block_size, d, _dtype_name(k_new))
+    if tuple(k_cache.shape) != ks or tuple(v_cache.shape) != vs:
         raise InvalidArg(-1, "pkv_reshape_and_cache", "cache shape does not match k_new / block_size")
     check(lib().pkv_reshape_and_cache(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
                                       _dev(v_cache, "v_cache"), _dev(slots, "slots"), T, H, d, block_size, nb,
@@ -280,9 +285,11 @@ def _attention(fn: str, out, q, k_cache, v_cache, block_tables, context_lens, ma
                partition_size: int = 0, workspace=None, stream=None) -> None:
     torch = _torch()
     S, Hq, d = q.shape
-    nb, Hkv, B, d2 = v_cache.shape
+    nb, Hkv, d2, B = v_cache.shape
     if d2 != d or out.shape != q.shape or out.dtype != torch.float32:
         raise InvalidArg(-1, fn, "shape mismatch")
+    if tuple(k_cache.shape) != cache_shapes(nb, Hkv, B, d, _dtype_name(q))[0]:
+        raise InvalidArg(-1, fn, "key cache shape mismatch")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise InvalidArg(-1, fn, "tables and lengths must be int32")
     if block_tables.shape[0] != S or context_lens.numel() != S or q.dtype != k_cache.dtype:

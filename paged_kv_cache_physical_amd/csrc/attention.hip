@@ -1,35 +1,36 @@
 // Paged decode attention for gfx950: one query token per sequence, keys and
 // values read through block tables, split-context partitions combined by a
-// log-sum-exp reduction.
+// log-sum-exp reduction (PagedAttention, "PagedAttention" section and its
+// figure of the per-block computation; the split follows the decoding page's
+// partitioned reduction).
 //
 // Unit of work: an item = (sequence, KV head, context partition of at most P
-// tokens).  A workgroup of 4 waves handles an item; wave w takes the 16-token
-// groups g = w, w + 4, ... of the partition.  Per group a wave
-//   - loads the group's 16 key rows (nontemporal 16-byte loads, one register
-//     ring slot per group),
-//   - computes the G logits of each token (raw q.k), writes them to its own LDS
-//     region and tracks per-head maxima, then refills the slot with the group's
-//     values, so the value loads overlap the rest of the QK work;
-// then reduces the maxima across the wave, turns logits into probabilities in
-// place (one fma + exp2 each), and accumulates p * V in fp32 from the ring.
-// The G query heads of a KV head share every key and value load (GQA).  The
-// four waves merge their (max, sum, acc) once, through LDS, and write the
-// output rows (one partition) or the partition's partials.
+// tokens).  A workgroup of four waves walks a strided list of items
+// (persistent grid).  Wave w takes the groups g = w, w + 4, ... of an item; a
+// group is one cache block (bf16) or 16 tokens (fp32).  Per group a wave
+//   - multiplies the group's keys with the G query heads of the KV head on the
+//     matrix cores (QK^T: rows = tokens, columns = heads),
+//   - folds the group into an online softmax per head (running maximum in the
+//     exp2 domain, rescaling the accumulator when the maximum grows),
+//   - multiplies the probabilities with the group's values on the matrix
+//     cores (rows = head dimensions, columns = heads), accumulating in fp32.
+// The groups' keys and values sit in a register ring of NBUF slots; after a
+// slot is consumed it is refilled with the group NBUF positions ahead, which
+// crosses into the next item of the workgroup, so loads stay in flight across
+// item boundaries.  The four waves merge their (max, sum, acc) through LDS
+// and write the item's output rows (one partition) or its partials.
 //
-// QK runs on the matrix cores (v_mfma_f32_16x16x32_bf16) for bf16 caches with
-// G >= 4, where each 16-token group is a real [16 x d] x [d x G] contraction;
-// on the vector ALUs (v_dot2_f32_bf16 or fp32 fma, 8-lane DPP sums) otherwise.
-// PV always runs on the vector ALUs in fp32: probabilities are never rounded.
+// Precision.  QK: exact bf16 (or fp32) products, fp32 accumulation.  PV with
+// bf16 caches: each probability p is split as p = hi + lo, hi its truncation
+// to bf16 and lo = bf16_rne(p - hi), so |p - hi - lo| <= 2^-16 p; both halves
+// multiply the exact bf16 values and PV keeps fp32-level accuracy.  fp32
+// caches use the fp32 matrix instructions throughout.
 //
-// Two kernels share these building blocks:
-//   paged_decode_persistent  partitions of at most 512 tokens (one ring batch
-//       per wave) and at most 4096 sequences: a grid sized to fill the chip
-//       walks the item list (built per workgroup from an LDS prefix sum of the
-//       partition counts); while a wave accumulates p * V of one item it
-//       refills each consumed ring slot with the keys of its next item, so the
-//       memory pipe stays busy across item boundaries.
-//   paged_decode_items       any partition size: one workgroup per item, the
-//       partition streamed in batches of ring slots with an online rescale.
+// Loads.  Keys, values and the query go through buffer resources.  A ring
+// slot with no group to hold uses a resource of size 0: the hardware returns
+// zeros without touching memory.  Every load is issued on every path, which
+// keeps the compiler's wait counters exact (a load behind a branch makes it
+// wait for all earlier loads where the paths join).
 
 #include <hip/hip_runtime.h>
 
@@ -41,8 +42,11 @@
 namespace pkv {
 namespace {
 
-constexpr int kGroup = 16;                // tokens of one group
-constexpr int kMaxPersistentSeqs = 4096;  // sequences the persistent kernel's LDS item list holds
+constexpr int kWaves = 4;  // waves per workgroup
+constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxListedSeqs = 4096;    // sequences whose item list fits the LDS prefix sums
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kLoadNT = 2;              // buffer-load cache policy: nontemporal
 
 struct AttnArgs {
   float* out;
@@ -62,8 +66,9 @@ struct AttnArgs {
   int32_t max_context_len;
   int32_t partition_size;  // tokens, multiple of block_size
   int32_t max_parts;
-  float c;          // |scale| * log2(e) (>= FLT_MIN): logits enter exp2 as fma(s, c, -m)
-  uint32_t q_sign;  // xor mask applied to q's bits: flips its sign when scale < 0
+  int32_t total_items;     // max_parts * num_seqs * num_kv_heads
+  float c;                 // |scale| * log2(e) (>= FLT_MIN): logits enter exp2 as fma(s, c, -m)
+  uint32_t q_sign;         // xor mask applied to q's bits: flips its sign when scale < 0
 };
 
 // Number of partitions of a sequence of n_raw tokens (1 for an empty or
@@ -75,610 +80,509 @@ __device__ __forceinline__ int seq_parts(const AttnArgs& a, int n_raw, bool* bad
   return (n_raw + a.partition_size - 1) / a.partition_size;
 }
 
+// Marks a value wave-uniform (values read from LDS land in vector registers).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Buffer resource over `bytes` bytes at p; bytes = 0 turns every load into zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
+}
+// voff: the lane's offset; soff: a wave-uniform offset added to it.  A load
+// stays inside its tile, and a size-0 resource rejects every load, so the
+// result does not depend on whether the range check includes soff.
+template <int kAux>
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAux);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+template <int kAux>
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kAux);
+  return make_uint2(v[0], v[1]);
+}
+
 // Per-instantiation geometry.
-template <class DT, int D, int G>
+//   K tile (one block, one KV head): [d / X][B][X], X = 16 bytes of scalars.
+//   V tile: [d][B].
+template <class DT, int D, int B>
 struct Geo {
+  static constexpr bool kBF16 = std::is_same<DT, BF16>::value;
   static constexpr int kItem = DT::kItem;
-  static constexpr int R = D * kItem;           // bytes of one token row
-  static constexpr int NP = R / kKeyPiece;      // key pieces per row
-  static constexpr int LR = R / 16;             // lanes covering one value row
-  static constexpr int TPL = kWave / LR;        // value rows per wave load
-  static constexpr int E = 16 / kItem;          // scalars per 16 bytes
-  static constexpr int NB16 = R / 64;           // 16-byte registers per lane per group (K or V)
-  // Waves per workgroup and ring slots (groups in flight) per wave: the ring
-  // (NBUF * NB16 * 4 VGPRs), the accumulators (G * E) and two items' query
-  // registers must fit 256 VGPRs for two waves per SIMD, so wide rows and
-  // head groups trade ring depth for waves.  W * NBUF stays 32 groups.
-  static constexpr int W = (G * NB16 >= 16) ? 8 : 4;
-  static constexpr int NBUF = 32 / W;
-  static constexpr int P1 = W * NBUF * kGroup;  // 512: longest partition one ring batch covers
-  static constexpr int RF = (NBUF * kGroup * G > G * D) ? NBUF * kGroup * G : G * D;  // floats per wave region
-  static constexpr int kThreads = W * kWave;
-  static constexpr int kMinWaves = 2;  // occupancy the register budget targets (per SIMD)
-  static_assert(R % kKeyPiece == 0 && kGroup % TPL == 0, "unsupported row size");
-  static_assert(2 * NP == NB16 && kGroup / TPL == NB16, "K and V groups must fill the same registers");
+  static constexpr int R = D * kItem;                    // bytes of one token row
+  static constexpr int TILE = B * R;                     // bytes of one (block, KV head) tile
+  static constexpr int GT = kBF16 ? B : 16;              // tokens per group
+  static constexpr int NT = GT / 16;                     // 16-token QK tiles per group
+  static constexpr int KS = R / 64;                      // key registers (16 B) per lane per QK tile
+  static constexpr int NDT = D / 16;                     // 16-row tiles of the head dimension
+  static constexpr int VW = (kBF16 && B == 16) ? 2 : 4;  // value dwords per lane per d-tile
+  static constexpr int NQ = KS;                          // query registers (16 B) per lane
+  static constexpr int SLOT = NT * KS * 4 + NDT * VW;    // VGPRs of one ring slot
+  static constexpr int NBUF = 128 / SLOT;                // ring slots: 128 VGPRs of loads in flight
+  static_assert(NBUF >= 2 && (NBUF & (NBUF - 1)) == 0, "ring depth");
 };
 
-template <class DT, int G>
-constexpr bool kUseMfmaQK = std::is_same<DT, BF16>::value && G >= 4;
+// One decoded item.  Every field is wave-uniform.
+struct Item {
+  int k;  // item index (>= total: none)
+  int seq, kvh, part;
+  int tok_begin, tok_end;
+  int nk;     // groups of this wave
+  int npad;   // ring positions of this wave: nk rounded up to NBUF, at least NBUF
+  int flags;  // kDirect | kSpecial | kBad
+};
+constexpr int kDirect = 1;   // single partition: write the output rows
+constexpr int kSpecial = 2;  // empty or invalid sequence: no groups, fill the rows
+constexpr int kBad = 4;      // invalid length: fill with NaN
 
-// Orders one wave's LDS writes before later LDS reads of other lanes of the
-// same wave (a wave's LDS ops execute in order; this stops the compiler from
-// moving them).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+template <int G, int D, bool LIST>
+struct Shared {
+  alignas(16) float region[kWaves][G][D + 4];  // per-wave partial output (padded rows)
+  float wm[kWaves][G];                         // per-wave running maximum (exp2 domain, scaled)
+  float wl[kWaves][G];                         // per-wave sum of probabilities
+  int32_t psum[LIST ? kMaxListedSeqs + 1 : 1]; // prefix sums of partition counts
+};
 
-// Row rotations used for reductions over lanes with equal (lane mod n) inside a
-// row of 16: x + ror_n(x) pairs lane i with lane (i + n) mod 16.
-template <int N>
-__device__ __forceinline__ float ror(float x) {
-  return dpp<0x120 + N>(x);
-}
+// LIST: items are the dense list (sequence, partition, KV head) built from
+// LDS prefix sums of the partition counts (at most kMaxListedSeqs sequences).
+// Otherwise items are numbered part-major over max_parts and the empty ones
+// (partition past the sequence's end) are skipped.
+template <class DT, int D, int G, int B, bool LIST>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_decode_kernel(AttnArgs a) {
+  using Gm = Geo<DT, D, B>;
+  constexpr int GT = Gm::GT, NT = Gm::NT, KS = Gm::KS, NDT = Gm::NDT, VW = Gm::VW, NQ = Gm::NQ;
+  constexpr int NBUF = Gm::NBUF, R = Gm::R, TILE = Gm::TILE;
+  constexpr bool kBF16 = Gm::kBF16;
+  __shared__ Shared<G, D, LIST> sh;
 
-// Sum over all lanes with the same (lane mod M), M a power of two <= 32.
-template <int M>
-__device__ __forceinline__ float sum_mod(float x) {
-  if constexpr (M <= 1) x += ror<1>(x);
-  if constexpr (M <= 2) x += ror<2>(x);
-  if constexpr (M <= 4) x += ror<4>(x);
-  if constexpr (M <= 8) x += ror<8>(x);
-  if constexpr (M <= 16) x = sum_xor16(x);
-  x = sum_xor32(x);
-  return x;
-}
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = uni(tid / kWave);
+  const int m16 = lane & 15, kq = lane >> 4;
+  const int S = a.num_seqs, Hkv = a.num_kv_heads;
+  const int grid = static_cast<int>(gridDim.x);
 
-template <bool V>
-using Bool = std::integral_constant<bool, V>;
-
-// ---------------------------------------------------------------------------
-// Per-group building blocks.
-// ---------------------------------------------------------------------------
-template <class DT, int D, int G, bool QKM>
-struct Ops {
-  using Gm = Geo<DT, D, G>;
-  static constexpr int NP = Gm::NP, E = Gm::E, R = Gm::R, TPL = Gm::TPL, LR = Gm::LR, NB16 = Gm::NB16;
-  static constexpr int NQ = QKM ? NB16 : G * NP;  // 16-byte query registers per lane
-  static constexpr int NM = QKM ? 1 : G;          // per-lane running maxima during QK
-
-  // Matrix path: lane l feeds token row l % 16 and head column l % 16 with
-  // bytes [64 st + 16 (l / 16), +16) of the row in step st, and receives the
-  // logits of tokens 4 (l / 16) + r, r < 4, for head l % 16 (columns >= G are
-  // zero).  Vector path: lane (l8, j8) holds the 16-byte column j8 of every
-  // 128-byte key piece of tokens l8 and l8 + 8.
-  __device__ __forceinline__ static void load_query(uint4 (&q)[NQ], const char* qrow, uint32_t sign, int lane) {
-    if constexpr (QKM) {
-      const int mi = lane & 15, mk = lane >> 4;
-#pragma unroll
-      for (int st = 0; st < NB16; ++st) {
-        // Columns >= G read row 0 and are zeroed: no load sits behind a branch.
-        const uint4 v = *reinterpret_cast<const uint4*>(qrow + (mi < G ? mi : 0) * R + st * 64 + mk * 16);
-        const uint32_t s = mi < G ? sign : 0u, z = mi < G ? ~0u : 0u;
-        q[st] = make_uint4((v.x ^ s) & z, (v.y ^ s) & z, (v.z ^ s) & z, (v.w ^ s) & z);
-      }
-    } else {
-      const int j8 = lane & 7;
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          const uint4 v = *reinterpret_cast<const uint4*>(qrow + h * R + i * kKeyPiece + j8 * 16);
-          q[h * NP + i] = make_uint4(v.x ^ sign, v.y ^ sign, v.z ^ sign, v.w ^ sign);
-        }
+  // ---- items ---------------------------------------------------------------
+  int total = a.total_items;
+  if constexpr (LIST) {
+    for (int s = tid; s < S; s += kThreads) {
+      bool bad;
+      sh.psum[s + 1] = seq_parts(a, a.context_lens[s], &bad);
     }
-  }
-
-  // The 16 key rows starting at row0 of the key tile at ktile.
-  __device__ __forceinline__ static void load_keys(uint4 (&kb)[NB16], const char* ktile, int row0, int B, int lane) {
-    if constexpr (QKM) {
-      const char* p = ktile + (row0 + (lane & 15)) * kKeyPiece + (lane >> 4) * 16;
+    __syncthreads();
+    if (wave == 0) {  // scan: each lane sums a chunk, then a wave-wide scan of the chunk sums
+      const int chunk = (S + kWave - 1) / kWave;
+      const int lo = lane * chunk, hi = min(S, lo + chunk);
+      int run = 0;
+      for (int i = lo; i < hi; ++i) run += sh.psum[i + 1];
+      int incl = run;
 #pragma unroll
-      for (int st = 0; st < NB16; ++st)
-        kb[st] = load_nt(p + static_cast<size_t>(st / 2) * B * kKeyPiece + (st % 2) * 64);
-    } else {
-      const char* p = ktile + (row0 + (lane >> 3)) * kKeyPiece + (lane & 7) * 16;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < NP; ++i)
-          kb[hh * NP + i] = load_nt(p + static_cast<size_t>(i) * B * kKeyPiece + hh * 8 * kKeyPiece);
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      int base = incl - run;
+      for (int i = lo; i < hi; ++i) {
+        base += sh.psum[i + 1];
+        sh.psum[i + 1] = base;
+      }
+      if (lane == 0) sh.psum[0] = 0;
     }
+    __syncthreads();
+    total = uni(sh.psum[S]) * Hkv;
   }
-
-  // The 16 value rows starting at row0 of the value tile at vtile: lane holds
-  // bytes [cv * 16, +16) of rows row0 + rv + TPL * jj.
-  __device__ __forceinline__ static void load_values(uint4 (&vb)[NB16], const char* vtile, int row0, int lane) {
-    const char* p = vtile + static_cast<size_t>(row0 + lane / LR) * R + (lane % LR) * 16;
-#pragma unroll
-    for (int jj = 0; jj < NB16; ++jj) vb[jj] = load_nt(p + static_cast<size_t>(jj) * TPL * R);
-  }
-
-  __device__ __forceinline__ static void max_init(float (&m)[NM]) {
-#pragma unroll
-    for (int h = 0; h < NM; ++h) m[h] = -INFINITY;
-  }
-
-  // Raw logits of one group into lg[t * G + h] (t < 16), -inf for tokens at
-  // or past tok_end; folds them into the running maxima m.
-  __device__ __forceinline__ static void qk_group(const uint4 (&q)[NQ], const uint4 (&kb)[NB16], float* lg, int t_first, int tok_end,
-                                  float (&m)[NM], int lane) {
-    if constexpr (QKM) {
-      const int mi = lane & 15, mk = lane >> 4;
-      f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int st = 0; st < NB16; ++st)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[st]), as_bf16x8(q[st]), sc, 0, 0, 0);
-      if (t_first + kGroup > tok_end) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t_first + 4 * mk + r >= tok_end) sc[r] = -INFINITY;
+  auto decode = [&](int k) __attribute__((always_inline)) {
+    Item it;
+    it.k = k;
+    it.kvh = k % Hkv;
+    const int r = k / Hkv;
+    if constexpr (LIST) {
+      int lo = 0, hi = S;  // psum[lo] <= r < psum[lo + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (uni(sh.psum[mid]) <= r)
+          lo = mid;
+        else
+          hi = mid;
       }
-      m[0] = fmaxf(m[0], fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-      if (mi < G) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lg[(4 * mk + r) * G + mi] = sc[r];
-      }
+      it.seq = lo;
+      it.part = r - uni(sh.psum[lo]);
     } else {
-      const int l8 = lane >> 3, j8 = lane & 7;
-      float s[2][G];
+      it.seq = r % S;
+      it.part = r / S;
+    }
+    const int n = a.context_lens[it.seq];
+    bool bad;
+    const int nparts = seq_parts(a, n, &bad);
+    const bool special = bad || n == 0;
+    it.flags = (nparts == 1 ? kDirect : 0) | (special ? kSpecial : 0) | (bad ? kBad : 0);
+    it.tok_begin = special ? 0 : it.part * a.partition_size;
+    it.tok_end = special ? 0 : min(n, it.tok_begin + a.partition_size);
+    const int ngroups = (it.tok_end - it.tok_begin + GT - 1) / GT;
+    it.nk = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
+    it.npad = it.nk <= NBUF ? NBUF : (it.nk + NBUF - 1) & ~(NBUF - 1);
+    return it;
+  };
+  // First item at or after k in this workgroup's stride that is not empty.
+  auto seek = [&](int k) __attribute__((always_inline)) {
+    if constexpr (!LIST) {
+      for (; k < total; k += grid) {
+        const int r = k / Hkv;
+        bool bad;
+        if (r / S < seq_parts(a, a.context_lens[r % S], &bad)) break;
+      }
+    }
+    return uni(k);
+  };
+
+  const int k0 = seek(static_cast<int>(blockIdx.x));
+  if (k0 >= total) return;
+  Item cur = decode(k0);
+  Item nxt = cur;
+  {
+    const int kn = seek(k0 + grid);
+    if (kn < total) nxt = decode(kn);
+    nxt.k = kn;
+  }
+
+  // ---- loads ---------------------------------------------------------------
+  const char* kcache = static_cast<const char*>(a.k_cache);
+  const char* vcache = static_cast<const char*>(a.v_cache);
+
+  // Query rows of the item's KV head as the QK B operand: lane (m16, kq) holds
+  // bytes [64 s + 16 kq, +16) of head m16 (zeros for heads >= G).
+  auto load_query = [&](uint4 (&q)[NQ], const Item& it) __attribute__((always_inline)) {
+    const char* base =
+        static_cast<const char*>(a.q) + (static_cast<size_t>(it.seq) * Hkv * G + static_cast<size_t>(it.kvh) * G) * R;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(base, G * R);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+    for (int s = 0; s < NQ; ++s) {
+      const uint4 v = bload16<0>(rq, m16 * R + 16 * kq, 64 * s);
+      q[s] = make_uint4(v.x ^ a.q_sign, v.y ^ a.q_sign, v.z ^ a.q_sign, v.w ^ a.q_sign);
+    }
+  };
+
+  // Ring position p counted from the current item's start: positions past its
+  // end belong to the next item (or to none after the last).  A position's
+  // group gives the K and V resources of its tile (size 0 when the position
+  // holds no group) and its first row in the tile (always 0 for bf16).
+  struct Target {
+    __amdgpu_buffer_rsrc_t kr, vr;
+    int row0;
+    bool poison;
+  };
+  struct Where {
+    int seq, kvh, tok, valid;  // tok: the group's first token (or the item's first)
+  };
+  auto where = [&](int p, bool has_next) __attribute__((always_inline)) {
+    const bool in_cur = p < cur.npad;
+    const int i = in_cur ? p : p - cur.npad;
+    const int nk = in_cur ? cur.nk : (has_next ? nxt.nk : 0);
+    const int tb = in_cur ? cur.tok_begin : nxt.tok_begin;
+    Where w;
+    w.seq = in_cur ? cur.seq : nxt.seq;
+    w.kvh = in_cur ? cur.kvh : nxt.kvh;
+    w.valid = i < nk;
+    w.tok = w.valid ? tb + GT * (wave + kWaves * i) : tb;
+    return w;
+  };
+  auto table_entry = [&](const Where& w) __attribute__((always_inline)) {
+    return a.block_tables[static_cast<size_t>(w.seq) * a.max_blocks + w.tok / B];
+  };
+  auto make_target = [&](const Where& w, int id) __attribute__((always_inline)) {
+    Target T;
+    const bool oob = static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks);
+    const size_t off = (static_cast<size_t>(oob ? 0 : id) * Hkv + w.kvh) * TILE;
+    const int bytes = w.valid ? TILE : 0;
+    T.kr = make_rsrc(kcache + off, bytes);
+    T.vr = make_rsrc(vcache + off, bytes);
+    T.row0 = kBF16 ? 0 : w.tok % B;
+    T.poison = w.valid && oob;
+    return T;
+  };
+  // K, QK A operand: lane (m16, kq) = token row m16 of QK tile t, key bytes
+  // [64 s + 16 kq, +16), which is the 16-byte piece 4 s + kq.
+  const int koff = (kq * B + m16) * 16;  // lane part of a key load
+  auto load_keys = [&](uint4 (&kb)[NT][KS], const Target& T) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float x = 0.0f;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int i = 0; i < NP; ++i) x = dot16(DT{}, q[h * NP + i], kb[hh * NP + i], x);
-          s[hh][h] = sum8(x);
-        }
-      if (t_first + kGroup > tok_end) {
+      for (int s = 0; s < KS; ++s) kb[t][s] = bload16<kLoadNT>(T.kr, koff, (4 * s * B + T.row0 + 16 * t) * 16);
+  };
+  // V, PV A operand: lane (m16, kq) = head-dimension row 16 dt + m16 and the
+  // tokens its PV form needs (bf16 B = 16: 4 kq .. 4 kq + 3; bf16 B = 32:
+  // 8 kq .. 8 kq + 7; fp32: 4 kq .. 4 kq + 3 of the group).
+  const int voff = (m16 * B + (kBF16 && B == 32 ? 8 : 4) * kq) * Gm::kItem;  // lane part of a value load
+  auto load_values = [&](uint32_t (&vb)[NDT][VW], const Target& T) __attribute__((always_inline)) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          if (t_first + hh * 8 + l8 >= tok_end) {
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int soff = (16 * dt * B + T.row0) * Gm::kItem;
+      if constexpr (VW == 2) {
+        const uint2 v = bload8<kLoadNT>(T.vr, voff, soff);
+        vb[dt][0] = v.x;
+        vb[dt][1] = v.y;
+      } else {
+        const uint4 v = bload16<kLoadNT>(T.vr, voff, soff);
+        vb[dt][0] = v.x;
+        vb[dt][1] = v.y;
+        vb[dt][2] = v.z;
+        vb[dt][3] = v.w;
+      }
+    }
+  };
+
+  // The next item's query is prefetched into registers when it is small (up
+  // to 16 VGPRs); otherwise it is loaded when the item starts.
+  constexpr bool kPrefetchQ = NQ <= 4;
+  uint4 q_cur[NQ], q_nxt[kPrefetchQ ? NQ : 1];
+  load_query(q_cur, cur);
+  if constexpr (kPrefetchQ) load_query(q_nxt, nxt.k < total ? nxt : cur);
+
+  uint4 kb[NBUF][NT][KS];
+  uint32_t vb[NBUF][NDT][VW];
+  bool pois_cur = false, pois_nxt = false;
+  // The ring starts with positions 0 .. NBUF-1 of the first item.
 #pragma unroll
-            for (int h = 0; h < G; ++h) s[hh][h] = -INFINITY;
+  for (int s = 0; s < NBUF; ++s) {
+    const Where w = where(s, false);
+    const Target T = make_target(w, table_entry(w));
+    pois_cur |= T.poison;
+    load_keys(kb[s], T);
+    load_values(vb[s], T);
+  }
+  // The block id of the next refill target is fetched one step ahead.
+  int pend_id = table_entry(where(NBUF, nxt.k < total));
+
+  const float c = a.c;
+  for (;;) {
+    f32x4_t acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;
+    const bool has_next = nxt.k < total;
+
+    for (int i0 = 0; i0 < cur.npad; i0 += NBUF) {
+#pragma unroll
+      for (int s = 0; s < NBUF; ++s) {
+        const int i = i0 + s;
+        const bool valid = i < cur.nk;
+        const int t_first = cur.tok_begin + GT * (wave + kWaves * i);
+
+        // Refill target of this slot: ring position i + NBUF.
+        const int ti = i + NBUF;
+        const Target T = make_target(where(ti, has_next), pend_id);
+        pend_id = table_entry(where(ti + 1, has_next));
+        if (ti < cur.npad)
+          pois_cur |= T.poison;
+        else
+          pois_nxt |= T.poison;
+
+        // QK^T on the matrix cores: sc[t] rows = tokens 16 t + 4 kq + r, column = head m16.
+        f32x4_t sc[NT];
+        if (valid) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            sc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+              const uint4 kv = kb[s][t][st], qv = q_cur[st];
+              if constexpr (kBF16) {
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qv), sc[t], 0, 0, 0);
+              } else {
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.x), __uint_as_float(qv.x), sc[t], 0, 0, 0);
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.y), __uint_as_float(qv.y), sc[t], 0, 0, 0);
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.z), __uint_as_float(qv.z), sc[t], 0, 0, 0);
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.w), __uint_as_float(qv.w), sc[t], 0, 0, 0);
+              }
+            }
           }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) m[h] = fmaxf(m[h], fmaxf(s[0][h], s[1][h]));
-      if (j8 == 0) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int h = 0; h < G; ++h) lg[(hh * 8 + l8) * G + h] = s[hh][h];
-      }
-    }
-  }
-
-  // Wave-uniform per-head maxima (raw logits) from the lane state.
-  __device__ __forceinline__ static void max_finish(const float (&m)[NM], float (&lmax)[G]) {
-    if constexpr (QKM) {
-      const float x = max_xor32(max_xor16(m[0]));  // lane l: maximum of head l % 16
-#pragma unroll
-      for (int h = 0; h < G; ++h) lmax[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), h));
-    } else {
-#pragma unroll
-      for (int h = 0; h < G; ++h) lmax[h] = max_xor32(max_xor16(fmaxf(m[h], ror<8>(m[h]))));
-    }
-  }
-
-  // acc[h][e] += p[t][h] * V[t][e] over the group's tokens before tok_end.
-  __device__ __forceinline__ static void pv_group(const uint4 (&vb)[NB16], const float* pg, int t_first, int tok_end,
-                                  float (&acc)[G][E], int lane) {
-    const int rv = lane / LR;
-#pragma unroll
-    for (int jj = 0; jj < NB16; ++jj) {
-      const int tl = jj * TPL + rv;  // token within the group
-      if (t_first + tl < tok_end) {
-        float v[E];
-        widen16(DT{}, vb[jj], v);
-        const float* pp = pg + tl * G;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = pp[h];
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
         }
-      }
-    }
-  }
-};
+        load_keys(kb[s], T);  // the slot's keys are consumed: refill
+        __builtin_amdgcn_sched_barrier(0);
 
-// ---------------------------------------------------------------------------
-// Softmax of one batch and the workgroup merge, shared by both kernels.
-// ---------------------------------------------------------------------------
+        if (valid) {
+          if (t_first + GT > cur.tok_end) {
+            // Tokens past the end: logit -inf and value 0 (the cache may hold anything there).
+            const int rel = cur.tok_end - t_first;  // valid tokens of the group
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (16 * t + 4 * kq + r >= rel) sc[t][r] = -INFINITY;
+            if constexpr (kBF16) {
+              const int first = (VW == 2 ? 4 : 8) * kq;
+              uint32_t mask[VW];
+#pragma unroll
+              for (int w = 0; w < VW; ++w)
+                mask[w] = (first + 2 * w < rel ? 0x0000ffffu : 0u) | (first + 2 * w + 1 < rel ? 0xffff0000u : 0u);
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int w = 0; w < VW; ++w) vb[s][dt][w] &= mask[w];
+            } else {
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int w = 0; w < VW; ++w)
+                  if (4 * kq + w >= rel) vb[s][dt][w] = 0u;
+            }
+          }
+          // Online softmax, per head (lane column m16).
+          float gm = -INFINITY;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) gm = fmaxf(gm, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
+          gm = max_xor32(max_xor16(gm));
+          const float m_new = fmaxf(m_run, gm * c);
+          if (__ballot(m_new > m_run)) {
+            const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              sc[t][r] = __builtin_amdgcn_exp2f(fmaf(sc[t][r], c, -m_run));
+              l_run += sc[t][r];
+            }
 
-// Folds a batch's maxima into the running state, rescales acc and l when an
-// earlier batch exists, and turns the batch's nlog logits in reg into
-// probabilities.  wm: this wave's slot of the per-wave maxima (LDS).
-template <int G, int E>
-__device__ __forceinline__ void softmax_batch(float* reg, int nlog, const float (&lmax)[G], float c, bool first,
-                                              float (&m_run)[G], float& m_mine_run, float& l_mine,
-                                              float (&acc)[G][E], float* wm, int lane) {
-  float m_new[G];
+          // PV on the matrix cores: acc[dt] rows = dims 16 dt + 4 kq + r, column = head m16.
+          if constexpr (!kBF16) {
+            // fp32: QK output register r of lane (kq, head) is the probability of token
+            // 4 kq + r, exactly the B operand of k-step r.
 #pragma unroll
-  for (int h = 0; h < G; ++h) m_new[h] = fmaxf(m_run[h], lmax[h] * c);
-  if (lane == 0) {
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int h = 0; h < G; ++h) wm[h] = m_new[h];
-  }
-  wave_lds_sync();
-  const float m_mine = wm[lane % G];
-  if (first) {
+              for (int r = 0; r < 4; ++r)
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb[s][dt][r]), sc[0][r], acc[dt], 0, 0, 0);
+          } else {
+            typedef float f2_t __attribute__((ext_vector_type(2)));
+            typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+            auto hi_bits = [](float p) __attribute__((always_inline)) { return __float_as_uint(p) & 0xffff0000u; };
+            auto pack_hi = [&](float x, float y) __attribute__((always_inline)) {
+              return (hi_bits(x) >> 16) | hi_bits(y);
+            };
+            auto pack_lo = [&](float x, float y) __attribute__((always_inline)) {
+              const f2_t l = {x - __uint_as_float(hi_bits(x)), y - __uint_as_float(hi_bits(y))};
+              return __builtin_bit_cast(uint32_t, __builtin_convertvector(l, b2_t));
+            };
+            if constexpr (VW == 2) {
+              // B = 16: 16x16x16 steps, k-slice kq = tokens 4 kq + r (r < 4): the QK
+              // output registers of the lane, once as hi and once as lo.
+              typedef short s4_t __attribute__((ext_vector_type(4)));
+              const u32x2_t ph = {pack_hi(sc[0][0], sc[0][1]), pack_hi(sc[0][2], sc[0][3])};
+              const u32x2_t pl = {pack_lo(sc[0][0], sc[0][1]), pack_lo(sc[0][2], sc[0][3])};
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+              for (int dt = 0; dt < NDT; ++dt) {
+                const u32x2_t av = {vb[s][dt][0], vb[s][dt][1]};
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, av),
+                                                                    __builtin_bit_cast(s4_t, ph), acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, av),
+                                                                    __builtin_bit_cast(s4_t, pl), acc[dt], 0, 0, 0);
+              }
+            } else {
+              // B = 32: k-slice kq = tokens 8 kq .. 8 kq + 7.  Two lane swaps move the QK
+              // rows (tokens 4 kq' + r of tiles 0 and 1) into that order:
+              // x[r] = token 8 kq + r, y[r] = token 8 kq + 4 + r.
+              float x[4], y[4];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
-  } else {
+              for (int r = 0; r < 4; ++r) {
+                const auto s32 =
+                    __builtin_amdgcn_permlane32_swap(__float_as_uint(sc[0][r]), __float_as_uint(sc[1][r]), false, false);
+                const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+                x[r] = __uint_as_float(s16[0]);
+                y[r] = __uint_as_float(s16[1]);
+              }
+              const u32x4_t bh = {pack_hi(x[0], x[1]), pack_hi(x[2], x[3]), pack_hi(y[0], y[1]), pack_hi(y[2], y[3])};
+              const u32x4_t bl = {pack_lo(x[0], x[1]), pack_lo(x[2], x[3]), pack_lo(y[0], y[1]), pack_lo(y[2], y[3])};
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float alpha = m_run[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - m_new[h]);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
-    }
-    l_mine *= m_mine_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_mine_run - m_mine);
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) m_run[h] = m_new[h];
-  m_mine_run = m_mine;
-  for (int e = lane; e < nlog; e += kWave) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(reg[e], c, -m_mine));
-    reg[e] = p;
-    l_mine += p;
-  }
-  wave_lds_sync();
-}
-
-template <int W, int RF, int G>
-struct MergeShared {
-  float region[W][RF];  // wave-private: logits, probabilities, then partial output
-  float wm[W][G];       // per-wave maximum (scaled, exp2 domain)
-  float wl[W][G];       // per-wave sum of probabilities
-};
-
-// Combine lanes, then waves; write the item's output rows (one partition) or
-// its partials.  Ends with a barrier so the regions can be reused.  An item
-// with fill set (an empty or invalid sequence) writes zeros, or NaN
-// when bad, instead.
-template <class DT, int D, int G, class SH>
-__device__ __forceinline__ void merge_item(const AttnArgs& a, SH& sh, float (&acc)[G][Geo<DT, D, G>::E], float l_mine,
-                                           bool poisoned, int seq, int kvh, int part, bool direct, bool fill = false,
-                                           bool bad = false) {
-  using Gm = Geo<DT, D, G>;
-  constexpr int E = Gm::E, LR = Gm::LR, W = Gm::W, kThreads = Gm::kThreads;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: keeps per-wave math scalar
-  l_mine = sum_mod<G>(l_mine);
-  if (poisoned) l_mine = __builtin_nanf("");
-  float* reg = sh.region[wave];
-  // One head at a time keeps the cross-lane temporaries few: the next item's
-  // keys already occupy the ring registers here.
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float x = sum_mod<LR>(acc[h][e]);
-      if (lane < LR) reg[h * D + (lane % LR) * E + e] = poisoned ? __builtin_nanf("") : x;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (lane < G) sh.wl[wave][lane] = l_mine;  // sh.wm[wave] already holds the final maxima
-  __syncthreads();
-  const int Hq = a.num_kv_heads * G;
-  float* out_rows = a.out + (static_cast<size_t>(seq) * Hq + static_cast<size_t>(kvh) * G) * D;
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int h = i / D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, sh.wm[w][h]);
-    float sa = 0.0f, sl = 0.0f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float wt = __builtin_amdgcn_exp2f(sh.wm[w][h] - M);  // 0 for a wave that saw no token
-      sa = fmaf(wt, sh.region[w][i], sa);
-      sl = fmaf(wt, sh.wl[w][h], sl);
-    }
-    if (fill) {
-      out_rows[i] = bad ? __builtin_nanf("") : 0.0f;
-    } else if (direct) {
-      out_rows[i] = sa / sl;
-    } else {
-      const size_t row = (static_cast<size_t>(seq) * Hq + static_cast<size_t>(kvh) * G + h) * a.max_parts + part;
-      a.ws_acc[row * D + i % D] = sa;
-      if (i % D == 0) {
-        a.ws_m[row] = M;
-        a.ws_l[row] = sl;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// Rows of an empty (zeros) or invalid (NaN) sequence.
-template <int D, int G, int kThreads>
-__device__ __forceinline__ void fill_rows(const AttnArgs& a, int seq, int kvh, bool bad) {
-  float* out_rows = a.out + (static_cast<size_t>(seq) * a.num_kv_heads * G + static_cast<size_t>(kvh) * G) * D;
-  const float fill = bad ? __builtin_nanf("") : 0.0f;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) out_rows[i] = fill;
-}
-
-// Block ids of this wave's groups j < nk, counted from the table entry bt of
-// the first group of the batch: lane j holds group j's id, lanes >= nk the id
-// of the batch's first entry (a valid address for the unused ring slots).
-// Out-of-range ids become 0; one read by a lane < nk sets *poisoned
-// (wave-uniform).  The load is unconditional: a load behind a branch makes
-// the compiler wait for every earlier load at the join.
-template <int W>
-__device__ __forceinline__ int load_ids(const AttnArgs& a, const int32_t* bt, int nk, int wave, int lane,
-                                        bool* poisoned) {
-  const int tok = lane < nk ? (wave + lane * W) * kGroup : 0;
-  int id = bt[tok / a.block_size];
-  const bool oob = static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks);
-  *poisoned = __ballot(oob && lane < nk) != 0;
-  return oob ? 0 : id;
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 1: one workgroup per item, any partition size.
-// ---------------------------------------------------------------------------
-template <class DT, int D, int G, bool QKM>
-__global__ __launch_bounds__((Geo<DT, D, G>::kThreads)) __attribute__((amdgpu_waves_per_eu(Geo<DT, D, G>::kMinWaves)))
-void paged_decode_items(AttnArgs a) {
-  using Gm = Geo<DT, D, G>;
-  using O = Ops<DT, D, G, QKM>;
-  constexpr int E = Gm::E, R = Gm::R, NB16 = Gm::NB16, NBUF = Gm::NBUF, W = Gm::W;
-  __shared__ MergeShared<W, Gm::RF, G> sh;
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: keeps per-wave math scalar
-  const int Hkv = a.num_kv_heads;
-  const int kvh = blockIdx.x % Hkv;
-  const int rest = blockIdx.x / Hkv;
-  const int seq = rest % a.num_seqs;
-  const int part = rest / a.num_seqs;
-  const int B = a.block_size;
-
-  const int n_raw = a.context_lens[seq];
-  bool bad_len;
-  const int nparts = seq_parts(a, n_raw, &bad_len);
-  if (part >= nparts) return;
-  if (bad_len || n_raw == 0) {
-    fill_rows<D, G, Gm::kThreads>(a, seq, kvh, bad_len);
-    return;
-  }
-  const int tok_begin = part * a.partition_size;
-  const int tok_end = min(n_raw, tok_begin + a.partition_size);
-  const int ngroups = (tok_end - tok_begin + kGroup - 1) / kGroup;
-  const int nk = wave < ngroups ? (ngroups - wave + W - 1) / W : 0;  // this wave's groups
-
-  const int32_t* bt = a.block_tables + static_cast<size_t>(seq) * a.max_blocks + tok_begin / B;
-  const char* kbase = static_cast<const char*>(a.k_cache) + static_cast<size_t>(kvh) * B * R;
-  const char* vbase = static_cast<const char*>(a.v_cache) + static_cast<size_t>(kvh) * B * R;
-  const char* qrow =
-      static_cast<const char*>(a.q) + (static_cast<size_t>(seq) * Hkv * G + static_cast<size_t>(kvh) * G) * R;
-  const size_t block_stride = static_cast<size_t>(Hkv) * B * R;
-  float* reg = sh.region[wave];
-
-  float m_run[G];
-  float acc[G][E];
-  float l_mine = 0.0f;
-  float m_mine_run = -INFINITY;
-  bool poisoned = false;
-#pragma unroll
-  for (int h = 0; h < G; ++h) m_run[h] = -INFINITY;
-
-  // Batches of NBUF groups; group b0 + j of this wave is partition group
-  // wave + (b0 + j) * W.  A wave without groups still runs one empty batch so
-  // that its state is defined.
-  for (int b0 = 0; b0 < nk || b0 == 0; b0 += NBUF) {
-    const int nb = min(NBUF, nk - b0);
-    bool pois;
-    const int idv = load_ids<W>(a, bt + (b0 * W * kGroup) / B, nb, wave, lane, &pois);
-    poisoned |= pois;
-    // Ring slot j >= nb repeats slot 0's addresses (the batch's first entry,
-    // row 0, when the wave has no group), so every load is issued on every
-    // path: a load behind a branch makes the compiler wait for all earlier
-    // loads where the paths join.
-    auto src = [&](int j) __attribute__((always_inline)) { return j < nb ? j : 0; };
-    auto row = [&](int j) __attribute__((always_inline)) {
-      return nb > 0 ? ((wave + (b0 + src(j)) * W) * kGroup) % B : 0;
-    };
-    auto t_first = [&](int j) __attribute__((always_inline)) { return tok_begin + (wave + (b0 + j) * W) * kGroup; };
-    auto tile = [&](int j) __attribute__((always_inline)) {
-      return static_cast<size_t>(__builtin_amdgcn_readlane(idv, src(j))) * block_stride;
-    };
-
-    // The query first: the load counter is in order, so the first group's
-    // logits wait only for it and that group's keys.
-    uint4 q[O::NQ];
-    O::load_query(q, qrow, a.q_sign, lane);
-    uint4 buf[NBUF][NB16];
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j) O::load_keys(buf[j], kbase + tile(j), row(j), B, lane);
-    float mstate[O::NM];
-    O::max_init(mstate);
-    {
-#pragma unroll
-      for (int j = 0; j < NBUF; ++j) {
-        if (j < nb) O::qk_group(q, buf[j], reg + j * kGroup * G, t_first(j), tok_end, mstate, lane);
-        O::load_values(buf[j], vbase + tile(j), row(j), lane);  // refill the consumed slot
+              for (int dt = 0; dt < NDT; ++dt) {
+                const u32x4_t av = {vb[s][dt][0], vb[s][dt][1], vb[s][dt][2], vb[s][dt][3]};
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                  __builtin_bit_cast(bf16x8_t, bh), acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                  __builtin_bit_cast(bf16x8_t, bl), acc[dt], 0, 0, 0);
+              }
+            }
+          }
+        }
+        load_values(vb[s], T);  // the slot's values are consumed: refill
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    float lmax[G];
-    O::max_finish(mstate, lmax);
-    softmax_batch<G, E>(reg, max(nb, 0) * kGroup * G, lmax, a.c, b0 == 0, m_run, m_mine_run, l_mine, acc,
-                        sh.wm[wave], lane);
+
+    // ---- merge the waves' partial results ------------------------------------
+    const float l_tot = sum_xor32(sum_xor16(l_run));  // over the four token rows of each head
+    if (m16 < G) {
+      float* reg = &sh.region[wave][m16][0];
 #pragma unroll
-    for (int j = 0; j < NBUF; ++j) {
-      if (j < nb) O::pv_group(buf[j], reg + j * kGroup * G, t_first(j), tok_end, acc, lane);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int dt = 0; dt < NDT; ++dt) {
+        f32x4_t v = acc[dt];
+        if (pois_cur) v = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        *reinterpret_cast<f32x4_t*>(reg + 16 * dt + 4 * kq) = v;
+      }
+      if (kq == 0) {
+        sh.wm[wave][m16] = m_run;
+        sh.wl[wave][m16] = pois_cur ? __builtin_nanf("") : l_tot;
+      }
     }
-    wave_lds_sync();  // the next batch rewrites the region
-  }
-  merge_item<DT, D, G>(a, sh, acc, l_mine, poisoned, seq, kvh, part, nparts == 1);
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 2: persistent workgroups over the item list, one ring batch per item.
-// ---------------------------------------------------------------------------
-template <int W, int RF, int G>
-struct PersistShared : MergeShared<W, RF, G> {
-  int32_t psum[kMaxPersistentSeqs + 1];  // prefix sums of partition counts
-};
-
-struct Item {
-  int seq, kvh, part, n, nparts, tok_begin, tok_end, nk;
-  bool special, bad;
-};
-
-template <class DT, int D, int G, bool QKM>
-__global__ __launch_bounds__((Geo<DT, D, G>::kThreads)) __attribute__((amdgpu_waves_per_eu(Geo<DT, D, G>::kMinWaves)))
-void paged_decode_persistent(AttnArgs a) {
-  using Gm = Geo<DT, D, G>;
-  using O = Ops<DT, D, G, QKM>;
-  constexpr int E = Gm::E, R = Gm::R, NB16 = Gm::NB16, NBUF = Gm::NBUF, W = Gm::W;
-  __shared__ PersistShared<W, Gm::RF, G> sh;
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: keeps per-wave math scalar
-  const int S = a.num_seqs;
-  const int Hkv = a.num_kv_heads;
-  const int B = a.block_size;
-  const size_t block_stride = static_cast<size_t>(Hkv) * B * R;
-
-  // Item list: prefix sums of the partition counts (wave 0 scans; S <= 4096).
-  for (int s = tid; s < S; s += Gm::kThreads) {
-    bool bad;
-    sh.psum[s + 1] = seq_parts(a, a.context_lens[s], &bad);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int chunk = (S + kWave - 1) / kWave;
-    const int lo = lane * chunk, hi = min(S, lo + chunk);
-    int run = 0;
-    for (int i = lo; i < hi; ++i) run += sh.psum[i + 1];
-    int incl = run;
+    __syncthreads();
+    {
+      const int Hq = Hkv * G;
+      float* out_rows = a.out + (static_cast<size_t>(cur.seq) * Hq + static_cast<size_t>(cur.kvh) * G) * D;
+      const bool direct = cur.flags & kDirect;
+      for (int e = tid; e < G * D; e += kThreads) {
+        const int h = e / D, d = e % D;
+        float M = -INFINITY;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
-    }
-    int base = incl - run;
-    for (int i = lo; i < hi; ++i) {
-      base += sh.psum[i + 1];
-      sh.psum[i + 1] = base;
-    }
-    if (lane == 0) sh.psum[0] = 0;
-  }
-  __syncthreads();
-  const int total = sh.psum[S] * Hkv;
-  int k = blockIdx.x;
-  if (k >= total) return;
-
-  auto decode = [&](int kk) __attribute__((always_inline)) {
-    Item it;
-    it.kvh = kk % Hkv;
-    const int pidx = kk / Hkv;
-    // LDS reads land in vector registers; readfirstlane marks them
-    // wave-uniform so that every branch on the item stays a scalar branch.
-    int lo = 0, hi = S;  // psum[lo] <= pidx < psum[lo + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(sh.psum[mid]) <= pidx)
-        lo = mid;
-      else
-        hi = mid;
-    }
-    it.seq = lo;
-    it.part = pidx - __builtin_amdgcn_readfirstlane(sh.psum[lo]);
-    it.n = a.context_lens[lo];
-    it.nparts = seq_parts(a, it.n, &it.bad);
-    it.special = it.bad || it.n == 0;
-    it.tok_begin = it.part * a.partition_size;
-    it.tok_end = min(it.n, it.tok_begin + a.partition_size);
-    const int ngroups = it.special ? 0 : (it.tok_end - it.tok_begin + kGroup - 1) / kGroup;
-    it.nk = wave < ngroups ? (ngroups - wave + W - 1) / W : 0;
-    return it;
-  };
-  auto ktile = [&](const Item& it, int idv, int j) __attribute__((always_inline)) {
-    return static_cast<const char*>(a.k_cache) + static_cast<size_t>(it.kvh) * B * R +
-           static_cast<size_t>(__builtin_amdgcn_readlane(idv, j < it.nk ? j : 0)) * block_stride;
-  };
-  auto vtile = [&](const Item& it, int idv, int j) __attribute__((always_inline)) {
-    return static_cast<const char*>(a.v_cache) + static_cast<size_t>(it.kvh) * B * R +
-           static_cast<size_t>(__builtin_amdgcn_readlane(idv, j < it.nk ? j : 0)) * block_stride;
-  };
-  // Ring slot j >= nk repeats slot 0's addresses (the item's first entry,
-  // row 0, when the wave has no group): every load is issued on every path.
-  auto src = [&](const Item& it, int j) __attribute__((always_inline)) { return j < it.nk ? j : 0; };
-  auto row = [&](const Item& it, int j) __attribute__((always_inline)) {
-    return it.nk > 0 ? ((wave + src(it, j) * W) * kGroup) % B : 0;
-  };
-  auto t_first = [&](const Item& it, int j) __attribute__((always_inline)) { return it.tok_begin + (wave + j * W) * kGroup; };
-  auto table = [&](const Item& it) __attribute__((always_inline)) {
-    return a.block_tables + static_cast<size_t>(it.seq) * a.max_blocks + it.tok_begin / B;
-  };
-  auto qrow = [&](const Item& it) __attribute__((always_inline)) {
-    return static_cast<const char*>(a.q) +
-           (static_cast<size_t>(it.seq) * Hkv * G + static_cast<size_t>(it.kvh) * G) * R;
-  };
-  float* reg = sh.region[wave];
-
-  Item cur = decode(k);
-  bool pois_cur;
-  int idv_cur = load_ids<W>(a, table(cur), cur.nk, wave, lane, &pois_cur);
-  uint4 q_cur[O::NQ];
-  O::load_query(q_cur, qrow(cur), a.q_sign, lane);
-  uint4 buf[NBUF][NB16];
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.wm[w][h]);
+        float sa = 0.0f, sl = 0.0f;
 #pragma unroll
-  for (int j = 0; j < NBUF; ++j) O::load_keys(buf[j], ktile(cur, idv_cur, j), row(cur, j), B, lane);
-
-  for (;;) {
-    // The next item: its ids and query are fetched now, its keys go into ring
-    // slots as the current item's values are consumed.  After the last item
-    // the current one stands in for it, so the loads stay unconditional.
-    const int kn = k + static_cast<int>(gridDim.x);
-    const bool has_next = kn < total;
-    Item nxt = cur;
-    if (has_next) nxt = decode(kn);
-    bool pois_next;
-    const int idv_next = load_ids<W>(a, table(nxt), nxt.nk, wave, lane, &pois_next);
-    uint4 q_next[O::NQ];
-    O::load_query(q_next, qrow(nxt), a.q_sign, lane);
-
-    // An empty or invalid item has no groups; it runs the same path and its
-    // merge writes zeros or NaN.
-    float mstate[O::NM];
-    O::max_init(mstate);
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j) {
-      if (j < cur.nk) O::qk_group(q_cur, buf[j], reg + j * kGroup * G, t_first(cur, j), cur.tok_end, mstate, lane);
-      O::load_values(buf[j], vtile(cur, idv_cur, j), row(cur, j), lane);  // refill the consumed slot
-      __builtin_amdgcn_sched_barrier(0);
+        for (int w = 0; w < kWaves; ++w) {
+          const float wt = __builtin_amdgcn_exp2f(sh.wm[w][h] - M);  // 0 for a wave that saw no token
+          sa = fmaf(wt, sh.region[w][h][d], sa);
+          sl = fmaf(wt, sh.wl[w][h], sl);
+        }
+        if (cur.flags & kSpecial) {
+          out_rows[e] = (cur.flags & kBad) ? __builtin_nanf("") : 0.0f;
+        } else if (direct) {
+          out_rows[e] = sa / sl;
+        } else {
+          const size_t row =
+              (static_cast<size_t>(cur.seq) * Hq + static_cast<size_t>(cur.kvh) * G + h) * a.max_parts + cur.part;
+          a.ws_acc[row * D + d] = sa;
+          if (d == 0) {
+            a.ws_m[row] = M;
+            a.ws_l[row] = sl;
+          }
+        }
+      }
     }
-    float lmax[G], m_run[G], acc[G][E];
-    float l_mine = 0.0f, m_mine_run = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < G; ++h) m_run[h] = -INFINITY;
-    O::max_finish(mstate, lmax);
-    softmax_batch<G, E>(reg, cur.nk * kGroup * G, lmax, a.c, true, m_run, m_mine_run, l_mine, acc, sh.wm[wave], lane);
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j) {
-      if (j < cur.nk) O::pv_group(buf[j], reg + j * kGroup * G, t_first(cur, j), cur.tok_end, acc, lane);
-      O::load_keys(buf[j], ktile(nxt, idv_next, j), row(nxt, j), B, lane);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    merge_item<DT, D, G>(a, sh, acc, l_mine, pois_cur, cur.seq, cur.kvh, cur.part, cur.nparts == 1, cur.special,
-                         cur.bad);
+    __syncthreads();
+
     if (!has_next) break;
+    // Advance: the ring already holds the next item's first NBUF positions.
     cur = nxt;
-    idv_cur = idv_next;
-    pois_cur = pois_next;
+    pois_cur = pois_nxt;
+    pois_nxt = false;
+    if constexpr (kPrefetchQ) {
 #pragma unroll
-    for (int i = 0; i < O::NQ; ++i) q_cur[i] = q_next[i];
-    k = kn;
+      for (int s = 0; s < NQ; ++s) q_cur[s] = q_nxt[s];
+    } else {
+      load_query(q_cur, cur);
+    }
+    {
+      const int kn = seek(cur.k + grid);
+      nxt = cur;
+      if (kn < total) nxt = decode(kn);
+      nxt.k = kn;
+    }
+    if constexpr (kPrefetchQ) load_query(q_nxt, nxt.k < total ? nxt : cur);
+    // Ring position NBUF of the new item: when the item has only NBUF
+    // positions it is the following item's first group, which the old item's
+    // look-ahead could not know.
+    pend_id = table_entry(where(NBUF, nxt.k < total));
   }
 }
 
@@ -738,10 +642,10 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t 
   return p;
 }
 
-// Workgroups of a kernel that fit the whole device at once, cached per
-// device and per instantiation (Tag makes each kernel its own cache).
-template <class Tag, class K>
-int resident_workgroups(K kernel, int threads) {
+// Workgroups of a kernel that fit the whole device at once, cached per device
+// and per instantiation (each kernel type gets its own static cache).
+template <class K, K kernel>
+int resident_workgroups() {
   static std::mutex mu;
   static int cache[64] = {0};
   int dev = 0;
@@ -750,44 +654,46 @@ int resident_workgroups(K kernel, int threads) {
   if (cache[dev] == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) return 0;
     cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
   }
   return cache[dev];
 }
 
-template <class DT, int D, int G>
-hipError_t launch_attention_g(const AttnArgs& a, int64_t items, hipStream_t stream) {
-  using Gm = Geo<DT, D, G>;
-  constexpr bool QKM = kUseMfmaQK<DT, G>;
-  if (a.partition_size <= Gm::P1 && a.num_seqs <= kMaxPersistentSeqs) {
-    auto kernel = paged_decode_persistent<DT, D, G, QKM>;
-    const int fill = resident_workgroups<Ops<DT, D, G, QKM>>(kernel, Gm::kThreads);
-    if (fill <= 0) return hipErrorInvalidValue;
-    const int64_t grid = items < fill ? items : fill;
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(Gm::kThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((paged_decode_items<DT, D, G, QKM>), dim3(static_cast<unsigned>(items)), dim3(Gm::kThreads),
-                       0, stream, a);
-  }
+template <class DT, int D, int G, int B, bool LIST>
+hipError_t launch_kernel(const AttnArgs& a, hipStream_t stream) {
+  using K = void (*)(AttnArgs);
+  constexpr K kernel = paged_decode_kernel<DT, D, G, B, LIST>;
+  const int fill = resident_workgroups<K, kernel>();
+  if (fill <= 0) return hipErrorInvalidValue;
+  const int grid = a.total_items < fill ? a.total_items : fill;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
+template <class DT, int D, int G>
+hipError_t launch_attention_g(const AttnArgs& a, hipStream_t stream) {
+  const bool list = a.num_seqs <= kMaxListedSeqs;
+  if (a.block_size == 16)
+    return list ? launch_kernel<DT, D, G, 16, true>(a, stream) : launch_kernel<DT, D, G, 16, false>(a, stream);
+  return list ? launch_kernel<DT, D, G, 32, true>(a, stream) : launch_kernel<DT, D, G, 32, false>(a, stream);
+}
+
 template <class DT, int D>
-hipError_t launch_attention_d(const AttnArgs& a, int G, int64_t items, hipStream_t stream) {
+hipError_t launch_attention_d(const AttnArgs& a, int G, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_attention_g<DT, D, 1>(a, items, stream);
-    case 2: return launch_attention_g<DT, D, 2>(a, items, stream);
-    case 4: return launch_attention_g<DT, D, 4>(a, items, stream);
-    case 8: return launch_attention_g<DT, D, 8>(a, items, stream);
+    case 1: return launch_attention_g<DT, D, 1>(a, stream);
+    case 2: return launch_attention_g<DT, D, 2>(a, stream);
+    case 4: return launch_attention_g<DT, D, 4>(a, stream);
+    case 8: return launch_attention_g<DT, D, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class DT>
-hipError_t launch_attention(const AttnArgs& a, int D, int G, int64_t items, hipStream_t stream) {
-  if (D == 64) return launch_attention_d<DT, 64>(a, G, items, stream);
-  if (D == 128) return launch_attention_d<DT, 128>(a, G, items, stream);
+hipError_t launch_attention(const AttnArgs& a, int D, int G, hipStream_t stream) {
+  if (D == 64) return launch_attention_d<DT, 64>(a, G, stream);
+  if (D == 128) return launch_attention_d<DT, 128>(a, G, stream);
   return hipErrorInvalidValue;
 }
 
@@ -816,7 +722,7 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
 
   const Plan plan = make_plan(num_seqs, num_q_heads, head_dim, block_size, max_context_len, partition_size);
   const int64_t items = static_cast<int64_t>(plan.max_parts) * num_seqs * num_kv_heads;
-  if (items > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (items > INT32_MAX / 2) return PKV_ERR_INVALID_ARG;
   AttnArgs a{};
   a.out = out;
   a.q = q;
@@ -839,6 +745,7 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
   a.max_context_len = max_context_len;
   a.partition_size = plan.P;
   a.max_parts = plan.max_parts;
+  a.total_items = static_cast<int32_t>(items);
   // Softmax of scale * (q . k) in the exp2 domain.  A negative scale is folded
   // into q's sign (exact in bf16 and fp32), so the kernel scales by |scale|;
   // a zero scale becomes the smallest normal float, which leaves every
@@ -848,8 +755,8 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
   a.q_sign = scale < 0.0f ? (kv_dtype == PKV_BF16 ? BF16::kSignMask : F32::kSignMask) : 0u;
 
   if (stages & kStagePartitions) {
-    const hipError_t err = kv_dtype == PKV_BF16 ? launch_attention<BF16>(a, head_dim, G, items, stream)
-                                                : launch_attention<F32>(a, head_dim, G, items, stream);
+    const hipError_t err = kv_dtype == PKV_BF16 ? launch_attention<BF16>(a, head_dim, G, stream)
+                                                : launch_attention<F32>(a, head_dim, G, stream);
     if (err != hipSuccess) return PKV_ERR_HIP;
   }
   if ((stages & kStageReduce) && plan.max_parts > 1) {

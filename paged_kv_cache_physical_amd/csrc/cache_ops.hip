@@ -8,14 +8,19 @@ namespace pkv {
 namespace {
 
 // One thread moves 16 bytes of K and 16 bytes of V of one (token, head).
+// K tile [d / X][B][X] (X = 16 bytes): the 16-byte chunk c of a key row is
+// piece c.  V tile [d][B]: the chunk's scalars go to rows c * E .. c * E + E-1
+// of the tile, column `off`.
+template <class T>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const char* __restrict__ k_new,
                                                                 const char* __restrict__ v_new,
                                                                 char* __restrict__ k_cache, char* __restrict__ v_cache,
                                                                 const int64_t* __restrict__ slots, int32_t num_tokens,
                                                                 int32_t num_heads, int32_t block_size, int32_t row_bytes,
                                                                 int64_t num_slots) {
+  constexpr int E = 16 / static_cast<int>(sizeof(T));  // scalars per 16-byte chunk
   const int chunks = row_bytes / 16;
-  const int pieces = row_bytes / kKeyPiece;
+  const int head_dim = chunks * E;
   const int64_t total = static_cast<int64_t>(num_tokens) * num_heads * chunks;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride) {
@@ -27,13 +32,13 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const char* __re
     if (slot < 0 || slot >= num_slots) continue;
     const int64_t blk = slot / block_size;
     const int off = static_cast<int>(slot % block_size);
-    const uint4 kv = *reinterpret_cast<const uint4*>(k_new + th * row_bytes + c * 16);
-    const uint4 vv = *reinterpret_cast<const uint4*>(v_new + th * row_bytes + c * 16);
-    const int piece = (c * 16) / kKeyPiece;
-    const int within = (c * 16) % kKeyPiece;
     const int64_t tile = blk * num_heads + h;
-    *reinterpret_cast<uint4*>(k_cache + ((tile * pieces + piece) * block_size + off) * kKeyPiece + within) = kv;
-    *reinterpret_cast<uint4*>(v_cache + (tile * block_size + off) * row_bytes + c * 16) = vv;
+    const uint4 kv = *reinterpret_cast<const uint4*>(k_new + th * row_bytes + c * 16);
+    *reinterpret_cast<uint4*>(k_cache + ((tile * chunks + c) * block_size + off) * 16) = kv;
+    const T* vs = reinterpret_cast<const T*>(v_new + th * row_bytes + c * 16);
+    T* vd = reinterpret_cast<T*>(v_cache) + (tile * head_dim + static_cast<int64_t>(c) * E) * block_size + off;
+#pragma unroll
+    for (int j = 0; j < E; ++j) vd[static_cast<int64_t>(j) * block_size] = vs[j];
   }
 }
 
@@ -106,7 +111,8 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_c
   const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (row_bytes / 16);
   const int64_t want = ceil_div64(total, 256);
   const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const char*>(k_new),
+  auto kernel = item == 4 ? reshape_and_cache_kernel<uint32_t> : reshape_and_cache_kernel<uint16_t>;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream, static_cast<const char*>(k_new),
                      static_cast<const char*>(v_new), static_cast<char*>(k_cache), static_cast<char*>(v_cache), slots,
                      num_tokens, num_kv_heads, block_size, row_bytes,
                      static_cast<int64_t>(num_blocks) * block_size);

@@ -1,14 +1,12 @@
 // Shared definitions of libpkv's gfx950 device code.
 //
 // Cache layout (fixed by pkv.h), per cache:
-//   V[num_blocks][H_kv][B][d]
-//   K[num_blocks][H_kv][d / X][B][X]   with X = 128 / bytes_per_scalar
-// A token's key row is cut into 128-byte pieces; piece p of all B tokens of a
-// block lies together.  One wave-wide 16-byte load (1 KiB) then covers piece
-// p of 8 consecutive tokens, giving each group of 8 lanes one token's piece;
-// two such loads per piece cover a 16-token group, so every lane ends up with
-// the same 16-byte columns of two tokens.  Values keep plain rows: a lane keeps
-// the same output dimensions for every token it visits.
+//   K[num_blocks][H_kv][d / X][B][X]   with X = 16 / bytes_per_scalar
+//   V[num_blocks][H_kv][d][B]
+// A token's key row is cut into 16-byte pieces and piece p of all B tokens of
+// a block lies together, so the 16 token rows of one matrix-core operand tile
+// read 4 pieces as contiguous runs; a value tile is stored transposed, one
+// row of B tokens per head dimension, which is the value operand's layout.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,12 +18,11 @@
 namespace pkv {
 
 constexpr int kWave = 64;
-constexpr int kKeyPiece = 128;  // bytes of one key piece
 
-typedef short bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 struct F32 {
   static constexpr int kItem = 4;
@@ -44,62 +41,9 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   const u32x4_t u = {v.x, v.y, v.z, v.w};
   return __builtin_bit_cast(bf16x8_t, u);
-}
-
-// Partial dot product of 16 bytes of q with 16 bytes of k, accumulated in fp32.
-__device__ __forceinline__ float dot16(BF16, const uint4& q, const uint4& k, float acc) {
-  // v_dot2_f32_bf16: two exact bf16 products added to an fp32 accumulator.
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.x), as_bf16x2(k.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.y), as_bf16x2(k.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.z), as_bf16x2(k.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w), as_bf16x2(k.w), acc, false);
-  return acc;
-}
-__device__ __forceinline__ float dot16(F32, const uint4& q, const uint4& k, float acc) {
-  acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
-  acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
-  acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
-  acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
-  return acc;
-}
-
-// Widen 16 bytes of stored values to fp32 (exact).
-__device__ __forceinline__ void widen16(BF16, const uint4& v, float* f) {
-  f[0] = __uint_as_float(v.x << 16);
-  f[1] = __uint_as_float(v.x & 0xffff0000u);
-  f[2] = __uint_as_float(v.y << 16);
-  f[3] = __uint_as_float(v.y & 0xffff0000u);
-  f[4] = __uint_as_float(v.z << 16);
-  f[5] = __uint_as_float(v.z & 0xffff0000u);
-  f[6] = __uint_as_float(v.w << 16);
-  f[7] = __uint_as_float(v.w & 0xffff0000u);
-}
-__device__ __forceinline__ void widen16(F32, const uint4& v, float* f) {
-  f[0] = __uint_as_float(v.x);
-  f[1] = __uint_as_float(v.y);
-  f[2] = __uint_as_float(v.z);
-  f[3] = __uint_as_float(v.w);
-}
-
-// DPP lane permutations inside a row of 16 lanes.
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
-}
-constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within each half-row of 8
-
-// Sum over the 8 lanes of a half-row (all lanes receive the total).
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  x += dpp<kRowHalfMirror>(x);
-  return x;
 }
 
 // Cross-row steps: lane l receives the partner value from lane l ^ 16 or

@@ -123,6 +123,23 @@ def test_ragged_boundaries():
     full_parity(w, [0, 64, 512])
 
 
+@pytest.mark.parametrize("dt,d,G,B", [("bf16", 128, 1, 16), ("bf16", 128, 8, 32), ("bf16", 64, 4, 16),
+                                       ("f32", 128, 2, 32)])
+def test_many_items_per_workgroup(dt, d, G, B):
+    # more items than the persistent grid holds: each workgroup walks several
+    # items, many shorter than one turn of its load ring, so the ring's
+    # look-ahead crosses item boundaries (into items of every length)
+    w = wl.small_decode(600, (1, 200), 2 * G, 2, d, B, dt, seed=11 + G + d + B)
+    full_parity(w, [0, 2 * B])
+
+
+def test_more_sequences_than_the_item_list_holds():
+    # above 4096 sequences the items are numbered without the LDS list and the
+    # empty ones are skipped
+    w = wl.small_decode(4200, (1, 40), 2, 1, 64, 16, "bf16", seed=21)
+    full_parity(w, [0, 16])
+
+
 @pytest.mark.parametrize("name,nsample", [("llama7b_bf16", 12), ("gqa_bf16_b16", 12), ("gqa_bf16_b32", 12),
                                           ("beam_cow_bf16", 16), ("long_bf16", 3)])
 def test_named_full_size(name, nsample):

@@ -11,11 +11,11 @@ from oracle import cache as oc
 
 @pytest.mark.parametrize("kv_dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64), ("f32", 128)])
 def test_layout_offsets(kv_dtype, d):
-    # Interface definition: V[nb][H][B][d]; K[nb][H][d/X][B][X] with X = 128 bytes / scalar size.
+    # Interface definition: K[nb][H][d/X][B][X] with X = 16 bytes / scalar size; V[nb][H][d][B].
     nb, H, B = 5, 3, 16
     k, v = oc.empty_caches(nb, H, B, d, kv_dtype)
     item = 4 if kv_dtype == "f32" else 2
-    X = 128 // item
+    X = 16 // item
     rng = np.random.default_rng(0)
     kt = wl.draw_values(rng, (1, H, d), kv_dtype)
     vt = wl.draw_values(rng, (1, H, d), kv_dtype)
@@ -26,7 +26,7 @@ def test_layout_offsets(kv_dtype, d):
     for h in range(H):
         for e in range(d):
             kidx = (((blk * H + h) * (d // X) + e // X) * B + off) * X + e % X
-            vidx = ((blk * H + h) * B + off) * d + e
+            vidx = ((blk * H + h) * d + e) * B + off
             assert kf[kidx].tobytes() == kt[0, h, e].tobytes()
             assert vf[vidx].tobytes() == vt[0, h, e].tobytes()
     # everything else is still poison
@@ -36,6 +36,11 @@ def test_layout_offsets(kv_dtype, d):
         for e in range(d):
             written_k[(((blk * H + h) * (d // X) + e // X) * B + off) * X + e % X] = True
     assert np.all(kf.view(poison.dtype)[~written_k] == poison)
+    written_v = np.zeros(vf.size, bool)
+    for h in range(H):
+        for e in range(d):
+            written_v[((blk * H + h) * d + e) * B + off] = True
+    assert np.all(vf.view(poison.dtype)[~written_v] == poison)
 
 
 def test_scatter_gather_against_slot_dictionary():

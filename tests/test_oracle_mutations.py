@@ -105,7 +105,7 @@ def test_gather_off_by_one_is_caught(monkeypatch):
         t = np.arange(n)
         blk = np.asarray(table)[t // B]
         off = (t + 1) % B
-        return k_cache[blk, :, :, off, :].reshape(n, H, npieces * X), v_cache[blk, :, off, :]
+        return k_cache[blk, :, :, off, :].reshape(n, H, npieces * X), v_cache[blk, :, :, off]
 
     pins = [t_cache.test_gather_reassembles_logical_order, t_cache.test_scatter_gather_against_slot_dictionary]
     assert not _fails_some(pins)
@@ -122,7 +122,7 @@ def test_key_piece_order_is_caught(monkeypatch):
         s = s[keep]
         # wrong: pieces reversed
         k_cache[s // B, :, :, s % B, :] = np.asarray(k_new)[keep].reshape(len(s), H, npieces, X)[:, :, ::-1, :]
-        v_cache[s // B, :, s % B, :] = np.asarray(v_new)[keep]
+        v_cache[s // B, :, :, s % B] = np.asarray(v_new)[keep]
 
     monkeypatch.setattr(oc, "scatter", bad_scatter)
     assert _fails_some([lambda: t_cache.test_layout_offsets("bf16", 128)])
