@@ -55,9 +55,11 @@ struct AttnArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_acc;  // [S][H_q][max_parts][d]
-  float* ws_m;    // [S][H_q][max_parts]   maximum logit, exp2 domain (scaled)
-  float* ws_l;    // [S][H_q][max_parts]   sum of exp2(logit - max)
+  float* ws_acc;  // [S][H_kv][max_parts][G][d]  one item's partials are one contiguous run
+  float* ws_m;    // [S][H_kv][max_parts][G]     maximum logit, exp2 domain (scaled)
+  float* ws_l;    // [S][H_kv][max_parts][G]     sum of exp2(logit - max)
+  int32_t* ws_seg;  // [S][H_kv][max_parts]      at a segment's first partition: its length in
+                    // partitions; at partition 0 of a sequence written whole: -1
   int32_t num_seqs;
   int32_t num_kv_heads;
   int32_t block_size;
@@ -67,8 +69,7 @@ struct AttnArgs {
   int32_t partition_size;  // tokens, multiple of block_size
   int32_t max_parts;
   int32_t total_items;     // max_parts * num_seqs * num_kv_heads
-  float c;                 // |scale| * log2(e) (>= FLT_MIN): logits enter exp2 as fma(s, c, -m)
-  uint32_t q_sign;         // xor mask applied to q's bits: flips its sign when scale < 0
+  float c;                 // scale * log2(e): the softmax runs on u = c * (q . k) in the exp2 domain
 };
 
 // Number of partitions of a sequence of n_raw tokens (1 for an empty or
@@ -82,6 +83,18 @@ __device__ __forceinline__ int seq_parts(const AttnArgs& a, int n_raw, bool* bad
 
 // Marks a value wave-uniform (values read from LDS land in vector registers).
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uni64(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
+}
+
+// Reads of the block tables and lengths go through the constant address space:
+// the kernel never writes them, so the compiler may use scalar loads, which
+// the vector loads' wait counter does not see.  (A vector load there makes
+// every later wait for it also wait for all the ring loads issued before.)
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int32_t ld_const(const int32_t* p, size_t i) {
+  return ((const_i32_ptr)p)[i];
+}
 
 // Buffer resource over `bytes` bytes at p; bytes = 0 turns every load into zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
@@ -121,31 +134,50 @@ struct Geo {
   static_assert(NBUF >= 2 && (NBUF & (NBUF - 1)) == 0, "ring depth");
 };
 
-// One decoded item.  Every field is wave-uniform.
+// One decoded item: a segment, i.e. partitions [part, part_end) of one
+// sequence for one KV head.  Every field is wave-uniform.
 struct Item {
-  int k;  // item index (>= total: none)
-  int seq, kvh, part;
+  int k;     // item index (>= the workgroup's end: none)
+  int next;  // the item after it in this workgroup's list
+  int seq, kvh, part, part_end;
   int tok_begin, tok_end;
   int nk;     // groups of this wave
   int npad;   // ring positions of this wave: nk rounded up to NBUF, at least NBUF
-  int flags;  // kDirect | kSpecial | kBad
+  int flags;  // kDirect | kSplitSeq | kSpecial | kBad
 };
-constexpr int kDirect = 1;   // single partition: write the output rows
-constexpr int kSpecial = 2;  // empty or invalid sequence: no groups, fill the rows
-constexpr int kBad = 4;      // invalid length: fill with NaN
+constexpr int kDirect = 1;    // the segment covers the whole sequence: write the output rows
+constexpr int kSplitSeq = 2;  // the sequence has several partitions
+constexpr int kSpecial = 4;   // empty or invalid sequence: no groups, fill the rows
+constexpr int kBad = 8;       // invalid length: fill with NaN
 
 template <int G, int D, bool LIST>
 struct Shared {
-  alignas(16) float region[kWaves][G][D + 4];  // per-wave partial output (padded rows)
-  float wm[kWaves][G];                         // per-wave running maximum (exp2 domain, scaled)
-  float wl[kWaves][G];                         // per-wave sum of probabilities
-  int32_t psum[LIST ? kMaxListedSeqs + 1 : 1]; // prefix sums of partition counts
+  struct Merge {
+    alignas(16) float region[kWaves][G][D + 4];  // per-wave partial output (padded rows)
+    float wm[kWaves][G];                         // per-wave running maximum (exp2 domain, scaled)
+    float wl[kWaves][G];                         // per-wave sum of probabilities
+  } mb[2];  // alternate items use alternate buffers: one barrier per item
+  int32_t psum[LIST ? kMaxListedSeqs + 1 : 1];   // prefix sums of partition counts
+  uint32_t csum[LIST ? kMaxListedSeqs + 1 : 1];  // prefix sums of sequence costs
 };
 
-// LIST: items are the dense list (sequence, partition, KV head) built from
-// LDS prefix sums of the partition counts (at most kMaxListedSeqs sequences).
-// Otherwise items are numbered part-major over max_parts and the empty ones
-// (partition past the sequence's end) are skipped.
+// Cost of a partition in the work split: its groups plus a fixed charge for
+// an item's start-up and merge.
+constexpr int kItemCharge = 2;
+
+// Workgroup b serves KV head b % H_kv (the grid is a multiple of H_kv), so the
+// H_kv workgroups of lane b / H_kv read the adjacent head tiles of the same
+// blocks at about the same time.
+// LIST (at most kMaxListedSeqs sequences): the (sequence, partition) pairs in
+// sequence order, from LDS prefix sums of the partition counts, are cut into
+// one contiguous run per lane, each starting where the cumulative cost
+// reaches L C / lanes (C the total), so the lanes get equal work to within
+// one partition.  A lane's run is walked one sequence at a time: an item is
+// the run's partitions of one sequence, processed as one softmax, so only a
+// sequence cut between lanes leaves partial results (one set per segment).
+// Otherwise every partition is an item: numbered part-major over max_parts,
+// dealt round-robin to the lanes, the empty ones (partition past the
+// sequence's end) skipped.
 template <class DT, int D, int G, int B, bool LIST>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_decode_kernel(AttnArgs a) {
@@ -162,87 +194,128 @@ void paged_decode_kernel(AttnArgs a) {
   const int grid = static_cast<int>(gridDim.x);
 
   // ---- items ---------------------------------------------------------------
-  int total = a.total_items;
+  const int P = a.partition_size;
+  const int full_cost = P / GT + kItemCharge;  // cost of a full partition
+  const int kvh_b = static_cast<int>(blockIdx.x) % Hkv;
+  const int lanes = grid / Hkv;
+  const int lane_b = static_cast<int>(blockIdx.x) / Hkv;
   if constexpr (LIST) {
     for (int s = tid; s < S; s += kThreads) {
       bool bad;
-      sh.psum[s + 1] = seq_parts(a, a.context_lens[s], &bad);
+      const int n = ld_const(a.context_lens, s);
+      const int np = seq_parts(a, n, &bad);
+      const int last = (bad || n == 0) ? 0 : n - (np - 1) * P;  // tokens of the last partition
+      sh.psum[s + 1] = np;
+      sh.csum[s + 1] = static_cast<uint32_t>(np - 1) * full_cost + (last + GT - 1) / GT + kItemCharge;
     }
     __syncthreads();
-    if (wave == 0) {  // scan: each lane sums a chunk, then a wave-wide scan of the chunk sums
+    if (wave < 2) {  // wave 0 scans the counts, wave 1 the costs: a chunk per lane, then a wave-wide scan
+      uint32_t* arr = wave == 0 ? reinterpret_cast<uint32_t*>(sh.psum) : sh.csum;
       const int chunk = (S + kWave - 1) / kWave;
       const int lo = lane * chunk, hi = min(S, lo + chunk);
-      int run = 0;
-      for (int i = lo; i < hi; ++i) run += sh.psum[i + 1];
-      int incl = run;
+      uint32_t run = 0;
+      for (int i = lo; i < hi; ++i) run += arr[i + 1];
+      uint32_t incl = run;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
-        const int t = __shfl_up(incl, off);
+        const uint32_t t = __shfl_up(incl, off);
         if (lane >= off) incl += t;
       }
-      int base = incl - run;
+      uint32_t base = incl - run;
       for (int i = lo; i < hi; ++i) {
-        base += sh.psum[i + 1];
-        sh.psum[i + 1] = base;
+        base += arr[i + 1];
+        arr[i + 1] = base;
       }
-      if (lane == 0) sh.psum[0] = 0;
+      if (lane == 0) arr[0] = 0;
     }
     __syncthreads();
-    total = uni(sh.psum[S]) * Hkv;
+  }
+  // Sequence holding pair pidx (LIST): psum[seq] <= pidx < psum[seq + 1].
+  auto seq_of = [&](int pidx) __attribute__((always_inline)) {
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (uni(sh.psum[mid]) <= pidx)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return lo;
+  };
+  // LIST: first pair whose cumulative cost start is >= T.
+  auto first_at = [&](uint64_t T) __attribute__((always_inline)) {
+    const int npairs = uni(sh.psum[S]);
+    if (T >= uni64(sh.csum[S])) return npairs;
+    int lo = 0, hi = S;  // csum[lo] <= T < csum[lo + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (uni64(sh.csum[mid]) <= T)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int np = uni(sh.psum[lo + 1]) - uni(sh.psum[lo]);
+    const uint64_t rel = T - uni64(sh.csum[lo]);
+    const uint64_t full_span = static_cast<uint64_t>(np - 1) * full_cost;  // the full partitions
+    const int pl = rel <= full_span ? static_cast<int>((rel + full_cost - 1) / full_cost) : np;
+    return uni(uni(sh.psum[lo]) + pl);
+  };
+  // Not LIST: first non-empty partition item at or after k in this workgroup's stride.
+  const int total = a.total_items;
+  auto seek = [&](int k) __attribute__((always_inline)) {
+    for (; k < total; k += grid) {
+      const int r = k / Hkv;
+      bool bad;
+      if (r / S < seq_parts(a, ld_const(a.context_lens, r % S), &bad)) break;
+    }
+    return uni(k);
+  };
+
+  int k_first, k_end;  // this workgroup's items: LIST pair indices, else partition item indices
+  if constexpr (LIST) {
+    const uint64_t C = uni64(sh.csum[S]);
+    k_first = first_at((static_cast<uint64_t>(lane_b) * C + lanes - 1) / lanes);
+    k_end = first_at((static_cast<uint64_t>(lane_b + 1) * C + lanes - 1) / lanes);
+  } else {
+    k_first = seek(static_cast<int>(blockIdx.x));
+    k_end = total;
   }
   auto decode = [&](int k) __attribute__((always_inline)) {
     Item it;
     it.k = k;
-    it.kvh = k % Hkv;
-    const int r = k / Hkv;
+    it.kvh = kvh_b;
     if constexpr (LIST) {
-      int lo = 0, hi = S;  // psum[lo] <= r < psum[lo + 1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (uni(sh.psum[mid]) <= r)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      it.seq = lo;
-      it.part = r - uni(sh.psum[lo]);
+      it.seq = seq_of(k);
+      const int base = uni(sh.psum[it.seq]);
+      it.part = k - base;
+      it.part_end = min(k_end, uni(sh.psum[it.seq + 1])) - base;
+      it.next = base + it.part_end;
     } else {
+      const int r = k / Hkv;
       it.seq = r % S;
       it.part = r / S;
+      it.part_end = it.part + 1;
+      it.next = seek(k + grid);
     }
-    const int n = a.context_lens[it.seq];
+    const int n = ld_const(a.context_lens, it.seq);
     bool bad;
     const int nparts = seq_parts(a, n, &bad);
     const bool special = bad || n == 0;
-    it.flags = (nparts == 1 ? kDirect : 0) | (special ? kSpecial : 0) | (bad ? kBad : 0);
-    it.tok_begin = special ? 0 : it.part * a.partition_size;
-    it.tok_end = special ? 0 : min(n, it.tok_begin + a.partition_size);
+    it.flags = (it.part == 0 && it.part_end == nparts ? kDirect : 0) | (nparts > 1 ? kSplitSeq : 0) |
+               (special ? kSpecial : 0) | (bad ? kBad : 0);
+    it.tok_begin = special ? 0 : it.part * P;
+    it.tok_end = special ? 0 : min(n, it.part_end * P);
     const int ngroups = (it.tok_end - it.tok_begin + GT - 1) / GT;
     it.nk = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
     it.npad = it.nk <= NBUF ? NBUF : (it.nk + NBUF - 1) & ~(NBUF - 1);
     return it;
   };
-  // First item at or after k in this workgroup's stride that is not empty.
-  auto seek = [&](int k) __attribute__((always_inline)) {
-    if constexpr (!LIST) {
-      for (; k < total; k += grid) {
-        const int r = k / Hkv;
-        bool bad;
-        if (r / S < seq_parts(a, a.context_lens[r % S], &bad)) break;
-      }
-    }
-    return uni(k);
-  };
 
-  const int k0 = seek(static_cast<int>(blockIdx.x));
-  if (k0 >= total) return;
-  Item cur = decode(k0);
+  if (k_first >= k_end) return;
+  Item cur = decode(k_first);
   Item nxt = cur;
-  {
-    const int kn = seek(k0 + grid);
-    if (kn < total) nxt = decode(kn);
-    nxt.k = kn;
-  }
+  if (cur.next < k_end) nxt = decode(cur.next);
+  nxt.k = cur.next;
 
   // ---- loads ---------------------------------------------------------------
   const char* kcache = static_cast<const char*>(a.k_cache);
@@ -256,8 +329,7 @@ void paged_decode_kernel(AttnArgs a) {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(base, G * R);
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
-      const uint4 v = bload16<0>(rq, m16 * R + 16 * kq, 64 * s);
-      q[s] = make_uint4(v.x ^ a.q_sign, v.y ^ a.q_sign, v.z ^ a.q_sign, v.w ^ a.q_sign);
+      q[s] = bload16<0>(rq, m16 * R + 16 * kq, 64 * s);
     }
   };
 
@@ -286,7 +358,7 @@ void paged_decode_kernel(AttnArgs a) {
     return w;
   };
   auto table_entry = [&](const Where& w) __attribute__((always_inline)) {
-    return a.block_tables[static_cast<size_t>(w.seq) * a.max_blocks + w.tok / B];
+    return ld_const(a.block_tables, static_cast<size_t>(w.seq) * a.max_blocks + w.tok / B);
   };
   auto make_target = [&](const Where& w, int id) __attribute__((always_inline)) {
     Target T;
@@ -335,7 +407,7 @@ void paged_decode_kernel(AttnArgs a) {
   constexpr bool kPrefetchQ = NQ <= 4;
   uint4 q_cur[NQ], q_nxt[kPrefetchQ ? NQ : 1];
   load_query(q_cur, cur);
-  if constexpr (kPrefetchQ) load_query(q_nxt, nxt.k < total ? nxt : cur);
+  if constexpr (kPrefetchQ) load_query(q_nxt, nxt.k < k_end ? nxt : cur);
 
   uint4 kb[NBUF][NT][KS];
   uint32_t vb[NBUF][NDT][VW];
@@ -350,15 +422,16 @@ void paged_decode_kernel(AttnArgs a) {
     load_values(vb[s], T);
   }
   // The block id of the next refill target is fetched one step ahead.
-  int pend_id = table_entry(where(NBUF, nxt.k < total));
+  int pend_id = table_entry(where(NBUF, nxt.k < k_end));
 
   const float c = a.c;
+  int parity = 0;  // LDS merge buffer of the current item
   for (;;) {
     f32x4_t acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;
-    const bool has_next = nxt.k < total;
+    const bool has_next = nxt.k < k_end;
 
     for (int i0 = 0; i0 < cur.npad; i0 += NBUF) {
 #pragma unroll
@@ -400,6 +473,9 @@ void paged_decode_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 
         if (valid) {
+          // Scaled logits u = c (q . k).
+#pragma unroll
+          for (int t = 0; t < NT; ++t) sc[t] *= c;
           if (t_first + GT > cur.tok_end) {
             // Tokens past the end: logit -inf and value 0 (the cache may hold anything there).
             const int rel = cur.tok_end - t_first;  // valid tokens of the group
@@ -431,7 +507,7 @@ void paged_decode_kernel(AttnArgs a) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) gm = fmaxf(gm, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
           gm = max_xor32(max_xor16(gm));
-          const float m_new = fmaxf(m_run, gm * c);
+          const float m_new = fmaxf(m_run, gm);
           if (__ballot(m_new > m_run)) {
             const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
 #pragma unroll
@@ -443,7 +519,7 @@ void paged_decode_kernel(AttnArgs a) {
           for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              sc[t][r] = __builtin_amdgcn_exp2f(fmaf(sc[t][r], c, -m_run));
+              sc[t][r] = __builtin_amdgcn_exp2f(sc[t][r] - m_run);
               l_run += sc[t][r];
             }
 
@@ -513,9 +589,14 @@ void paged_decode_kernel(AttnArgs a) {
     }
 
     // ---- merge the waves' partial results ------------------------------------
+    // Each wave parks (acc, max, sum) in this item's LDS buffer; after one
+    // barrier every thread combines four consecutive dims of one head.  The
+    // buffers alternate between items, so the next item's barrier is what
+    // orders the reuse of this one.
     const float l_tot = sum_xor32(sum_xor16(l_run));  // over the four token rows of each head
+    auto& mb = sh.mb[parity];
     if (m16 < G) {
-      float* reg = &sh.region[wave][m16][0];
+      float* reg = &mb.region[wave][m16][0];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         f32x4_t v = acc[dt];
@@ -523,43 +604,64 @@ void paged_decode_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4_t*>(reg + 16 * dt + 4 * kq) = v;
       }
       if (kq == 0) {
-        sh.wm[wave][m16] = m_run;
-        sh.wl[wave][m16] = pois_cur ? __builtin_nanf("") : l_tot;
+        mb.wm[wave][m16] = m_run;
+        mb.wl[wave][m16] = pois_cur ? __builtin_nanf("") : l_tot;
       }
     }
     __syncthreads();
     {
-      const int Hq = Hkv * G;
-      float* out_rows = a.out + (static_cast<size_t>(cur.seq) * Hq + static_cast<size_t>(cur.kvh) * G) * D;
+      constexpr int kNowhere = 0x40000000;  // an offset past every resource below
+      // Every thread issues the same stores on every path (buffer stores; the
+      // ones that must not land use a size-0 resource or an offset past the
+      // resource and are dropped by the hardware): stores count in the same
+      // wait counter as the ring's loads, and a store behind a branch would
+      // make the compiler wait for all earlier loads after the merge.
+      // A segment covering its whole sequence writes the output rows (and, for
+      // a sequence of several partitions, marks partition 0 done for the
+      // reduction); any other segment writes its partials at its first
+      // partition, with its length.
       const bool direct = cur.flags & kDirect;
-      for (int e = tid; e < G * D; e += kThreads) {
-        const int h = e / D, d = e % D;
+      const size_t head0 = static_cast<size_t>(cur.seq) * Hkv * G + static_cast<size_t>(cur.kvh) * G;
+      const size_t prow = (static_cast<size_t>(cur.seq) * Hkv + cur.kvh) * a.max_parts + cur.part;
+      const bool split = a.max_parts > 1;  // the workspace exists
+      const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + head0 * D, direct ? G * D * 4 : 0);
+      const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(split ? a.ws_acc + prow * G * D : a.out, direct ? 0 : G * D * 4);
+      const __amdgpu_buffer_rsrc_t r_m = make_rsrc(split ? a.ws_m + prow * G : a.out, direct ? 0 : G * 4);
+      const __amdgpu_buffer_rsrc_t r_l = make_rsrc(split ? a.ws_l + prow * G : a.out, direct ? 0 : G * 4);
+      const bool seg_store = split && (!direct || (cur.flags & kSplitSeq));
+      const __amdgpu_buffer_rsrc_t r_seg =
+          make_rsrc(split ? static_cast<const void*>(a.ws_seg + prow) : static_cast<const void*>(a.out), seg_store ? 4 : 0);
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(direct ? -1 : cur.part_end - cur.part), r_seg,
+                                            tid == 0 ? 0 : kNowhere, 0, 0);
+      constexpr int NC = D / 4;  // float4 chunks of one head's row
+      constexpr int ITERS = (G * NC + kThreads - 1) / kThreads;
+      const float fill = (cur.flags & kBad) ? __builtin_nanf("") : 0.0f;
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
+        const int cidx = tid + it * kThreads;
+        const bool live = cidx < G * NC;
+        const int h = live ? cidx / NC : 0, d4 = live ? (cidx % NC) * 4 : 0;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.wm[w][h]);
-        float sa = 0.0f, sl = 0.0f;
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mb.wm[w][h]);
+        f32x4_t sa = {0.0f, 0.0f, 0.0f, 0.0f};
+        float sl = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float wt = __builtin_amdgcn_exp2f(sh.wm[w][h] - M);  // 0 for a wave that saw no token
-          sa = fmaf(wt, sh.region[w][h][d], sa);
-          sl = fmaf(wt, sh.wl[w][h], sl);
+          const float wt = __builtin_amdgcn_exp2f(mb.wm[w][h] - M);  // 0 for a wave that saw no token
+          sa += wt * *reinterpret_cast<const f32x4_t*>(&mb.region[w][h][d4]);
+          sl = fmaf(wt, mb.wl[w][h], sl);
         }
-        if (cur.flags & kSpecial) {
-          out_rows[e] = (cur.flags & kBad) ? __builtin_nanf("") : 0.0f;
-        } else if (direct) {
-          out_rows[e] = sa / sl;
-        } else {
-          const size_t row =
-              (static_cast<size_t>(cur.seq) * Hq + static_cast<size_t>(cur.kvh) * G + h) * a.max_parts + cur.part;
-          a.ws_acc[row * D + d] = sa;
-          if (d == 0) {
-            a.ws_m[row] = M;
-            a.ws_l[row] = sl;
-          }
-        }
+        const f32x4_t o = (cur.flags & kSpecial) ? f32x4_t{fill, fill, fill, fill} : sa / sl;
+        const int voff = live ? (h * D + d4) * 4 : kNowhere;
+        const int soff = live && d4 == 0 ? h * 4 : kNowhere;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), r_out, voff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sa), r_acc, voff, 0, kLoadNT);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), r_m, soff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sl), r_l, soff, 0, 0);
       }
     }
-    __syncthreads();
+    parity ^= 1;
 
     if (!has_next) break;
     // Advance: the ring already holds the next item's first NBUF positions.
@@ -573,16 +675,16 @@ void paged_decode_kernel(AttnArgs a) {
       load_query(q_cur, cur);
     }
     {
-      const int kn = seek(cur.k + grid);
+      const int kn = cur.next;
       nxt = cur;
-      if (kn < total) nxt = decode(kn);
+      if (kn < k_end) nxt = decode(kn);
       nxt.k = kn;
     }
-    if constexpr (kPrefetchQ) load_query(q_nxt, nxt.k < total ? nxt : cur);
+    if constexpr (kPrefetchQ) load_query(q_nxt, nxt.k < k_end ? nxt : cur);
     // Ring position NBUF of the new item: when the item has only NBUF
     // positions it is the following item's first group, which the old item's
     // look-ahead could not know.
-    pend_id = table_entry(where(NBUF, nxt.k < total));
+    pend_id = table_entry(where(NBUF, nxt.k < k_end));
   }
 }
 
@@ -595,21 +697,31 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(AttnArgs a, int num_q
   const int row = blockIdx.x;  // seq * H_q + h
   const int seq = row / num_q_heads;
   bool bad;
-  const int nparts = seq_parts(a, a.context_lens[seq], &bad);
+  const int nparts = seq_parts(a, ld_const(a.context_lens, seq), &bad);
   if (nparts <= 1) return;  // written directly by the attention kernel
   const int lane = threadIdx.x;
-  const size_t base = static_cast<size_t>(row) * a.max_parts;
+  const int G = num_q_heads / a.num_kv_heads;
+  const int h = row % num_q_heads, kvh = h / G, g = h % G;
+  // Partials of the segment starting at partition p: entry ((seq * H_kv + kvh) * max_parts + p) * G + g;
+  // its length sits in ws_seg at (seq * H_kv + kvh) * max_parts + p.
+  const size_t srow = (static_cast<size_t>(seq) * a.num_kv_heads + kvh) * a.max_parts;
+  const int32_t* seg = a.ws_seg + srow;
+  if (seg[0] < 0) return;  // the sequence was written whole
+  // Segment lengths are >= 1; the clamp keeps the walk finite whatever the
+  // workspace holds.
+  auto step = [&](int p) { return max(1, seg[p]); };
   float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.ws_m[base + p]);
+  for (int p = 0; p < nparts; p += step(p)) M = fmaxf(M, a.ws_m[(srow + p) * G + g]);
   constexpr int PER = D / kWave;
   float o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.0f;
   float L = 0.0f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = __builtin_amdgcn_exp2f(a.ws_m[base + p] - M);
-    L = fmaf(w, a.ws_l[base + p], L);
-    const float* ap = a.ws_acc + (base + p) * D;
+  for (int p = 0; p < nparts; p += step(p)) {
+    const size_t e_p = (srow + p) * G + g;
+    const float w = __builtin_amdgcn_exp2f(a.ws_m[e_p] - M);
+    L = fmaf(w, a.ws_l[e_p], L);
+    const float* ap = a.ws_acc + e_p * D;
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = fmaf(w, ap[lane + e * kWave], o[e]);
   }
@@ -624,7 +736,7 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(AttnArgs a, int num_q
 struct Plan {
   int32_t P;          // effective partition size
   int32_t max_parts;  // partitions of the longest sequence
-  size_t off_m, off_l, bytes;
+  size_t off_m, off_l, off_seg, bytes;
 };
 
 Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t block_size, int32_t max_context_len,
@@ -638,7 +750,8 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t 
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   p.off_m = up(rows * head_dim * sizeof(float));
   p.off_l = p.off_m + up(rows * sizeof(float));
-  p.bytes = p.off_l + up(rows * sizeof(float));
+  p.off_seg = p.off_l + up(rows * sizeof(float));
+  p.bytes = p.off_seg + up(rows * sizeof(int32_t));
   return p;
 }
 
@@ -666,14 +779,23 @@ hipError_t launch_kernel(const AttnArgs& a, hipStream_t stream) {
   constexpr K kernel = paged_decode_kernel<DT, D, G, B, LIST>;
   const int fill = resident_workgroups<K, kernel>();
   if (fill <= 0) return hipErrorInvalidValue;
-  const int grid = a.total_items < fill ? a.total_items : fill;
+  // A multiple of H_kv: with the KV head varying fastest in the item order,
+  // workgroup b always serves head b % H_kv and the workgroups of all heads
+  // of one partition run side by side, reading adjacent tiles of the same
+  // blocks (and, for shared prefixes, the same blocks).
+  const int want = a.total_items < fill ? a.total_items : fill;
+  const int grid = want >= a.num_kv_heads ? want / a.num_kv_heads * a.num_kv_heads : a.num_kv_heads;
   hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <class DT, int D, int G>
 hipError_t launch_attention_g(const AttnArgs& a, hipStream_t stream) {
-  const bool list = a.num_seqs <= kMaxListedSeqs;
+  // The item list needs its LDS prefix sums to fit, and the summed costs
+  // (groups of at least 16 tokens plus the per-partition charge) to fit 32 bits.
+  const uint64_t seq_cost_bound =
+      static_cast<uint64_t>(a.max_context_len) / 16 + 1 + static_cast<uint64_t>(kItemCharge) * a.max_parts;
+  const bool list = a.num_seqs <= kMaxListedSeqs && static_cast<uint64_t>(a.num_seqs) * seq_cost_bound < (1ull << 32);
   if (a.block_size == 16)
     return list ? launch_kernel<DT, D, G, 16, true>(a, stream) : launch_kernel<DT, D, G, 16, false>(a, stream);
   return list ? launch_kernel<DT, D, G, 32, true>(a, stream) : launch_kernel<DT, D, G, 32, false>(a, stream);
@@ -736,6 +858,7 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
     a.ws_acc = reinterpret_cast<float*>(ws);
     a.ws_m = reinterpret_cast<float*>(ws + plan.off_m);
     a.ws_l = reinterpret_cast<float*>(ws + plan.off_l);
+    a.ws_seg = reinterpret_cast<int32_t*>(ws + plan.off_seg);
   }
   a.num_seqs = num_seqs;
   a.num_kv_heads = num_kv_heads;
@@ -746,13 +869,9 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
   a.partition_size = plan.P;
   a.max_parts = plan.max_parts;
   a.total_items = static_cast<int32_t>(items);
-  // Softmax of scale * (q . k) in the exp2 domain.  A negative scale is folded
-  // into q's sign (exact in bf16 and fp32), so the kernel scales by |scale|;
-  // a zero scale becomes the smallest normal float, which leaves every
-  // weight equal to 1 up to a relative 1e-34.
-  const float c = fabsf(scale) * 1.4426950408889634f;
-  a.c = c > FLT_MIN ? c : FLT_MIN;
-  a.q_sign = scale < 0.0f ? (kv_dtype == PKV_BF16 ? BF16::kSignMask : F32::kSignMask) : 0u;
+  // Softmax of scale * (q . k), run in the exp2 domain (any sign of scale; a
+  // zero scale gives equal weights).
+  a.c = scale * 1.4426950408889634f;
 
   if (stages & kStagePartitions) {
     const hipError_t err = kv_dtype == PKV_BF16 ? launch_attention<BF16>(a, head_dim, G, stream)

@@ -26,11 +26,9 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 struct F32 {
   static constexpr int kItem = 4;
-  static constexpr uint32_t kSignMask = 0x80000000u;
 };
 struct BF16 {
   static constexpr int kItem = 2;
-  static constexpr uint32_t kSignMask = 0x80008000u;
 };
 
 // 16-byte load marked non-temporal: K/V tiles are read once per step, and the
