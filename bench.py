@@ -77,6 +77,16 @@ def time_launches(fn, n, stream):
     return float(t.mean()), float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
+def unique_kv_bytes(w, tables, lens) -> int:
+    """Bytes of the distinct physical slots the step reads (shared prefix blocks counted once)."""
+    B = w.spec.block_size
+    slots = set()
+    for t, n in zip(tables, lens):
+        for pos in range(int(n)):
+            slots.add(int(t[pos // B]) * B + pos % B)
+    return len(slots) * w.kv_bytes_per_token
+
+
 def measure(w, steps, warmup, stream):
     import torch
     from paged_kv_cache_physical_amd.runner import GpuBatch
@@ -116,6 +126,10 @@ def measure(w, steps, warmup, stream):
         "kv_gbps_partition_kernel": w.kv_bytes / (part[0] * 1e-3) / 1e9,
         "kv_gbps_attention": w.kv_bytes / (attn[0] * 1e-3) / 1e9,
     }
+    if w.spec.kind == "beam":  # shared prefixes: logical bytes count them per sequence, unique bytes once
+        ub = unique_kv_bytes(w, gb.tables_host, gb.lens_host)
+        res["unique_kv_bytes"] = ub
+        res["unique_kv_gbps_partition_kernel"] = ub / (part[0] * 1e-3) / 1e9
     del gb
     torch.cuda.empty_cache()
     return res
@@ -170,6 +184,52 @@ def cpu_baseline(w, budget_s=12.0):
                       f"{elapsed:.1f}s"}
 
 
+def copy_probe(stream, nbytes=1 << 30):
+    """A plain device copy of known size (reads and writes nbytes): the reference dispatch that
+    scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+    torch.cuda.empty_cache()
+
+
+def traffic_summary(pmc_dirs, workload: str, nbytes=1 << 30):
+    """HBM bytes per partition-kernel dispatch from rocprofv3 --pmc CSVs (one run with FETCH_SIZE, one with
+    WRITE_SIZE), each counter scaled by its reading on the copy probe of nbytes."""
+    import csv
+    import glob
+    vals = {}
+    for d in pmc_dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                name, ctr = r["Kernel_Name"], r["Counter_Name"]
+                kind = ("decode" if "paged_decode_kernel" in name else
+                        "copy" if "copy" in name.lower() else None)
+                if kind is None:
+                    continue
+                gsize = int(r.get("Grid_Size", 0) or 0)
+                vals.setdefault((kind, ctr), []).append((gsize, float(r["Counter_Value"])))
+    out = {"workload": workload, "kernel_source_sha": kernel_sha()}
+    for ctr, key in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
+        dec = [v for _, v in vals.get(("decode", ctr), [])]
+        cpy = [v for _, v in vals.get(("copy", ctr), [])]
+        if not dec or not cpy:
+            continue
+        cpy_kib = float(np.median(sorted(cpy)[-3:]))  # the three copies of nbytes (largest readings)
+        scale = nbytes / (cpy_kib * 1024.0)
+        out[f"{key}_scale"] = scale
+        out[f"{key}_bytes_per_launch"] = float(np.median(dec)) * 1024.0 * scale
+        out[f"{key}_dispatches"] = len(dec)
+    if "read_bytes_per_launch" in out:
+        out["hbm_bytes_per_launch"] = out["read_bytes_per_launch"] + out.get("write_bytes_per_launch", 0.0)
+    return out
+
+
 def traffic_from_profiles(workload: str):
     path = os.path.join(ROOT, "profiles", f"paged_decode_{workload}_traffic.json")
     if not os.path.exists(path):
@@ -191,7 +251,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated extra workloads")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (the reference dispatch for rocprofv3 byte counters)")
+    ap.add_argument("--traffic-from", nargs="+", metavar="DIR",
+                    help="write profiles/paged_decode_<workload>_traffic.json from rocprofv3 --pmc output dirs "
+                         "(FETCH_SIZE and WRITE_SIZE runs of this script with --copy-probe) and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        rec = traffic_summary(args.traffic_from, args.workload)
+        path = os.path.join(ROOT, "profiles", f"paged_decode_{args.workload}_traffic.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
@@ -219,8 +291,10 @@ def main():
             r["pct_hbm_peak_partition_kernel"] = 100 * r["kv_gbps_partition_kernel"] / HBM_PEAK_GBPS
             extra[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
             log(f"[bench] {name}: {json.dumps(extra[name])}")
+    if args.copy_probe:
+        copy_probe(stream)
     ceiling = hbm_read_ceiling(stream)
-    log(f"[bench] torch sum read ceiling {ceiling:.0f} GB/s")
+    log(f"[bench] streaming-read probe {ceiling:.0f} GB/s")
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     if cpu:
         log(f"[bench] cpu baseline {json.dumps(cpu)}")
@@ -250,7 +324,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(w.spec.name),
                      "kernel": "paged_decode_kernel (partition pass)",
-                     "bytes_per_launch": w.kv_bytes},
+                     "bytes_per_launch": w.kv_bytes,
+                     "launch_us": round(head["partition_kernel_us"]["mean"], 2)},
         "hbm_read_ceiling_gbps": round(ceiling, 1),
         "cpu_baseline": cpu,
         "other_workloads": extra,

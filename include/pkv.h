@@ -221,13 +221,18 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int3
  *   context_lens: device int32 [num_seqs]; n_s counts the token just written.
  *     n_s == 0 gives an all-zero output row; n_s < 0, n_s > max_context_len,
  *     n_s > max_blocks * B, or a block id outside [0, num_blocks) gives NaN.
+ *   scale: any finite value (negative and zero included).
  *   partition_size: tokens per context partition (a multiple of B), or 0 for
- *     one partition per sequence.  Sequences longer than one partition are
- *     computed as independent partitions combined by a log-sum-exp reduction
- *     (split context); that needs `workspace` (device, workspace_bytes >=
- *     pkv_attention_workspace_bytes(...)).
+ *     one partition per sequence.  The work is split at partition boundaries:
+ *     a sequence is computed as one or more segments of consecutive
+ *     partitions, and the segments' partial results are combined by a
+ *     log-sum-exp reduction (split context); that needs `workspace` (device,
+ *     workspace_bytes >= pkv_attention_workspace_bytes(...)) whenever a
+ *     sequence can span more than one partition.  Its contents are private.
  * Arithmetic: fp32 accumulation; bf16 inputs are multiplied exactly and summed
- * in fp32.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+ * in fp32 (probabilities enter the value product as two bf16 terms whose sum
+ * is within 2^-16 of the fp32 value).  Errors: INVALID_ARG, UNSUPPORTED,
+ * WORKSPACE, HIP. */
 pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_tables, const int32_t* context_lens,
                                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -240,9 +245,10 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_c
  * time them separately.  Same arguments and errors; issue `partitions` then
  * `reduce` on one stream.
  * pkv_paged_attention_partitions: one pass over every (sequence, KV head,
- *   partition); writes the final rows of sequences that fit one partition and
- *   the per-partition (acc, max, sum) of the others into the workspace.
- * pkv_paged_attention_reduce: combines the partitions of every sequence that
+ *   segment of consecutive partitions); writes the final rows of sequences
+ *   computed in one segment, and the (acc, max, sum) of every other segment
+ *   with its extent into the workspace.
+ * pkv_paged_attention_reduce: combines the segments of every sequence that
  *   has more than one (log-sum-exp weights); a no-op when none has. */
 pkv_status pkv_paged_attention_partitions(float* out, const void* q, const void* k_cache, const void* v_cache,
                                           const int32_t* block_tables, const int32_t* context_lens,
@@ -260,7 +266,7 @@ pkv_status pkv_paged_attention_reduce(float* out, const void* q, const void* k_c
                                       hipStream_t stream);
 
 /* Calibration: read `bytes` (a multiple of 16) of device memory once with a
- * plain streaming kernel (16-byte loads, 8 in flight per thread) and discard
+ * plain streaming kernel (16-byte loads, 16 in flight per thread) and discard
  * the data.  Used to measure the practical HBM read ceiling next to the
  * attention kernel's KV read rate.  sink: device uint32[1], never written in
  * practice.  Errors: INVALID_ARG, HIP. */

@@ -11,7 +11,7 @@ What it follows:
     that is not yet full copies it first ([P3] section 3; [P4] beam-search
     sharing figure; [P2] key technical point 3).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * The free blocks form a FIFO queue seeded by a given order: allocation pops
     the head, a freed block joins the tail.
   * Copy-on-write fires on append when the sequence's last block is partly

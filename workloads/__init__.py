@@ -17,7 +17,7 @@ The five named workloads follow the decode batches the pages' problem
 statement calls for (a tiny fp32 step over the worked example's lengths
 37/91/128/201/511, a Llama-7B-shaped MHA batch, a GQA batch with lognormal
 lengths, beam search over a shared 1000-token prompt, and long 32768-token
-contexts); their sizes are restated in the design doc's input recipe.
+contexts); the sizes of each are in NAMED below.
 """
 
 from __future__ import annotations
