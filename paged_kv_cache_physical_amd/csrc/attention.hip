@@ -58,8 +58,8 @@ struct AttnArgs {
   float* ws_acc;  // [S][H_kv][max_parts][G][d]  one item's partials are one contiguous run
   float* ws_m;    // [S][H_kv][max_parts][G]     maximum logit, exp2 domain (scaled)
   float* ws_l;    // [S][H_kv][max_parts][G]     sum of exp2(logit - max)
-  int32_t* ws_seg;  // [S][H_kv][max_parts]      at a segment's first partition: its length in
-                    // partitions; at partition 0 of a sequence written whole: -1
+  int32_t* ws_seg;  // [S][H_kv][max_parts]      at a segment's slot: the slot of the sequence's next
+                    // segment (num partitions after the last); at slot 0 of a sequence written whole: -1
   int32_t num_seqs;
   int32_t num_kv_heads;
   int32_t block_size;
@@ -134,12 +134,14 @@ struct Geo {
   static_assert(NBUF >= 2 && (NBUF & (NBUF - 1)) == 0, "ring depth");
 };
 
-// One decoded item: a segment, i.e. partitions [part, part_end) of one
+// One decoded item: a segment, i.e. tokens [tok_begin, tok_end) of one
 // sequence for one KV head.  Every field is wave-uniform.
 struct Item {
   int k;     // item index (>= the workgroup's end: none)
   int next;  // the item after it in this workgroup's list
-  int seq, kvh, part, part_end;
+  int seq, kvh;
+  int part;       // workspace slot of the segment
+  int part_next;  // slot of the sequence's next segment (num partitions after the last)
   int tok_begin, tok_end;
   int nk;     // groups of this wave
   int npad;   // ring positions of this wave: nk rounded up to NBUF, at least NBUF
@@ -157,7 +159,6 @@ struct Shared {
     float wm[kWaves][G];                         // per-wave running maximum (exp2 domain, scaled)
     float wl[kWaves][G];                         // per-wave sum of probabilities
   } mb[2];  // alternate items use alternate buffers: one barrier per item
-  int32_t psum[LIST ? kMaxListedSeqs + 1 : 1];   // prefix sums of partition counts
   uint32_t csum[LIST ? kMaxListedSeqs + 1 : 1];  // prefix sums of sequence costs
 };
 
@@ -168,16 +169,16 @@ constexpr int kItemCharge = 2;
 // Workgroup b serves KV head b % H_kv (the grid is a multiple of H_kv), so the
 // H_kv workgroups of lane b / H_kv read the adjacent head tiles of the same
 // blocks at about the same time.
-// LIST (at most kMaxListedSeqs sequences): the (sequence, partition) pairs in
-// sequence order, from LDS prefix sums of the partition counts, are cut into
-// one contiguous run per lane, each starting where the cumulative cost
-// reaches L C / lanes (C the total), so the lanes get equal work to within
-// one partition.  A lane's run is walked one sequence at a time: an item is
-// the run's partitions of one sequence, processed as one softmax, so only a
-// sequence cut between lanes leaves partial results (one set per segment).
-// Otherwise every partition is an item: numbered part-major over max_parts,
-// dealt round-robin to the lanes, the empty ones (partition past the
-// sequence's end) skipped.
+// LIST (at most kMaxListedSeqs sequences): the sequences' work, laid out in
+// order with LDS prefix sums of a cost per sequence (its groups plus a charge
+// per partition), is cut into one contiguous run per lane, each starting
+// where the cumulative cost reaches L C / lanes (C the total): the lanes get
+// equal work to within one group.  A lane's run is walked one sequence at a
+// time: an item is the run's tokens of one sequence, computed as one softmax,
+// so only a sequence cut between lanes leaves partial results (one set per
+// segment).  Otherwise every partition is an item: numbered part-major over
+// max_parts, dealt round-robin to the lanes, the empty ones (partition past
+// the sequence's end) skipped.
 template <class DT, int D, int G, int B, bool LIST>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_decode_kernel(AttnArgs a) {
@@ -205,12 +206,11 @@ void paged_decode_kernel(AttnArgs a) {
       const int n = ld_const(a.context_lens, s);
       const int np = seq_parts(a, n, &bad);
       const int last = (bad || n == 0) ? 0 : n - (np - 1) * P;  // tokens of the last partition
-      sh.psum[s + 1] = np;
       sh.csum[s + 1] = static_cast<uint32_t>(np - 1) * full_cost + (last + GT - 1) / GT + kItemCharge;
     }
     __syncthreads();
-    if (wave < 2) {  // wave 0 scans the counts, wave 1 the costs: a chunk per lane, then a wave-wide scan
-      uint32_t* arr = wave == 0 ? reinterpret_cast<uint32_t*>(sh.psum) : sh.csum;
+    if (wave == 0) {  // scan of the costs: a chunk per lane, then a wave-wide scan of the chunk sums
+      uint32_t* arr = sh.csum;
       const int chunk = (S + kWave - 1) / kWave;
       const int lo = lane * chunk, hi = min(S, lo + chunk);
       uint32_t run = 0;
@@ -230,22 +230,20 @@ void paged_decode_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
-  // Sequence holding pair pidx (LIST): psum[seq] <= pidx < psum[seq + 1].
-  auto seq_of = [&](int pidx) __attribute__((always_inline)) {
-    int lo = 0, hi = S;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (uni(sh.psum[mid]) <= pidx)
-        lo = mid;
-      else
-        hi = mid;
-    }
-    return lo;
+  // LIST: the cut at cost position T, as (sequence, first token).  A sequence's
+  // cost is laid out partition by partition: the charge, then one unit per
+  // group.  T maps to the first group whose cost starts at or after it
+  // ("fine" cuts), or, when lanes are short, to the first partition start at
+  // or after it; a single-partition sequence is never cut (the nearer end
+  // wins).  The result is monotone in T, so consecutive lanes tile the work.
+  struct Cut {
+    int seq, tok;
   };
-  // LIST: first pair whose cumulative cost start is >= T.
-  auto first_at = [&](uint64_t T) __attribute__((always_inline)) {
-    const int npairs = uni(sh.psum[S]);
-    if (T >= uni64(sh.csum[S])) return npairs;
+  const uint64_t C = LIST ? uni64(sh.csum[S]) : 0;
+  const bool fine = C >= static_cast<uint64_t>(4) * lanes * full_cost;
+  auto cut_at = [&](uint64_t T) __attribute__((always_inline)) {
+    Cut c{S, 0};
+    if (T >= C) return c;
     int lo = 0, hi = S;  // csum[lo] <= T < csum[lo + 1]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -254,11 +252,26 @@ void paged_decode_kernel(AttnArgs a) {
       else
         hi = mid;
     }
-    const int np = uni(sh.psum[lo + 1]) - uni(sh.psum[lo]);
+    const int n = ld_const(a.context_lens, lo);
+    bool bad;
+    const int np = seq_parts(a, n, &bad);
     const uint64_t rel = T - uni64(sh.csum[lo]);
-    const uint64_t full_span = static_cast<uint64_t>(np - 1) * full_cost;  // the full partitions
-    const int pl = rel <= full_span ? static_cast<int>((rel + full_cost - 1) / full_cost) : np;
-    return uni(uni(sh.psum[lo]) + pl);
+    if (bad || n == 0) {  // no tokens: the sequence starts the run that holds its first cost unit
+      c.seq = rel == 0 ? lo : lo + 1;
+      return c;
+    }
+    const int p = rel >= static_cast<uint64_t>(np - 1) * full_cost ? np - 1 : static_cast<int>(rel / full_cost);
+    const int u = static_cast<int>(rel - static_cast<uint64_t>(p) * full_cost);
+    int tok;
+    if (fine) {
+      tok = p * P + max(0, u - kItemCharge) * GT;
+      if (np == 1 && tok > 0 && tok < n) tok = tok < n / 2 ? 0 : n;
+    } else {
+      tok = (u == 0 ? p : p + 1) * P;
+    }
+    c.seq = tok >= n ? lo + 1 : lo;
+    c.tok = tok >= n ? 0 : tok;
+    return c;
   };
   // Not LIST: first non-empty partition item at or after k in this workgroup's stride.
   const int total = a.total_items;
@@ -271,40 +284,57 @@ void paged_decode_kernel(AttnArgs a) {
     return uni(k);
   };
 
-  int k_first, k_end;  // this workgroup's items: LIST pair indices, else partition item indices
+  // This workgroup's items: LIST, the sequences of its lane's run (first and
+  // last possibly cut); otherwise partition items of its stride.
+  int k_first, k_end;
+  Cut run_begin{0, 0}, run_end{0, 0};
   if constexpr (LIST) {
-    const uint64_t C = uni64(sh.csum[S]);
-    k_first = first_at((static_cast<uint64_t>(lane_b) * C + lanes - 1) / lanes);
-    k_end = first_at((static_cast<uint64_t>(lane_b + 1) * C + lanes - 1) / lanes);
+    run_begin = cut_at((static_cast<uint64_t>(lane_b) * C + lanes - 1) / lanes);
+    run_end = cut_at((static_cast<uint64_t>(lane_b + 1) * C + lanes - 1) / lanes);
+    k_first = run_begin.seq;
+    k_end = run_end.tok > 0 ? run_end.seq + 1 : run_end.seq;
+    if (run_end.seq == run_begin.seq && run_end.tok <= run_begin.tok) k_end = k_first;  // empty run
   } else {
     k_first = seek(static_cast<int>(blockIdx.x));
     k_end = total;
   }
+  // Workspace slot of a segment starting at token t of a sequence: its
+  // partition, except that a start inside partition 0 (other than 0) uses
+  // slot 1.  Lanes hold at least 4 partitions of cost when cuts are fine, so
+  // no two segments of one sequence share a slot.
+  auto slot_of = [&](int t) __attribute__((always_inline)) { return t == 0 ? 0 : max(1, t / P); };
   auto decode = [&](int k) __attribute__((always_inline)) {
     Item it;
     it.k = k;
     it.kvh = kvh_b;
+    int n, nparts;
+    bool bad;
     if constexpr (LIST) {
-      it.seq = seq_of(k);
-      const int base = uni(sh.psum[it.seq]);
-      it.part = k - base;
-      it.part_end = min(k_end, uni(sh.psum[it.seq + 1])) - base;
-      it.next = base + it.part_end;
+      it.seq = k;
+      it.next = k + 1;
+      n = ld_const(a.context_lens, it.seq);
+      nparts = seq_parts(a, n, &bad);
+      it.tok_begin = k == run_begin.seq ? run_begin.tok : 0;
+      it.tok_end = k == run_end.seq ? run_end.tok : n;
     } else {
       const int r = k / Hkv;
       it.seq = r % S;
-      it.part = r / S;
-      it.part_end = it.part + 1;
+      const int part = r / S;
       it.next = seek(k + grid);
+      n = ld_const(a.context_lens, it.seq);
+      nparts = seq_parts(a, n, &bad);
+      it.tok_begin = part * P;
+      it.tok_end = min(n, it.tok_begin + P);
     }
-    const int n = ld_const(a.context_lens, it.seq);
-    bool bad;
-    const int nparts = seq_parts(a, n, &bad);
     const bool special = bad || n == 0;
-    it.flags = (it.part == 0 && it.part_end == nparts ? kDirect : 0) | (nparts > 1 ? kSplitSeq : 0) |
-               (special ? kSpecial : 0) | (bad ? kBad : 0);
-    it.tok_begin = special ? 0 : it.part * P;
-    it.tok_end = special ? 0 : min(n, it.part_end * P);
+    if (special) {
+      it.tok_begin = 0;
+      it.tok_end = 0;
+    }
+    const bool whole = special || (it.tok_begin == 0 && it.tok_end == n);
+    it.part = slot_of(it.tok_begin);
+    it.part_next = it.tok_end == n ? nparts : slot_of(it.tok_end);
+    it.flags = (whole ? kDirect : 0) | (nparts > 1 ? kSplitSeq : 0) | (special ? kSpecial : 0) | (bad ? kBad : 0);
     const int ngroups = (it.tok_end - it.tok_begin + GT - 1) / GT;
     it.nk = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
     it.npad = it.nk <= NBUF ? NBUF : (it.nk + NBUF - 1) & ~(NBUF - 1);
@@ -631,7 +661,7 @@ void paged_decode_kernel(AttnArgs a) {
       const bool seg_store = split && (!direct || (cur.flags & kSplitSeq));
       const __amdgpu_buffer_rsrc_t r_seg =
           make_rsrc(split ? static_cast<const void*>(a.ws_seg + prow) : static_cast<const void*>(a.out), seg_store ? 4 : 0);
-      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(direct ? -1 : cur.part_end - cur.part), r_seg,
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(direct ? -1 : cur.part_next), r_seg,
                                             tid == 0 ? 0 : kNowhere, 0, 0);
       constexpr int NC = D / 4;  // float4 chunks of one head's row
       constexpr int ITERS = (G * NC + kThreads - 1) / kThreads;
@@ -707,17 +737,17 @@ __global__ __launch_bounds__(kWave) void lse_reduce_kernel(AttnArgs a, int num_q
   const size_t srow = (static_cast<size_t>(seq) * a.num_kv_heads + kvh) * a.max_parts;
   const int32_t* seg = a.ws_seg + srow;
   if (seg[0] < 0) return;  // the sequence was written whole
-  // Segment lengths are >= 1; the clamp keeps the walk finite whatever the
-  // workspace holds.
-  auto step = [&](int p) { return max(1, seg[p]); };
+  // Each segment records the slot of the next one; the walk always moves
+  // forward, so it ends whatever the workspace holds.
+  auto next = [&](int p) { return max(p + 1, seg[p]); };
   float M = -INFINITY;
-  for (int p = 0; p < nparts; p += step(p)) M = fmaxf(M, a.ws_m[(srow + p) * G + g]);
+  for (int p = 0; p < nparts; p = next(p)) M = fmaxf(M, a.ws_m[(srow + p) * G + g]);
   constexpr int PER = D / kWave;
   float o[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.0f;
   float L = 0.0f;
-  for (int p = 0; p < nparts; p += step(p)) {
+  for (int p = 0; p < nparts; p = next(p)) {
     const size_t e_p = (srow + p) * G + g;
     const float w = __builtin_amdgcn_exp2f(a.ws_m[e_p] - M);
     L = fmaf(w, a.ws_l[e_p], L);
