@@ -723,41 +723,42 @@ void paged_decode_kernel(AttnArgs a) {
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kWave) void lse_reduce_kernel(AttnArgs a, int num_q_heads) {
-  const int row = blockIdx.x;  // seq * H_q + h
-  const int seq = row / num_q_heads;
+__global__ __launch_bounds__(kThreads) void lse_reduce_kernel(AttnArgs a, int num_q_heads) {
+  // One workgroup per (sequence, KV head); wave w takes the query heads
+  // g = w, w + 4, ... of the group.
+  const int seq = blockIdx.x / a.num_kv_heads, kvh = blockIdx.x % a.num_kv_heads;
   bool bad;
   const int nparts = seq_parts(a, ld_const(a.context_lens, seq), &bad);
   if (nparts <= 1) return;  // written directly by the attention kernel
-  const int lane = threadIdx.x;
-  const int G = num_q_heads / a.num_kv_heads;
-  const int h = row % num_q_heads, kvh = h / G, g = h % G;
-  // Partials of the segment starting at partition p: entry ((seq * H_kv + kvh) * max_parts + p) * G + g;
-  // its length sits in ws_seg at (seq * H_kv + kvh) * max_parts + p.
+  // Partials of the segment in slot p: entry ((seq * H_kv + kvh) * max_parts + p) * G + g; ws_seg at
+  // (seq * H_kv + kvh) * max_parts + p holds the slot of the sequence's next segment.
   const size_t srow = (static_cast<size_t>(seq) * a.num_kv_heads + kvh) * a.max_parts;
   const int32_t* seg = a.ws_seg + srow;
   if (seg[0] < 0) return;  // the sequence was written whole
-  // Each segment records the slot of the next one; the walk always moves
-  // forward, so it ends whatever the workspace holds.
+  // The walk always moves forward, so it ends whatever the workspace holds.
   auto next = [&](int p) { return max(p + 1, seg[p]); };
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; p = next(p)) M = fmaxf(M, a.ws_m[(srow + p) * G + g]);
+  const int G = num_q_heads / a.num_kv_heads;
+  const int lane = threadIdx.x & (kWave - 1);
   constexpr int PER = D / kWave;
-  float o[PER];
+  for (int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); g < G; g += kWaves) {
+    float M = -INFINITY;
+    for (int p = 0; p < nparts; p = next(p)) M = fmaxf(M, a.ws_m[(srow + p) * G + g]);
+    float o[PER];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.0f;
-  float L = 0.0f;
-  for (int p = 0; p < nparts; p = next(p)) {
-    const size_t e_p = (srow + p) * G + g;
-    const float w = __builtin_amdgcn_exp2f(a.ws_m[e_p] - M);
-    L = fmaf(w, a.ws_l[e_p], L);
-    const float* ap = a.ws_acc + e_p * D;
+    for (int e = 0; e < PER; ++e) o[e] = 0.0f;
+    float L = 0.0f;
+    for (int p = 0; p < nparts; p = next(p)) {
+      const size_t e_p = (srow + p) * G + g;
+      const float w = __builtin_amdgcn_exp2f(a.ws_m[e_p] - M);
+      L = fmaf(w, a.ws_l[e_p], L);
+      const float* ap = a.ws_acc + e_p * D;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = fmaf(w, ap[lane + e * kWave], o[e]);
+      for (int e = 0; e < PER; ++e) o[e] = fmaf(w, ap[lane + e * kWave], o[e]);
+    }
+    float* out = a.out + (static_cast<size_t>(seq) * num_q_heads + static_cast<size_t>(kvh) * G + g) * D;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[lane + e * kWave] = o[e] / L;
   }
-  float* out = a.out + static_cast<size_t>(row) * D;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) out[lane + e * kWave] = o[e] / L;
 }
 
 // ---------------------------------------------------------------------------
@@ -909,11 +910,11 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
     if (err != hipSuccess) return PKV_ERR_HIP;
   }
   if ((stages & kStageReduce) && plan.max_parts > 1) {
-    const dim3 rg(static_cast<unsigned>(num_seqs) * num_q_heads);
+    const dim3 rg(static_cast<unsigned>(num_seqs) * num_kv_heads);
     if (head_dim == 64)
-      hipLaunchKernelGGL((lse_reduce_kernel<64>), rg, dim3(kWave), 0, stream, a, num_q_heads);
+      hipLaunchKernelGGL((lse_reduce_kernel<64>), rg, dim3(kThreads), 0, stream, a, num_q_heads);
     else
-      hipLaunchKernelGGL((lse_reduce_kernel<128>), rg, dim3(kWave), 0, stream, a, num_q_heads);
+      hipLaunchKernelGGL((lse_reduce_kernel<128>), rg, dim3(kThreads), 0, stream, a, num_q_heads);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;

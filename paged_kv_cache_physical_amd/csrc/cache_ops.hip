@@ -7,39 +7,35 @@
 namespace pkv {
 namespace {
 
-// One thread moves 16 bytes of K and 16 bytes of V of one (token, head).
-// K tile [d / X][B][X] (X = 16 bytes): the 16-byte chunk c of a key row is
-// piece c.  V tile [d][B]: the chunk's scalars go to rows c * E .. c * E + E-1
-// of the tile, column `off`.
+// One wave moves the key and value of one (token, head).  K tile
+// [d / X][B][X] (X = 16 bytes): lane c < d / X stores piece c of the key row.
+// V tile [d][B]: lane l stores the values of dims l, l + 64, ... into column
+// `off` of the tile, so a store instruction covers consecutive rows.
 template <class T>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const char* __restrict__ k_new,
                                                                 const char* __restrict__ v_new,
                                                                 char* __restrict__ k_cache, char* __restrict__ v_cache,
                                                                 const int64_t* __restrict__ slots, int32_t num_tokens,
-                                                                int32_t num_heads, int32_t block_size, int32_t row_bytes,
+                                                                int32_t num_heads, int32_t block_size, int32_t head_dim,
                                                                 int64_t num_slots) {
-  constexpr int E = 16 / static_cast<int>(sizeof(T));  // scalars per 16-byte chunk
-  const int chunks = row_bytes / 16;
-  const int head_dim = chunks * E;
-  const int64_t total = static_cast<int64_t>(num_tokens) * num_heads * chunks;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total; idx += stride) {
-    const int c = static_cast<int>(idx % chunks);
-    const int64_t th = idx / chunks;  // token * H + head
-    const int64_t t = th / num_heads;
-    const int h = static_cast<int>(th % num_heads);
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t blk = slot / block_size;
-    const int off = static_cast<int>(slot % block_size);
-    const int64_t tile = blk * num_heads + h;
-    const uint4 kv = *reinterpret_cast<const uint4*>(k_new + th * row_bytes + c * 16);
-    *reinterpret_cast<uint4*>(k_cache + ((tile * chunks + c) * block_size + off) * 16) = kv;
-    const T* vs = reinterpret_cast<const T*>(v_new + th * row_bytes + c * 16);
-    T* vd = reinterpret_cast<T*>(v_cache) + (tile * head_dim + static_cast<int64_t>(c) * E) * block_size + off;
-#pragma unroll
-    for (int j = 0; j < E; ++j) vd[static_cast<int64_t>(j) * block_size] = vs[j];
-  }
+  const int lane = threadIdx.x & 63;
+  const int64_t th = static_cast<int64_t>(blockIdx.x) * (blockDim.x / 64) + threadIdx.x / 64;  // token * H + head
+  if (th >= static_cast<int64_t>(num_tokens) * num_heads) return;
+  const int64_t t = th / num_heads;
+  const int h = static_cast<int>(th % num_heads);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int off = static_cast<int>(slot % block_size);
+  const int64_t tile = blk * num_heads + h;
+  const int pieces = head_dim * static_cast<int>(sizeof(T)) / 16;
+  const T* krow = reinterpret_cast<const T*>(k_new) + th * head_dim;
+  const T* vrow = reinterpret_cast<const T*>(v_new) + th * head_dim;
+  for (int c = lane; c < pieces; c += 64)
+    *reinterpret_cast<uint4*>(k_cache + ((tile * pieces + c) * block_size + off) * 16) =
+        *reinterpret_cast<const uint4*>(krow + c * (16 / sizeof(T)));
+  T* vt = reinterpret_cast<T*>(v_cache) + tile * head_dim * block_size + off;
+  for (int e = lane; e < head_dim; e += 64) vt[static_cast<int64_t>(e) * block_size] = vrow[e];
 }
 
 // grid = (pairs, 2 caches, splits): each workgroup copies a slice of one block.
@@ -107,14 +103,13 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_c
   if (!k_new || !v_new || !k_cache || !v_cache || !slots) return PKV_ERR_INVALID_ARG;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_ERR_INVALID_ARG;
-  const int row_bytes = head_dim * item;
-  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (row_bytes / 16);
-  const int64_t want = ceil_div64(total, 256);
-  const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
+  const int64_t waves = static_cast<int64_t>(num_tokens) * num_kv_heads;  // one per (token, head)
+  const int64_t grid = ceil_div64(waves, 4);
+  if (grid > 0x7fffffff) return PKV_ERR_INVALID_ARG;
   auto kernel = item == 4 ? reshape_and_cache_kernel<uint32_t> : reshape_and_cache_kernel<uint16_t>;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream, static_cast<const char*>(k_new),
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, static_cast<const char*>(k_new),
                      static_cast<const char*>(v_new), static_cast<char*>(k_cache), static_cast<char*>(v_cache), slots,
-                     num_tokens, num_kv_heads, block_size, row_bytes,
+                     num_tokens, num_kv_heads, block_size, head_dim,
                      static_cast<int64_t>(num_blocks) * block_size);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
