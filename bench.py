@@ -126,6 +126,14 @@ def measure(w, steps, warmup, stream):
         "kv_gbps_partition_kernel": w.kv_bytes / (part[0] * 1e-3) / 1e9,
         "kv_gbps_attention": w.kv_bytes / (attn[0] * 1e-3) / 1e9,
     }
+    pairs = [p for p in gb.pairs if len(p)]
+    if pairs:  # copy-on-write copies made while building the batch (A4), re-issued: idempotent
+        pd = torch.from_numpy(np.concatenate(pairs)).to("cuda")
+        from paged_kv_cache_physical_amd import pkv_copy_blocks
+        with torch.cuda.stream(stream):
+            cb = time_launches(lambda: pkv_copy_blocks(gb.k_cache, gb.v_cache, pd, stream), n_k, stream)
+        res["copy_blocks_pairs"] = int(pd.shape[0])
+        res["copy_blocks_us"] = 1e3 * cb[0]
     if w.spec.kind == "beam":  # shared prefixes: logical bytes count them per sequence, unique bytes once
         ub = unique_kv_bytes(w, gb.tables_host, gb.lens_host)
         res["unique_kv_bytes"] = ub
@@ -133,6 +141,33 @@ def measure(w, steps, warmup, stream):
     del gb
     torch.cuda.empty_cache()
     return res
+
+
+def host_allocator_step_us(w, reps=20):
+    """Host side of a decode step (append one token to every sequence, then refresh the block tables
+    and lengths), timed on a host-only replay of the batch's allocator script."""
+    from paged_kv_cache_physical_amd import Pool
+    from workloads import Append, Create, Fork
+    pool = Pool(w.num_blocks, w.spec.block_size, w.free_order)
+    ids = []
+    for op in w.script():
+        if isinstance(op, Create):
+            ids.extend(pool.create() for _ in range(op.count))
+        elif isinstance(op, Fork):
+            ids.append(pool.fork(op.parent))
+        elif isinstance(op, Append):
+            pool.append(op.seqs, op.counts)
+    seqs = np.asarray(sorted(ids), dtype=np.int32)
+    ones = np.ones(len(seqs), dtype=np.int32)
+    # table width sized once, with room for the appended tokens (a server keeps a fixed-width table)
+    mb = max(pool.info(int(i))[1] for i in seqs) + reps // w.spec.block_size + 1
+    t = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        pool.append(seqs, ones)
+        pool.block_tables(seqs, mb)
+        t.append(time.perf_counter() - t0)
+    return 1e6 * float(np.median(t))
 
 
 def hbm_read_ceiling(stream):
@@ -293,6 +328,10 @@ def main():
             log(f"[bench] {name}: {json.dumps(extra[name])}")
     if args.copy_probe:
         copy_probe(stream)
+    try:
+        head["host_allocator_us_per_step"] = host_allocator_step_us(w)
+    except Exception as e:  # a full pool cannot take another token per sequence
+        log(f"[bench] host allocator step not timed: {e}")
     ceiling = hbm_read_ceiling(stream)
     log(f"[bench] streaming-read probe {ceiling:.0f} GB/s")
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
@@ -316,6 +355,7 @@ def main():
         "config": describe(w),
         "seq_steps_per_s": round(head["seq_steps_per_s"], 1),
         "pct_hbm_peak_step": round(100 * head["kv_gbps_step"] / HBM_PEAK_GBPS, 2),
+        "host_allocator_us_per_step": round(head.get("host_allocator_us_per_step", float("nan")), 2),
         "kernels_us": {"paged_decode_partitions": round(head["partition_kernel_us"]["mean"], 2),
                        "lse_reduce": round(head["reduce_kernel_us"], 2),
                        "reshape_and_cache": round(head["reshape_and_cache_us"], 2),

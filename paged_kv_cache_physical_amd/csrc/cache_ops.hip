@@ -18,24 +18,31 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const char* __re
                                                                 const int64_t* __restrict__ slots, int32_t num_tokens,
                                                                 int32_t num_heads, int32_t block_size, int32_t head_dim,
                                                                 int64_t num_slots) {
+  constexpr int E = 16 / static_cast<int>(sizeof(T));  // scalars per key piece
   const int lane = threadIdx.x & 63;
-  const int64_t th = static_cast<int64_t>(blockIdx.x) * (blockDim.x / 64) + threadIdx.x / 64;  // token * H + head
+  // token * H + head, wave-uniform
+  const int64_t th = static_cast<int64_t>(blockIdx.x) * (blockDim.x / 64) +
+                     __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
   if (th >= static_cast<int64_t>(num_tokens) * num_heads) return;
   const int64_t t = th / num_heads;
   const int h = static_cast<int>(th % num_heads);
-  const int64_t slot = slots[t];
+  const int pieces = head_dim / E;  // <= 64
+  // The row loads do not depend on the slot: issue them first.
+  const T* krow = reinterpret_cast<const T*>(k_new) + th * head_dim;
+  const T* vrow = reinterpret_cast<const T*>(v_new) + th * head_dim;
+  const uint4 kv = *reinterpret_cast<const uint4*>(krow + (lane < pieces ? lane : 0) * E);
+  const T v0 = vrow[lane];
+  const T v1 = head_dim > 64 ? vrow[64 + lane] : T(0);
+  // The slot list is never written here: a scalar load through the constant address space.
+  const int64_t slot = ((const __attribute__((address_space(4))) int64_t*)slots)[t];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size;
   const int off = static_cast<int>(slot % block_size);
   const int64_t tile = blk * num_heads + h;
-  const int pieces = head_dim * static_cast<int>(sizeof(T)) / 16;
-  const T* krow = reinterpret_cast<const T*>(k_new) + th * head_dim;
-  const T* vrow = reinterpret_cast<const T*>(v_new) + th * head_dim;
-  for (int c = lane; c < pieces; c += 64)
-    *reinterpret_cast<uint4*>(k_cache + ((tile * pieces + c) * block_size + off) * 16) =
-        *reinterpret_cast<const uint4*>(krow + c * (16 / sizeof(T)));
+  if (lane < pieces) *reinterpret_cast<uint4*>(k_cache + ((tile * pieces + lane) * block_size + off) * 16) = kv;
   T* vt = reinterpret_cast<T*>(v_cache) + tile * head_dim * block_size + off;
-  for (int e = lane; e < head_dim; e += 64) vt[static_cast<int64_t>(e) * block_size] = vrow[e];
+  vt[static_cast<int64_t>(lane) * block_size] = v0;
+  if (head_dim > 64) vt[static_cast<int64_t>(64 + lane) * block_size] = v1;
 }
 
 // grid = (pairs, 2 caches, splits): each workgroup copies a slice of one block.
