@@ -233,6 +233,32 @@ def test_split_matches_unsplit():
         assert float(np.linalg.norm(a - b) / np.linalg.norm(a)) <= 1e-5
 
 
+def test_fine_lane_cuts_match_oracle():
+    # enough work per lane that runs are cut at group granularity: segments
+    # start mid-partition (partition 0 included, which uses slot 1)
+    w = wl.small_decode(300, (100, 2000), 8, 2, 128, 16, "bf16", seed=13)
+    full_parity(w, [256, 512])
+
+
+@pytest.mark.parametrize("nseq,lens,P", [(300, (100, 2000), 256), (6, (200, 1500), 48)])
+def test_two_stage_equals_fused_with_stale_workspace(nseq, lens, P):
+    # partitions then reduce (separate calls) give the fused call's bits, and
+    # whatever the workspace held before does not leak into the result
+    GpuBatch = runner()
+    w = wl.small_decode(nseq, lens, 8, 2, 128, 16, "bf16", seed=17)
+    gb = GpuBatch(w)
+    fused = gb.attention(P).clone()
+    ws = gb.workspace(P)
+    assert ws is not None
+    for fill in (0x00, 0x7F, 0xFF):
+        ws.fill_(fill)
+        gb.out.fill_(float("nan"))
+        gb.attention_partitions(P)
+        gb.attention_reduce(P)
+        torch.cuda.synchronize()
+        assert torch.equal(gb.out, fused), fill
+
+
 def test_edge_lengths_and_bad_inputs():
     GpuBatch = runner()
     w = wl.small_decode(5, (40, 300), 8, 2, 128, 16, "bf16", seed=4)
