@@ -244,13 +244,16 @@ void paged_decode_kernel(AttnArgs a) {
   auto cut_at = [&](uint64_t T) __attribute__((always_inline)) {
     Cut c{S, 0};
     if (T >= C) return c;
-    int lo = 0, hi = S;  // csum[lo] <= T < csum[lo + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (uni64(sh.csum[mid]) <= T)
-        lo = mid;
-      else
-        hi = mid;
+    // csum[lo] <= T < csum[lo + 1]: csum rises strictly, so the lanes of a wave
+    // test 64 evenly spaced candidates and narrow the range 64-fold per round
+    // (two rounds for up to 4096 sequences).
+    int lo = 0, span = S;
+    while (span > 1) {
+      const int step = (span + kWave - 1) / kWave, end = lo + span;
+      const int idx = lo + lane * step;
+      const uint64_t below = __ballot(idx < end && sh.csum[idx] <= T);
+      lo += (__popcll(below) - 1) * step;
+      span = min(step, end - lo);
     }
     const int n = ld_const(a.context_lens, lo);
     bool bad;

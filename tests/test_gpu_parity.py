@@ -259,6 +259,47 @@ def test_two_stage_equals_fused_with_stale_workspace(nseq, lens, P):
         assert torch.equal(gb.out, fused), fill
 
 
+@pytest.mark.parametrize("name", ["gqa_bf16_b16", "long_bf16"])
+def test_repeated_calls_are_bitwise_stable(name):
+    # the same inputs give the same bits on every call
+    GpuBatch = runner()
+    w = wl.named(name, seed=3)
+    gb = GpuBatch(w)
+    P = w.spec.partition_size
+    first = gb.attention(P).clone()
+    for i in range(12):
+        gb.out.fill_(float("nan"))
+        gb.attention(P)
+        torch.cuda.synchronize()
+        assert torch.equal(gb.out, first), i
+
+
+def test_step_replays_as_a_graph():
+    # the decode step (token write, partitions, reduction) captured as a HIP
+    # graph gives the eager step's bits on every replay, with eager work and
+    # synchronisations between the replays
+    GpuBatch = runner()
+    w = wl.small_decode(40, (100, 3000), 16, 4, 128, 16, "bf16", seed=23)
+    gb = GpuBatch(w)
+    P = 256
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        eager = gb.step(P, stream=s).clone()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            gb.step(P, stream=s)
+        for i in range(4):
+            gb.out.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(gb.out, eager), i
+            gb.out.fill_(float("nan"))
+            gb.attention(P, stream=s)
+            torch.cuda.synchronize()
+            assert torch.equal(gb.out, eager), i
+
+
 def test_edge_lengths_and_bad_inputs():
     GpuBatch = runner()
     w = wl.small_decode(5, (40, 300), 8, 2, 128, 16, "bf16", seed=4)
