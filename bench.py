@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,12 +40,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """Source text without comments and blank lines: edits to comments keep the hash."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in src.splitlines())
+    return "\n".join(line for line in lines if line.strip())
+
+
 def kernel_sha() -> str:
-    """Hash of the attention kernel's sources (ties profile-derived numbers to the code they measured)."""
+    """Hash of the attention kernel's code (ties profile-derived numbers to the code they measured)."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,10 +4,12 @@
 // figure of the per-block computation; the split follows the decoding page's
 // partitioned reduction).
 //
-// Unit of work: an item = (sequence, KV head, context partition of at most P
-// tokens).  A workgroup of four waves walks a strided list of items
-// (persistent grid).  Wave w takes the groups g = w, w + 4, ... of an item; a
-// group is one cache block (bf16) or 16 tokens (fp32).  Per group a wave
+// Unit of work: an item = the tokens of one sequence that a workgroup computes
+// for one KV head: a segment of its run of the cost-ordered work (up to 4096
+// sequences, see the kernel), or one context partition of at most P tokens.
+// A workgroup of four waves walks its list of items (persistent grid).  Wave
+// w takes the groups g = w, w + 4, ... of an item; a group is one cache block
+// (bf16) or 16 tokens (fp32).  Per group a wave
 //   - multiplies the group's keys with the G query heads of the KV head on the
 //     matrix cores (QK^T: rows = tokens, columns = heads),
 //   - folds the group into an online softmax per head (running maximum in the
