@@ -116,6 +116,24 @@ def test_multi_chunk_unsplit(G, lens):
     full_parity(w, [0, 4096 // G + 16 * 3])
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_random_batches_match_oracle(case):
+    # seeded random batches: every (dtype, d, G) pair, random block size, KV
+    # head count, batch size, lengths and partition sizes, so each kernel
+    # instantiation sees runs cut at many places and ragged tails
+    rng = np.random.default_rng(1000 + case)
+    dt = ("f32", "bf16")[case % 2]
+    d = (64, 128)[(case // 2) % 2]
+    G = (1, 2, 4, 8)[(case // 4) % 4]
+    B = (16, 32)[int(rng.integers(2))]
+    Hkv = int(rng.choice([1, 2, 4]))
+    S = int(rng.integers(20, 200))
+    hi = int(rng.integers(64, 3000))
+    w = wl.small_decode(S, (1, hi), G * Hkv, Hkv, d, B, dt, seed=case)
+    parts = sorted({0, B * int(rng.integers(1, 9)), B * int(rng.integers(8, 40))})
+    full_parity(w, parts)
+
+
 def test_ragged_boundaries():
     # lengths at block, partition and chunk edges
     lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025]
