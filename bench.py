@@ -2,10 +2,12 @@
 """Benchmark of the paged decode-attention step on one MI355X.
 
 A step is one pass of the decode hot path over a synthetic batch already
-resident in HBM: write each sequence's new K/V token into its slot
-(reshape_and_cache), then paged decode attention over every context (the
-partition kernel plus, when a context spans several partitions, the
-log-sum-exp reduce).  The block pool, tables and the rest of the context are
+resident in HBM: write each sequence's new K/V token into its slot, then
+paged decode attention over every context (the partition kernel plus, when a
+context spans several partitions, the log-sum-exp reduce).  The step is one
+pkv_decode_step call, whose partition kernel writes the new tokens in its
+set-up; the same step as two calls (reshape_and_cache, then attention) is
+timed beside it.  The block pool, tables and the rest of the context are
 built once before timing by the library's own allocator and kernels.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -121,6 +123,7 @@ def measure(w, steps, warmup, stream):
         red = time_launches(lambda: gb.attention_reduce(stream=stream), n_k, stream)
         rc = time_launches(lambda: gb.write_decode_token(stream=stream), n_k, stream)
         attn = time_launches(lambda: gb.attention(stream=stream), n_k, stream)
+        sep = time_launches(lambda: gb.step_separate(stream=stream), n_k, stream)
     res = {
         "ms_per_step": ms_step,
         "wall_ms_per_step": 1e3 * wall / steps,
@@ -131,11 +134,12 @@ def measure(w, steps, warmup, stream):
         "reduce_kernel_us": 1e3 * red[0],
         "reshape_and_cache_us": 1e3 * rc[0],
         "attention_us": 1e3 * attn[0],
+        "separate_calls_step_us": 1e3 * sep[0],
         "kv_gbps_partition_kernel": w.kv_bytes / (part[0] * 1e-3) / 1e9,
         "kv_gbps_attention": w.kv_bytes / (attn[0] * 1e-3) / 1e9,
     }
     pairs = [p for p in gb.pairs if len(p)]
-    if pairs:  # copy-on-write copies made while building the batch (A4), re-issued: idempotent
+    if pairs:  # copy-on-write copies made while building the batch, re-issued: idempotent
         pd = torch.from_numpy(np.concatenate(pairs)).to("cuda")
         from paged_kv_cache_physical_amd import pkv_copy_blocks
         with torch.cuda.stream(stream):
@@ -241,6 +245,15 @@ def copy_probe(stream, nbytes=1 << 30):
     torch.cuda.empty_cache()
 
 
+def is_partition_pass(kernel_name: str) -> bool:
+    """The plain partition kernel; its last template flag is set only in the decode step's variant, which also
+    writes the new tokens."""
+    if "paged_decode_kernel<" not in kernel_name:
+        return False
+    flags = kernel_name.split("paged_decode_kernel<", 1)[1].split(">", 1)[0].split(",")
+    return flags[-1].strip() == "false"
+
+
 def traffic_summary(pmc_dirs, workload: str, nbytes=1 << 30):
     """HBM bytes per partition-kernel dispatch from rocprofv3 --pmc CSVs (one run with FETCH_SIZE, one with
     WRITE_SIZE), each counter scaled by its reading on the copy probe of nbytes."""
@@ -251,7 +264,7 @@ def traffic_summary(pmc_dirs, workload: str, nbytes=1 << 30):
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 name, ctr = r["Kernel_Name"], r["Counter_Name"]
-                kind = ("decode" if "paged_decode_kernel" in name else
+                kind = ("decode" if is_partition_pass(name) else
                         "copy" if "copy" in name.lower() else None)
                 if kind is None:
                     continue
@@ -367,7 +380,8 @@ def main():
         "kernels_us": {"paged_decode_partitions": round(head["partition_kernel_us"]["mean"], 2),
                        "lse_reduce": round(head["reduce_kernel_us"], 2),
                        "reshape_and_cache": round(head["reshape_and_cache_us"], 2),
-                       "attention_call": round(head["attention_us"], 2)},
+                       "attention_call": round(head["attention_us"], 2),
+                       "step_as_separate_calls": round(head["separate_calls_step_us"], 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(w.spec.name),

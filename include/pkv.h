@@ -89,7 +89,8 @@ typedef struct pkv_stats {
 /* Human-readable name of a status code (static string). */
 const char* pkv_status_string(pkv_status status);
 
-/* Interface version; bumped whenever a signature or the cache layout changes. */
+/* Interface version; bumped whenever a signature, an entry point or the cache
+ * layout changes. */
 int32_t pkv_abi_version(void);
 
 /* ---------------------------------------------------------------------------
@@ -240,6 +241,27 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_c
                                       int32_t max_blocks, int32_t max_context_len, float scale,
                                       int32_t partition_size, void* workspace, size_t workspace_bytes,
                                       int32_t kv_dtype, hipStream_t stream);
+
+/* One decode step: write each sequence's new token, then attend.  k_new and
+ * v_new: device [num_seqs][H_kv][d] in the cache's scalar type, the key and
+ * value of the token at position n_s - 1 of sequence s.  Equivalent to
+ * pkv_reshape_and_cache with slot = block_tables[s][(n_s - 1) / B] * B +
+ * (n_s - 1) % B (the allocator's slot for that token; sequences with an
+ * invalid length or block id are not written), followed by
+ * pkv_paged_attention_decode with the remaining arguments (k_cache and v_cache
+ * serve both); the output and the caches are bit for bit those of the two
+ * calls.  With up to 4096 sequences the write happens inside the attention
+ * kernel: the workgroup that reads a sequence's last token writes it first
+ * ([P2] key technical point 1: the kernel fetches blocks through the table;
+ * [P2] core idea: each step appends one token per sequence).
+ * Errors: as pkv_paged_attention_decode, and INVALID_ARG for a missing or
+ * misaligned k_new / v_new. */
+pkv_status pkv_decode_step(const void* k_new, const void* v_new, float* out, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_blocks, int32_t max_context_len,
+                           float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           int32_t kv_dtype, hipStream_t stream);
 
 /* The two stages of pkv_paged_attention_decode, for callers that schedule or
  * time them separately.  Same arguments and errors; issue `partitions` then

@@ -26,7 +26,8 @@ __all__ = [
     "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_create", "pkv_seq_fork", "pkv_seq_free", "pkv_append_tokens",
     "pkv_block_tables", "pkv_seq_info", "pkv_pool_stats", "pkv_block_refcount", "pkv_pool_free_list",
     "pkv_pool_validate", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_attention_workspace_bytes",
-    "pkv_paged_attention_decode", "pkv_paged_attention_partitions", "pkv_paged_attention_reduce", "pkv_abi_version", "pkv_hbm_read_probe", "Pool", "cache_shapes", "empty_caches", "PkvError",
+    "pkv_paged_attention_decode", "pkv_paged_attention_partitions", "pkv_paged_attention_reduce",
+    "pkv_decode_step", "pkv_abi_version", "pkv_hbm_read_probe", "Pool", "cache_shapes", "empty_caches", "PkvError",
     "OutOfBlocks", "NoSuchSeq", "InvalidArg",
 ]
 
@@ -282,7 +283,7 @@ def pkv_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size, m
 
 
 def _attention(fn: str, out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int, scale: float,
-               partition_size: int = 0, workspace=None, stream=None) -> None:
+               partition_size: int = 0, workspace=None, stream=None, new_kv=None) -> None:
     torch = _torch()
     S, Hq, d = q.shape
     nb, Hkv, d2, B = v_cache.shape
@@ -298,10 +299,18 @@ def _attention(fn: str, out, q, k_cache, v_cache, block_tables, context_lens, ma
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
-    check(getattr(lib(), fn)(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                             _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, Hq, Hkv, d,
-                             B, nb, max_blocks, int(max_context_len), float(scale), int(partition_size), ws_ptr,
-                             ws_bytes, _dtype_code(q), _stream(stream)), fn)
+    lead = []
+    if new_kv is not None:
+        k_new, v_new = new_kv
+        if tuple(k_new.shape) != (S, Hkv, d) or tuple(v_new.shape) != (S, Hkv, d) or \
+                k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+            raise InvalidArg(-1, fn, "new token shape or dtype mismatch")
+        lead = [_dev(k_new, "k_new"), _dev(v_new, "v_new")]
+    check(getattr(lib(), fn)(*lead, _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                             _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                             _dev(context_lens, "context_lens"), S, Hq, Hkv, d, B, nb, max_blocks,
+                             int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
+                             _dtype_code(q), _stream(stream)), fn)
 
 
 def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
@@ -310,6 +319,14 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
     context_lens int32 [S]; workspace: uint8 tensor of >= pkv_attention_workspace_bytes(...) bytes."""
     _attention("pkv_paged_attention_decode", out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                scale, partition_size, workspace, stream)
+
+
+def pkv_decode_step(k_new, v_new, out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                    scale: float, partition_size: int = 0, workspace=None, stream=None) -> None:
+    """One decode step: write k_new, v_new ([S][H_kv][d], cache dtype; the token at position n_s - 1 of each
+    sequence) into the caches through the block tables, then pkv_paged_attention_decode (same arguments)."""
+    _attention("pkv_decode_step", out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+               partition_size, workspace, stream, new_kv=(k_new, v_new))
 
 
 def pkv_paged_attention_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,

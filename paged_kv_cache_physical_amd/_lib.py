@@ -77,6 +77,7 @@ _SIGS = {
     "pkv_paged_attention_decode": (i32, _ATTN),
     "pkv_paged_attention_partitions": (i32, _ATTN),
     "pkv_paged_attention_reduce": (i32, _ATTN),
+    "pkv_decode_step": (i32, [vp, vp] + _ATTN),
 }
 
 _lib = None

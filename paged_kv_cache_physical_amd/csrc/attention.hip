@@ -47,7 +47,6 @@ namespace {
 constexpr int kWaves = 4;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxListedSeqs = 4096;    // sequences whose item list fits the LDS prefix sums
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kLoadNT = 2;              // buffer-load cache policy: nontemporal
 
 struct AttnArgs {
@@ -57,6 +56,8 @@ struct AttnArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const void* k_new;  // decode step: the new token of each sequence [S][H_kv][d], written to the caches
+  const void* v_new;  // (nullptr: no write)
   float* ws_acc;  // [S][H_kv][max_parts][G][d]  one item's partials are one contiguous run
   float* ws_m;    // [S][H_kv][max_parts][G]     maximum logit, exp2 domain (scaled)
   float* ws_l;    // [S][H_kv][max_parts][G]     sum of exp2(logit - max)
@@ -98,10 +99,6 @@ __device__ __forceinline__ int32_t ld_const(const int32_t* p, size_t i) {
   return ((const_i32_ptr)p)[i];
 }
 
-// Buffer resource over `bytes` bytes at p; bytes = 0 turns every load into zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
-}
 // voff: the lane's offset; soff: a wave-uniform offset added to it.  A load
 // stays inside its tile, and a size-0 resource rejects every load, so the
 // result does not depend on whether the range check includes soff.
@@ -180,8 +177,9 @@ constexpr int kItemCharge = 2;
 // so only a sequence cut between lanes leaves partial results (one set per
 // segment).  Otherwise every partition is an item: numbered part-major over
 // max_parts, dealt round-robin to the lanes, the empty ones (partition past
-// the sequence's end) skipped.
-template <class DT, int D, int G, int B, bool LIST>
+// the sequence's end) skipped.  WRITE (LIST only): the decode step's variant,
+// which also stores each sequence's new token before reading.
+template <class DT, int D, int G, int B, bool LIST, bool WRITE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_decode_kernel(AttnArgs a) {
   using Gm = Geo<DT, D, B>;
@@ -347,6 +345,35 @@ void paged_decode_kernel(AttnArgs a) {
   };
 
   if (k_first >= k_end) return;
+  if constexpr (LIST && WRITE) {
+    // The decode step's new tokens.  The run holds the last token of every
+    // sequence in [k_first, run_end.seq) (a sequence cut at run_end goes on in
+    // the next run), and only this workgroup reads that token for its head, so
+    // it writes it here, before its first load, through L2 (a partly written
+    // line left dirty there stalls the read that follows); the waves wait for
+    // the stores and meet at a barrier before the ring starts.
+    using T = typename std::conditional<kBF16, uint16_t, uint32_t>::type;
+    constexpr int E = 16 / static_cast<int>(sizeof(T));
+    for (int s = k_first + wave; s < run_end.seq; s += kWaves) {
+      const int n = ld_const(a.context_lens, s);
+      bool bad;
+      seq_parts(a, n, &bad);
+      if (bad || n == 0) continue;
+      const int id = ld_const(a.block_tables, static_cast<size_t>(s) * a.max_blocks + (n - 1) / B);
+      if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) continue;
+      const size_t row = (static_cast<size_t>(s) * Hkv + kvh_b) * D;
+      const T* krow = static_cast<const T*>(a.k_new) + row;
+      const T* vrow = static_cast<const T*>(a.v_new) + row;
+      const uint4 kv = *reinterpret_cast<const uint4*>(krow + (lane < D / E ? lane : 0) * E);
+      const T v0 = vrow[lane];
+      const T v1 = D > 64 ? vrow[64 + lane] : T(0);
+      store_token_rows<T, kStoreThrough>(const_cast<char*>(static_cast<const char*>(a.k_cache)),
+                                         const_cast<char*>(static_cast<const char*>(a.v_cache)),
+                                         static_cast<int64_t>(id) * Hkv + kvh_b, (n - 1) % B, B, D, lane, kv, v0, v1);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have reached the cache hierarchy
+    __syncthreads();
+  }
   Item cur = decode(k_first);
   Item nxt = cur;
   if (cur.next < k_end) nxt = decode(cur.next);
@@ -645,7 +672,6 @@ void paged_decode_kernel(AttnArgs a) {
     }
     __syncthreads();
     {
-      constexpr int kNowhere = 0x40000000;  // an offset past every resource below
       // Every thread issues the same stores on every path (buffer stores; the
       // ones that must not land use a size-0 resource or an offset past the
       // resource and are dropped by the hardware): stores count in the same
@@ -769,6 +795,14 @@ __global__ __launch_bounds__(kThreads) void lse_reduce_kernel(AttnArgs a, int nu
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
+// The item list needs its LDS prefix sums to fit, and the summed costs
+// (groups of at least 16 tokens plus the per-partition charge) to fit 32 bits.
+bool use_list(int32_t num_seqs, int32_t max_context_len, int32_t max_parts) {
+  const uint64_t seq_cost_bound =
+      static_cast<uint64_t>(max_context_len) / 16 + 1 + static_cast<uint64_t>(kItemCharge) * max_parts;
+  return num_seqs <= kMaxListedSeqs && static_cast<uint64_t>(num_seqs) * seq_cost_bound < (1ull << 32);
+}
+
 struct Plan {
   int32_t P;          // effective partition size
   int32_t max_parts;  // partitions of the longest sequence
@@ -809,10 +843,10 @@ int resident_workgroups() {
   return cache[dev];
 }
 
-template <class DT, int D, int G, int B, bool LIST>
+template <class DT, int D, int G, int B, bool LIST, bool WRITE = false>
 hipError_t launch_kernel(const AttnArgs& a, hipStream_t stream) {
   using K = void (*)(AttnArgs);
-  constexpr K kernel = paged_decode_kernel<DT, D, G, B, LIST>;
+  constexpr K kernel = paged_decode_kernel<DT, D, G, B, LIST, WRITE>;
   const int fill = resident_workgroups<K, kernel>();
   if (fill <= 0) return hipErrorInvalidValue;
   // A multiple of H_kv: with the KV head varying fastest in the item order,
@@ -827,14 +861,14 @@ hipError_t launch_kernel(const AttnArgs& a, hipStream_t stream) {
 
 template <class DT, int D, int G>
 hipError_t launch_attention_g(const AttnArgs& a, hipStream_t stream) {
-  // The item list needs its LDS prefix sums to fit, and the summed costs
-  // (groups of at least 16 tokens plus the per-partition charge) to fit 32 bits.
-  const uint64_t seq_cost_bound =
-      static_cast<uint64_t>(a.max_context_len) / 16 + 1 + static_cast<uint64_t>(kItemCharge) * a.max_parts;
-  const bool list = a.num_seqs <= kMaxListedSeqs && static_cast<uint64_t>(a.num_seqs) * seq_cost_bound < (1ull << 32);
-  if (a.block_size == 16)
-    return list ? launch_kernel<DT, D, G, 16, true>(a, stream) : launch_kernel<DT, D, G, 16, false>(a, stream);
-  return list ? launch_kernel<DT, D, G, 32, true>(a, stream) : launch_kernel<DT, D, G, 32, false>(a, stream);
+  // k_new is set only where the listed split applies (attention_stages)
+  const bool list = use_list(a.num_seqs, a.max_context_len, a.max_parts);
+  if (a.block_size == 16) {
+    if (!list) return launch_kernel<DT, D, G, 16, false>(a, stream);
+    return a.k_new ? launch_kernel<DT, D, G, 16, true, true>(a, stream) : launch_kernel<DT, D, G, 16, true>(a, stream);
+  }
+  if (!list) return launch_kernel<DT, D, G, 32, false>(a, stream);
+  return a.k_new ? launch_kernel<DT, D, G, 32, true, true>(a, stream) : launch_kernel<DT, D, G, 32, true>(a, stream);
 }
 
 template <class DT, int D>
@@ -857,8 +891,9 @@ hipError_t launch_attention(const AttnArgs& a, int D, int G, hipStream_t stream)
 
 enum : int { kStagePartitions = 1, kStageReduce = 2 };
 
-pkv_status attention_stages(int stages, float* out, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+pkv_status attention_stages(int stages, const void* k_new, const void* v_new, float* out, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs,
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             int32_t num_blocks, int32_t max_blocks, int32_t max_context_len, float scale,
                             int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t kv_dtype,
@@ -877,6 +912,8 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
+  if ((k_new != nullptr) != (v_new != nullptr)) return PKV_ERR_INVALID_ARG;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_INVALID_ARG;
 
   const Plan plan = make_plan(num_seqs, num_q_heads, head_dim, block_size, max_context_len, partition_size);
   const int64_t items = static_cast<int64_t>(plan.max_parts) * num_seqs * num_kv_heads;
@@ -910,6 +947,18 @@ pkv_status attention_stages(int stages, float* out, const void* q, const void* k
   a.c = scale * 1.4426950408889634f;
 
   if (stages & kStagePartitions) {
+    if (k_new) {
+      // The listed split writes the new tokens inside the attention kernel;
+      // partition items take a separate write first.
+      if (use_list(num_seqs, max_context_len, plan.max_parts)) {
+        a.k_new = k_new;
+        a.v_new = v_new;
+      } else if (launch_write_last_token(k_new, v_new, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                                         block_tables, context_lens, num_seqs, num_kv_heads, head_dim, block_size,
+                                         num_blocks, max_blocks, max_context_len, kv_dtype, stream) != hipSuccess) {
+        return PKV_ERR_HIP;
+      }
+    }
     const hipError_t err = kv_dtype == PKV_BF16 ? launch_attention<BF16>(a, head_dim, G, stream)
                                                 : launch_attention<F32>(a, head_dim, G, stream);
     if (err != hipSuccess) return PKV_ERR_HIP;
@@ -951,14 +1000,21 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int3
       kv_dtype, stream
 
 pkv_status pkv_paged_attention_decode(PKV_ATTN_PARAMS) {
-  return attention_stages(kStagePartitions | kStageReduce, PKV_ATTN_ARGS);
+  return attention_stages(kStagePartitions | kStageReduce, nullptr, nullptr, PKV_ATTN_ARGS);
 }
 
 pkv_status pkv_paged_attention_partitions(PKV_ATTN_PARAMS) {
-  return attention_stages(kStagePartitions, PKV_ATTN_ARGS);
+  return attention_stages(kStagePartitions, nullptr, nullptr, PKV_ATTN_ARGS);
 }
 
-pkv_status pkv_paged_attention_reduce(PKV_ATTN_PARAMS) { return attention_stages(kStageReduce, PKV_ATTN_ARGS); }
+pkv_status pkv_paged_attention_reduce(PKV_ATTN_PARAMS) {
+  return attention_stages(kStageReduce, nullptr, nullptr, PKV_ATTN_ARGS);
+}
+
+pkv_status pkv_decode_step(const void* k_new, const void* v_new, PKV_ATTN_PARAMS) {
+  if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
+  return attention_stages(kStagePartitions | kStageReduce, k_new, v_new, PKV_ATTN_ARGS);
+}
 
 #undef PKV_ATTN_PARAMS
 #undef PKV_ATTN_ARGS

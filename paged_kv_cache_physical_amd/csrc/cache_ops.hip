@@ -10,7 +10,10 @@ namespace {
 // One wave moves the key and value of one (token, head).  K tile
 // [d / X][B][X] (X = 16 bytes): lane c < d / X stores piece c of the key row.
 // V tile [d][B]: lane l stores the values of dims l, l + 64, ... into column
-// `off` of the tile, so a store instruction covers consecutive rows.
+// `off` of the tile, so a store instruction covers consecutive rows.  The
+// stores take the default write-back policy: when many tokens of one block
+// are written, L2 merges their partial lines before they reach HBM (measured
+// on MI355X: 1.2 TB/s for a 64K-token fill, 0.2 TB/s written through).
 template <class T>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const char* __restrict__ k_new,
                                                                 const char* __restrict__ v_new,
@@ -38,11 +41,43 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(const char* __re
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size;
   const int off = static_cast<int>(slot % block_size);
-  const int64_t tile = blk * num_heads + h;
-  if (lane < pieces) *reinterpret_cast<uint4*>(k_cache + ((tile * pieces + lane) * block_size + off) * 16) = kv;
-  T* vt = reinterpret_cast<T*>(v_cache) + tile * head_dim * block_size + off;
-  vt[static_cast<int64_t>(lane) * block_size] = v0;
-  if (head_dim > 64) vt[static_cast<int64_t>(64 + lane) * block_size] = v1;
+  store_token_rows<T, kStoreDefault>(k_cache, v_cache, blk * num_heads + h, off, block_size, head_dim, lane, kv, v0, v1);
+}
+
+// The decode step's token write when the attention kernel cannot do it: one
+// wave per (sequence, head) stores the token at position n - 1 into the slot
+// its block table gives (block_tables[s][(n - 1) / B], offset (n - 1) % B).
+// Sequences with n <= 0, n > max_context_len or n > max_blocks * B, and block
+// ids outside the pool, are skipped.  One token per block leaves every line it
+// touches partly written, so the stores go through L2 (kStoreThrough): the
+// attention kernel that reads the tile next does not stall on them.
+template <class T>
+__global__ __launch_bounds__(256) void write_last_token_kernel(const char* __restrict__ k_new,
+                                                               const char* __restrict__ v_new, char* k_cache,
+                                                               char* v_cache, const int32_t* __restrict__ block_tables,
+                                                               const int32_t* __restrict__ context_lens,
+                                                               int32_t num_seqs, int32_t num_heads, int32_t block_size,
+                                                               int32_t head_dim, int32_t num_blocks, int32_t max_blocks,
+                                                               int32_t max_context_len) {
+  constexpr int E = 16 / static_cast<int>(sizeof(T));
+  const int lane = threadIdx.x & 63;
+  const int64_t sh = static_cast<int64_t>(blockIdx.x) * (blockDim.x / 64) +
+                     __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
+  if (sh >= static_cast<int64_t>(num_seqs) * num_heads) return;
+  const int64_t s = sh / num_heads;
+  const int h = static_cast<int>(sh % num_heads);
+  const int n = context_lens[s];
+  if (n <= 0 || n > max_context_len || static_cast<int64_t>(n) > static_cast<int64_t>(max_blocks) * block_size) return;
+  const int32_t blk = block_tables[s * max_blocks + (n - 1) / block_size];
+  if (static_cast<unsigned>(blk) >= static_cast<unsigned>(num_blocks)) return;
+  const int pieces = head_dim / E;
+  const T* krow = reinterpret_cast<const T*>(k_new) + sh * head_dim;
+  const T* vrow = reinterpret_cast<const T*>(v_new) + sh * head_dim;
+  const uint4 kv = *reinterpret_cast<const uint4*>(krow + (lane < pieces ? lane : 0) * E);
+  const T v0 = vrow[lane];
+  const T v1 = head_dim > 64 ? vrow[64 + lane] : T(0);
+  store_token_rows<T, kStoreThrough>(k_cache, v_cache, static_cast<int64_t>(blk) * num_heads + h, (n - 1) % block_size,
+                                     block_size, head_dim, lane, kv, v0, v1);
 }
 
 // grid = (pairs, 2 caches, splits): each workgroup copies a slice of one block.
@@ -93,6 +128,22 @@ __global__ __launch_bounds__(256) void hbm_read_probe_kernel(const uint4* __rest
 }
 
 }  // namespace
+
+hipError_t launch_write_last_token(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks, int32_t max_context_len, int32_t kv_dtype, hipStream_t stream) {
+  const int64_t grid = ceil_div64(static_cast<int64_t>(num_seqs) * num_kv_heads, 4);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  auto kernel = item_size(kv_dtype) == 4 ? write_last_token_kernel<uint32_t> : write_last_token_kernel<uint16_t>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, static_cast<const char*>(k_new),
+                     static_cast<const char*>(v_new), static_cast<char*>(k_cache), static_cast<char*>(v_cache),
+                     block_tables, context_lens, num_seqs, num_kv_heads, block_size, head_dim, num_blocks, max_blocks,
+                     max_context_len);
+  return hipGetLastError();
+}
+
 }  // namespace pkv
 
 using namespace pkv;

@@ -9,7 +9,8 @@ from typing import List, Optional
 
 import numpy as np
 
-from . import (Pool, empty_caches, pkv_attention_workspace_bytes, pkv_copy_blocks, pkv_paged_attention_decode,
+from . import (Pool, empty_caches, pkv_attention_workspace_bytes, pkv_copy_blocks, pkv_decode_step,
+               pkv_paged_attention_decode,
                pkv_paged_attention_partitions, pkv_paged_attention_reduce, pkv_reshape_and_cache)
 
 
@@ -63,10 +64,13 @@ class GpuBatch:
                     pkv_reshape_and_cache(kd, vd, self.k_cache, self.v_cache, sd, s.block_size)
                     if op.decode:
                         self.decode = DecodeInputs(kd, vd, sd)
+                        decode_seqs = np.asarray(op.seqs)
                     del k, v
             else:
                 raise TypeError(op)
         ids = sorted(self.seq_ids)
+        # pkv_decode_step pairs row i of the new K/V with row i of the block table
+        self.decode_rows_match = self.decode is not None and np.array_equal(decode_seqs, np.asarray(ids))
         self.max_blocks = max(1, max(self.pool.info(i)[1] for i in ids)) if ids else 1
         tables, lens = self.pool.block_tables(ids, self.max_blocks)
         self.tables_host, self.lens_host = tables, lens
@@ -116,6 +120,17 @@ class GpuBatch:
                               self.workload.spec.block_size, stream)
 
     def step(self, partition_size: Optional[int] = None, stream=None):
-        """One decode step: write each sequence's new token, then attend over its context."""
+        """One decode step: write each sequence's new token, then attend over its context (one call)."""
+        p = self.workload.spec.partition_size if partition_size is None else partition_size
+        d = self.decode
+        if not self.decode_rows_match:
+            raise ValueError("the decode token rows are not in block-table row order")
+        pkv_decode_step(d.k_new, d.v_new, self.out, self.q, self.k_cache, self.v_cache, self.block_tables,
+                        self.context_lens, self.max_context_len, float(self.workload.scale), p, self.workspace(p),
+                        stream)
+        return self.out
+
+    def step_separate(self, partition_size: Optional[int] = None, stream=None):
+        """The same step as two calls: pkv_reshape_and_cache, then pkv_paged_attention_decode."""
         self.write_decode_token(stream)
         return self.attention(partition_size, stream=stream)

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(libpkv):
     assert len(syms) >= 18
     missing = [s for s in syms if not hasattr(libpkv, s)]
     assert missing == []
-    assert pk.pkv_abi_version() == 3
+    assert pk.pkv_abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert libpkv.pkv_status_string(code)
 
@@ -191,6 +191,12 @@ def test_workspace_size_and_device_arg_checks(libpkv):
                                         None, 0, 1, None) == _lib.PKV_OK  # empty batch: no-op
     assert L.pkv_paged_attention_decode(None, None, None, None, None, None, 2, 8, 8, 128, 16, 10, 4, 64, 1.0, 0,
                                         None, 0, 1, None) == _lib.PKV_ERR_INVALID_ARG  # NULL buffers
+    buf = [vp(4096)] * 6  # aligned stand-ins: every call below is rejected before any device work
+    step_args = (2, 8, 8, 128, 16, 10, 4, 64, 1.0, 0, None, 0, 1, None)
+    assert L.pkv_decode_step(None, None, *buf, *step_args) == _lib.PKV_ERR_INVALID_ARG  # no new token
+    assert L.pkv_decode_step(vp(4096), None, *buf, *step_args) == _lib.PKV_ERR_INVALID_ARG  # K without V
+    assert L.pkv_decode_step(vp(4104), vp(4096), *buf, *step_args) == _lib.PKV_ERR_INVALID_ARG  # misaligned K
+    assert L.pkv_decode_step(vp(4096), vp(4096), None, *buf[1:], *step_args) == _lib.PKV_ERR_INVALID_ARG
     assert L.pkv_reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 10, 1, None) == _lib.PKV_OK
     assert L.pkv_reshape_and_cache(None, None, None, None, None, 3, 8, 128, 16, 10, 1, None) == _lib.PKV_ERR_INVALID_ARG
     assert L.pkv_reshape_and_cache(None, None, None, None, None, 3, 8, 128, 24, 10, 1, None) == _lib.PKV_ERR_UNSUPPORTED

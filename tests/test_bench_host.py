@@ -1,0 +1,43 @@
+"""Host logic of bench.py: reading HBM traffic out of rocprofv3 counter CSVs."""
+
+import csv
+import os
+
+import bench
+
+PLAIN = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, false>(pkv::AttnArgs)"
+STEP = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, true>(pkv::AttnArgs)"
+COPY = "void pkv::(anonymous namespace)::copy_probe_kernel(uint4 const*, uint4*, long)"
+
+
+def write_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value", "Grid_Size"])
+        w.writeheader()
+        for name, ctr, val in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": ctr, "Counter_Value": val, "Grid_Size": 512})
+
+
+def test_partition_pass_name():
+    assert bench.is_partition_pass(PLAIN)
+    assert not bench.is_partition_pass(STEP)
+    assert bench.is_partition_pass(PLAIN.replace("true, false", "false, false"))
+    assert not bench.is_partition_pass("void pkv::(anonymous namespace)::lse_reduce_kernel<128>(pkv::AttnArgs)")
+
+
+def test_traffic_summary_scales_by_the_copy_and_skips_the_step_variant(tmp_path):
+    gib = 1 << 30
+    # the copy reads 1 GiB but its counter reads half of that: a scale of 2; writes read true
+    fetch = [(COPY, "FETCH_SIZE", gib / 2 / 1024)] * 3 + [(PLAIN, "FETCH_SIZE", 1000.0)] * 5 + \
+            [(STEP, "FETCH_SIZE", 9999.0)] * 9
+    write = [(COPY, "WRITE_SIZE", gib / 1024)] * 3 + [(PLAIN, "WRITE_SIZE", 10.0)] * 5 + \
+            [(STEP, "WRITE_SIZE", 9999.0)] * 9
+    write_csv(str(tmp_path / "f" / "p_counter_collection.csv"), fetch)
+    write_csv(str(tmp_path / "w" / "p_counter_collection.csv"), write)
+    out = bench.traffic_summary([str(tmp_path / "f"), str(tmp_path / "w")], "llama7b_bf16")
+    assert out["read_scale"] == 2.0 and out["write_scale"] == 1.0
+    assert out["read_dispatches"] == 5 and out["write_dispatches"] == 5
+    assert out["read_bytes_per_launch"] == 1000.0 * 1024 * 2
+    assert out["write_bytes_per_launch"] == 10.0 * 1024
+    assert out["hbm_bytes_per_launch"] == 1000.0 * 1024 * 2 + 10.0 * 1024

@@ -318,6 +318,122 @@ def test_step_replays_as_a_graph():
             assert torch.equal(gb.out, eager), i
 
 
+def cache_bits(t):
+    """Integer view of a device cache, so NaN poison compares bit for bit."""
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+def poison_decode_slots(gb):
+    """Overwrite every sequence's decode-token slot with NaN."""
+    import paged_kv_cache_physical_amd as pk
+    d = gb.decode
+    pk.pkv_reshape_and_cache(torch.full_like(d.k_new, float("nan")), torch.full_like(d.v_new, float("nan")),
+                             gb.k_cache, gb.v_cache, d.slots, gb.workload.spec.block_size)
+
+
+DECODE_STEP_CASES = [
+    # (seqs, lengths, G, H_kv, d, B, dtype, P): split runs with a workspace, the
+    # unsplit kernel, fine lane cuts, fp32, and more sequences than the listed
+    # split takes (partition items, with a separate token write)
+    (40, (100, 3000), 4, 4, 128, 16, "bf16", 256),
+    (40, (100, 3000), 4, 4, 128, 16, "bf16", 0),
+    (300, (100, 2000), 4, 2, 128, 16, "bf16", 256),
+    (30, (1, 700), 8, 2, 64, 32, "f32", 64),
+    (25, (1, 400), 1, 4, 128, 32, "bf16", 32),
+    (4200, (1, 90), 2, 2, 64, 16, "bf16", 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DECODE_STEP_CASES)))
+def test_decode_step_equals_separate_calls(case):
+    # pkv_decode_step (token write inside the attention call) gives the bits of
+    # pkv_reshape_and_cache followed by pkv_paged_attention_decode: the same
+    # output and the same caches, starting from caches whose decode slots hold NaN
+    GpuBatch = runner()
+    nseq, lens, G, Hkv, d, B, dt, P = DECODE_STEP_CASES[case]
+    say(f"case {case}: S={nseq} lens={lens} G={G} Hkv={Hkv} d={d} B={B} {dt} P={P}")
+    w = wl.small_decode(nseq, lens, G * Hkv, Hkv, d, B, dt, seed=31 + case)
+    gb = GpuBatch(w)
+    assert gb.decode_rows_match
+    ref = gb.step_separate(P).clone()
+    k0, v0 = cache_bits(gb.k_cache).clone(), cache_bits(gb.v_cache).clone()
+    for i in range(2):
+        poison_decode_slots(gb)
+        assert not torch.equal(cache_bits(gb.k_cache), k0)
+        gb.out.fill_(float("nan"))
+        gb.step(P)
+        torch.cuda.synchronize()
+        assert torch.equal(cache_bits(gb.k_cache), k0), i
+        assert torch.equal(cache_bits(gb.v_cache), v0), i
+        assert torch.equal(gb.out, ref), i
+
+
+@pytest.mark.parametrize("name", ["llama7b_bf16", "gqa_bf16_b16", "gqa_bf16_b32", "beam_cow_bf16", "long_bf16"])
+def test_decode_step_named_full_size(name):
+    # the benchmarked step at full size, copy-on-write forks included: the
+    # fused call writes every new token and matches the separate calls bitwise
+    GpuBatch = runner()
+    w = wl.named(name, seed=5)
+    say(f"case {name}: S={w.num_seqs} max_n={w.max_context_len}")
+    gb = GpuBatch(w)
+    assert gb.decode_rows_match
+    P = w.spec.partition_size
+    ref = gb.step_separate(P).clone()
+    k0, v0 = cache_bits(gb.k_cache).clone(), cache_bits(gb.v_cache).clone()
+    poison_decode_slots(gb)
+    gb.out.fill_(float("nan"))
+    gb.step(P)
+    torch.cuda.synchronize()
+    assert torch.equal(cache_bits(gb.k_cache), k0)
+    assert torch.equal(cache_bits(gb.v_cache), v0)
+    assert torch.equal(gb.out, ref)
+
+
+@pytest.mark.parametrize("nseq", [5, 4100])
+def test_decode_step_skips_bad_sequences(nseq):
+    # a sequence with a zero, negative or too-long length, or whose last block
+    # id is out of range, gets no token write; the others are written as usual
+    import paged_kv_cache_physical_amd as pk
+    GpuBatch = runner()
+    w = wl.small_decode(nseq, (40, 300), 8, 2, 128, 16, "bf16", seed=4)
+    gb = GpuBatch(w)
+    ref = gb.step_separate(64).cpu().numpy()
+    good_k, good_v = cache_bits(gb.k_cache).clone(), cache_bits(gb.v_cache).clone()
+    poison_decode_slots(gb)
+    # the expected caches: the four bad sequences keep their poisoned slots
+    d = gb.decode
+    bad_rows = [0, 1, 2, 3]
+    keep = torch.ones(nseq, dtype=torch.bool, device="cuda")
+    keep[bad_rows] = False
+    kc, vc = gb.k_cache.clone(), gb.v_cache.clone()
+    pk.pkv_reshape_and_cache(d.k_new[keep].contiguous(), d.v_new[keep].contiguous(), kc, vc,
+                             d.slots[keep].contiguous(), 16)
+    exp_k, exp_v = cache_bits(kc), cache_bits(vc)
+    lens = gb.context_lens.clone()
+    bad_lens = lens.clone()
+    bad_lens[0], bad_lens[1], bad_lens[2] = 0, -3, gb.max_context_len + 1
+    gb.context_lens.copy_(bad_lens)
+    tables = gb.block_tables.clone()
+    bad_tables = tables.clone()
+    bad_tables[3, (int(lens[3]) - 1) // 16] = w.num_blocks
+    gb.block_tables.copy_(bad_tables)
+    gb.out.fill_(float("nan"))
+    gb.step(64)
+    torch.cuda.synchronize()
+    assert torch.equal(cache_bits(gb.k_cache), exp_k)
+    assert torch.equal(cache_bits(gb.v_cache), exp_v)
+    out = gb.out.cpu().numpy()
+    assert np.all(out[0] == 0)
+    assert np.all(np.isnan(out[1:4]))
+    np.testing.assert_array_equal(out[4:], ref[4:])
+    gb.context_lens.copy_(lens)
+    gb.block_tables.copy_(tables)
+    gb.step(64)
+    torch.cuda.synchronize()
+    assert torch.equal(cache_bits(gb.k_cache), good_k) and torch.equal(cache_bits(gb.v_cache), good_v)
+    np.testing.assert_array_equal(gb.out.cpu().numpy(), ref)
+
+
 def test_edge_lengths_and_bad_inputs():
     GpuBatch = runner()
     w = wl.small_decode(5, (40, 300), 8, 2, 128, 16, "bf16", seed=4)
