@@ -10,6 +10,10 @@ What it follows:
     count tied to request lifetime; a branch that writes into a shared block
     that is not yet full copies it first ([P3] section 3; [P4] beam-search
     sharing figure; [P2] key technical point 3).
+  * Preemption by swapping: the blocks of sequences that must wait are moved
+    to host memory and brought back when device blocks are free again
+    ([P2] section 4 "scheduling: first come first served plus preemption";
+    [P4] "Preemption", swapping).
 
 Readings where the pages are silent:
   * The free blocks form a FIFO queue seeded by a given order: allocation pops
@@ -21,6 +25,14 @@ Readings where the pages are silent:
     writes in place; full blocks are never written again and so never copied.
   * An append batch is all or nothing: if the pool runs out, nothing changes.
   * Token position p of a sequence lives in slot table[p // B] * B + p % B.
+  * Swapping works on whole sharing groups: every holder of a block moves with
+    it (beams of one request move together), so a listed set whose blocks are
+    also held by an unlisted sequence is refused.  The host tier has its own
+    FIFO queue of host block ids 0, 1, 2, ...  Swap-out meets the listed
+    sequences' blocks in list order, then logical order; each distinct device
+    block takes the next host block, which inherits its refcount, and the
+    device block joins the device queue's tail.  Swap-in mirrors it.  Both are
+    all or nothing.  A swapped-out sequence can only be swapped in or freed.
 
 This model applies each batch to a deep copy of the state and commits the copy
 only on success, which makes the all-or-nothing rule evident.
@@ -52,16 +64,22 @@ class InvalidArg(PoolError):
     pass
 
 
+class WrongTier(PoolError):
+    """The sequence is on the other tier (swapped out, or not swapped out)."""
+
+
 @dataclass
 class _Seq:
     table: List[int] = field(default_factory=list)
     length: int = 0
+    on_host: bool = False  # swapped out: the table holds host block ids
 
 
 class BlockPool:
-    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
-        if num_blocks <= 0 or block_size <= 0:
-            raise InvalidArg("num_blocks and block_size must be positive")
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None,
+                 host_blocks: int = 0):
+        if num_blocks <= 0 or block_size <= 0 or host_blocks < 0:
+            raise InvalidArg("num_blocks and block_size must be positive, host_blocks not negative")
         order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
         if sorted(order) != list(range(num_blocks)):
             raise InvalidArg("free_order must be a permutation of the block ids")
@@ -71,6 +89,9 @@ class BlockPool:
         self.refcount = [0] * num_blocks
         self.seqs: Dict[int, _Seq] = {}
         self.next_id = 0
+        self.host_blocks = host_blocks
+        self.host_free: deque = deque(range(host_blocks))
+        self.host_refcount = [0] * host_blocks
 
     # -- sequences -----------------------------------------------------------
     def create(self) -> int:
@@ -84,9 +105,15 @@ class BlockPool:
             raise NoSuchSeq(sid)
         return self.seqs[sid]
 
+    def _on_device(self, sid: int) -> _Seq:
+        s = self._get(sid)
+        if s.on_host:
+            raise WrongTier(sid)
+        return s
+
     def fork(self, parent: int) -> int:
         """New sequence sharing every block of ``parent``; each shared block's count rises by one."""
-        p = self._get(parent)
+        p = self._on_device(parent)
         sid = self.create()
         self.seqs[sid] = _Seq(table=list(p.table), length=p.length)
         for b in p.table:
@@ -96,10 +123,11 @@ class BlockPool:
     def free_seq(self, sid: int) -> None:
         """Release ``sid``: counts drop in logical order; blocks reaching zero join the queue's tail."""
         s = self._get(sid)
+        refcount, queue = (self.host_refcount, self.host_free) if s.on_host else (self.refcount, self.free)
         for b in s.table:
-            self.refcount[b] -= 1
-            if self.refcount[b] == 0:
-                self.free.append(b)
+            refcount[b] -= 1
+            if refcount[b] == 0:
+                queue.append(b)
         del self.seqs[sid]
 
     # -- appends ---------------------------------------------------------------
@@ -145,6 +173,8 @@ class BlockPool:
             raise InvalidArg("negative count")
         for sid in seqs:
             self._get(sid)
+        for sid in seqs:
+            self._on_device(sid)
         trial = copy.deepcopy(self)
         slots: List[int] = []
         pairs: List[Tuple[int, int]] = []
@@ -152,6 +182,65 @@ class BlockPool:
             trial._append_one(sid, c, slots, pairs)
         self.__dict__.update(trial.__dict__)
         return np.asarray(slots, dtype=np.int64), np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+
+    # -- swapping --------------------------------------------------------------------
+    def _swap(self, seqs: Sequence[int], out: bool) -> np.ndarray:
+        seqs = [int(x) for x in seqs]
+        if len(set(seqs)) != len(seqs):
+            raise InvalidArg("a sequence appears twice in one swap")
+        for sid in seqs:
+            self._get(sid)
+        for sid in seqs:
+            if self.seqs[sid].on_host == out:
+                raise WrongTier(sid)
+        src_ref, src_queue = (self.refcount, self.free) if out else (self.host_refcount, self.host_free)
+        dst_ref, dst_queue = (self.host_refcount, self.host_free) if out else (self.refcount, self.free)
+        # the blocks in the order they are met, and how often the listed tables hold each
+        met: List[int] = []
+        held: Dict[int, int] = {}
+        for sid in seqs:
+            for b in self.seqs[sid].table:
+                if b not in held:
+                    held[b] = 0
+                    met.append(b)
+                held[b] += 1
+        if any(held[b] != src_ref[b] for b in met):
+            raise InvalidArg("a block of the listed sequences is also held by an unlisted one")
+        if len(met) > len(dst_queue):
+            raise OutOfBlocks()
+        moved: Dict[int, int] = {}
+        for b in met:
+            nb = dst_queue.popleft()
+            dst_ref[nb] = src_ref[b]
+            src_ref[b] = 0
+            src_queue.append(b)
+            moved[b] = nb
+        for sid in seqs:
+            s = self.seqs[sid]
+            s.table = [moved[b] for b in s.table]
+            s.on_host = out
+        return np.asarray([(b, moved[b]) for b in met], dtype=np.int32).reshape(-1, 2)
+
+    def swap_out(self, seqs: Sequence[int]) -> np.ndarray:
+        """Move the listed sequences (a whole sharing group) to the host tier.
+
+        Returns int32 pairs (device block, host block) in the order the blocks
+        are met; the caller copies each device block to its host block before
+        the freed device blocks are written again.  Raises InvalidArg (a block
+        also held outside the list), WrongTier (already on the host),
+        OutOfBlocks (host tier too small); the state is then unchanged.
+        """
+        return self._swap(seqs, True)
+
+    def swap_in(self, seqs: Sequence[int]) -> np.ndarray:
+        """Bring swapped-out sequences back; pairs are (host block, device block)."""
+        return self._swap(seqs, False)
+
+    def on_host(self, sid: int) -> bool:
+        return self._get(sid).on_host
+
+    def host_free_list(self) -> List[int]:
+        return list(self.host_free)
 
     # -- views ---------------------------------------------------------------------
     def length(self, sid: int) -> int:
@@ -164,6 +253,8 @@ class BlockPool:
         """Dense int32 tables ``[n][max_blocks]`` padded with -1, and the context lengths."""
         out = np.full((len(seqs), max_blocks), -1, dtype=np.int32)
         lens = np.zeros(len(seqs), dtype=np.int32)
+        for sid in seqs:
+            self._on_device(int(sid))
         for i, sid in enumerate(seqs):
             s = self._get(int(sid))
             if len(s.table) > max_blocks:
@@ -174,17 +265,24 @@ class BlockPool:
 
     def stats(self) -> Dict[str, int]:
         used = sum(1 for r in self.refcount if r > 0)
-        logical_blocks = sum(len(s.table) for s in self.seqs.values())
+        resident = [s for s in self.seqs.values() if not s.on_host]
+        swapped = [s for s in self.seqs.values() if s.on_host]
+        logical_blocks = sum(len(s.table) for s in resident)
         return {
             "num_blocks": self.num_blocks,
             "free_blocks": len(self.free),
             "used_blocks": used,
             "sum_refcount": sum(self.refcount),
             "num_seqs": len(self.seqs),
-            "logical_tokens": sum(s.length for s in self.seqs.values()),
+            "logical_tokens": sum(s.length for s in resident),
             "logical_blocks": logical_blocks,
             "allocated_slots": used * self.block_size,
             "table_bytes": 4 * logical_blocks,
+            "host_blocks": self.host_blocks,
+            "host_free_blocks": len(self.host_free),
+            "host_used_blocks": sum(1 for r in self.host_refcount if r > 0),
+            "swapped_seqs": len(swapped),
+            "swapped_tokens": sum(s.length for s in swapped),
         }
 
     def free_list(self) -> List[int]:

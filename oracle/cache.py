@@ -85,6 +85,17 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs: np.ndarray) -> 
         v_cache[dst] = v_cache[src]
 
 
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray, pairs) -> None:
+    """Copy whole blocks from one cache pair to another: dst block j <- src block i for each (i, j).
+
+    The data half of preemption by swapping: a waiting sequence's blocks move
+    to host memory and later back ([P2] section 4; [P4] "Preemption").
+    """
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]
+
+
 def gather(k_cache: np.ndarray, v_cache: np.ndarray, table, n: int) -> Tuple[np.ndarray, np.ndarray]:
     """Logical K and V ``[n][H_kv][d]`` of a sequence, read through its block table."""
     nb, H, npieces, B, X = k_cache.shape

@@ -15,16 +15,16 @@ from oracle import run as orun
 
 
 def check_invariants(pool: al.BlockPool):
-    live = [b for s in pool.seqs.values() for b in s.table]
-    assert sum(pool.refcount) == len(live)
-    counts = np.bincount(np.asarray(live, dtype=np.int64), minlength=pool.num_blocks) if live else \
-        np.zeros(pool.num_blocks, np.int64)
-    assert list(counts) == pool.refcount
-    free = pool.free_list()
-    assert len(set(free)) == len(free)
-    assert all(pool.refcount[b] == 0 for b in free)
-    used = sum(1 for r in pool.refcount if r > 0)
-    assert len(free) + used == pool.num_blocks
+    for on_host, refcount, free, n in ((False, pool.refcount, pool.free_list(), pool.num_blocks),
+                                       (True, pool.host_refcount, pool.host_free_list(), pool.host_blocks)):
+        live = [b for s in pool.seqs.values() if s.on_host == on_host for b in s.table]
+        assert sum(refcount) == len(live)
+        counts = np.bincount(np.asarray(live, dtype=np.int64), minlength=n) if live else np.zeros(n, np.int64)
+        assert list(counts) == refcount
+        assert len(set(free)) == len(free)
+        assert all(refcount[b] == 0 for b in free)
+        used = sum(1 for r in refcount if r > 0)
+        assert len(free) + used == n
     for s in pool.seqs.values():
         assert len(s.table) == cf.blocks_for(s.length, pool.block_size)
 
@@ -191,3 +191,165 @@ def test_full_pool_long_context():
     assert st["free_blocks"] == 0 and st["used_blocks"] == 16384
     with pytest.raises(al.OutOfBlocks):
         rp.pool.append([0], [1])
+
+
+def swap_scenario():
+    """The hand-traced swapping scenario (see test_swap_by_hand); returns the pool and the ids."""
+    pool = al.BlockPool(6, 4, host_blocks=4)
+    a = pool.create()
+    pool.append([a], [6])  # device blocks 0, 1
+    b = pool.fork(a)
+    _, cow = pool.append([b], [1])  # b writes into shared partial block 1: copied to block 2
+    c = pool.create()
+    pool.append([c], [4])  # block 3
+    return pool, a, b, c, cow
+
+
+def test_swap_by_hand():
+    pool, a, b, c, cow = swap_scenario()
+    assert cow.tolist() == [[1, 2]]
+    assert pool.table(a) == [0, 1] and pool.table(b) == [0, 2] and pool.table(c) == [3]
+    assert pool.free_list() == [4, 5]
+    # c alone: its block 3 takes host block 0 and joins the device queue's tail
+    assert pool.swap_out([c]).tolist() == [[3, 0]]
+    assert pool.free_list() == [4, 5, 3] and pool.table(c) == [0] and pool.on_host(c)
+    # a without b is not a whole sharing group (block 0 is held by both)
+    with pytest.raises(al.InvalidArg):
+        pool.swap_out([a])
+    # a then b: blocks met in order 0, 1, 2 take host blocks 1, 2, 3; block 0 keeps its count of 2
+    assert pool.swap_out([a, b]).tolist() == [[0, 1], [1, 2], [2, 3]]
+    assert pool.table(a) == [1, 2] and pool.table(b) == [1, 3]
+    assert pool.host_refcount == [1, 2, 1, 1] and pool.refcount == [0] * 6
+    assert pool.free_list() == [4, 5, 3, 0, 1, 2] and pool.host_free_list() == []
+    # b listed first: host blocks met in order 1, 3, 2 take device blocks 4, 5, 3
+    assert pool.swap_in([b, a]).tolist() == [[1, 4], [3, 5], [2, 3]]
+    assert pool.table(b) == [4, 5] and pool.table(a) == [4, 3]
+    assert pool.refcount[3:6] == [1, 2, 1] and pool.host_refcount == [1, 0, 0, 0]
+    assert pool.host_free_list() == [1, 3, 2] and pool.free_list() == [0, 1, 2]
+    assert pool.swap_in([c]).tolist() == [[0, 0]]
+    assert pool.table(c) == [0] and pool.host_free_list() == [1, 3, 2, 0] and pool.free_list() == [1, 2]
+    # the swapped-in sequences append as before: a's partial block 3 is its own, b's block 5 too
+    slots, pairs = pool.append([a, b], [1, 1])
+    assert pairs.shape == (0, 2) and list(slots) == [3 * 4 + 2, 5 * 4 + 3]
+    check_invariants(pool)
+
+
+def test_swap_errors_change_nothing():
+    pool, a, b, c, _ = swap_scenario()
+    snap = lambda: (pool.free_list(), pool.host_free_list(), list(pool.refcount), list(pool.host_refcount),
+                    [pool.table(x) for x in (a, b, c)], [pool.on_host(x) for x in (a, b, c)])
+    before = snap()
+    with pytest.raises(al.InvalidArg):
+        pool.swap_out([a])  # block 0 also held by b
+    with pytest.raises(al.InvalidArg):
+        pool.swap_out([c, c])
+    with pytest.raises(al.NoSuchSeq):
+        pool.swap_out([9])
+    with pytest.raises(al.WrongTier):
+        pool.swap_in([c])  # not swapped out
+    small = al.BlockPool(6, 4, host_blocks=2)
+    x = small.create()
+    small.append([x], [9])  # 3 blocks > 2 host blocks
+    with pytest.raises(al.OutOfBlocks):
+        small.swap_out([x])
+    assert small.table(x) == [0, 1, 2] and not small.on_host(x)
+    assert snap() == before
+    pool.swap_out([c])
+    with pytest.raises(al.WrongTier):
+        pool.swap_out([c])
+    with pytest.raises(al.WrongTier):
+        pool.append([c], [1])
+    with pytest.raises(al.WrongTier):
+        pool.fork(c)
+    with pytest.raises(al.WrongTier):
+        pool.block_tables([c], 4)
+    # freeing a swapped-out sequence returns its host blocks
+    pool.free_seq(c)
+    assert pool.host_free_list() == [1, 2, 3, 0]
+    check_invariants(pool)
+
+
+def test_swap_round_trip_keeps_every_token():
+    # brute force: distinct values per device slot, swap a group out, let other
+    # sequences overwrite the freed blocks, swap it back and read every token
+    from oracle import cache as oc
+    rng = np.random.default_rng(5)
+    B, H, d = 4, 2, 64
+    pool = al.BlockPool(12, B, rng.permutation(12), host_blocks=8)
+    kc, vc = oc.empty_caches(12, H, B, d, "f32")
+    hk, hv = oc.empty_caches(8, H, B, d, "f32")
+    p = pool.create()
+    slots, _ = pool.append([p], [10])
+    kv = rng.standard_normal((2, 10, H, d)).astype(np.float32)
+    oc.scatter(kc, vc, kv[0], kv[1], slots)
+    kids = [pool.fork(p) for _ in range(2)]
+    toks = {p: (kv[0], kv[1])}
+    for kid in kids:  # each child adds 3 tokens: copy-on-write of the shared partial block first
+        slots, pairs = pool.append([kid], [3])
+        oc.copy_blocks(kc, vc, pairs)
+        new = rng.standard_normal((2, 3, H, d)).astype(np.float32)
+        oc.scatter(kc, vc, new[0], new[1], slots)
+        toks[kid] = (np.concatenate([kv[0], new[0]]), np.concatenate([kv[1], new[1]]))
+    group = [p] + kids
+    out_pairs = pool.swap_out(group)
+    oc.swap_blocks(kc, vc, hk, hv, out_pairs)
+    other = pool.create()
+    slots, _ = pool.append([other], [4 * len(pool.free_list())])  # takes every free device block
+    junk = np.full((len(slots), H, d), 7.0, np.float32)
+    oc.scatter(kc, vc, junk, junk, slots)
+    pool.free_seq(other)
+    in_pairs = pool.swap_in(group[::-1])
+    oc.swap_blocks(hk, hv, kc, vc, in_pairs)
+    for sid in group:
+        k, v = oc.gather(kc, vc, pool.table(sid), pool.length(sid))
+        assert np.array_equal(k, toks[sid][0]) and np.array_equal(v, toks[sid][1])
+    # sharing survives: the prefix blocks are still one physical block per position
+    assert pool.table(p)[:2] == pool.table(kids[0])[:2] == pool.table(kids[1])[:2]
+    check_invariants(pool)
+
+
+def test_random_swaps_keep_invariants():
+    rng = np.random.default_rng(321)
+    for trial in range(20):
+        nb, hb, B = int(rng.integers(4, 40)), int(rng.integers(0, 30)), int(rng.choice([1, 2, 4, 16]))
+        pool = al.BlockPool(nb, B, rng.permutation(nb), host_blocks=hb)
+        for _ in range(60):
+            op = int(rng.integers(0, 6))
+            dev = [s for s in pool.seqs if not pool.on_host(s)]
+            host = [s for s in pool.seqs if pool.on_host(s)]
+            total = sum(pool.refcount) + sum(pool.host_refcount)
+            if op == 0 or not pool.seqs:
+                pool.create()
+            elif op == 1 and dev:
+                pool.fork(int(rng.choice(dev)))
+            elif op == 2:
+                pool.free_seq(int(rng.choice(list(pool.seqs))))
+            elif op == 3 and dev:
+                k = int(rng.integers(1, len(dev) + 1))
+                try:
+                    pool.append(list(rng.choice(dev, size=k, replace=False)), list(rng.integers(0, 20, size=k)))
+                except al.OutOfBlocks:
+                    pass
+            elif op in (4, 5):
+                tier = dev if op == 4 else host
+                if tier:
+                    group = group_of(pool, int(rng.choice(tier)))
+                    try:
+                        pairs = pool.swap_out(group) if op == 4 else pool.swap_in(group)
+                        assert sum(pool.refcount) + sum(pool.host_refcount) == total
+                        assert len(set(pairs[:, 1].tolist())) == len(pairs)
+                    except al.OutOfBlocks:
+                        pass
+            check_invariants(pool)
+
+
+def group_of(pool: al.BlockPool, sid: int):
+    """The sharing group of sid: sequences linked by a common block in the same tier."""
+    group, todo = {sid}, [sid]
+    while todo:
+        s = pool.seqs[todo.pop()]
+        for o, t in pool.seqs.items():
+            if o not in group and t.on_host == s.on_host and set(t.table) & set(s.table):
+                group.add(o)
+                todo.append(o)
+    return sorted(group)

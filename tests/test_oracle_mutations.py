@@ -2,8 +2,10 @@
 
 Each mutant replaces one oracle function by a plausible wrong version (wrong head
 grouping, missing scale, swapped operands, no max subtraction, off-by-one slot
-offset, LIFO reuse, copy-on-write that forgets the refcount) and reruns pin
-tests, which must then fail.
+offset, LIFO reuse, copy-on-write that forgets the refcount, a swap that drops
+the refcount, skips the sharing-group check or releases LIFO, a block copy read
+backwards) and reruns pin tests, which must then fail (an assertion, an
+expected error that is not raised, or an index out of range).
 """
 
 import numpy as np
@@ -84,7 +86,7 @@ def _fails_some(pins):
     for pin in pins:
         try:
             pin()
-        except (AssertionError, ValueError, FloatingPointError):
+        except (AssertionError, ValueError, FloatingPointError, IndexError, pytest.fail.Exception):
             return True
     return False
 
@@ -181,3 +183,50 @@ def test_cow_on_full_blocks_is_caught(monkeypatch):
 
     monkeypatch.setattr(al.BlockPool, "_append_one", bad_append_one)
     assert _fails_some([t_alloc.test_fork_and_copy_on_write_by_hand])
+
+
+def _swap_variant(carry_refcount=True, check_group=True, lifo=False):
+    """A swap with one planted mistake (refcount not carried, no sharing-group check, or LIFO release)."""
+    def swap(self, seqs, out):
+        seqs = [int(x) for x in seqs]
+        src_ref, src_q = (self.refcount, self.free) if out else (self.host_refcount, self.host_free)
+        dst_ref, dst_q = (self.host_refcount, self.host_free) if out else (self.refcount, self.free)
+        met, held = [], {}
+        for sid in seqs:
+            for b in self.seqs[sid].table:
+                if b not in held:
+                    held[b] = 0
+                    met.append(b)
+                held[b] += 1
+        if check_group and any(held[b] != src_ref[b] for b in met):
+            raise al.InvalidArg("not a whole group")
+        if len(met) > len(dst_q):
+            raise al.OutOfBlocks()
+        moved = {}
+        for b in met:
+            nb = dst_q.popleft()
+            dst_ref[nb] = src_ref[b] if carry_refcount else 1
+            src_ref[b] = 0
+            src_q.appendleft(b) if lifo else src_q.append(b)
+            moved[b] = nb
+        for sid in seqs:
+            self.seqs[sid].table = [moved[b] for b in self.seqs[sid].table]
+            self.seqs[sid].on_host = out
+        return np.asarray([(b, moved[b]) for b in met], dtype=np.int32).reshape(-1, 2)
+    return swap
+
+
+@pytest.mark.parametrize("kw", [{"carry_refcount": False}, {"check_group": False}, {"lifo": True}])
+def test_swap_mutants_are_caught(monkeypatch, kw):
+    monkeypatch.setattr(al.BlockPool, "_swap", _swap_variant(**kw))
+    assert _fails_some([t_alloc.test_swap_by_hand, t_alloc.test_swap_round_trip_keeps_every_token])
+
+
+def test_swap_copy_direction_is_caught(monkeypatch):
+    def reversed_pairs(src_k, src_v, dst_k, dst_v, pairs):
+        for a, b in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+            dst_k[a] = src_k[b]  # wrong: pair read as (to, from)
+            dst_v[a] = src_v[b]
+
+    monkeypatch.setattr(oc, "swap_blocks", reversed_pairs)
+    assert _fails_some([t_alloc.test_swap_round_trip_keeps_every_token])
