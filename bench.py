@@ -231,6 +231,64 @@ def cpu_baseline(w, budget_s=12.0):
                       f"{elapsed:.1f}s"}
 
 
+HOST_LINK_PEAK_GBPS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes, 128b/130b coding
+
+
+def measure_swap(stream, block_tokens=(1, 4, 16, 32), per_cache=256 << 20):
+    """Preemption by swapping, at the Llama-7B layer shape (H_kv 32, d 128, bf16): move per_cache bytes of
+    scattered device blocks of each cache to consecutive page-locked host blocks and back, with pkv_swap_blocks
+    (one launch for every block of both caches) and with one DMA copy per block (hipMemcpyAsync through torch,
+    whose per-call host cost is part of what it measures), at several block sizes; one contiguous DMA copy of
+    the same bytes gives the link's ceiling."""
+    import torch
+    from paged_kv_cache_physical_amd import pkv_swap_blocks
+    H, d = 32, 128
+    rng = np.random.default_rng(0)
+    out = {}
+    for bt in block_tokens:
+        bb = bt * H * d * 2  # bytes of one block of one cache
+        n = per_cache // bb
+        dk = torch.zeros((2 * n, bb // 2), dtype=torch.bfloat16, device="cuda")
+        dv = torch.zeros_like(dk)
+        hk = torch.zeros((n, bb // 2), dtype=torch.bfloat16).pin_memory()
+        hv = torch.zeros((n, bb // 2), dtype=torch.bfloat16).pin_memory()
+        src = rng.choice(2 * n, size=n, replace=False)
+        p_out = np.stack([src, np.arange(n)], 1).astype(np.int32)
+        p_in = np.ascontiguousarray(p_out[:, ::-1])
+        po, pi = torch.from_numpy(p_out).cuda(), torch.from_numpy(p_in).cuda()
+        moved = 2 * n * bb
+        with torch.cuda.stream(stream):
+            k_out = time_launches(lambda: pkv_swap_blocks(dk, dv, hk, hv, po, stream), 4, stream)
+            k_in = time_launches(lambda: pkv_swap_blocks(hk, hv, dk, dv, pi, stream), 4, stream)
+
+            def dma(pairs, sk, sv, tk, tv):
+                for i, j in pairs.tolist():
+                    tk[j].copy_(sk[i], non_blocking=True)
+                    tv[j].copy_(sv[i], non_blocking=True)
+
+            d_out = time_launches(lambda: dma(p_out, dk, dv, hk, hv), 1, stream)
+            d_in = time_launches(lambda: dma(p_in, hk, hv, dk, dv), 1, stream)
+
+            def bulk(sk, sv, tk, tv):  # one contiguous copy per cache: the DMA engines' own ceiling
+                tk[:n].copy_(sk[:n], non_blocking=True)
+                tv[:n].copy_(sv[:n], non_blocking=True)
+
+            b_out = time_launches(lambda: bulk(dk, dv, hk, hv), 4, stream)
+            b_in = time_launches(lambda: bulk(hk, hv, dk, dv), 4, stream)
+        torch.cuda.synchronize()
+        gbps = lambda ms: moved / (ms * 1e-3) / 1e9
+        out[f"block_tokens_{bt}"] = {
+            "block_bytes": bb, "blocks_per_cache": n, "bytes_each_way": moved,
+            "kernel_out_gbps": round(gbps(k_out[1]), 2), "kernel_in_gbps": round(gbps(k_in[1]), 2),
+            "dma_per_block_out_gbps": round(gbps(d_out[0]), 2), "dma_per_block_in_gbps": round(gbps(d_in[0]), 2),
+            "dma_contiguous_out_gbps": round(gbps(b_out[1]), 2), "dma_contiguous_in_gbps": round(gbps(b_in[1]), 2),
+            "kernel_out_us": round(1e3 * k_out[1], 1), "kernel_in_us": round(1e3 * k_in[1], 1)}
+        log(f"[bench] swap, {bt}-token blocks: {json.dumps(out[f'block_tokens_{bt}'])}")
+        del dk, dv, hk, hv, po, pi
+        torch.cuda.empty_cache()
+    return {"shape": "H_kv 32, d 128, bf16, both caches", "host_link_peak_gbps": HOST_LINK_PEAK_GBPS, **out}
+
+
 def copy_probe(stream, nbytes=1 << 30):
     """A plain device copy of known size (reads and writes nbytes): the reference dispatch that
     scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -305,6 +363,7 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-extra", action="store_true", help="skip the other decode batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-swap", action="store_true", help="skip the device <-> host swap measurement")
     ap.add_argument("--partition", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated extra workloads")
     ap.add_argument("--copy-probe", action="store_true",
@@ -355,6 +414,7 @@ def main():
         log(f"[bench] host allocator step not timed: {e}")
     ceiling = hbm_read_ceiling(stream)
     log(f"[bench] streaming-read probe {ceiling:.0f} GB/s")
+    swap = None if args.no_swap else measure_swap(stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     if cpu:
         log(f"[bench] cpu baseline {json.dumps(cpu)}")
@@ -389,6 +449,7 @@ def main():
                      "bytes_per_launch": w.kv_bytes,
                      "launch_us": round(head["partition_kernel_us"]["mean"], 2)},
         "hbm_read_ceiling_gbps": round(ceiling, 1),
+        "swap": swap,
         "cpu_baseline": cpu,
         "other_workloads": extra,
         "kernel_source_sha": kernel_sha(),

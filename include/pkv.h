@@ -11,19 +11,21 @@
  *   [P3] auturnal.com analytical guide "paged-attention-serving" (sections
  *        1-6, "Equations and derivations" Eq. (1)-(3), "Verification protocol").
  *   [P4] cayang0802.github.io blog "paged-attention" (KV block and block
- *        table figure, beam-search sharing, preemption).
+ *        table figure, beam-search sharing, preemption by swapping).
  *
  * Two halves:
  *   - a host block pool (pkv_pool_*, pkv_seq_*, pkv_append_tokens,
- *     pkv_block_tables): fixed-size blocks, per-sequence block tables,
- *     on-demand allocation, refcounted sharing and copy-on-write.  Host
- *     memory only; no GPU is touched, so these calls also work on a machine
- *     without one.
- *   - device calls (pkv_reshape_and_cache, pkv_copy_blocks,
- *     pkv_paged_attention_decode): HIP kernels enqueued on the caller's
- *     stream.  Every pointer they take is caller-owned device memory; they
- *     allocate nothing, never synchronise, validate arguments on the host and
- *     return the error synchronously; a failed launch returns PKV_ERR_HIP.
+ *     pkv_block_tables, pkv_swap_out / pkv_swap_in): fixed-size blocks,
+ *     per-sequence block tables, on-demand allocation, refcounted sharing,
+ *     copy-on-write, and an optional host tier for preemption by swapping.
+ *     Host memory only; no GPU is touched, so these calls also work on a
+ *     machine without one.
+ *   - device calls (pkv_reshape_and_cache, pkv_copy_blocks, pkv_swap_blocks,
+ *     pkv_paged_attention_decode, pkv_decode_step): HIP kernels enqueued on
+ *     the caller's stream.  Every pointer they take is caller-owned memory the
+ *     GPU can reach; they allocate nothing, never synchronise, validate
+ *     arguments on the host and return the error synchronously; a failed
+ *     launch returns PKV_ERR_HIP.
  *
  * Status codes: 0 on success, negative on error.  On any error from the
  * pool, the pool's state is unchanged.
@@ -67,7 +69,8 @@ enum {
   PKV_ERR_REFCOUNT = -4,      /* pkv_pool_validate found a broken invariant */
   PKV_ERR_UNSUPPORTED = -5,   /* shape or dtype outside the supported set */
   PKV_ERR_HIP = -6,           /* a kernel launch failed */
-  PKV_ERR_WORKSPACE = -7      /* attention workspace missing or too small */
+  PKV_ERR_WORKSPACE = -7,     /* attention workspace missing or too small */
+  PKV_ERR_SWAPPED = -8        /* the sequence is on the other tier (swapped out, or not) */
 };
 
 enum { PKV_F32 = 0, PKV_BF16 = 1 };
@@ -79,11 +82,16 @@ typedef struct pkv_stats {
   int64_t free_blocks;     /* blocks in the free queue */
   int64_t used_blocks;     /* physical blocks with refcount > 0 */
   int64_t sum_refcount;    /* equals logical_blocks while the pool is sound */
-  int64_t num_seqs;        /* live sequences */
-  int64_t logical_tokens;  /* sum of live sequence lengths */
-  int64_t logical_blocks;  /* sum of live block-table lengths */
+  int64_t num_seqs;        /* live sequences, swapped out or not */
+  int64_t logical_tokens;  /* sum of the lengths of live sequences on the device */
+  int64_t logical_blocks;  /* sum of their block-table lengths */
   int64_t allocated_slots; /* used_blocks * B: Eq. (2)'s A_B summed, [P3] */
   int64_t table_bytes;     /* 4 * logical_blocks */
+  int64_t host_blocks;      /* host tier capacity (0: no host tier) */
+  int64_t host_free_blocks; /* host blocks in the host free queue */
+  int64_t host_used_blocks; /* host blocks with refcount > 0 */
+  int64_t swapped_seqs;     /* live sequences on the host tier */
+  int64_t swapped_tokens;   /* sum of their lengths */
 } pkv_stats;
 
 /* Human-readable name of a status code (static string). */
@@ -152,11 +160,13 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
  * row i = the physical blocks of seqs[i] in logical order, padded with -1;
  * out_context_lens[i] = its length in tokens ([P2] key technical point 1).
  * Errors: INVALID_ARG (a table longer than max_blocks, NULL arrays),
- * NO_SUCH_SEQ. */
+ * NO_SUCH_SEQ, SWAPPED (a sequence is swapped out: its blocks are host
+ * blocks, which the device calls cannot read). */
 pkv_status pkv_block_tables(const pkv_pool* pool, const int32_t* seqs, int32_t n, int32_t max_blocks,
                             int32_t* out_tables, int32_t* out_context_lens);
 
-/* Length in tokens and number of blocks of one sequence.  Errors: NO_SUCH_SEQ. */
+/* Length in tokens and number of blocks of one sequence (either tier).
+ * Errors: NO_SUCH_SEQ. */
 pkv_status pkv_seq_info(const pkv_pool* pool, int32_t seq, int32_t* out_len, int32_t* out_num_blocks);
 
 /* Pool counters ([P3] Eq. (2)-(3) and section 6's accounting categories). */
@@ -169,15 +179,62 @@ int32_t pkv_block_refcount(const pkv_pool* pool, int32_t block);
  * Errors: INVALID_ARG if cap < the queue length. */
 pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* out_n);
 
-/* Check the pool's invariants: each block's refcount equals the number of live
- * tables holding it; a free block has refcount 0 and appears once; free plus
- * used equals capacity; each table has ceil(length / B) entries.  [P3] section
- * 3 asks tests to check refcounts and reuse.  Errors: REFCOUNT. */
+/* Check the pool's invariants, per tier: each block's refcount equals the
+ * number of live tables of that tier holding it; a free block has refcount 0
+ * and appears once; free plus used equals capacity; each table has
+ * ceil(length / B) entries.  [P3] section 3 asks tests to check refcounts and
+ * reuse.  Errors: REFCOUNT. */
 pkv_status pkv_pool_validate(const pkv_pool* pool);
+
+/* Preemption by swapping ([P2] section 4: waiting sequences' KV cache moves
+ * out to CPU memory and comes back when needed, like an operating system's
+ * swap; [P4] "Preemption": swapping, which moves poorly with small blocks).
+ *
+ * pkv_pool_set_host_blocks: give the pool a host tier of num_host_blocks
+ * blocks of the same size, ids 0..num_host_blocks-1, free queue in id order.
+ * Allowed while no sequence is swapped out (it resets the host tier).
+ * Errors: INVALID_ARG. */
+pkv_status pkv_pool_set_host_blocks(pkv_pool* pool, int32_t num_host_blocks);
+
+/* Move seqs[0..n) to the host tier (pkv_swap_out) or back (pkv_swap_in), all
+ * or nothing.  The list must be a whole sharing group: every holder of each of
+ * its blocks is listed (beams of one request move together).  The blocks are
+ * met in list order, then logical order; each distinct block takes the next
+ * block from the other tier's free queue, which inherits its refcount, and the
+ * block it leaves joins the tail of its own tier's free queue.  The tables are
+ * renamed to the new ids.
+ * out_pairs: host int32[2 * pairs_cap] receiving (from, to) block pairs in the
+ *   order met: (device, host) for a swap-out, (host, device) for a swap-in.
+ *   The caller copies the blocks with pkv_swap_blocks before the blocks left
+ *   behind are written again (a swap-out's device blocks are free at once).
+ * out_n_pairs: receives the number of pairs.
+ * Errors (pool unchanged): INVALID_ARG (n < 0, NULL arrays, a sequence listed
+ *   twice, a block also held by an unlisted sequence, pairs_cap too small, in
+ *   which case *out_n_pairs holds the number needed), NO_SUCH_SEQ, SWAPPED (a
+ *   sequence already on the target tier), OUT_OF_BLOCKS (the target tier has
+ *   too few free blocks). */
+pkv_status pkv_swap_out(pkv_pool* pool, const int32_t* seqs, int32_t n, int32_t* out_pairs, int32_t pairs_cap,
+                        int32_t* out_n_pairs);
+pkv_status pkv_swap_in(pkv_pool* pool, const int32_t* seqs, int32_t n, int32_t* out_pairs, int32_t pairs_cap,
+                       int32_t* out_n_pairs);
+
+/* One sequence's table in its current tier: host int32 out[cap] receives its
+ * block ids in logical order, *out_n their number, *out_on_host (may be NULL)
+ * 1 if it is swapped out, else 0.  Errors: NO_SUCH_SEQ, INVALID_ARG (cap too
+ * small; *out_n is still set). */
+pkv_status pkv_seq_table(const pkv_pool* pool, int32_t seq, int32_t* out, int32_t cap, int32_t* out_n,
+                         int32_t* out_on_host);
+
+/* Refcount of one host block, or -1 for an id out of range. */
+int32_t pkv_host_block_refcount(const pkv_pool* pool, int32_t block);
+
+/* Copy the host free queue, head first (as pkv_pool_free_list). */
+pkv_status pkv_pool_host_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* out_n);
 
 /* ---------------------------------------------------------------------------
  * Device calls (HIP, gfx950).  All pointers are device memory owned by the
- * caller, 16-byte aligned; `stream` may be NULL (the default stream).
+ * caller, 16-byte aligned (pkv_swap_blocks also takes page-locked host
+ * memory); `stream` may be NULL (the default stream).
  * ------------------------------------------------------------------------- */
 
 /* Write token i's key and value (k_new, v_new: [num_tokens][H_kv][d], the
@@ -202,6 +259,25 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_c
  * Errors: INVALID_ARG (block_bytes not a positive multiple of 16), HIP. */
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
                            int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
+
+/* Copy whole blocks between two cache pairs: for each pair (i, j),
+ * dst_k block j <- src_k block i and dst_v block j <- src_v block i.  The
+ * device half of swapping: src on the device and dst in host memory for a
+ * swap-out, the reverse for a swap-in ([P2] section 4; [P4] "Preemption").
+ * One kernel moves every pair, whatever the block size.
+ * src_k, src_v, dst_k, dst_v: 16-byte aligned; each either device memory or
+ *   page-locked host memory from the HIP allocator (hipHostMalloc; a pinned
+ *   torch tensor), which the kernel reads or writes over the host link.
+ *   Other host memory is refused.  The source and destination ranges must not
+ *   overlap.
+ * pairs: int32[n_pairs][2] in device or page-locked host memory, as returned
+ *   by pkv_swap_out / pkv_swap_in; a pair with an id outside [0, src_blocks) or
+ *   [0, dst_blocks) is skipped.  Destination blocks must be distinct.
+ * block_bytes: bytes of one block in one cache (a positive multiple of 16).
+ * Errors: INVALID_ARG (sizes, alignment, memory the GPU cannot reach), HIP. */
+pkv_status pkv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int32_t* pairs,
+                           int32_t n_pairs, int32_t src_blocks, int32_t dst_blocks, int64_t block_bytes,
+                           hipStream_t stream);
 
 /* Bytes of workspace pkv_paged_attention_decode needs for these sizes (0 when
  * no sequence can span more than one partition). */

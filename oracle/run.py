@@ -30,12 +30,13 @@ class Replay:
     max_blocks: int = 0
 
 
-def replay(workload, with_cache: bool = True) -> Replay:
-    """Run ``workload.script()``; with ``with_cache=False`` only the allocator is replayed."""
+def replay(workload, with_cache: bool = True, host_blocks: int = 0) -> Replay:
+    """Run ``workload.script()``; with ``with_cache=False`` only the allocator is replayed.  ``host_blocks``
+    gives the pool a host tier for later swaps."""
     from workloads import Append, Create, Fork  # input structure only
 
     s = workload.spec
-    pool = _alloc.BlockPool(workload.num_blocks, s.block_size, workload.free_order)
+    pool = _alloc.BlockPool(workload.num_blocks, s.block_size, workload.free_order, host_blocks=host_blocks)
     if with_cache:
         kc, vc = _cache.empty_caches(workload.num_blocks, s.num_kv_heads, s.block_size, s.head_dim, s.kv_dtype)
     else:

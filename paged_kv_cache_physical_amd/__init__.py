@@ -8,8 +8,9 @@ streams, nothing else).  The library must have been built first
 (``python -m paged_kv_cache_physical_amd.build``); otherwise every call raises.
 
 Cache tensors use the interface's physical layout:
-  key cache    [num_blocks][H_kv][d / X][B][X],  X = 128 / bytes_per_scalar
-  value cache  [num_blocks][H_kv][B][d]
+  key cache    [num_blocks][H_kv][d / X][B][X],  X = 16 / bytes_per_scalar
+  value cache  [num_blocks][H_kv][d][B]
+Host caches for swapping have the same layout in page-locked host memory.
 """
 
 from __future__ import annotations
@@ -19,16 +20,17 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-from ._lib import (PKV_BF16, PKV_F32, InvalidArg, NoSuchSeq, OutOfBlocks, PkvError, Stats, check,  # noqa: F401
-                   header_symbols, lib)
+from ._lib import (PKV_BF16, PKV_ERR_INVALID_ARG, PKV_F32, InvalidArg, NoSuchSeq, OutOfBlocks, PkvError, Stats, WrongTier,  # noqa: F401
+                   check, header_symbols, lib)
 
 __all__ = [
     "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_create", "pkv_seq_fork", "pkv_seq_free", "pkv_append_tokens",
     "pkv_block_tables", "pkv_seq_info", "pkv_pool_stats", "pkv_block_refcount", "pkv_pool_free_list",
-    "pkv_pool_validate", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_attention_workspace_bytes",
+    "pkv_pool_validate", "pkv_pool_set_host_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_seq_table",
+    "pkv_host_block_refcount", "pkv_pool_host_free_list", "pkv_swap_blocks", "empty_host_caches", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_attention_workspace_bytes",
     "pkv_paged_attention_decode", "pkv_paged_attention_partitions", "pkv_paged_attention_reduce",
     "pkv_decode_step", "pkv_abi_version", "pkv_hbm_read_probe", "Pool", "cache_shapes", "empty_caches", "PkvError",
-    "OutOfBlocks", "NoSuchSeq", "InvalidArg",
+    "OutOfBlocks", "NoSuchSeq", "InvalidArg", "WrongTier",
 ]
 
 
@@ -114,12 +116,61 @@ def pkv_block_refcount(pool, block: int) -> int:
     return int(lib().pkv_block_refcount(pool, block))
 
 
-def pkv_pool_free_list(pool) -> np.ndarray:
+def _free_list(fn, name, pool) -> np.ndarray:
     n = ctypes.c_int32()
-    lib().pkv_pool_free_list(pool, None, 0, ctypes.byref(n))
+    fn(pool, None, 0, ctypes.byref(n))
     out = np.empty(n.value, dtype=np.int32)
-    check(lib().pkv_pool_free_list(pool, _ptr(out), out.size, ctypes.byref(n)), "pkv_pool_free_list")
+    check(fn(pool, _ptr(out), out.size, ctypes.byref(n)), name)
     return out
+
+
+def pkv_pool_free_list(pool) -> np.ndarray:
+    return _free_list(lib().pkv_pool_free_list, "pkv_pool_free_list", pool)
+
+
+def pkv_pool_host_free_list(pool) -> np.ndarray:
+    return _free_list(lib().pkv_pool_host_free_list, "pkv_pool_host_free_list", pool)
+
+
+def pkv_pool_set_host_blocks(pool, num_host_blocks: int) -> None:
+    check(lib().pkv_pool_set_host_blocks(pool, num_host_blocks), "pkv_pool_set_host_blocks")
+
+
+def _swap(fn, name, pool, seqs) -> np.ndarray:
+    seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+    if seqs.ndim != 1:
+        raise InvalidArg(-1, name, "seqs must be 1-D")
+    n = ctypes.c_int32()
+    pairs = np.empty((64, 2), dtype=np.int32)
+    st = fn(pool, _ptr(seqs), len(seqs), _ptr(pairs), pairs.shape[0], ctypes.byref(n))
+    if st == PKV_ERR_INVALID_ARG and n.value > pairs.shape[0]:  # more pairs than the first guess: make room
+        pairs = np.empty((n.value, 2), dtype=np.int32)
+        st = fn(pool, _ptr(seqs), len(seqs), _ptr(pairs), pairs.shape[0], ctypes.byref(n))
+    check(st, name)
+    return pairs[:n.value].copy()
+
+
+def pkv_swap_out(pool, seqs: Sequence[int]) -> np.ndarray:
+    """Move a whole sharing group to the host tier; returns (device block, host block) pairs."""
+    return _swap(lib().pkv_swap_out, "pkv_swap_out", pool, seqs)
+
+
+def pkv_swap_in(pool, seqs: Sequence[int]) -> np.ndarray:
+    """Bring swapped-out sequences back; returns (host block, device block) pairs."""
+    return _swap(lib().pkv_swap_in, "pkv_swap_in", pool, seqs)
+
+
+def pkv_seq_table(pool, seq: int) -> Tuple[np.ndarray, bool]:
+    """One sequence's block ids in its current tier, and whether it is swapped out."""
+    n, host = ctypes.c_int32(), ctypes.c_int32()
+    lib().pkv_seq_table(pool, seq, None, 0, ctypes.byref(n), ctypes.byref(host))
+    out = np.empty(n.value, dtype=np.int32)
+    check(lib().pkv_seq_table(pool, seq, _ptr(out), out.size, ctypes.byref(n), ctypes.byref(host)), "pkv_seq_table")
+    return out, bool(host.value)
+
+
+def pkv_host_block_refcount(pool, block: int) -> int:
+    return int(lib().pkv_host_block_refcount(pool, block))
 
 
 def pkv_pool_validate(pool) -> None:
@@ -129,10 +180,13 @@ def pkv_pool_validate(pool) -> None:
 class Pool:
     """Owning wrapper around a pkv_pool handle; methods map 1:1 onto the C calls."""
 
-    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+    def __init__(self, num_blocks: int, block_size: int, free_order=None, host_blocks: int = 0):
         self.handle = pkv_pool_create(num_blocks, block_size, free_order)
         self.num_blocks = num_blocks
         self.block_size = block_size
+        self.host_blocks = host_blocks
+        if host_blocks:
+            pkv_pool_set_host_blocks(self.handle, host_blocks)
 
     def close(self):
         if self.handle is not None:
@@ -174,6 +228,24 @@ class Pool:
 
     def validate(self) -> None:
         pkv_pool_validate(self.handle)
+
+    def swap_out(self, seqs) -> np.ndarray:
+        return pkv_swap_out(self.handle, seqs)
+
+    def swap_in(self, seqs) -> np.ndarray:
+        return pkv_swap_in(self.handle, seqs)
+
+    def table(self, seq: int) -> np.ndarray:
+        return pkv_seq_table(self.handle, seq)[0]
+
+    def on_host(self, seq: int) -> bool:
+        return pkv_seq_table(self.handle, seq)[1]
+
+    def host_refcount(self, block: int) -> int:
+        return pkv_host_block_refcount(self.handle, block)
+
+    def host_free_list(self) -> np.ndarray:
+        return pkv_pool_host_free_list(self.handle)
 
 
 # ---------------------------------------------------------------------------
@@ -233,6 +305,42 @@ def empty_caches(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype: str, 
             k.view(torch.int16).fill_(0x7FC0)
             v.view(torch.int16).fill_(0x7FC0)
     return k, v
+
+
+def empty_host_caches(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype: str):
+    """Key/value caches of the host tier: the interface layout in page-locked host memory."""
+    torch = _torch()
+    dt = torch.float32 if kv_dtype == "f32" else torch.bfloat16
+    ks, vs = cache_shapes(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype)
+    return torch.empty(ks, dtype=dt, pin_memory=True), torch.empty(vs, dtype=dt, pin_memory=True)
+
+
+def _reachable(t, name):
+    """A tensor the GPU can reach: on the GPU, or in page-locked host memory."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise InvalidArg(-1, name, "tensor must be on the GPU or in page-locked host memory")
+    if not t.is_contiguous():
+        raise InvalidArg(-1, name, "tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def pkv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:
+    """Copy blocks src -> dst for each (src block, dst block) in pairs (int32[n][2], GPU or pinned); the caches
+    are device or page-locked host tensors of one layout (the pairs of pkv_swap_out / pkv_swap_in)."""
+    torch = _torch()
+    if pairs.dtype != torch.int32 or (pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2)):
+        raise InvalidArg(-1, "pkv_swap_blocks", "pairs must be int32[n][2]")
+    if src_k.shape[1:] != dst_k.shape[1:] or src_v.shape[1:] != dst_v.shape[1:] or \
+            src_k.shape[0] != src_v.shape[0] or dst_k.shape[0] != dst_v.shape[0] or \
+            len({src_k.dtype, src_v.dtype, dst_k.dtype, dst_v.dtype}) != 1 or src_k[0].numel() != src_v[0].numel():
+        raise InvalidArg(-1, "pkv_swap_blocks", "the caches must share a block layout and dtype")
+    n = pairs.shape[0] if pairs.numel() else 0
+    if n == 0:
+        return
+    block_bytes = src_k[0].numel() * src_k.element_size()
+    check(lib().pkv_swap_blocks(_reachable(src_k, "src_k"), _reachable(src_v, "src_v"), _reachable(dst_k, "dst_k"),
+                                _reachable(dst_v, "dst_v"), _reachable(pairs, "pairs"), n, src_k.shape[0],
+                                dst_k.shape[0], block_bytes, _stream(stream)), "pkv_swap_blocks")
 
 
 def pkv_reshape_and_cache(k_new, v_new, k_cache, v_cache, slots, block_size: int, stream=None) -> None:

@@ -18,6 +18,7 @@ PKV_ERR_REFCOUNT = -4
 PKV_ERR_UNSUPPORTED = -5
 PKV_ERR_HIP = -6
 PKV_ERR_WORKSPACE = -7
+PKV_ERR_SWAPPED = -8
 PKV_F32 = 0
 PKV_BF16 = 1
 
@@ -40,10 +41,15 @@ class InvalidArg(PkvError):
     pass
 
 
+class WrongTier(PkvError):
+    """The sequence is swapped out (or, for a swap-in, is not)."""
+
+
 class Stats(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in (
         "num_blocks", "free_blocks", "used_blocks", "sum_refcount", "num_seqs",
-        "logical_tokens", "logical_blocks", "allocated_slots", "table_bytes")]
+        "logical_tokens", "logical_blocks", "allocated_slots", "table_bytes",
+        "host_blocks", "host_free_blocks", "host_used_blocks", "swapped_seqs", "swapped_tokens")]
 
     def as_dict(self):
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
@@ -70,6 +76,13 @@ _SIGS = {
     "pkv_block_refcount": (i32, [vp, i32]),
     "pkv_pool_free_list": (i32, [vp, vp, i32, P_i32]),
     "pkv_pool_validate": (i32, [vp]),
+    "pkv_pool_set_host_blocks": (i32, [vp, i32]),
+    "pkv_swap_out": (i32, [vp, vp, i32, vp, i32, P_i32]),
+    "pkv_swap_in": (i32, [vp, vp, i32, vp, i32, P_i32]),
+    "pkv_seq_table": (i32, [vp, i32, vp, i32, P_i32, P_i32]),
+    "pkv_host_block_refcount": (i32, [vp, i32]),
+    "pkv_pool_host_free_list": (i32, [vp, vp, i32, P_i32]),
+    "pkv_swap_blocks": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp]),
     "pkv_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
     "pkv_copy_blocks": (i32, [vp, vp, vp, i32, i32, i64, vp]),
     "pkv_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
@@ -109,5 +122,5 @@ def check(status: int, call: str) -> None:
         return
     msg = lib().pkv_status_string(status).decode()
     cls = {PKV_ERR_OUT_OF_BLOCKS: OutOfBlocks, PKV_ERR_NO_SUCH_SEQ: NoSuchSeq,
-           PKV_ERR_INVALID_ARG: InvalidArg}.get(status, PkvError)
+           PKV_ERR_INVALID_ARG: InvalidArg, PKV_ERR_SWAPPED: WrongTier}.get(status, PkvError)
     raise cls(status, call, msg)

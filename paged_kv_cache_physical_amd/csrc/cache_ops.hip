@@ -1,6 +1,7 @@
 // Cache writes and copies for gfx950: the slot scatter of new tokens'
-// keys/values (reshape_and_cache), whole-block copies for copy-on-write, and a
-// plain streaming-read probe used to measure the HBM read ceiling.
+// keys/values (reshape_and_cache), whole-block copies for copy-on-write and for
+// swapping between device and host memory, and a plain streaming-read probe
+// used to measure the HBM read ceiling.
 
 #include "device_common.h"
 
@@ -98,6 +99,40 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* k_cache, char* v
     d[i] = s[i];
 }
 
+// grid = (pairs, 2 caches, splits): each workgroup copies a slice of one block
+// from one cache pair to the other.  One side may be page-locked host memory,
+// reached over the host link: each thread keeps kSwapUnroll 16-byte loads in
+// flight before storing, so that reads across the link overlap.
+constexpr int kSwapUnroll = 4;
+
+__global__ __launch_bounds__(256) void swap_blocks_kernel(const char* src_k, const char* src_v, char* dst_k,
+                                                          char* dst_v, const int32_t* pairs, int32_t src_blocks,
+                                                          int32_t dst_blocks, int64_t block_bytes) {
+  const int pair = blockIdx.x;
+  const int32_t src = pairs[2 * pair];
+  const int32_t dst = pairs[2 * pair + 1];
+  if (static_cast<unsigned>(src) >= static_cast<unsigned>(src_blocks) ||
+      static_cast<unsigned>(dst) >= static_cast<unsigned>(dst_blocks))
+    return;
+  const uint4* s = reinterpret_cast<const uint4*>((blockIdx.y ? src_v : src_k) + src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>((blockIdx.y ? dst_v : dst_k) + dst * block_bytes);
+  const int64_t n16 = block_bytes / 16;
+  const int64_t step = static_cast<int64_t>(gridDim.z) * blockDim.x * kSwapUnroll;
+  for (int64_t i = static_cast<int64_t>(blockIdx.z) * blockDim.x * kSwapUnroll + threadIdx.x; i < n16; i += step) {
+    uint4 v[kSwapUnroll];
+#pragma unroll
+    for (int u = 0; u < kSwapUnroll; ++u) {
+      const int64_t j = i + static_cast<int64_t>(u) * blockDim.x;
+      if (j < n16) v[u] = s[j];
+    }
+#pragma unroll
+    for (int u = 0; u < kSwapUnroll; ++u) {
+      const int64_t j = i + static_cast<int64_t>(u) * blockDim.x;
+      if (j < n16) d[j] = v[u];
+    }
+  }
+}
+
 // Plain streaming read: each workgroup owns consecutive 256 KiB chunks and
 // its threads keep 16 non-temporal 16-byte loads in flight; the words are
 // xor-folded and stored only for an impossible value, which keeps the loads
@@ -182,6 +217,74 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
   const unsigned z = static_cast<unsigned>(splits < 16 ? splits : 16);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(n_pairs, 2, z), dim3(256), 0, stream, static_cast<char*>(k_cache),
                      static_cast<char*>(v_cache), pairs, num_blocks, block_bytes);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+namespace {
+// The address the GPU uses for `bytes` bytes at p, or nullptr when p is not
+// device memory or page-locked HIP host memory, or the range runs past the
+// allocation.
+const void* gpu_reachable(const void* p, int64_t bytes) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of a refused query
+    return nullptr;
+  }
+  void* base = nullptr;
+  size_t size = 0;
+  const void* dp = nullptr;
+  if (attr.type == hipMemoryTypeDevice) {
+    dp = p;
+  } else if (attr.type == hipMemoryTypeHost) {
+    void* mapped = nullptr;
+    if (hipHostGetDevicePointer(&mapped, const_cast<void*>(p), 0) != hipSuccess || !mapped) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    dp = mapped;
+  } else {
+    return nullptr;
+  }
+  // the allocation holding p (looked up by the GPU address, else by p itself)
+  const void* probe = dp;
+  if (hipMemGetAddressRange(reinterpret_cast<hipDeviceptr_t*>(&base), &size, const_cast<void*>(dp)) != hipSuccess) {
+    (void)hipGetLastError();
+    probe = p;
+    if (dp == p || hipMemGetAddressRange(reinterpret_cast<hipDeviceptr_t*>(&base), &size, const_cast<void*>(p)) !=
+                       hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(probe);
+  if (q < b || q - b > size || static_cast<uint64_t>(bytes) > size - (q - b)) return nullptr;
+  return dp;
+}
+}  // namespace
+
+pkv_status pkv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int32_t* pairs,
+                           int32_t n_pairs, int32_t src_blocks, int32_t dst_blocks, int64_t block_bytes,
+                           hipStream_t stream) {
+  if (n_pairs < 0 || src_blocks <= 0 || dst_blocks <= 0 || block_bytes <= 0 || block_bytes % 16)
+    return PKV_ERR_INVALID_ARG;
+  if (n_pairs == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v)) return PKV_ERR_INVALID_ARG;
+  if (src_blocks > INT64_MAX / block_bytes || dst_blocks > INT64_MAX / block_bytes) return PKV_ERR_INVALID_ARG;
+  const int64_t src_bytes = src_blocks * block_bytes, dst_bytes = dst_blocks * block_bytes;
+  const void* sk = gpu_reachable(src_k, src_bytes);
+  const void* sv = gpu_reachable(src_v, src_bytes);
+  const void* dk = gpu_reachable(dst_k, dst_bytes);
+  const void* dv = gpu_reachable(dst_v, dst_bytes);
+  const void* pp = gpu_reachable(pairs, static_cast<int64_t>(n_pairs) * 8);
+  if (!sk || !sv || !dk || !dv || !pp) return PKV_ERR_INVALID_ARG;
+  const int64_t n16 = block_bytes / 16;
+  const int64_t splits = ceil_div64(n16, 256 * kSwapUnroll);
+  const unsigned z = static_cast<unsigned>(splits < 16 ? splits : 16);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(n_pairs, 2, z), dim3(256), 0, stream, static_cast<const char*>(sk),
+                     static_cast<const char*>(sv), static_cast<char*>(const_cast<void*>(dk)),
+                     static_cast<char*>(const_cast<void*>(dv)), static_cast<const int32_t*>(pp), src_blocks,
+                     dst_blocks, block_bytes);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

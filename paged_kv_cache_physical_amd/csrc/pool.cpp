@@ -9,6 +9,11 @@
 // to the tail.  An append batch is checked first (blocks needed, including the
 // copies that refcounts will force) and only then applied, so a failure leaves
 // the pool untouched.
+//
+// Preemption by swapping ([P2] section 4, "first come first served plus
+// preemption"; [P4] "Preemption"): an optional host tier with its own FIFO
+// ring of host block ids.  A swap moves a whole sharing group between the
+// tiers; a block keeps its refcount, and the sequences' tables are renamed.
 
 #include <algorithm>
 #include <cstring>
@@ -21,25 +26,30 @@
 namespace {
 
 struct Seq {
-  std::vector<int32_t> table;
+  std::vector<int32_t> table;  // block ids of the sequence's tier
   int64_t length = 0;
   bool live = false;
+  bool on_host = false;  // swapped out
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-}  // namespace
-
-struct pkv_pool {
+// One tier's blocks: refcounts and the FIFO ring of free ids.
+struct Tier {
   int32_t num_blocks = 0;
-  int32_t block_size = 0;
   std::vector<int32_t> ring;  // capacity num_blocks
   int64_t head = 0;
   int64_t count = 0;
   std::vector<int32_t> refcount;
-  std::vector<Seq> seqs;  // index = sequence id
-  int64_t live = 0;
 
+  void reset(int32_t n) {
+    num_blocks = n;
+    ring.resize(n);
+    for (int32_t i = 0; i < n; ++i) ring[i] = i;
+    head = 0;
+    count = n;
+    refcount.assign(n, 0);
+  }
   int32_t pop() {
     int32_t b = ring[head];
     head = (head + 1) % num_blocks;
@@ -51,6 +61,18 @@ struct pkv_pool {
     ring[(head + count) % num_blocks] = b;
     ++count;
   }
+  int32_t free_at(int64_t i) const { return ring[(head + i) % num_blocks]; }
+};
+
+}  // namespace
+
+struct pkv_pool {
+  int32_t block_size = 0;
+  Tier dev;
+  Tier host;
+  std::vector<Seq> seqs;  // index = sequence id
+  int64_t live = 0;
+
   Seq* get(int32_t id) {
     if (id < 0 || static_cast<size_t>(id) >= seqs.size() || !seqs[id].live) return nullptr;
     return &seqs[id];
@@ -73,11 +95,12 @@ const char* pkv_status_string(pkv_status s) {
     case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PKV_ERR_HIP: return "HIP launch error";
     case PKV_ERR_WORKSPACE: return "attention workspace missing or too small";
+    case PKV_ERR_SWAPPED: return "sequence is on the other tier (swapped out, or not)";
     default: return "unknown status";
   }
 }
 
-int32_t pkv_abi_version(void) { return 4; }
+int32_t pkv_abi_version(void) { return 5; }
 
 pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
                            pkv_pool** out) {
@@ -85,10 +108,8 @@ pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t
   *out = nullptr;
   pkv_pool* p = new (std::nothrow) pkv_pool;
   if (!p) return PKV_ERR_INVALID_ARG;
-  p->num_blocks = num_blocks;
   p->block_size = block_size;
-  p->ring.resize(num_blocks);
-  p->refcount.assign(num_blocks, 0);
+  p->dev.reset(num_blocks);
   if (free_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -98,14 +119,19 @@ pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t
         return PKV_ERR_INVALID_ARG;
       }
       seen[b] = 1;
-      p->ring[i] = b;
+      p->dev.ring[i] = b;
     }
-  } else {
-    for (int32_t i = 0; i < num_blocks; ++i) p->ring[i] = i;
   }
-  p->head = 0;
-  p->count = num_blocks;
   *out = p;
+  return PKV_OK;
+}
+
+pkv_status pkv_pool_set_host_blocks(pkv_pool* pool, int32_t num_host_blocks) {
+  if (!pool || num_host_blocks < 0) return PKV_ERR_INVALID_ARG;
+  for (const Seq& s : pool->seqs) {
+    if (s.live && s.on_host) return PKV_ERR_INVALID_ARG;
+  }
+  pool->host.reset(num_host_blocks);
   return PKV_OK;
 }
 
@@ -124,12 +150,13 @@ pkv_status pkv_seq_create(pkv_pool* pool, int32_t* out_seq) {
 pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* out_child) {
   if (!pool || !out_child) return PKV_ERR_INVALID_ARG;
   if (!pool->get(parent)) return PKV_ERR_NO_SUCH_SEQ;
+  if (pool->seqs[parent].on_host) return PKV_ERR_SWAPPED;
   if (pool->seqs.size() >= static_cast<size_t>(INT32_MAX)) return PKV_ERR_INVALID_ARG;
   Seq child;
   child.table = pool->seqs[parent].table;  // copy before emplace may reallocate
   child.length = pool->seqs[parent].length;
   child.live = true;
-  for (int32_t b : child.table) ++pool->refcount[b];
+  for (int32_t b : child.table) ++pool->dev.refcount[b];
   pool->seqs.push_back(std::move(child));
   ++pool->live;
   *out_child = static_cast<int32_t>(pool->seqs.size() - 1);
@@ -140,13 +167,15 @@ pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq) {
   if (!pool) return PKV_ERR_INVALID_ARG;
   Seq* s = pool->get(seq);
   if (!s) return PKV_ERR_NO_SUCH_SEQ;
+  Tier& tier = s->on_host ? pool->host : pool->dev;
   for (int32_t b : s->table) {
-    if (--pool->refcount[b] == 0) pool->push(b);
+    if (--tier.refcount[b] == 0) tier.push(b);
   }
   s->table.clear();
   s->table.shrink_to_fit();
   s->length = 0;
   s->live = false;
+  s->on_host = false;
   --pool->live;
   return PKV_OK;
 }
@@ -169,6 +198,9 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
   for (int32_t i = 0; i < n; ++i) {
     if (!pool->get(seqs[i])) return PKV_ERR_NO_SUCH_SEQ;
   }
+  for (int32_t i = 0; i < n; ++i) {
+    if (pool->seqs[seqs[i]].on_host) return PKV_ERR_SWAPPED;
+  }
   std::unordered_map<int32_t, int32_t> dropped;  // refcount drops from copies earlier in the batch
   int64_t total_slots = 0, need = 0;
   int32_t cows = 0;
@@ -180,7 +212,7 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
     if (L % B != 0) {
       const int32_t last = s->table.back();
       auto it = dropped.find(last);
-      const int32_t rc = pool->refcount[last] - (it == dropped.end() ? 0 : it->second);
+      const int32_t rc = pool->dev.refcount[last] - (it == dropped.end() ? 0 : it->second);
       if (rc > 1) {
         ++need;
         ++cows;
@@ -194,7 +226,7 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
     *out_n_cow = cows;
     return PKV_ERR_INVALID_ARG;
   }
-  if (need > pool->count) return PKV_ERR_OUT_OF_BLOCKS;
+  if (need > pool->dev.count) return PKV_ERR_OUT_OF_BLOCKS;
 
   // Pass 2: apply.
   int64_t k = 0;
@@ -205,17 +237,17 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
     if (c == 0) continue;
     if (L % B != 0) {
       const int32_t last = s.table.back();
-      if (pool->refcount[last] > 1) {
-        const int32_t fresh = pool->pop();
+      if (pool->dev.refcount[last] > 1) {
+        const int32_t fresh = pool->dev.pop();
         out_cow_pairs[2 * npairs] = last;
         out_cow_pairs[2 * npairs + 1] = fresh;
         ++npairs;
-        --pool->refcount[last];
+        --pool->dev.refcount[last];
         s.table.back() = fresh;
       }
     }
     for (int64_t p = L; p < L + c; ++p) {
-      if (p % B == 0) s.table.push_back(pool->pop());
+      if (p % B == 0) s.table.push_back(pool->dev.pop());
       out_slots[k++] = static_cast<int64_t>(s.table[p / B]) * B + p % B;
     }
     s.length = L + c;
@@ -232,6 +264,7 @@ pkv_status pkv_block_tables(const pkv_pool* pool, const int32_t* seqs, int32_t n
   for (int32_t i = 0; i < n; ++i) {
     const Seq* s = pool->get(seqs[i]);
     if (!s) return PKV_ERR_NO_SUCH_SEQ;
+    if (s->on_host) return PKV_ERR_SWAPPED;
     if (s->table.size() > static_cast<size_t>(max_blocks) || s->length > INT32_MAX) return PKV_ERR_INVALID_ARG;
   }
   for (int32_t i = 0; i < n; ++i) {
@@ -254,64 +287,178 @@ pkv_status pkv_seq_info(const pkv_pool* pool, int32_t seq, int32_t* out_len, int
   return PKV_OK;
 }
 
+pkv_status pkv_seq_table(const pkv_pool* pool, int32_t seq, int32_t* out, int32_t cap, int32_t* out_n,
+                         int32_t* out_on_host) {
+  if (!pool || !out_n) return PKV_ERR_INVALID_ARG;
+  const Seq* s = pool->get(seq);
+  if (!s) return PKV_ERR_NO_SUCH_SEQ;
+  const int64_t nb = static_cast<int64_t>(s->table.size());
+  *out_n = static_cast<int32_t>(nb);
+  if (out_on_host) *out_on_host = s->on_host ? 1 : 0;
+  if (cap < nb || (nb > 0 && !out)) return PKV_ERR_INVALID_ARG;
+  if (nb) std::memcpy(out, s->table.data(), nb * sizeof(int32_t));
+  return PKV_OK;
+}
+
+static pkv_status swap_tier(pkv_pool* pool, const int32_t* seqs, int32_t n, int32_t* out_pairs, int32_t pairs_cap,
+                            int32_t* out_n_pairs, bool out) {
+  if (!pool || n < 0 || !out_n_pairs) return PKV_ERR_INVALID_ARG;
+  *out_n_pairs = 0;
+  if (n == 0) return PKV_OK;
+  if (!seqs) return PKV_ERR_INVALID_ARG;
+  std::unordered_map<int32_t, int32_t> listed;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!listed.emplace(seqs[i], i).second) return PKV_ERR_INVALID_ARG;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (!pool->get(seqs[i])) return PKV_ERR_NO_SUCH_SEQ;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (pool->seqs[seqs[i]].on_host == out) return PKV_ERR_SWAPPED;
+  }
+  Tier& src = out ? pool->dev : pool->host;
+  Tier& dst = out ? pool->host : pool->dev;
+  // The listed tables' blocks in the order met, and how often the list holds each.
+  std::vector<int32_t> met;
+  std::unordered_map<int32_t, int32_t> held;
+  for (int32_t i = 0; i < n; ++i) {
+    for (int32_t b : pool->seqs[seqs[i]].table) {
+      auto r = held.emplace(b, 0);
+      if (r.second) met.push_back(b);
+      ++r.first->second;
+    }
+  }
+  for (int32_t b : met) {
+    if (held[b] != src.refcount[b]) return PKV_ERR_INVALID_ARG;  // also held outside the list
+  }
+  const int64_t k = static_cast<int64_t>(met.size());
+  if (k > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  if (k > dst.count) return PKV_ERR_OUT_OF_BLOCKS;
+  if (k > 0 && (!out_pairs || pairs_cap < k)) {
+    *out_n_pairs = static_cast<int32_t>(k);
+    return PKV_ERR_INVALID_ARG;
+  }
+  std::unordered_map<int32_t, int32_t> moved;
+  for (int64_t j = 0; j < k; ++j) {
+    const int32_t b = met[j];
+    const int32_t nb = dst.pop();
+    dst.refcount[nb] = src.refcount[b];
+    src.refcount[b] = 0;
+    src.push(b);
+    moved[b] = nb;
+    out_pairs[2 * j] = b;
+    out_pairs[2 * j + 1] = nb;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    Seq& s = pool->seqs[seqs[i]];
+    for (int32_t& b : s.table) b = moved[b];
+    s.on_host = out;
+  }
+  *out_n_pairs = static_cast<int32_t>(k);
+  return PKV_OK;
+}
+
+pkv_status pkv_swap_out(pkv_pool* pool, const int32_t* seqs, int32_t n, int32_t* out_pairs, int32_t pairs_cap,
+                        int32_t* out_n_pairs) {
+  return swap_tier(pool, seqs, n, out_pairs, pairs_cap, out_n_pairs, true);
+}
+
+pkv_status pkv_swap_in(pkv_pool* pool, const int32_t* seqs, int32_t n, int32_t* out_pairs, int32_t pairs_cap,
+                       int32_t* out_n_pairs) {
+  return swap_tier(pool, seqs, n, out_pairs, pairs_cap, out_n_pairs, false);
+}
+
 pkv_status pkv_pool_stats(const pkv_pool* pool, pkv_stats* out) {
   if (!pool || !out) return PKV_ERR_INVALID_ARG;
   pkv_stats st{};
-  st.num_blocks = pool->num_blocks;
-  st.free_blocks = pool->count;
-  for (int32_t r : pool->refcount) {
+  st.num_blocks = pool->dev.num_blocks;
+  st.free_blocks = pool->dev.count;
+  for (int32_t r : pool->dev.refcount) {
     if (r > 0) ++st.used_blocks;
     st.sum_refcount += r;
   }
   st.num_seqs = pool->live;
   for (const Seq& s : pool->seqs) {
     if (!s.live) continue;
-    st.logical_tokens += s.length;
-    st.logical_blocks += static_cast<int64_t>(s.table.size());
+    if (s.on_host) {
+      ++st.swapped_seqs;
+      st.swapped_tokens += s.length;
+    } else {
+      st.logical_tokens += s.length;
+      st.logical_blocks += static_cast<int64_t>(s.table.size());
+    }
   }
   st.allocated_slots = st.used_blocks * pool->block_size;
   st.table_bytes = 4 * st.logical_blocks;
+  st.host_blocks = pool->host.num_blocks;
+  st.host_free_blocks = pool->host.count;
+  for (int32_t r : pool->host.refcount) {
+    if (r > 0) ++st.host_used_blocks;
+  }
   *out = st;
   return PKV_OK;
 }
 
 int32_t pkv_block_refcount(const pkv_pool* pool, int32_t block) {
-  if (!pool || block < 0 || block >= pool->num_blocks) return -1;
-  return pool->refcount[block];
+  if (!pool || block < 0 || block >= pool->dev.num_blocks) return -1;
+  return pool->dev.refcount[block];
 }
 
-pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* out_n) {
-  if (!pool || !out_n) return PKV_ERR_INVALID_ARG;
-  *out_n = static_cast<int32_t>(pool->count);
-  if (cap < pool->count || (pool->count > 0 && !out)) return PKV_ERR_INVALID_ARG;
-  for (int64_t i = 0; i < pool->count; ++i) out[i] = pool->ring[(pool->head + i) % pool->num_blocks];
+int32_t pkv_host_block_refcount(const pkv_pool* pool, int32_t block) {
+  if (!pool || block < 0 || block >= pool->host.num_blocks) return -1;
+  return pool->host.refcount[block];
+}
+
+namespace {
+pkv_status copy_free_list(const Tier& t, int32_t* out, int32_t cap, int32_t* out_n) {
+  if (!out_n) return PKV_ERR_INVALID_ARG;
+  *out_n = static_cast<int32_t>(t.count);
+  if (cap < t.count || (t.count > 0 && !out)) return PKV_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < t.count; ++i) out[i] = t.free_at(i);
   return PKV_OK;
+}
+
+// Refcounts equal the holders among live tables of this tier; the free ring
+// holds each zero-count block once; used plus free is the capacity.
+bool tier_sound(const Tier& t, const std::vector<int64_t>& held) {
+  int64_t used = 0;
+  for (int32_t b = 0; b < t.num_blocks; ++b) {
+    if (held[b] != t.refcount[b]) return false;
+    if (held[b] > 0) ++used;
+  }
+  std::vector<char> in_free(t.num_blocks, 0);
+  for (int64_t i = 0; i < t.count; ++i) {
+    const int32_t b = t.free_at(i);
+    if (b < 0 || b >= t.num_blocks || in_free[b] || t.refcount[b] != 0) return false;
+    in_free[b] = 1;
+  }
+  return used + t.count == t.num_blocks;
+}
+}  // namespace
+
+pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* out_n) {
+  if (!pool) return PKV_ERR_INVALID_ARG;
+  return copy_free_list(pool->dev, out, cap, out_n);
+}
+
+pkv_status pkv_pool_host_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* out_n) {
+  if (!pool) return PKV_ERR_INVALID_ARG;
+  return copy_free_list(pool->host, out, cap, out_n);
 }
 
 pkv_status pkv_pool_validate(const pkv_pool* pool) {
   if (!pool) return PKV_ERR_INVALID_ARG;
-  const int32_t NB = pool->num_blocks;
-  std::vector<int64_t> held(NB, 0);
+  std::vector<int64_t> held_dev(pool->dev.num_blocks, 0), held_host(pool->host.num_blocks, 0);
   for (const Seq& s : pool->seqs) {
     if (!s.live) continue;
     if (static_cast<int64_t>(s.table.size()) != ceil_div(s.length, pool->block_size)) return PKV_ERR_REFCOUNT;
+    std::vector<int64_t>& held = s.on_host ? held_host : held_dev;
     for (int32_t b : s.table) {
-      if (b < 0 || b >= NB) return PKV_ERR_REFCOUNT;
+      if (b < 0 || static_cast<size_t>(b) >= held.size()) return PKV_ERR_REFCOUNT;
       ++held[b];
     }
   }
-  int64_t used = 0;
-  for (int32_t b = 0; b < NB; ++b) {
-    if (held[b] != pool->refcount[b]) return PKV_ERR_REFCOUNT;
-    if (held[b] > 0) ++used;
-  }
-  std::vector<char> in_free(NB, 0);
-  for (int64_t i = 0; i < pool->count; ++i) {
-    const int32_t b = pool->ring[(pool->head + i) % NB];
-    if (b < 0 || b >= NB || in_free[b] || pool->refcount[b] != 0) return PKV_ERR_REFCOUNT;
-    in_free[b] = 1;
-  }
-  if (used + pool->count != NB) return PKV_ERR_REFCOUNT;
+  if (!tier_sound(pool->dev, held_dev) || !tier_sound(pool->host, held_host)) return PKV_ERR_REFCOUNT;
   return PKV_OK;
 }
 

@@ -19,22 +19,26 @@ def test_exports_every_declared_symbol(libpkv):
     assert len(syms) >= 18
     missing = [s for s in syms if not hasattr(libpkv, s)]
     assert missing == []
-    assert pk.pkv_abi_version() == 4
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
-        assert libpkv.pkv_status_string(code)
+    assert pk.pkv_abi_version() == 5
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        assert libpkv.pkv_status_string(code) != b"unknown status"
+    assert libpkv.pkv_status_string(-9) == b"unknown status"
 
 
 def same_state(cpool: pk.Pool, opool: al.BlockPool):
     assert list(cpool.free_list()) == opool.free_list()
     assert [cpool.refcount(b) for b in range(opool.num_blocks)] == opool.refcount
+    assert list(cpool.host_free_list()) == opool.host_free_list()
+    assert [cpool.host_refcount(b) for b in range(opool.host_blocks)] == opool.host_refcount
     st = cpool.stats()
     assert st == {**opool.stats()}
     for sid, s in opool.seqs.items():
         n, nb = cpool.info(sid)
         assert (n, nb) == (s.length, len(s.table))
-    if opool.seqs:
-        ids = sorted(opool.seqs)
-        mb = max(1, max(len(s.table) for s in opool.seqs.values()))
+        assert list(cpool.table(sid)) == s.table and cpool.on_host(sid) == s.on_host
+    ids = sorted(sid for sid, s in opool.seqs.items() if not s.on_host)
+    if ids:
+        mb = max(1, max(len(opool.seqs[i].table) for i in ids))
         ct, cl = cpool.block_tables(ids, mb)
         ot, ol = opool.block_tables(ids, mb)
         assert np.array_equal(ct, ot) and np.array_equal(cl, ol)
@@ -50,22 +54,41 @@ def test_worked_example(libpkv):
         assert st["logical_tokens"] == 968 and st["used_blocks"] == blocks and st["allocated_slots"] == blocks * B
 
 
+def sharing_group(opool: al.BlockPool, sid: int):
+    """sid and every sequence linked to it by a common block in the same tier."""
+    group, todo = {sid}, [sid]
+    while todo:
+        s = opool.seqs[todo.pop()]
+        for o, t in opool.seqs.items():
+            if o not in group and t.on_host == s.on_host and set(t.table) & set(s.table):
+                group.add(o)
+                todo.append(o)
+    return sorted(group)
+
+
 def test_random_operations_match_oracle(libpkv):
     rng = np.random.default_rng(2024)
+    errors = {al.OutOfBlocks: pk.OutOfBlocks, al.InvalidArg: pk.InvalidArg, al.WrongTier: pk.WrongTier}
+    outcomes = {}
     for trial in range(30):
         nb = int(rng.integers(4, 60))
         B = int(rng.choice([1, 2, 4, 16, 32]))
+        hb = int(rng.integers(0, 40))
         order = rng.permutation(nb)
-        c, o = pk.Pool(nb, B, order), al.BlockPool(nb, B, order)
+        c, o = pk.Pool(nb, B, order, host_blocks=hb), al.BlockPool(nb, B, order, host_blocks=hb)
         live = []
         for _ in range(80):
-            op = int(rng.integers(0, 5))
+            op = int(rng.integers(0, 8))
             if op == 0 or not live:
                 a, b = c.create(), o.create()
                 assert a == b
                 live.append(a)
             elif op == 1:
                 p = int(rng.choice(live))
+                if o.on_host(p):
+                    with pytest.raises(pk.WrongTier):
+                        c.fork(p)
+                    continue
                 a, b = c.fork(p), o.fork(p)
                 assert a == b
                 live.append(a)
@@ -74,20 +97,39 @@ def test_random_operations_match_oracle(libpkv):
                 c.free_seq(sid)
                 o.free_seq(sid)
                 live.remove(sid)
-            else:
+            elif op <= 4:
                 k = int(rng.integers(1, len(live) + 1))
                 seqs = [int(x) for x in rng.choice(live, size=k, replace=False)]
                 counts = [int(x) for x in rng.integers(0, 3 * B + 2, size=k)]
                 try:
                     so, po = o.append(seqs, counts)
-                except al.OutOfBlocks:
-                    with pytest.raises(pk.OutOfBlocks):
+                except (al.OutOfBlocks, al.WrongTier) as e:
+                    with pytest.raises(errors[type(e)]):
                         c.append(seqs, counts)
                 else:
                     sc, pc = c.append(seqs, counts)
                     assert np.array_equal(sc, so)
                     assert np.array_equal(pc, po)
+            else:
+                # swap a whole sharing group out or in; sometimes only part of it, or the wrong tier
+                sid = int(rng.choice(live))
+                group = sharing_group(o, sid)
+                if op == 7 and len(group) > 1:
+                    group = group[:-1]
+                out = not o.on_host(sid) if op != 6 else o.on_host(sid)
+                try:
+                    po = o.swap_out(group) if out else o.swap_in(group)
+                except (al.OutOfBlocks, al.InvalidArg, al.WrongTier) as e:
+                    outcomes[type(e).__name__] = outcomes.get(type(e).__name__, 0) + 1
+                    with pytest.raises(errors[type(e)]):
+                        c.swap_out(group) if out else c.swap_in(group)
+                else:
+                    outcomes["out" if out else "in"] = outcomes.get("out" if out else "in", 0) + 1
+                    pc = c.swap_out(group) if out else c.swap_in(group)
+                    assert np.array_equal(pc, po)
             same_state(c, o)
+    # every path was taken: swaps both ways and each refusal
+    assert all(outcomes.get(k, 0) >= 5 for k in ("out", "in", "OutOfBlocks", "InvalidArg", "WrongTier")), outcomes
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "llama7b_bf16", "gqa_bf16_b16", "gqa_bf16_b32", "beam_cow_bf16",
@@ -138,6 +180,57 @@ def test_errors_leave_pool_unchanged(libpkv):
     with pytest.raises(pk.NoSuchSeq):
         c.free_seq(a)  # double free
     assert c.refcount(-1) == -1 and c.refcount(5) == -1
+
+
+def test_swap_errors_leave_pool_unchanged(libpkv):
+    c = pk.Pool(6, 4, host_blocks=4)
+    a = c.create()
+    c.append([a], [6])
+    b = c.fork(a)
+    c.append([b], [1])
+    x = c.create()
+    c.append([x], [4])
+    snap = lambda: (list(c.free_list()), list(c.host_free_list()), [c.refcount(i) for i in range(6)],
+                    [c.host_refcount(i) for i in range(4)], [list(c.table(s)) for s in (a, b, x)])
+    before = snap()
+    with pytest.raises(pk.InvalidArg):
+        c.swap_out([a])  # block 0 is also b's
+    with pytest.raises(pk.InvalidArg):
+        c.swap_out([a, a])
+    with pytest.raises(pk.NoSuchSeq):
+        c.swap_out([a, 42])
+    with pytest.raises(pk.WrongTier):
+        c.swap_in([a, b])
+    c2 = pk.Pool(6, 4, host_blocks=2)
+    y = c2.create()
+    c2.append([y], [9])
+    with pytest.raises(pk.OutOfBlocks):
+        c2.swap_out([y])
+    assert snap() == before
+    c.swap_out([x])
+    for call in (lambda: c.append([x], [1]), lambda: c.fork(x), lambda: c.block_tables([x], 4),
+                 lambda: c.swap_out([x])):
+        with pytest.raises(pk.WrongTier):
+            call()
+    with pytest.raises(pk.InvalidArg):
+        pk.pkv_pool_set_host_blocks(c.handle, 8)  # a sequence is swapped out
+    c.swap_in([x])
+    pk.pkv_pool_set_host_blocks(c.handle, 8)
+    assert c.stats()["host_blocks"] == 8 and list(c.host_free_list()) == list(range(8))
+    c.validate()
+
+
+def test_swap_pairs_capacity_reports_need(libpkv):
+    L = libpkv
+    c = pk.Pool(8, 4, host_blocks=8)
+    s = c.create()
+    c.append([s], [12])  # 3 blocks
+    seqs = np.array([s], np.int32)
+    n = ctypes.c_int32()
+    st = L.pkv_swap_out(c.handle, seqs.ctypes.data_as(ctypes.c_void_p), 1, None, 0, ctypes.byref(n))
+    assert st == _lib.PKV_ERR_INVALID_ARG and n.value == 3
+    assert not c.on_host(s)
+    c.validate()
 
 
 def test_pool_create_rejects_bad_orders(libpkv):
