@@ -364,6 +364,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other decode batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-swap", action="store_true", help="skip the device <-> host swap measurement")
+    ap.add_argument("--swap-only", action="store_true",
+                    help="run only the swap measurement and print its JSON object (for profiling pkv_swap_blocks)")
     ap.add_argument("--partition", type=int, default=None, help="override the workload's partition size")
     ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated extra workloads")
     ap.add_argument("--copy-probe", action="store_true",
@@ -392,6 +394,9 @@ def main():
         sys.exit("bench.py needs a GPU")
     _lib.lib()  # fail loudly if the HIP library is not built
     stream = torch.cuda.Stream()  # default priority
+    if args.swap_only:
+        print(json.dumps(measure_swap(stream)), flush=True)
+        return
 
     over = {} if args.partition is None else {"partition_size": args.partition}
     w = wl.named(args.workload, seed=0, **over)
