@@ -14,6 +14,10 @@ What it follows:
     to host memory and brought back when device blocks are free again
     ([P2] section 4 "scheduling: first come first served plus preemption";
     [P4] "Preemption", swapping).
+  * Automatic prefix caching: a full block is found again by a key hashed
+    from its own tokens and every token before it, and two blocks are the
+    same only if that whole run of tokens is the same ([P4] the note on
+    identical KV blocks, and the prefix-caching paragraph; [P2] section 3).
 
 Readings where the pages are silent:
   * The free blocks form a FIFO queue seeded by a given order: allocation pops
@@ -33,6 +37,19 @@ Readings where the pages are silent:
     block takes the next host block, which inherits its refcount, and the
     device block joins the device queue's tail.  Swap-in mirrors it.  Both are
     all or nothing.  A swapped-out sequence can only be swapped in or freed.
+  * Prefix keys.  key(block 0) = FNV-1a-64 of the 8 little-endian bytes of 0
+    then the block's B token ids as 4-byte little-endian integers; key(block
+    i) chains the same way from key(block i-1).  A block is registered when an
+    append that carries token ids fills it and its key is not yet registered.
+    A lookup hits only if the key is registered and the block's stored
+    parent key and tokens equal the query (so a hash collision is a miss).
+    A new sequence takes the longest run of leading hits, at most
+    (n - 1) // B blocks of its n prompt tokens (one token is always left to
+    compute).  A hit block with refcount 0 leaves the free queue wherever it
+    sits.  Freed blocks keep their key while they wait in the queue; a block
+    loses it when it is popped for new use (eviction, oldest freed first) or
+    moved to the host tier.  An append without token ids stops a sequence's
+    key chain; blocks brought back from the host are not registered again.
 
 This model applies each batch to a deep copy of the state and commits the copy
 only on success, which makes the all-or-nothing rule evident.
@@ -68,11 +85,32 @@ class WrongTier(PoolError):
     """The sequence is on the other tier (swapped out, or not swapped out)."""
 
 
+FNV64_OFFSET = 0xCBF29CE484222325
+FNV64_PRIME = 0x100000001B3
+
+
+def fnv1a64(data: bytes) -> int:
+    """FNV-1a, 64-bit (Fowler, Noll, Vo): xor each byte in, then multiply by the prime, modulo 2^64."""
+    h = FNV64_OFFSET
+    for byte in data:
+        h = ((h ^ byte) * FNV64_PRIME) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def block_key(parent: int, tokens: Sequence[int]) -> int:
+    """Prefix key of a full block whose preceding block has key ``parent`` (0 for the first block)."""
+    data = int(parent).to_bytes(8, "little") + b"".join(int(t).to_bytes(4, "little", signed=True) for t in tokens)
+    return fnv1a64(data)
+
+
 @dataclass
 class _Seq:
     table: List[int] = field(default_factory=list)
     length: int = 0
     on_host: bool = False  # swapped out: the table holds host block ids
+    tracked: bool = True  # every token so far came with its id: the key chain is known
+    last_key: int = 0  # key of the last full block (0 before the first)
+    partial: List[int] = field(default_factory=list)  # token ids of the partly filled last block
 
 
 class BlockPool:
@@ -92,6 +130,8 @@ class BlockPool:
         self.host_blocks = host_blocks
         self.host_free: deque = deque(range(host_blocks))
         self.host_refcount = [0] * host_blocks
+        self.cached: Dict[int, int] = {}  # prefix key -> device block
+        self.block_keys: Dict[int, Tuple[int, int, Tuple[int, ...]]] = {}  # block -> (key, parent key, tokens)
 
     # -- sequences -----------------------------------------------------------
     def create(self) -> int:
@@ -115,7 +155,8 @@ class BlockPool:
         """New sequence sharing every block of ``parent``; each shared block's count rises by one."""
         p = self._on_device(parent)
         sid = self.create()
-        self.seqs[sid] = _Seq(table=list(p.table), length=p.length)
+        self.seqs[sid] = _Seq(table=list(p.table), length=p.length, tracked=p.tracked, last_key=p.last_key,
+                              partial=list(p.partial))
         for b in p.table:
             self.refcount[b] += 1
         return sid
@@ -135,8 +176,15 @@ class BlockPool:
         if not self.free:
             raise OutOfBlocks()
         b = self.free.popleft()
+        self._forget(b)  # a cached block taken for new use loses its key
         self.refcount[b] = 1
         return b
+
+    def _forget(self, b: int) -> None:
+        if b in self.block_keys:
+            key = self.block_keys.pop(b)[0]
+            if self.cached.get(key) == b:
+                del self.cached[key]
 
     def _append_one(self, sid: int, count: int, slots: List[int], pairs: List[Tuple[int, int]]) -> None:
         B = self.block_size
@@ -156,17 +204,41 @@ class BlockPool:
             slots.append(s.table[p // B] * B + p % B)
         s.length += count
 
-    def append(self, seqs: Sequence[int], counts: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    def _track(self, sid: int, ids: Sequence[int]) -> None:
+        """Extend sid's key chain by the ids just appended, registering every block they fill."""
+        s = self.seqs[sid]
+        B = self.block_size
+        if not s.tracked:
+            return
+        pos = s.length - len(ids)
+        for t in ids:
+            s.partial.append(int(t))
+            if len(s.partial) == B:
+                b = s.table[pos // B]
+                key = block_key(s.last_key, s.partial)
+                if key not in self.cached:
+                    self.cached[key] = b
+                    self.block_keys[b] = (key, s.last_key, tuple(s.partial))
+                s.last_key = key
+                s.partial = []
+            pos += 1
+
+    def append(self, seqs: Sequence[int], counts: Sequence[int],
+               token_ids: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
         """Append ``counts[i]`` tokens to ``seqs[i]``, in order; all or nothing.
 
         Returns ``(slots int64[sum counts], pairs int32[k][2])``; slots are in
         sequence-major, position order.  Raises OutOfBlocks (state unchanged)
-        when the pool cannot hold the whole batch.
+        when the pool cannot hold the whole batch.  ``token_ids`` (sequence-
+        major, one per new token) extends the sequences' prefix keys; without
+        it, the appended sequences stop being keyed.
         """
         seqs = [int(x) for x in seqs]
         counts = [int(c) for c in counts]
         if len(seqs) != len(counts):
             raise InvalidArg("seqs and counts differ in length")
+        if token_ids is not None and len(token_ids) != sum(max(c, 0) for c in counts):
+            raise InvalidArg("one token id per appended token")
         if len(set(seqs)) != len(seqs):
             raise InvalidArg("a sequence appears twice in one batch")
         if any(c < 0 for c in counts):
@@ -180,8 +252,44 @@ class BlockPool:
         pairs: List[Tuple[int, int]] = []
         for sid, c in zip(seqs, counts):
             trial._append_one(sid, c, slots, pairs)
+        k = 0
+        for sid, c in zip(seqs, counts):
+            if c == 0:
+                continue
+            if token_ids is None:
+                trial.seqs[sid].tracked = False
+                trial.seqs[sid].partial = []
+            else:
+                trial._track(sid, token_ids[k:k + c])
+            k += c
         self.__dict__.update(trial.__dict__)
         return np.asarray(slots, dtype=np.int64), np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+
+    # -- prefix caching ----------------------------------------------------------------
+    def create_prefixed(self, token_ids: Sequence[int]) -> Tuple[int, int]:
+        """New sequence whose prompt is ``token_ids``: it starts with the longest run of cached leading blocks.
+
+        Returns ``(sequence id, cached tokens)``; the caller appends the
+        remaining ``token_ids[cached:]`` (with their ids) and computes only
+        their keys and values.
+        """
+        ids = [int(t) for t in token_ids]
+        B = self.block_size
+        sid = self.create()
+        s = self.seqs[sid]
+        for i in range((len(ids) - 1) // B if ids else 0):
+            toks = tuple(ids[i * B:(i + 1) * B])
+            key = block_key(s.last_key, toks)
+            b = self.cached.get(key)
+            if b is None or self.block_keys[b] != (key, s.last_key, toks):
+                break
+            if self.refcount[b] == 0:
+                self.free.remove(b)
+            self.refcount[b] += 1
+            s.table.append(b)
+            s.length += B
+            s.last_key = key
+        return sid, s.length
 
     # -- swapping --------------------------------------------------------------------
     def _swap(self, seqs: Sequence[int], out: bool) -> np.ndarray:
@@ -210,7 +318,11 @@ class BlockPool:
             raise OutOfBlocks()
         moved: Dict[int, int] = {}
         for b in met:
+            if out:
+                self._forget(b)  # keys name device blocks only
             nb = dst_queue.popleft()
+            if not out:
+                self._forget(nb)
             dst_ref[nb] = src_ref[b]
             src_ref[b] = 0
             src_queue.append(b)
@@ -283,6 +395,8 @@ class BlockPool:
             "host_used_blocks": sum(1 for r in self.host_refcount if r > 0),
             "swapped_seqs": len(swapped),
             "swapped_tokens": sum(s.length for s in swapped),
+            "cached_blocks": len(self.cached),
+            "cached_free_blocks": sum(1 for b in self.free if b in self.block_keys),
         }
 
     def free_list(self) -> List[int]:

@@ -353,3 +353,128 @@ def group_of(pool: al.BlockPool, sid: int):
                 group.add(o)
                 todo.append(o)
     return sorted(group)
+
+
+def test_fnv1a64_published_vectors():
+    # the FNV reference test vectors for the 64-bit FNV-1a hash
+    assert al.fnv1a64(b"") == 0xCBF29CE484222325
+    assert al.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert al.fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def test_prefix_cache_by_hand():
+    pool = al.BlockPool(8, 4)
+    a = pool.create()
+    slots, _ = pool.append([a], [10], token_ids=list(range(1, 11)))
+    assert pool.table(a) == [0, 1, 2] and list(slots) == list(range(10))
+    k0 = al.block_key(0, [1, 2, 3, 4])
+    k1 = al.block_key(k0, [5, 6, 7, 8])
+    assert pool.cached == {k0: 0, k1: 1}  # the partial block 2 has no key
+    b, hit = pool.create_prefixed([1, 2, 3, 4, 5, 6, 7, 8, 11, 12])
+    assert hit == 8 and pool.table(b) == [0, 1] and pool.refcount[:2] == [2, 2]
+    slots, pairs = pool.append([b], [2], token_ids=[11, 12])
+    assert pool.table(b) == [0, 1, 3] and list(slots) == [12, 13] and pairs.shape == (0, 2)
+    # a prompt of exactly two blocks may take only the first: one token is always computed
+    c, hit = pool.create_prefixed([1, 2, 3, 4, 5, 6, 7, 8])
+    assert hit == 4 and pool.table(c) == [0] and pool.refcount[0] == 3
+    pool.append([c], [4], token_ids=[5, 6, 7, 8])
+    assert pool.table(c) == [0, 4] and pool.cached == {k0: 0, k1: 1}  # k1 already names block 1
+    pool.free_seq(a)
+    pool.free_seq(b)
+    assert pool.free_list() == [5, 6, 7, 2, 1, 3]  # block 1 waits in the queue with its key
+    assert pool.stats()["cached_free_blocks"] == 1
+    d, hit = pool.create_prefixed([1, 2, 3, 4, 5, 6, 7, 8, 9])
+    assert hit == 8 and pool.table(d) == [0, 1]
+    assert pool.free_list() == [5, 6, 7, 2, 3] and pool.refcount[:2] == [2, 1]  # block 1 left the queue
+    e = pool.create()
+    pool.append([e], [16])  # no ids: e is not keyed
+    assert pool.table(e) == [5, 6, 7, 2] and len(pool.cached) == 2
+    pool.free_seq(d)
+    assert pool.free_list() == [3, 1]
+    f = pool.create()
+    pool.append([f], [8])  # takes 3, then 1: block 1 is evicted
+    assert pool.table(f) == [3, 1] and pool.cached == {k0: 0}
+    g, hit = pool.create_prefixed([1, 2, 3, 4, 5, 6, 7, 8, 9])
+    assert hit == 4 and pool.table(g) == [0]
+    check_invariants(pool)
+
+
+def test_prefix_keys_cover_the_whole_preceding_run():
+    pool = al.BlockPool(16, 4)
+    a = pool.create()
+    pool.append([a], [13], token_ids=list(range(100, 113)))  # three full blocks
+    # one token changed in block 1: blocks from there on miss
+    ids = list(range(100, 113))
+    ids[5] = 0
+    _, hit = pool.create_prefixed(ids)
+    assert hit == 4
+    # block 1's tokens after a different block 0 are not the same block
+    ids = [0, 0, 0, 0] + list(range(104, 113))
+    _, hit = pool.create_prefixed(ids)
+    assert hit == 0
+    # the same prompt hits every full block it may take
+    _, hit = pool.create_prefixed(list(range(100, 113)))
+    assert hit == 12
+    # a cached block 0 followed by tokens that are cached only after another block 0
+    x = pool.create()
+    pool.append([x], [9], token_ids=[7, 7, 7, 7, 8, 8, 8, 8, 1])
+    _, hit = pool.create_prefixed([7, 7, 7, 7] + list(range(104, 109)))
+    assert hit == 4
+    check_invariants(pool)
+
+
+def test_prefix_cache_refuses_hash_collisions(monkeypatch):
+    monkeypatch.setattr(al, "block_key", lambda parent, tokens: 7)  # every block collides
+    pool = al.BlockPool(8, 4)
+    a = pool.create()
+    pool.append([a], [5], token_ids=[1, 2, 3, 4, 5])
+    _, hit = pool.create_prefixed([9, 9, 9, 9, 9])
+    assert hit == 0  # same key, other tokens: a miss
+    _, hit = pool.create_prefixed([1, 2, 3, 4, 5])
+    assert hit == 4
+    check_invariants(pool)
+
+
+def test_prefix_cache_random_operations():
+    rng = np.random.default_rng(77)
+    for trial in range(15):
+        B = int(rng.choice([1, 2, 4]))
+        pool = al.BlockPool(int(rng.integers(8, 40)), B, host_blocks=int(rng.integers(0, 20)))
+        prompts = [list(rng.integers(0, 3, size=int(rng.integers(1, 12)))) for _ in range(4)]
+        for _ in range(60):
+            op = int(rng.integers(0, 5))
+            dev = [s for s in pool.seqs if not pool.on_host(s)]
+            if op == 0 or not dev:
+                ids = [int(x) for x in prompts[int(rng.integers(0, 4))]] + [int(x) for x in
+                                                                           rng.integers(0, 3, size=int(rng.integers(0, 6)))]
+                sid, hit = pool.create_prefixed(ids)
+                assert hit % B == 0 and hit <= max(len(ids) - 1, 0)
+                for i in range(hit // B):  # every reused block holds exactly this prompt's tokens
+                    assert pool.block_keys[pool.table(sid)[i]][2] == tuple(ids[i * B:(i + 1) * B])
+                try:
+                    pool.append([sid], [len(ids) - hit], token_ids=ids[hit:])
+                except al.OutOfBlocks:
+                    pool.free_seq(sid)
+            elif op == 1:
+                pool.free_seq(int(rng.choice(list(pool.seqs))))
+            elif op == 2:
+                sid = int(rng.choice(dev))
+                n = int(rng.integers(1, 5))
+                try:
+                    pool.append([sid], [n], token_ids=[int(x) for x in rng.integers(0, 3, size=n)])
+                except al.OutOfBlocks:
+                    pass
+            elif op == 3:
+                pool.fork(int(rng.choice(dev)))
+            else:
+                tier = [s for s in pool.seqs if pool.on_host(s) == (op == 4 and rng.random() < 0.5)]
+                if tier:
+                    try:
+                        g = group_of(pool, int(rng.choice(tier)))
+                        pool.swap_in(g) if pool.on_host(g[0]) else pool.swap_out(g)
+                    except al.OutOfBlocks:
+                        pass
+            check_invariants(pool)
+            for key, b in pool.cached.items():  # registered keys name live or queued device blocks
+                assert pool.block_keys[b][0] == key
+                assert pool.refcount[b] > 0 or b in pool.free

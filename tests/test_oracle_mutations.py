@@ -230,3 +230,31 @@ def test_swap_copy_direction_is_caught(monkeypatch):
 
     monkeypatch.setattr(oc, "swap_blocks", reversed_pairs)
     assert _fails_some([t_alloc.test_swap_round_trip_keeps_every_token])
+
+
+def test_prefix_key_without_the_preceding_run_is_caught(monkeypatch):
+    def loose_create_prefixed(self, token_ids):
+        ids = [int(t) for t in token_ids]
+        B = self.block_size
+        sid = self.create()
+        s = self.seqs[sid]
+        for i in range((len(ids) - 1) // B if ids else 0):
+            toks = tuple(ids[i * B:(i + 1) * B])
+            hit = [b for b, (_, _, t) in self.block_keys.items() if t == toks]  # wrong: ignores what precedes
+            if not hit:
+                break
+            b = hit[0]
+            if self.refcount[b] == 0:
+                self.free.remove(b)
+            self.refcount[b] += 1
+            s.table.append(b)
+            s.length += B
+        return sid, s.length
+
+    monkeypatch.setattr(al.BlockPool, "create_prefixed", loose_create_prefixed)
+    assert _fails_some([t_alloc.test_prefix_keys_cover_the_whole_preceding_run])
+
+
+def test_prefix_cache_that_never_evicts_is_caught(monkeypatch):
+    monkeypatch.setattr(al.BlockPool, "_forget", lambda self, b: None)
+    assert _fails_some([t_alloc.test_prefix_cache_by_hand])
