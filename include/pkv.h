@@ -92,6 +92,8 @@ typedef struct pkv_stats {
   int64_t host_used_blocks; /* host blocks with refcount > 0 */
   int64_t swapped_seqs;     /* live sequences on the host tier */
   int64_t swapped_tokens;   /* sum of their lengths */
+  int64_t cached_blocks;      /* device blocks findable by prefix key */
+  int64_t cached_free_blocks; /* of those, blocks waiting in the free queue */
 } pkv_stats;
 
 /* Human-readable name of a status code (static string). */
@@ -142,6 +144,16 @@ pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
  *      record the pair (old, new), decrement old, point the table at new;
  *   2. for each position p in [L, L + c): if p % B == 0 pop a fresh block;
  *      emit slot table[p / B] * B + p % B.
+ * A block popped from the free queue loses its prefix key (eviction).
+ * token_ids: host int32[sum(counts)], the new tokens' ids, sequence-major, or
+ *   NULL.  With ids, each block the batch fills is registered for automatic
+ *   prefix caching ([P4] prefix-caching paragraph) under
+ *     key = FNV-1a-64( parent key as 8 little-endian bytes,
+ *                      the block's B ids as 4-byte little-endian integers ),
+ *   parent key = the previous block's key, 0 for a sequence's first block,
+ *   unless that key is already registered; keys are registered after every
+ *   block of the batch has been taken.  Without ids, the listed sequences
+ *   (count > 0) stop being keyed for the rest of their life.
  * out_slots: host int64[slots_cap] receiving sum(counts) slots, sequence-major
  *   and in position order.
  * out_cow_pairs: host int32[2 * cow_cap] receiving (src, dst) block pairs; the
@@ -153,8 +165,33 @@ pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
  *   the last case *out_n_cow holds the number needed), NO_SUCH_SEQ,
  *   OUT_OF_BLOCKS (the batch needs more blocks than are free). */
 pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t* counts, int32_t n,
-                             int64_t* out_slots, int64_t slots_cap, int32_t* out_cow_pairs,
-                             int32_t cow_cap, int32_t* out_n_cow);
+                             const int32_t* token_ids, int64_t* out_slots, int64_t slots_cap,
+                             int32_t* out_cow_pairs, int32_t cow_cap, int32_t* out_n_cow);
+
+/* Automatic prefix caching ([P4] the note that identical KV blocks can be
+ * shared, and the prefix-caching paragraph; [P2] section 3, sharing of a
+ * common prompt).  Create a sequence for a prompt of n_tokens ids (host
+ * int32[n_tokens]) that starts with the longest run of its leading full
+ * blocks already registered, at most (n_tokens - 1) / B of them so that at
+ * least one prompt token is left to compute.  Block i hits when the key
+ * chained from the hits before it is registered and the block holding it
+ * stored the same parent key and the same B ids (a hash collision is a miss).
+ * Each hit block's refcount rises by one; a hit block with refcount 0 leaves
+ * the free queue from wherever it sits.  *out_cached_tokens receives the
+ * tokens mapped (a multiple of B); the caller appends the remaining ids with
+ * pkv_append_tokens (token_ids given) and writes only their keys and values.
+ * A freed block keeps its key while it waits in the free queue; it loses it
+ * when popped for new use or moved to the host tier (blocks brought back from
+ * the host are not registered again).
+ * Errors: INVALID_ARG (NULL pointers, n_tokens < 0). */
+pkv_status pkv_seq_create_prefixed(pkv_pool* pool, const int32_t* token_ids, int32_t n_tokens, int32_t* out_seq,
+                                   int32_t* out_cached_tokens);
+
+/* The registered prefix keys and their device blocks, in increasing key order:
+ * host out_keys[cap], out_blocks[cap]; *out_n = their number.
+ * Errors: INVALID_ARG (cap too small; *out_n is still set). */
+pkv_status pkv_pool_cached_blocks(const pkv_pool* pool, uint64_t* out_keys, int32_t* out_blocks, int32_t cap,
+                                  int32_t* out_n);
 
 /* Dense block tables for seqs[0..n): host int32 out_tables[n][max_blocks],
  * row i = the physical blocks of seqs[i] in logical order, padded with -1;
@@ -182,7 +219,8 @@ pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, i
 /* Check the pool's invariants, per tier: each block's refcount equals the
  * number of live tables of that tier holding it; a free block has refcount 0
  * and appears once; free plus used equals capacity; each table has
- * ceil(length / B) entries.  [P3] section 3 asks tests to check refcounts and
+ * ceil(length / B) entries; the prefix-key map and the keyed blocks match one
+ * to one.  [P3] section 3 asks tests to check refcounts and
  * reuse.  Errors: REFCOUNT. */
 pkv_status pkv_pool_validate(const pkv_pool* pool);
 

@@ -25,6 +25,7 @@ from ._lib import (PKV_BF16, PKV_ERR_INVALID_ARG, PKV_F32, InvalidArg, NoSuchSeq
 
 __all__ = [
     "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_create", "pkv_seq_fork", "pkv_seq_free", "pkv_append_tokens",
+    "pkv_seq_create_prefixed", "pkv_pool_cached_blocks",
     "pkv_block_tables", "pkv_seq_info", "pkv_pool_stats", "pkv_block_refcount", "pkv_pool_free_list",
     "pkv_pool_validate", "pkv_pool_set_host_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_seq_table",
     "pkv_host_block_refcount", "pkv_pool_host_free_list", "pkv_swap_blocks", "empty_host_caches", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_attention_workspace_bytes",
@@ -76,19 +77,51 @@ def pkv_seq_free(pool, seq: int) -> None:
     check(lib().pkv_seq_free(pool, seq), "pkv_seq_free")
 
 
-def pkv_append_tokens(pool, seqs: Sequence[int], counts: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
-    """Returns (slots int64[sum counts], copy-on-write pairs int32[k][2])."""
+def pkv_append_tokens(pool, seqs: Sequence[int], counts: Sequence[int],
+                      token_ids: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Returns (slots int64[sum counts], copy-on-write pairs int32[k][2]); token_ids (one per new token,
+    sequence-major) keys the blocks the batch fills for prefix caching."""
     seqs = np.ascontiguousarray(seqs, dtype=np.int32)
     counts = np.ascontiguousarray(counts, dtype=np.int32)
     if seqs.shape != counts.shape or seqs.ndim != 1:
         raise InvalidArg(-1, "pkv_append_tokens", "seqs and counts must be 1-D and equal in length")
     total = int(counts[counts > 0].sum()) if counts.size else 0
+    ids = None
+    if token_ids is not None:
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+        if ids.ndim != 1 or ids.size != total:
+            raise InvalidArg(-1, "pkv_append_tokens", "one token id per appended token")
     slots = np.empty(max(total, 0), dtype=np.int64)
     pairs = np.empty((max(len(seqs), 1), 2), dtype=np.int32)
     n_cow = ctypes.c_int32()
-    check(lib().pkv_append_tokens(pool, _ptr(seqs), _ptr(counts), len(seqs), _ptr(slots), slots.size,
+    # an empty id list is still "ids given": pass a valid pointer
+    ids_ptr = None if ids is None else ids.ctypes.data_as(ctypes.c_void_p) if ids.size else \
+        np.zeros(1, dtype=np.int32).ctypes.data_as(ctypes.c_void_p)
+    check(lib().pkv_append_tokens(pool, _ptr(seqs), _ptr(counts), len(seqs), ids_ptr, _ptr(slots), slots.size,
                                   _ptr(pairs), pairs.shape[0], ctypes.byref(n_cow)), "pkv_append_tokens")
     return slots, pairs[:n_cow.value].copy()
+
+
+def pkv_seq_create_prefixed(pool, token_ids: Sequence[int]) -> Tuple[int, int]:
+    """New sequence for a prompt: maps its longest run of cached leading blocks; returns (seq, cached tokens)."""
+    ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+    if ids.ndim != 1:
+        raise InvalidArg(-1, "pkv_seq_create_prefixed", "token_ids must be 1-D")
+    sid, hit = ctypes.c_int32(), ctypes.c_int32()
+    check(lib().pkv_seq_create_prefixed(pool, _ptr(ids), ids.size, ctypes.byref(sid), ctypes.byref(hit)),
+          "pkv_seq_create_prefixed")
+    return sid.value, hit.value
+
+
+def pkv_pool_cached_blocks(pool) -> dict:
+    """The prefix cache: {key: device block}."""
+    n = ctypes.c_int32()
+    lib().pkv_pool_cached_blocks(pool, None, None, 0, ctypes.byref(n))
+    keys = np.empty(n.value, dtype=np.uint64)
+    blocks = np.empty(n.value, dtype=np.int32)
+    check(lib().pkv_pool_cached_blocks(pool, _ptr(keys), _ptr(blocks), n.value, ctypes.byref(n)),
+          "pkv_pool_cached_blocks")
+    return {int(k): int(b) for k, b in zip(keys, blocks)}
 
 
 def pkv_block_tables(pool, seqs: Sequence[int], max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -208,8 +241,14 @@ class Pool:
     def free_seq(self, seq: int) -> None:
         pkv_seq_free(self.handle, seq)
 
-    def append(self, seqs, counts):
-        return pkv_append_tokens(self.handle, seqs, counts)
+    def append(self, seqs, counts, token_ids=None):
+        return pkv_append_tokens(self.handle, seqs, counts, token_ids)
+
+    def create_prefixed(self, token_ids):
+        return pkv_seq_create_prefixed(self.handle, token_ids)
+
+    def cached(self) -> dict:
+        return pkv_pool_cached_blocks(self.handle)
 
     def block_tables(self, seqs, max_blocks):
         return pkv_block_tables(self.handle, seqs, max_blocks)

@@ -49,7 +49,8 @@ class Stats(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in (
         "num_blocks", "free_blocks", "used_blocks", "sum_refcount", "num_seqs",
         "logical_tokens", "logical_blocks", "allocated_slots", "table_bytes",
-        "host_blocks", "host_free_blocks", "host_used_blocks", "swapped_seqs", "swapped_tokens")]
+        "host_blocks", "host_free_blocks", "host_used_blocks", "swapped_seqs", "swapped_tokens",
+        "cached_blocks", "cached_free_blocks")]
 
     def as_dict(self):
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
@@ -69,7 +70,9 @@ _SIGS = {
     "pkv_seq_create": (i32, [vp, P_i32]),
     "pkv_seq_fork": (i32, [vp, i32, P_i32]),
     "pkv_seq_free": (i32, [vp, i32]),
-    "pkv_append_tokens": (i32, [vp, vp, vp, i32, vp, i64, vp, i32, P_i32]),
+    "pkv_append_tokens": (i32, [vp, vp, vp, i32, vp, vp, i64, vp, i32, P_i32]),
+    "pkv_seq_create_prefixed": (i32, [vp, vp, i32, P_i32, P_i32]),
+    "pkv_pool_cached_blocks": (i32, [vp, vp, vp, i32, P_i32]),
     "pkv_block_tables": (i32, [vp, vp, i32, i32, vp, vp]),
     "pkv_seq_info": (i32, [vp, i32, P_i32, P_i32]),
     "pkv_pool_stats": (i32, [vp, ctypes.POINTER(Stats)]),

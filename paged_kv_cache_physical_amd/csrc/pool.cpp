@@ -5,7 +5,7 @@
 // (sharing, refcounts tied to request lifetime, copy-on-write of a shared block
 // that is not full, reclamation on finish/cancel); [P4] beam-search sharing.
 //
-// Free blocks sit in a FIFO ring: allocation takes the head, release appends
+// Free blocks sit in a FIFO queue: allocation takes the head, release appends
 // to the tail.  An append batch is checked first (blocks needed, including the
 // copies that refcounts will force) and only then applied, so a failure leaves
 // the pool untouched.
@@ -14,6 +14,13 @@
 // preemption"; [P4] "Preemption"): an optional host tier with its own FIFO
 // ring of host block ids.  A swap moves a whole sharing group between the
 // tiers; a block keeps its refcount, and the sequences' tables are renamed.
+//
+// Automatic prefix caching ([P4] the note on identical KV blocks and the
+// prefix-caching paragraph; [P2] section 3): a full block written with known
+// token ids is registered under a key chained over every token before it and
+// its own; a new prompt maps its longest run of registered leading blocks
+// instead of computing them again.  Freed blocks stay findable until they are
+// taken for new use (oldest freed first) or moved to the host tier.
 
 #include <algorithm>
 #include <cstring>
@@ -30,39 +37,75 @@ struct Seq {
   int64_t length = 0;
   bool live = false;
   bool on_host = false;  // swapped out
+  bool tracked = true;    // every token so far came with its id
+  uint64_t last_key = 0;  // key of the last full block (0 before the first)
+  std::vector<int32_t> partial;  // ids of the tokens in the partly filled last block
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// One tier's blocks: refcounts and the FIFO ring of free ids.
+// One tier's blocks: refcounts and the FIFO queue of free ids, kept as a
+// doubly linked list through the block ids so that a cached block found again
+// can leave the queue from wherever it sits.
 struct Tier {
   int32_t num_blocks = 0;
-  std::vector<int32_t> ring;  // capacity num_blocks
-  int64_t head = 0;
+  std::vector<int32_t> next, prev;  // queue links; -1 past either end
+  std::vector<char> queued;
+  int32_t head = -1, tail = -1;
   int64_t count = 0;
   std::vector<int32_t> refcount;
 
   void reset(int32_t n) {
     num_blocks = n;
-    ring.resize(n);
-    for (int32_t i = 0; i < n; ++i) ring[i] = i;
-    head = 0;
-    count = n;
+    next.assign(n, -1);
+    prev.assign(n, -1);
+    queued.assign(n, 0);
+    head = tail = -1;
+    count = 0;
     refcount.assign(n, 0);
   }
-  int32_t pop() {
-    int32_t b = ring[head];
-    head = (head + 1) % num_blocks;
+  void push(int32_t b) {
+    prev[b] = tail;
+    next[b] = -1;
+    if (tail >= 0) next[tail] = b; else head = b;
+    tail = b;
+    queued[b] = 1;
+    ++count;
+  }
+  void remove(int32_t b) {
+    if (prev[b] >= 0) next[prev[b]] = next[b]; else head = next[b];
+    if (next[b] >= 0) prev[next[b]] = prev[b]; else tail = prev[b];
+    prev[b] = next[b] = -1;
+    queued[b] = 0;
     --count;
+  }
+  int32_t pop() {
+    const int32_t b = head;
+    remove(b);
     refcount[b] = 1;
     return b;
   }
-  void push(int32_t b) {
-    ring[(head + count) % num_blocks] = b;
-    ++count;
-  }
-  int32_t free_at(int64_t i) const { return ring[(head + i) % num_blocks]; }
 };
+
+// FNV-1a, 64-bit (Fowler, Noll, Vo): xor in each byte, multiply by the prime.
+constexpr uint64_t kFnvOffset = 0xCBF29CE484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001B3ull;
+
+uint64_t fnv_bytes(uint64_t h, uint64_t v, int nbytes) {
+  for (int i = 0; i < nbytes; ++i) {
+    h ^= (v >> (8 * i)) & 0xFF;
+    h *= kFnvPrime;
+  }
+  return h;
+}
+
+// Key of a full block: the parent block's key as 8 little-endian bytes, then
+// the block's token ids as 4-byte little-endian integers.
+uint64_t block_key(uint64_t parent, const int32_t* tokens, int64_t B) {
+  uint64_t h = fnv_bytes(kFnvOffset, parent, 8);
+  for (int64_t i = 0; i < B; ++i) h = fnv_bytes(h, static_cast<uint32_t>(tokens[i]), 4);
+  return h;
+}
 
 }  // namespace
 
@@ -72,6 +115,12 @@ struct pkv_pool {
   Tier host;
   std::vector<Seq> seqs;  // index = sequence id
   int64_t live = 0;
+  // Prefix cache: key -> device block, and per device block its key, parent
+  // key and token ids (tokens stored B per block, allocated on first use).
+  std::unordered_map<uint64_t, int32_t> cached;
+  std::vector<char> keyed;
+  std::vector<uint64_t> bkey, bparent;
+  std::vector<int32_t> btokens;
 
   Seq* get(int32_t id) {
     if (id < 0 || static_cast<size_t>(id) >= seqs.size() || !seqs[id].live) return nullptr;
@@ -80,6 +129,46 @@ struct pkv_pool {
   const Seq* get(int32_t id) const {
     if (id < 0 || static_cast<size_t>(id) >= seqs.size() || !seqs[id].live) return nullptr;
     return &seqs[id];
+  }
+  // A block leaving the device tier's pool of findable blocks loses its key.
+  void forget(int32_t b) {
+    if (!keyed[b]) return;
+    auto it = cached.find(bkey[b]);
+    if (it != cached.end() && it->second == b) cached.erase(it);
+    keyed[b] = 0;
+  }
+  // Taking a free device block for new use evicts its key.
+  int32_t pop_dev() {
+    const int32_t b = dev.pop();
+    forget(b);
+    return b;
+  }
+  bool matches(int32_t b, uint64_t key, uint64_t parent, const int32_t* tokens) const {
+    return keyed[b] && bkey[b] == key && bparent[b] == parent &&
+           std::equal(tokens, tokens + block_size, btokens.begin() + static_cast<int64_t>(b) * block_size);
+  }
+  // Extend s's key chain by the ids just appended (the last ids.size()
+  // positions), registering each block they fill whose key is new.
+  void track(Seq& s, const int32_t* ids, int64_t c) {
+    if (!s.tracked) return;
+    const int64_t B = block_size;
+    int64_t pos = s.length - c;
+    for (int64_t i = 0; i < c; ++i, ++pos) {
+      s.partial.push_back(ids[i]);
+      if (static_cast<int64_t>(s.partial.size()) < B) continue;
+      const int32_t b = s.table[pos / B];
+      const uint64_t key = block_key(s.last_key, s.partial.data(), B);
+      if (cached.find(key) == cached.end()) {
+        if (btokens.empty()) btokens.resize(static_cast<size_t>(dev.num_blocks) * B);
+        cached.emplace(key, b);
+        keyed[b] = 1;
+        bkey[b] = key;
+        bparent[b] = s.last_key;
+        std::copy(s.partial.begin(), s.partial.end(), btokens.begin() + static_cast<int64_t>(b) * B);
+      }
+      s.last_key = key;
+      s.partial.clear();
+    }
   }
 };
 
@@ -100,7 +189,7 @@ const char* pkv_status_string(pkv_status s) {
   }
 }
 
-int32_t pkv_abi_version(void) { return 5; }
+int32_t pkv_abi_version(void) { return 6; }
 
 pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
                            pkv_pool** out) {
@@ -119,9 +208,14 @@ pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t
         return PKV_ERR_INVALID_ARG;
       }
       seen[b] = 1;
-      p->dev.ring[i] = b;
     }
+    for (int32_t i = 0; i < num_blocks; ++i) p->dev.push(free_order[i]);
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) p->dev.push(i);
   }
+  p->keyed.assign(num_blocks, 0);
+  p->bkey.assign(num_blocks, 0);
+  p->bparent.assign(num_blocks, 0);
   *out = p;
   return PKV_OK;
 }
@@ -132,6 +226,7 @@ pkv_status pkv_pool_set_host_blocks(pkv_pool* pool, int32_t num_host_blocks) {
     if (s.live && s.on_host) return PKV_ERR_INVALID_ARG;
   }
   pool->host.reset(num_host_blocks);
+  for (int32_t i = 0; i < num_host_blocks; ++i) pool->host.push(i);
   return PKV_OK;
 }
 
@@ -155,6 +250,9 @@ pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* out_child) {
   Seq child;
   child.table = pool->seqs[parent].table;  // copy before emplace may reallocate
   child.length = pool->seqs[parent].length;
+  child.tracked = pool->seqs[parent].tracked;
+  child.last_key = pool->seqs[parent].last_key;
+  child.partial = pool->seqs[parent].partial;
   child.live = true;
   for (int32_t b : child.table) ++pool->dev.refcount[b];
   pool->seqs.push_back(std::move(child));
@@ -173,6 +271,8 @@ pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq) {
   }
   s->table.clear();
   s->table.shrink_to_fit();
+  s->partial.clear();
+  s->partial.shrink_to_fit();
   s->length = 0;
   s->live = false;
   s->on_host = false;
@@ -181,8 +281,8 @@ pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq) {
 }
 
 pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t* counts, int32_t n,
-                             int64_t* out_slots, int64_t slots_cap, int32_t* out_cow_pairs,
-                             int32_t cow_cap, int32_t* out_n_cow) {
+                             const int32_t* token_ids, int64_t* out_slots, int64_t slots_cap,
+                             int32_t* out_cow_pairs, int32_t cow_cap, int32_t* out_n_cow) {
   if (!pool || n < 0 || !out_n_cow) return PKV_ERR_INVALID_ARG;
   *out_n_cow = 0;
   if (n == 0) return PKV_OK;
@@ -238,7 +338,7 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
     if (L % B != 0) {
       const int32_t last = s.table.back();
       if (pool->dev.refcount[last] > 1) {
-        const int32_t fresh = pool->dev.pop();
+        const int32_t fresh = pool->pop_dev();
         out_cow_pairs[2 * npairs] = last;
         out_cow_pairs[2 * npairs + 1] = fresh;
         ++npairs;
@@ -247,10 +347,25 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
       }
     }
     for (int64_t p = L; p < L + c; ++p) {
-      if (p % B == 0) s.table.push_back(pool->dev.pop());
+      if (p % B == 0) s.table.push_back(pool->pop_dev());
       out_slots[k++] = static_cast<int64_t>(s.table[p / B]) * B + p % B;
     }
     s.length = L + c;
+  }
+  // Pass 3: prefix keys, after every block of the batch has been taken (a
+  // taken block's key is gone before any new key is registered).
+  int64_t t = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Seq& s = pool->seqs[seqs[i]];
+    const int64_t c = counts[i];
+    if (c == 0) continue;
+    if (token_ids) {
+      pool->track(s, token_ids + t, c);
+    } else {
+      s.tracked = false;
+      s.partial.clear();
+    }
+    t += c;
   }
   *out_n_cow = npairs;
   return PKV_OK;
@@ -341,7 +456,9 @@ static pkv_status swap_tier(pkv_pool* pool, const int32_t* seqs, int32_t n, int3
   std::unordered_map<int32_t, int32_t> moved;
   for (int64_t j = 0; j < k; ++j) {
     const int32_t b = met[j];
+    if (out) pool->forget(b);  // keys name device blocks only
     const int32_t nb = dst.pop();
+    if (!out) pool->forget(nb);
     dst.refcount[nb] = src.refcount[b];
     src.refcount[b] = 0;
     src.push(b);
@@ -395,6 +512,10 @@ pkv_status pkv_pool_stats(const pkv_pool* pool, pkv_stats* out) {
   for (int32_t r : pool->host.refcount) {
     if (r > 0) ++st.host_used_blocks;
   }
+  st.cached_blocks = static_cast<int64_t>(pool->cached.size());
+  for (int32_t b = pool->dev.head; b >= 0; b = pool->dev.next[b]) {
+    if (pool->keyed[b]) ++st.cached_free_blocks;
+  }
   *out = st;
   return PKV_OK;
 }
@@ -414,7 +535,8 @@ pkv_status copy_free_list(const Tier& t, int32_t* out, int32_t cap, int32_t* out
   if (!out_n) return PKV_ERR_INVALID_ARG;
   *out_n = static_cast<int32_t>(t.count);
   if (cap < t.count || (t.count > 0 && !out)) return PKV_ERR_INVALID_ARG;
-  for (int64_t i = 0; i < t.count; ++i) out[i] = t.free_at(i);
+  int64_t i = 0;
+  for (int32_t b = t.head; b >= 0; b = t.next[b]) out[i++] = b;
   return PKV_OK;
 }
 
@@ -427,12 +549,19 @@ bool tier_sound(const Tier& t, const std::vector<int64_t>& held) {
     if (held[b] > 0) ++used;
   }
   std::vector<char> in_free(t.num_blocks, 0);
-  for (int64_t i = 0; i < t.count; ++i) {
-    const int32_t b = t.free_at(i);
-    if (b < 0 || b >= t.num_blocks || in_free[b] || t.refcount[b] != 0) return false;
+  int64_t walked = 0;
+  int32_t before = -1;
+  for (int32_t b = t.head; b >= 0; b = t.next[b]) {
+    if (b >= t.num_blocks || in_free[b] || !t.queued[b] || t.refcount[b] != 0 || t.prev[b] != before) return false;
+    if (++walked > t.count) return false;
     in_free[b] = 1;
+    before = b;
   }
-  return used + t.count == t.num_blocks;
+  if (before != t.tail) return false;
+  for (int32_t b = 0; b < t.num_blocks; ++b) {
+    if (t.queued[b] != in_free[b]) return false;
+  }
+  return walked == t.count && used + t.count == t.num_blocks;
 }
 }  // namespace
 
@@ -459,6 +588,56 @@ pkv_status pkv_pool_validate(const pkv_pool* pool) {
     }
   }
   if (!tier_sound(pool->dev, held_dev) || !tier_sound(pool->host, held_host)) return PKV_ERR_REFCOUNT;
+  // Prefix cache: the key map and the keyed blocks name each other one to one.
+  int64_t keyed = 0;
+  for (int32_t b = 0; b < pool->dev.num_blocks; ++b) {
+    if (!pool->keyed[b]) continue;
+    ++keyed;
+    auto it = pool->cached.find(pool->bkey[b]);
+    if (it == pool->cached.end() || it->second != b) return PKV_ERR_REFCOUNT;
+  }
+  if (keyed != static_cast<int64_t>(pool->cached.size())) return PKV_ERR_REFCOUNT;
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_create_prefixed(pkv_pool* pool, const int32_t* token_ids, int32_t n_tokens, int32_t* out_seq,
+                                   int32_t* out_cached_tokens) {
+  if (!pool || !out_seq || !out_cached_tokens || n_tokens < 0 || (n_tokens > 0 && !token_ids)) {
+    return PKV_ERR_INVALID_ARG;
+  }
+  const pkv_status st = pkv_seq_create(pool, out_seq);
+  if (st != PKV_OK) return st;
+  Seq& s = pool->seqs[*out_seq];
+  const int64_t B = pool->block_size;
+  const int64_t reusable = n_tokens > 0 ? (n_tokens - 1) / B : 0;  // one token is always left to compute
+  for (int64_t i = 0; i < reusable; ++i) {
+    const int32_t* toks = token_ids + i * B;
+    const uint64_t key = block_key(s.last_key, toks, B);
+    auto it = pool->cached.find(key);
+    if (it == pool->cached.end() || !pool->matches(it->second, key, s.last_key, toks)) break;
+    const int32_t b = it->second;
+    if (pool->dev.refcount[b] == 0) pool->dev.remove(b);
+    ++pool->dev.refcount[b];
+    s.table.push_back(b);
+    s.length += B;
+    s.last_key = key;
+  }
+  *out_cached_tokens = static_cast<int32_t>(s.length);
+  return PKV_OK;
+}
+
+pkv_status pkv_pool_cached_blocks(const pkv_pool* pool, uint64_t* out_keys, int32_t* out_blocks, int32_t cap,
+                                  int32_t* out_n) {
+  if (!pool || !out_n) return PKV_ERR_INVALID_ARG;
+  const int64_t n = static_cast<int64_t>(pool->cached.size());
+  *out_n = static_cast<int32_t>(n);
+  if (cap < n || (n > 0 && (!out_keys || !out_blocks))) return PKV_ERR_INVALID_ARG;
+  std::vector<std::pair<uint64_t, int32_t>> all(pool->cached.begin(), pool->cached.end());
+  std::sort(all.begin(), all.end());
+  for (int64_t i = 0; i < n; ++i) {
+    out_keys[i] = all[i].first;
+    out_blocks[i] = all[i].second;
+  }
   return PKV_OK;
 }
 

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(libpkv):
     assert len(syms) >= 18
     missing = [s for s in syms if not hasattr(libpkv, s)]
     assert missing == []
-    assert pk.pkv_abi_version() == 5
+    assert pk.pkv_abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert libpkv.pkv_status_string(code) != b"unknown status"
     assert libpkv.pkv_status_string(-9) == b"unknown status"
@@ -32,6 +32,7 @@ def same_state(cpool: pk.Pool, opool: al.BlockPool):
     assert [cpool.host_refcount(b) for b in range(opool.host_blocks)] == opool.host_refcount
     st = cpool.stats()
     assert st == {**opool.stats()}
+    assert cpool.cached() == opool.cached
     for sid, s in opool.seqs.items():
         n, nb = cpool.info(sid)
         assert (n, nb) == (s.length, len(s.table))
@@ -255,7 +256,7 @@ def test_cow_capacity_error_reports_need(libpkv):
     slots = np.empty(2, np.int64)
     n = ctypes.c_int32()
     st = L.pkv_append_tokens(c.handle, seqs.ctypes.data_as(ctypes.c_void_p), counts.ctypes.data_as(ctypes.c_void_p),
-                             2, slots.ctypes.data_as(ctypes.c_void_p), 2, None, 0, ctypes.byref(n))
+                             2, None, slots.ctypes.data_as(ctypes.c_void_p), 2, None, 0, ctypes.byref(n))
     assert st == _lib.PKV_ERR_INVALID_ARG and n.value == 2
     c.validate()
 
@@ -296,3 +297,120 @@ def test_workspace_size_and_device_arg_checks(libpkv):
     assert L.pkv_copy_blocks(None, None, None, 0, 10, 4096, None) == _lib.PKV_OK
     assert L.pkv_copy_blocks(None, None, None, 2, 10, 4096, None) == _lib.PKV_ERR_INVALID_ARG
     assert L.pkv_copy_blocks(vp(16), vp(16), vp(16), 2, 10, 4100, None) == _lib.PKV_ERR_INVALID_ARG
+
+
+def test_prefix_cache_by_hand_matches_oracle(libpkv):
+    """The oracle's hand-traced prefix-cache scenario, replayed on both pools in lockstep."""
+    c, o = pk.Pool(8, 4), al.BlockPool(8, 4)
+
+    def both(fn):
+        a, b = fn(c), fn(o)
+        same_state(c, o)
+        return a, b
+
+    a, _ = both(lambda p: p.create())
+    (sc, _), (so, _) = both(lambda p: p.append([a], [10], token_ids=list(range(1, 11))))
+    assert np.array_equal(sc, so)
+    k0 = al.block_key(0, [1, 2, 3, 4])
+    assert c.cached() == {k0: 0, al.block_key(k0, [5, 6, 7, 8]): 1}  # FNV-1a chain in C equals the oracle's
+    (b, hc), (_, ho) = both(lambda p: p.create_prefixed([1, 2, 3, 4, 5, 6, 7, 8, 11, 12]))
+    assert hc == ho == 8
+    both(lambda p: p.append([b], [2], token_ids=[11, 12]))
+    (cc, hc), (_, ho) = both(lambda p: p.create_prefixed([1, 2, 3, 4, 5, 6, 7, 8]))
+    assert hc == ho == 4
+    both(lambda p: p.append([cc], [4], token_ids=[5, 6, 7, 8]))
+    both(lambda p: p.free_seq(a))
+    both(lambda p: p.free_seq(b))
+    (d, _), _ = both(lambda p: p.create_prefixed([1, 2, 3, 4, 5, 6, 7, 8, 9]))
+    e, _ = both(lambda p: p.create())
+    both(lambda p: p.append([e], [16]))
+    both(lambda p: p.free_seq(d))
+    f, _ = both(lambda p: p.create())
+    both(lambda p: p.append([f], [8]))
+    (_, hc), (_, ho) = both(lambda p: p.create_prefixed([1, 2, 3, 4, 5, 6, 7, 8, 9]))
+    assert hc == ho == 4
+    c.validate()
+
+
+def test_prefix_cache_random_operations_match_oracle(libpkv):
+    """Random prompts from a few shared stems, appends with and without ids, forks, frees and swaps: the C pool
+    and the oracle agree on every slot, copy pair, hit length, table, queue and key after every step."""
+    rng = np.random.default_rng(91)
+    hits = 0
+    for trial in range(25):
+        B = int(rng.choice([1, 2, 4, 16]))
+        nb, hb = int(rng.integers(8, 60)), int(rng.integers(0, 30))
+        order = rng.permutation(nb)
+        c, o = pk.Pool(nb, B, order, host_blocks=hb), al.BlockPool(nb, B, order, host_blocks=hb)
+        stems = [[int(x) for x in rng.integers(0, 3, size=int(rng.integers(1, 3 * B + 3)))] for _ in range(4)]
+        for _ in range(70):
+            op = int(rng.integers(0, 7))
+            dev = [s for s in o.seqs if not o.on_host(s)]
+            if op == 0 or not dev:
+                ids = stems[int(rng.integers(0, 4))] + [int(x) for x in rng.integers(0, 3, size=int(rng.integers(0, 6)))]
+                sc, hc = c.create_prefixed(ids)
+                so, ho = o.create_prefixed(ids)
+                assert (sc, hc) == (so, ho)
+                hits += hc // B
+                try:
+                    res_o = o.append([so], [len(ids) - ho], token_ids=ids[ho:])
+                except al.OutOfBlocks:
+                    with pytest.raises(pk.OutOfBlocks):
+                        c.append([sc], [len(ids) - hc], token_ids=ids[hc:])
+                    c.free_seq(sc)
+                    o.free_seq(so)
+                else:
+                    res_c = c.append([sc], [len(ids) - hc], token_ids=ids[hc:])
+                    assert all(np.array_equal(x, y) for x, y in zip(res_c, res_o))
+            elif op == 1:
+                sid = int(rng.choice(list(o.seqs)))
+                c.free_seq(sid)
+                o.free_seq(sid)
+            elif op in (2, 3):
+                k = int(rng.integers(1, len(dev) + 1))
+                seqs = [int(x) for x in rng.choice(dev, size=k, replace=False)]
+                counts = [int(x) for x in rng.integers(0, 2 * B + 2, size=k)]
+                ids = None if op == 3 and rng.random() < 0.4 else [int(x) for x in rng.integers(0, 3, size=sum(counts))]
+                try:
+                    res_o = o.append(seqs, counts, token_ids=ids)
+                except al.OutOfBlocks:
+                    with pytest.raises(pk.OutOfBlocks):
+                        c.append(seqs, counts, token_ids=ids)
+                else:
+                    res_c = c.append(seqs, counts, token_ids=ids)
+                    assert all(np.array_equal(x, y) for x, y in zip(res_c, res_o))
+            elif op == 4:
+                p = int(rng.choice(dev))
+                assert c.fork(p) == o.fork(p)
+            else:
+                sid = int(rng.choice(list(o.seqs)))
+                group = sharing_group(o, sid)
+                out = not o.on_host(sid)
+                try:
+                    po = o.swap_out(group) if out else o.swap_in(group)
+                except (al.OutOfBlocks, al.InvalidArg) as e:
+                    with pytest.raises({al.OutOfBlocks: pk.OutOfBlocks, al.InvalidArg: pk.InvalidArg}[type(e)]):
+                        c.swap_out(group) if out else c.swap_in(group)
+                else:
+                    pc = c.swap_out(group) if out else c.swap_in(group)
+                    assert np.array_equal(pc, po)
+            same_state(c, o)
+    assert hits > 100  # the stems make the cache hit often
+
+
+def test_prefix_cache_argument_errors(libpkv):
+    c = pk.Pool(8, 4)
+    with pytest.raises(pk.InvalidArg):
+        c.append([c.create()], [3], token_ids=[1, 2])  # one id per token
+    sid, hit = c.create_prefixed([])
+    assert hit == 0 and c.info(sid) == (0, 0)
+    n_seq, hit = ctypes.c_int32(), ctypes.c_int32()
+    assert libpkv.pkv_seq_create_prefixed(c.handle, None, 3, ctypes.byref(n_seq), ctypes.byref(hit)) == \
+        _lib.PKV_ERR_INVALID_ARG
+    assert libpkv.pkv_seq_create_prefixed(c.handle, None, -1, ctypes.byref(n_seq), ctypes.byref(hit)) == \
+        _lib.PKV_ERR_INVALID_ARG
+    n = ctypes.c_int32()
+    c.append([sid], [4], token_ids=[1, 2, 3, 4])
+    assert libpkv.pkv_pool_cached_blocks(c.handle, None, None, 0, ctypes.byref(n)) == _lib.PKV_ERR_INVALID_ARG
+    assert n.value == 1
+    c.validate()

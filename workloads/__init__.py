@@ -38,6 +38,10 @@ STREAM_KV = 4
 STREAM_TAIL_LENS = 5
 STREAM_TAIL_KV = 6
 STREAM_NEW_KV = 7  # the decode step's new token of each sequence
+STREAM_STEM = 8  # prefix-sharing requests: stem lengths and token ids
+STREAM_STEM_KV = 9  # K/V of a stem's tokens, per (stem, position)
+STREAM_REQ = 10  # a request's stem choice, tail length and tail token ids
+STREAM_REQ_KV = 11  # K/V of a request's own tail tokens
 
 # Bit patterns used to poison never-written cache slots.  A read that is not
 # masked turns the attention output into NaN.
@@ -348,3 +352,57 @@ def small_decode(num_seqs: int, lens_range: Tuple[int, int], num_q_heads: int, n
                 len_dist=None if lens is not None else ("uniform", lens_range[0], lens_range[1]),
                 pool_factor=pool_factor, num_blocks=num_blocks)
     return Workload(spec)
+
+
+@dataclass
+class PrefixRequests:
+    """Requests whose prompts start with one of a few shared stems (a system prompt, a few-shot header).
+
+    Request r's prompt is ``stems[stem_of[r]]`` followed by its own tail.  A
+    token's key and value depend on the run of tokens up to it, so every stem
+    token carries the same K/V in every request that shares the stem (drawn
+    per (stem, position)), and tail tokens carry the request's own.  Token ids
+    are small integers; K/V are N(0, 1) in the cache dtype.  Inputs only:
+    which blocks are shared is for each side's allocator to find.
+    """
+
+    seed: int
+    num_requests: int
+    num_stems: int
+    stem_range: Tuple[int, int]
+    tail_range: Tuple[int, int]
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    kv_dtype: str
+    vocab: int = 32000
+
+    def __post_init__(self):
+        rs = rng_for(self.seed, STREAM_STEM)
+        lo, hi = self.stem_range
+        self.stems = [[int(t) for t in rs.integers(0, self.vocab, size=int(rs.integers(lo, hi + 1)))]
+                      for _ in range(self.num_stems)]
+        self.stem_of, self.tails = [], []
+        for r in range(self.num_requests):
+            rr = rng_for(self.seed, STREAM_REQ, r)
+            self.stem_of.append(int(rr.integers(0, self.num_stems)))
+            n = int(rr.integers(self.tail_range[0], self.tail_range[1] + 1))
+            self.tails.append([int(t) for t in rr.integers(0, self.vocab, size=n)])
+
+    def prompt(self, r: int) -> List[int]:
+        return self.stems[self.stem_of[r]] + self.tails[r]
+
+    def kv(self, r: int) -> Tuple[np.ndarray, np.ndarray]:
+        """K and V ``[n][H_kv][d]`` (storage dtype) of every prompt token of request r."""
+        shape = (self.num_kv_heads, self.head_dim)
+        st = self.stem_of[r]
+        k = [draw_values(rng_for(self.seed, STREAM_STEM_KV, st, 0), (len(self.stems[st]),) + shape, self.kv_dtype),
+             draw_values(rng_for(self.seed, STREAM_REQ_KV, r, 0), (len(self.tails[r]),) + shape, self.kv_dtype)]
+        v = [draw_values(rng_for(self.seed, STREAM_STEM_KV, st, 1), (len(self.stems[st]),) + shape, self.kv_dtype),
+             draw_values(rng_for(self.seed, STREAM_REQ_KV, r, 1), (len(self.tails[r]),) + shape, self.kv_dtype)]
+        return np.concatenate(k), np.concatenate(v)
+
+    def q(self) -> np.ndarray:
+        """One query per request ``[R][H_q][d]`` (storage dtype)."""
+        return draw_values(rng_for(self.seed, STREAM_Q), (self.num_requests, self.num_q_heads, self.head_dim),
+                           self.kv_dtype)
