@@ -21,13 +21,15 @@ Sources (four web pages about the PagedAttention / vLLM paper):
 Modules:
   closed_forms  Eq. (1)-(3) of [P3]: KV bytes, allocated slots, tail waste,
                 slot utilisation.
-  allocator     block pool with a FIFO free queue, refcounts, fork, free and
-                copy-on-write appends.
+  allocator     block pool with a FIFO free queue, refcounts, fork, free,
+                copy-on-write appends, swapping to a host tier, prefix keys
+                and rollback by truncation.
   cache         the physical cache layout, scatter of token K/V into slots,
                 whole-block copies and the gather through a block table.
   attention     contiguous scaled dot-product attention in float64, the paged
-                variant (gather, then contiguous) and the split-context
-                log-sum-exp combination.
+                variant (gather, then contiguous), the split-context
+                log-sum-exp combination, and runs of causal queries per
+                sequence (prefill, speculative verification).
   run           replays a workload's allocator script with the pieces above.
 
 Every function here is pinned by CPU tests against values printed on the pages,

@@ -50,6 +50,14 @@ Readings where the pages are silent:
     loses it when it is popped for new use (eviction, oldest freed first) or
     moved to the host tier.  An append without token ids stops a sequence's
     key chain; blocks brought back from the host are not registered again.
+  * Rollback (speculative decoding stages KV positions and drops the ones its
+    verification rejects, [P3] section 5).  truncate(s, n') keeps the first n'
+    tokens: the table keeps ceil(n' / B) blocks and the rest are released in
+    logical order, as a free does.  A truncated sequence stops being keyed (the
+    ids of the tokens it keeps are not all held).  A block that becomes
+    partly filled keeps its bytes and any key until it is written again: an
+    append that writes in place into a keyed last block first drops its key,
+    and a shared one is copied on write as usual.
 
 This model applies each batch to a deep copy of the state and commits the copy
 only on success, which makes the all-or-nothing rule evident.
@@ -198,6 +206,8 @@ class BlockPool:
                 pairs.append((last, new))
                 self.refcount[last] -= 1
                 s.table[-1] = new
+            else:
+                self._forget(last)  # written in place: a key it kept from before a rollback no longer holds
         for p in range(s.length, s.length + count):
             if p % B == 0:
                 s.table.append(self._pop())
@@ -264,6 +274,24 @@ class BlockPool:
             k += c
         self.__dict__.update(trial.__dict__)
         return np.asarray(slots, dtype=np.int64), np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+
+    def truncate(self, sid: int, new_len: int) -> None:
+        """Keep the first ``new_len`` tokens of ``sid``; blocks past ceil(new_len / B) are released in logical order."""
+        s = self._on_device(sid)
+        new_len = int(new_len)
+        if new_len < 0 or new_len > s.length:
+            raise InvalidArg("new length outside [0, length]")
+        if new_len == s.length:
+            return
+        keep = -(-new_len // self.block_size)
+        for b in s.table[keep:]:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.free.append(b)
+        s.table = s.table[:keep]
+        s.length = new_len
+        s.tracked = False
+        s.partial = []
 
     # -- prefix caching ----------------------------------------------------------------
     def create_prefixed(self, token_ids: Sequence[int]) -> Tuple[int, int]:

@@ -16,6 +16,17 @@ computed in float64 from the exact stored bits, softmax taken in two passes
 with the maximum subtracted.  ``scale`` is the float32 value the library
 receives, widened to float64.
 
+``paged_attention_multi`` is the same definition for several queries per
+sequence, each at its own position: the last q_s positions of a sequence of n_s
+tokens (all of them already written to the cache) form a run of queries, and
+the query at position p sees tokens t <= p only.  A run of q_s = n_s is the
+prompt's own attention (the prefill that computes a whole prompt's KV in one
+pass, [P4] "Preemption", recomputation); a short run over a longer context is
+what speculative decoding verifies before it keeps or rolls back the staged
+positions, and what a prompt whose leading blocks came from the prefix cache
+computes for its remaining tokens ([P3] section 5: blockwise attention and
+paging compose; speculative decoding stages and rolls back KV positions).
+
 ``attention_split`` is the split-context form: each partition of P tokens
 yields (m_p, l_p, acc_p) = (max s, sum e^(s - m_p), sum e^(s - m_p) v) and the
 results combine as out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with
@@ -109,4 +120,36 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, blo
         k, v = _cache.gather(k_cache, v_cache, block_tables[s], n)
         out[s] = attention_contiguous(_cache.to_f64(q[s], kv_dtype), _cache.to_f64(k, kv_dtype),
                                       _cache.to_f64(v, kv_dtype), scale)
+    return out
+
+
+def paged_attention_multi(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_tables: np.ndarray,
+                          context_lens: Sequence[int], query_start: Sequence[int], scale: float,
+                          kv_dtype: str) -> np.ndarray:
+    """out[T][H_q][d] (float64) for runs of queries over paged K/V.
+
+    Sequence s owns query rows ``query_start[s] .. query_start[s+1] - 1``
+    (``q`` is ``[T][H_q][d]`` in the cache's storage dtype); they are its last
+    q_s positions n_s - q_s .. n_s - 1, and row i of the run (position
+    p = n_s - q_s + i) attends to tokens 0 .. p of the sequence, read through
+    its block table.  Written out as that definition: gather, then one
+    contiguous attention per query over its visible prefix.
+    """
+    T, Hq, d = q.shape
+    out = np.full((T, Hq, d), np.nan)
+    starts = [int(x) for x in query_start]
+    for s in range(len(starts) - 1):
+        n = int(context_lens[s])
+        qs = starts[s + 1] - starts[s]
+        if qs < 0 or qs > n:
+            raise ValueError("a run of queries longer than its context")
+        if qs == 0:
+            continue
+        k, v = _cache.gather(k_cache, v_cache, block_tables[s], n)
+        k = _cache.to_f64(k, kv_dtype)
+        v = _cache.to_f64(v, kv_dtype)
+        for i in range(qs):
+            p = n - qs + i
+            row = starts[s] + i
+            out[row] = attention_contiguous(_cache.to_f64(q[row], kv_dtype), k[:p + 1], v[:p + 1], scale)
     return out

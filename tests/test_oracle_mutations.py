@@ -18,6 +18,7 @@ from oracle import cache as oc
 import test_oracle_allocator as t_alloc
 import test_oracle_attention as t_attn
 import test_oracle_cache as t_cache
+import test_oracle_multi as t_multi
 
 _true_attention = oa.attention_contiguous
 
@@ -258,3 +259,71 @@ def test_prefix_key_without_the_preceding_run_is_caught(monkeypatch):
 def test_prefix_cache_that_never_evicts_is_caught(monkeypatch):
     monkeypatch.setattr(al.BlockPool, "_forget", lambda self, b: None)
     assert _fails_some([t_alloc.test_prefix_cache_by_hand])
+
+
+# -- runs of queries and rollback ---------------------------------------------------------------------
+
+MULTI_PINS = [t_multi.test_short_runs_are_the_last_rows_of_the_whole_prompt, t_multi.test_brute_force_scalar_loops,
+              t_multi.test_future_tokens_are_invisible,
+              lambda: t_multi.test_whole_prompt_runs_match_torch_causal_sdpa(8, 2, 32, 16)]
+
+
+def _multi_variant(shift):
+    """paged_attention_multi whose query at position p sees tokens up to p + shift."""
+    def multi(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, kv_dtype):
+        T, Hq, d = q.shape
+        out = np.full((T, Hq, d), np.nan)
+        for s in range(len(query_start) - 1):
+            n, qs = int(context_lens[s]), int(query_start[s + 1]) - int(query_start[s])
+            k, v = oc.gather(k_cache, v_cache, block_tables[s], n)
+            k, v = oc.to_f64(k, kv_dtype), oc.to_f64(v, kv_dtype)
+            for i in range(qs):
+                p = n - qs + i
+                hi = min(max(p + 1 + shift, 1), n)
+                out[int(query_start[s]) + i] = oa.attention_contiguous(oc.to_f64(q[int(query_start[s]) + i], kv_dtype),
+                                                                       k[:hi], v[:hi], scale)
+        return out
+    return multi
+
+
+@pytest.mark.parametrize("shift", [-1, 1])
+def test_causal_off_by_one_is_caught(monkeypatch, shift):
+    assert not _fails_some(MULTI_PINS)
+    monkeypatch.setattr(oa, "paged_attention_multi", _multi_variant(shift))
+    assert _fails_some(MULTI_PINS)
+
+
+def test_truncate_releasing_backwards_is_caught(monkeypatch):
+    def backwards(self, sid, new_len):
+        s = self._on_device(sid)
+        keep = -(-int(new_len) // self.block_size)
+        for b in reversed(s.table[keep:]):
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.free.append(b)
+        s.table = s.table[:keep]
+        s.length = int(new_len)
+        s.tracked = False
+        s.partial = []
+    monkeypatch.setattr(al.BlockPool, "truncate", backwards)
+    assert _fails_some([t_multi.test_truncate_by_hand])
+
+
+def test_in_place_write_keeping_a_stale_key_is_caught(monkeypatch):
+    def append_one(self, sid, count, slots, pairs):
+        B = self.block_size
+        s = self._get(sid)
+        if count == 0:
+            return
+        if s.length % B != 0 and self.refcount[s.table[-1]] > 1:
+            new = self._pop()
+            pairs.append((s.table[-1], new))
+            self.refcount[s.table[-1]] -= 1
+            s.table[-1] = new
+        for p in range(s.length, s.length + count):
+            if p % B == 0:
+                s.table.append(self._pop())
+            slots.append(s.table[p // B] * B + p % B)
+        s.length += count
+    monkeypatch.setattr(al.BlockPool, "_append_one", append_one)
+    assert _fails_some([t_multi.test_truncate_drops_keys_only_when_written_again])
