@@ -193,6 +193,17 @@ pkv_status pkv_seq_create_prefixed(pkv_pool* pool, const int32_t* token_ids, int
 pkv_status pkv_pool_cached_blocks(const pkv_pool* pool, uint64_t* out_keys, int32_t* out_blocks, int32_t cap,
                                   int32_t* out_n);
 
+/* Roll a sequence back to its first new_len tokens (speculative decoding
+ * stages KV positions and drops the ones verification rejects, [P3] section
+ * 5).  The table keeps ceil(new_len / B) blocks; the others are released in
+ * logical order as pkv_seq_free releases them.  The sequence stops being keyed
+ * for prefix caching.  A block left partly filled keeps its bytes (and any
+ * prefix key) until the next append writes into it: a shared one is copied on
+ * write, an unshared one is written in place and loses its key then.
+ * new_len == current length changes nothing.
+ * Errors: NO_SUCH_SEQ, SWAPPED, INVALID_ARG (new_len outside [0, length]). */
+pkv_status pkv_seq_truncate(pkv_pool* pool, int32_t seq, int32_t new_len);
+
 /* Dense block tables for seqs[0..n): host int32 out_tables[n][max_blocks],
  * row i = the physical blocks of seqs[i] in logical order, padded with -1;
  * out_context_lens[i] = its length in tokens ([P2] key technical point 1).
@@ -376,6 +387,39 @@ pkv_status pkv_decode_step(const void* k_new, const void* v_new, float* out, con
                            int32_t block_size, int32_t num_blocks, int32_t max_blocks, int32_t max_context_len,
                            float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                            int32_t kv_dtype, hipStream_t stream);
+
+/* Runs of causal queries over the paged cache ([P3] section 5: blockwise
+ * attention composes with paging, and speculative decoding stages KV positions
+ * that verification keeps or rolls back; [P4] "Preemption": a whole prompt's
+ * KV is computed in one parallel pass).  Sequence s owns query rows
+ * query_start[s] .. query_start[s+1] - 1, a run of q_s rows that are its last
+ * q_s positions; row i is at position p = n_s - q_s + i and, for query head h
+ * and g = h / (H_q / H_kv),
+ *   out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_s[t][g]) V_s[t][g].
+ * q_s = n_s is a prompt's own attention; a shorter run is the rest of a prompt
+ * whose leading blocks came from the prefix cache, or a set of speculated
+ * tokens under verification.  Every row's K/V (the run's own included) must
+ * already be in the cache (pkv_reshape_and_cache at the run's slots).
+ *   out: fp32 [num_query_rows][H_q][d]; q: [num_query_rows][H_q][d] in the
+ *     cache's scalar type.
+ *   query_start: device int32 [num_seqs + 1], non-decreasing.
+ *   block_tables, context_lens: as for pkv_paged_attention_decode.
+ *   max_query_len: a bound on every q_s (it sizes the launch).
+ * Rows of a run with q_s > n_s, q_s > max_query_len, n_s > max_context_len,
+ * n_s > max_blocks * B, or a block id outside [0, num_blocks) are NaN (for
+ * q_s > max_query_len, only its first max_query_len rows are written); a run
+ * with query_start[s] < 0 or query_start[s+1] > num_query_rows is not
+ * written.  Supported shapes and dtypes as for decode.  Arithmetic: fp32
+ * accumulation, products on the matrix cores; bf16 probabilities enter the
+ * value product as two bf16 terms.  Allocates nothing; needs no workspace.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     const int32_t* query_start, int32_t num_seqs, int32_t num_query_rows,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks, int32_t max_blocks,
+                                     int32_t max_context_len, int32_t max_query_len, float scale, int32_t kv_dtype,
+                                     hipStream_t stream);
 
 /* The two stages of pkv_paged_attention_decode, for callers that schedule or
  * time them separately.  Same arguments and errors; issue `partitions` then

@@ -25,7 +25,7 @@ from ._lib import (PKV_BF16, PKV_ERR_INVALID_ARG, PKV_F32, InvalidArg, NoSuchSeq
 
 __all__ = [
     "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_create", "pkv_seq_fork", "pkv_seq_free", "pkv_append_tokens",
-    "pkv_seq_create_prefixed", "pkv_pool_cached_blocks",
+    "pkv_seq_create_prefixed", "pkv_pool_cached_blocks", "pkv_seq_truncate", "pkv_paged_attention_multi",
     "pkv_block_tables", "pkv_seq_info", "pkv_pool_stats", "pkv_block_refcount", "pkv_pool_free_list",
     "pkv_pool_validate", "pkv_pool_set_host_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_seq_table",
     "pkv_host_block_refcount", "pkv_pool_host_free_list", "pkv_swap_blocks", "empty_host_caches", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_attention_workspace_bytes",
@@ -100,6 +100,10 @@ def pkv_append_tokens(pool, seqs: Sequence[int], counts: Sequence[int],
     check(lib().pkv_append_tokens(pool, _ptr(seqs), _ptr(counts), len(seqs), ids_ptr, _ptr(slots), slots.size,
                                   _ptr(pairs), pairs.shape[0], ctypes.byref(n_cow)), "pkv_append_tokens")
     return slots, pairs[:n_cow.value].copy()
+
+
+def pkv_seq_truncate(pool, seq: int, new_len: int) -> None:
+    check(lib().pkv_seq_truncate(pool, seq, new_len), "pkv_seq_truncate")
 
 
 def pkv_seq_create_prefixed(pool, token_ids: Sequence[int]) -> Tuple[int, int]:
@@ -243,6 +247,12 @@ class Pool:
 
     def append(self, seqs, counts, token_ids=None):
         return pkv_append_tokens(self.handle, seqs, counts, token_ids)
+
+    def truncate(self, seq: int, new_len: int) -> None:
+        pkv_seq_truncate(self.handle, seq, new_len)
+
+    def length(self, seq: int) -> int:
+        return self.info(seq)[0]
 
     def create_prefixed(self, token_ids):
         return pkv_seq_create_prefixed(self.handle, token_ids)
@@ -474,6 +484,36 @@ def pkv_decode_step(k_new, v_new, out, q, k_cache, v_cache, block_tables, contex
     sequence) into the caches through the block tables, then pkv_paged_attention_decode (same arguments)."""
     _attention("pkv_decode_step", out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                partition_size, workspace, stream, new_kv=(k_new, v_new))
+
+
+def pkv_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                              max_context_len: int, max_query_len: int, scale: float, stream=None) -> None:
+    """Runs of causal queries: out fp32 [T][H_q][d]; q [T][H_q][d] (cache dtype); query_start int32 [S+1]
+    (rows of sequence s: its last query_start[s+1] - query_start[s] positions); block_tables int32
+    [S][max_blocks]; context_lens int32 [S]."""
+    torch = _torch()
+    fn = "pkv_paged_attention_multi"
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != torch.float32:
+        raise InvalidArg(-1, fn, "out and q must be [T][H_q][d], out fp32")
+    T, Hq, d = q.shape
+    nb, Hkv, d2, B = v_cache.shape
+    if d2 != d or q.dtype != k_cache.dtype or q.dtype != v_cache.dtype:
+        raise InvalidArg(-1, fn, "q and caches disagree in d or dtype")
+    ks, vs = cache_shapes(nb, Hkv, B, d, _dtype_name(q))
+    if tuple(k_cache.shape) != ks:
+        raise InvalidArg(-1, fn, "key cache shape")
+    S = context_lens.numel()
+    for t, name, shape in ((block_tables, "block_tables", None), (context_lens, "context_lens", (S,)),
+                           (query_start, "query_start", (S + 1,))):
+        if t.dtype != torch.int32 or (shape is not None and tuple(t.shape) != shape):
+            raise InvalidArg(-1, fn, f"{name} must be int32" + (f" of shape {shape}" if shape else ""))
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise InvalidArg(-1, fn, "block_tables must be [S][max_blocks]")
+    check(lib().pkv_paged_attention_multi(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                          _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                                          _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), S, T,
+                                          Hq, Hkv, d, B, nb, block_tables.shape[1], max_context_len, max_query_len,
+                                          scale, _dtype_code(q), _stream(stream)), fn)
 
 
 def pkv_paged_attention_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,

@@ -72,6 +72,7 @@ _SIGS = {
     "pkv_seq_free": (i32, [vp, i32]),
     "pkv_append_tokens": (i32, [vp, vp, vp, i32, vp, vp, i64, vp, i32, P_i32]),
     "pkv_seq_create_prefixed": (i32, [vp, vp, i32, P_i32, P_i32]),
+    "pkv_seq_truncate": (i32, [vp, i32, i32]),
     "pkv_pool_cached_blocks": (i32, [vp, vp, vp, i32, P_i32]),
     "pkv_block_tables": (i32, [vp, vp, i32, i32, vp, vp]),
     "pkv_seq_info": (i32, [vp, i32, P_i32, P_i32]),
@@ -94,6 +95,8 @@ _SIGS = {
     "pkv_paged_attention_partitions": (i32, _ATTN),
     "pkv_paged_attention_reduce": (i32, _ATTN),
     "pkv_decode_step": (i32, [vp, vp] + _ATTN),
+    "pkv_paged_attention_multi": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                        i32, f32, i32, vp]),
 }
 
 _lib = None

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
-SOURCES = [os.path.join(CSRC, "pool.cpp"), os.path.join(CSRC, "cache_ops.hip"), os.path.join(CSRC, "attention.hip")]
+SOURCES = [os.path.join(CSRC, "pool.cpp"), os.path.join(CSRC, "cache_ops.hip"), os.path.join(CSRC, "attention.hip"),
+           os.path.join(CSRC, "multi_query.hip")]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

@@ -189,7 +189,7 @@ const char* pkv_status_string(pkv_status s) {
   }
 }
 
-int32_t pkv_abi_version(void) { return 6; }
+int32_t pkv_abi_version(void) { return 7; }
 
 pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
                            pkv_pool** out) {
@@ -344,6 +344,8 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
         ++npairs;
         --pool->dev.refcount[last];
         s.table.back() = fresh;
+      } else {
+        pool->forget(last);  // written in place: a key kept from before a rollback no longer holds
       }
     }
     for (int64_t p = L; p < L + c; ++p) {
@@ -368,6 +370,25 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
     t += c;
   }
   *out_n_cow = npairs;
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_truncate(pkv_pool* pool, int32_t seq, int32_t new_len) {
+  if (!pool) return PKV_ERR_INVALID_ARG;
+  Seq* s = pool->get(seq);
+  if (!s) return PKV_ERR_NO_SUCH_SEQ;
+  if (s->on_host) return PKV_ERR_SWAPPED;
+  if (new_len < 0 || new_len > s->length) return PKV_ERR_INVALID_ARG;
+  if (new_len == s->length) return PKV_OK;
+  const size_t keep = static_cast<size_t>(ceil_div(new_len, pool->block_size));
+  for (size_t i = keep; i < s->table.size(); ++i) {
+    const int32_t b = s->table[i];
+    if (--pool->dev.refcount[b] == 0) pool->dev.push(b);
+  }
+  s->table.resize(keep);
+  s->length = new_len;
+  s->tracked = false;
+  s->partial.clear();
   return PKV_OK;
 }
 

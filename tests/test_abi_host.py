@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(libpkv):
     assert len(syms) >= 18
     missing = [s for s in syms if not hasattr(libpkv, s)]
     assert missing == []
-    assert pk.pkv_abi_version() == 6
+    assert pk.pkv_abi_version() == 7
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert libpkv.pkv_status_string(code) != b"unknown status"
     assert libpkv.pkv_status_string(-9) == b"unknown status"
@@ -414,3 +414,90 @@ def test_prefix_cache_argument_errors(libpkv):
     assert libpkv.pkv_pool_cached_blocks(c.handle, None, None, 0, ctypes.byref(n)) == _lib.PKV_ERR_INVALID_ARG
     assert n.value == 1
     c.validate()
+
+
+def test_truncate_matches_oracle(libpkv):
+    """The oracle's hand-traced rollbacks and random operations with truncation, on both pools in lockstep."""
+    for B, script in ((4, "hand"), (4, "keys")):
+        c, o = pk.Pool(8 if script == "hand" else 6, B), al.BlockPool(8 if script == "hand" else 6, B)
+        if script == "hand":
+            a = c.create(); o.create()
+            c.append([a], [10]); o.append([a], [10])
+            b = c.fork(a); o.fork(a)
+            c.truncate(b, 5); o.truncate(b, 5)
+            same_state(c, o)
+            (sc, pc), (so, po) = c.append([b], [1]), o.append([b], [1])
+            assert np.array_equal(sc, so) and np.array_equal(pc, po) and pc.tolist() == [[1, 3]]
+            c.truncate(a, 0); o.truncate(a, 0)
+            same_state(c, o)
+            c.truncate(b, 4); o.truncate(b, 4)
+            for bad in (5, -1):
+                with pytest.raises(pk.InvalidArg):
+                    c.truncate(b, bad)
+        else:
+            a = c.create(); o.create()
+            ids = [1, 2, 3, 4, 5, 6, 7, 8]
+            c.append([a], [8], token_ids=ids); o.append([a], [8], token_ids=ids)
+            c.truncate(a, 6); o.truncate(a, 6)
+            assert c.create_prefixed(ids + [9]) == o.create_prefixed(ids + [9])
+            c.append([a], [1]); o.append([a], [1])
+            x = c.create(); o.create()
+            c.append([x], [8], token_ids=[9, 9, 9, 9, 8, 8, 8, 8]); o.append([x], [8], token_ids=[9, 9, 9, 9, 8, 8, 8, 8])
+            c.truncate(x, 5); o.truncate(x, 5)
+            c.append([x], [1]); o.append([x], [1])
+            c.append([x], [2], token_ids=[8, 8]); o.append([x], [2], token_ids=[8, 8])
+        same_state(c, o)
+        c.validate()
+    rng = np.random.default_rng(33)
+    for trial in range(20):
+        B = int(rng.choice([1, 2, 4, 16]))
+        nb, hb = int(rng.integers(8, 50)), int(rng.integers(0, 20))
+        order = rng.permutation(nb)
+        c, o = pk.Pool(nb, B, order, host_blocks=hb), al.BlockPool(nb, B, order, host_blocks=hb)
+        stem = [int(x) for x in rng.integers(0, 2, size=2 * B + 1)]
+        for _ in range(80):
+            op = int(rng.integers(0, 7))
+            dev = [s for s in o.seqs if not o.on_host(s)]
+            if op == 0 or not dev:
+                ids = stem + [int(x) for x in rng.integers(0, 2, size=int(rng.integers(0, 4)))]
+                assert c.create_prefixed(ids) == o.create_prefixed(ids)
+            elif op == 1:
+                sid = int(rng.choice(dev))
+                n = int(rng.integers(1, 2 * B + 2))
+                ids = [int(x) for x in rng.integers(0, 2, size=n)] if rng.random() < 0.8 else None
+                try:
+                    res_o = o.append([sid], [n], token_ids=ids)
+                except al.OutOfBlocks:
+                    with pytest.raises(pk.OutOfBlocks):
+                        c.append([sid], [n], token_ids=ids)
+                else:
+                    res_c = c.append([sid], [n], token_ids=ids)
+                    assert all(np.array_equal(x, y) for x, y in zip(res_c, res_o))
+            elif op == 2:
+                p = int(rng.choice(dev))
+                assert c.fork(p) == o.fork(p)
+            elif op in (3, 4):
+                sid = int(rng.choice(list(o.seqs)))
+                if o.on_host(sid):
+                    with pytest.raises(pk.WrongTier):
+                        c.truncate(sid, 0)
+                    continue
+                n = int(rng.integers(0, o.length(sid) + 1))
+                c.truncate(sid, n)
+                o.truncate(sid, n)
+            elif op == 5:
+                sid = int(rng.choice(list(o.seqs)))
+                c.free_seq(sid)
+                o.free_seq(sid)
+            else:
+                sid = int(rng.choice(list(o.seqs)))
+                group = sharing_group(o, sid)
+                out = not o.on_host(sid)
+                try:
+                    po = o.swap_out(group) if out else o.swap_in(group)
+                except (al.OutOfBlocks, al.InvalidArg) as e:
+                    with pytest.raises({al.OutOfBlocks: pk.OutOfBlocks, al.InvalidArg: pk.InvalidArg}[type(e)]):
+                        c.swap_out(group) if out else c.swap_in(group)
+                else:
+                    assert np.array_equal(c.swap_out(group) if out else c.swap_in(group), po)
+            same_state(c, o)

@@ -1,0 +1,272 @@
+"""GPU parity of runs of causal queries (pkv_paged_attention_multi) against the
+float64 oracle, through the C-ABI: whole prompts, short runs over long
+contexts, the uncached rest of prefix-cached prompts, and speculative
+verification followed by a rollback (pkv_seq_truncate) and a decode step.
+
+Bars as for decode: fp32 max abs <= 1e-5; bf16 max abs <= 1e-2 and relative
+L2 <= 2e-3; every case also relative L2 <= 1e-4."""
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import allocator as al
+from oracle import attention as oa
+from oracle import cache as oc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(libpkv):
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU is required for the gpu-marked tests")
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(a, dt):
+    a = np.ascontiguousarray(a)
+    if dt == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def check_close(out, ref, dt, what):
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(out - ref)))
+    rl2 = float(np.linalg.norm(out - ref) / np.linalg.norm(ref))
+    say(f"  {what}: max_abs={err:.3e} rel_l2={rl2:.3e}")
+    if dt == "f32":
+        assert err <= 1e-5, (what, err)
+    else:
+        assert err <= 1e-2 and rl2 <= 2e-3, (what, err, rl2)
+    assert rl2 <= 1e-4, (what, rl2)
+
+
+class Batch:
+    """Sequences of given lengths written through the C pool (GPU caches) and the oracle pool (host caches)."""
+
+    def __init__(self, lens, Hq, Hkv, d, B, dt, seed, spare=8):
+        import paged_kv_cache_physical_amd as pk
+        self.pk, self.lens, self.Hq, self.Hkv, self.d, self.B, self.dt = pk, list(lens), Hq, Hkv, d, B, dt
+        self.seed = seed
+        nb = sum(-(-n // B) for n in lens) + spare
+        order = wl.rng_for(seed, wl.STREAM_PERM).permutation(nb).astype(np.int32)
+        self.nb = nb
+        self.pool, self.opool = pk.Pool(nb, B, order), al.BlockPool(nb, B, order)
+        self.caches = pk.empty_caches(nb, Hkv, B, d, dt)
+        self.ocaches = oc.empty_caches(nb, Hkv, B, d, dt)
+        self.ids = [self.pool.create() for _ in lens]
+        assert self.ids == [self.opool.create() for _ in lens]
+        self.k = [wl.draw_values(wl.rng_for(seed, wl.STREAM_KV, i, 0), (n, Hkv, d), dt) for i, n in enumerate(lens)]
+        self.v = [wl.draw_values(wl.rng_for(seed, wl.STREAM_KV, i, 1), (n, Hkv, d), dt) for i, n in enumerate(lens)]
+        self.write(list(range(len(lens))), [0] * len(lens), list(lens))
+
+    def write(self, which, starts, counts):
+        """Append counts[j] tokens to sequence which[j] (positions starts[j]...) and write their K/V on both sides."""
+        seqs = [self.ids[i] for i in which]
+        slots, pairs = self.pool.append(seqs, counts)
+        oslots, opairs = self.opool.append(seqs, counts)
+        assert np.array_equal(slots, oslots) and np.array_equal(pairs, opairs)
+        if len(pairs):
+            self.pk.pkv_copy_blocks(*self.caches, torch.from_numpy(pairs).cuda())
+            oc.copy_blocks(*self.ocaches, opairs)
+        k = np.concatenate([self.k[i][s:s + c] for i, s, c in zip(which, starts, counts)])
+        v = np.concatenate([self.v[i][s:s + c] for i, s, c in zip(which, starts, counts)])
+        self.pk.pkv_reshape_and_cache(to_dev(k, self.dt), to_dev(v, self.dt), *self.caches,
+                                      torch.from_numpy(slots).cuda(), self.B)
+        oc.scatter(*self.ocaches, k, v, oslots)
+
+    def tables(self):
+        mb = max(1, max(-(-self.pool.length(i) // self.B) for i in self.ids))
+        t, l = self.pool.block_tables(self.ids, mb)
+        ot, ol = self.opool.block_tables(self.ids, mb)
+        assert np.array_equal(t, ot) and np.array_equal(l, ol)
+        return t, l
+
+    def multi(self, runs, q, tables=None, lens=None, query_start=None, max_query_len=None, out=None):
+        t, l = self.tables() if tables is None else (tables, lens)
+        starts = np.concatenate([[0], np.cumsum(runs)]).astype(np.int32) if query_start is None else query_start
+        T = q.shape[0]
+        out = torch.full((T, self.Hq, self.d), float("nan"), dtype=torch.float32, device="cuda") if out is None else out
+        self.pk.pkv_paged_attention_multi(out, to_dev(q, self.dt), *self.caches, torch.from_numpy(t).cuda(),
+                                          torch.from_numpy(l).cuda(), torch.from_numpy(starts).cuda(),
+                                          int(max(l.max(), 1)), int(max(runs) if max_query_len is None else max_query_len),
+                                          1.0 / np.sqrt(self.d))
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), t, l, starts
+
+    def oracle(self, q, t, l, starts):
+        return oa.paged_attention_multi(q, *self.ocaches, t, l, starts, np.float32(1.0 / np.sqrt(self.d)), self.dt)
+
+
+GRID = [(dt, d, G, B) for dt in ("f32", "bf16") for d in (64, 128) for G in (1, 2, 4, 8) for B in (16, 32)]
+
+
+@pytest.mark.parametrize("dt,d,G,B", GRID)
+def test_runs_grid(dt, d, G, B):
+    rng = wl.rng_for(G * 100 + d + B, 99)
+    lens = [int(x) for x in rng.integers(1, 300, size=6)] + [1, 17]
+    runs = [n if i % 3 == 0 else int(rng.integers(1, min(n, 40) + 1)) for i, n in enumerate(lens)]
+    runs[-1] = 17  # a whole 17-token prompt
+    Hkv = 2
+    say(f"case {dt} d={d} G={G} B={B}: lens={lens} runs={runs}")
+    b = Batch(lens, G * Hkv, Hkv, d, B, dt, seed=G + d + B)
+    q = wl.draw_values(wl.rng_for(5, wl.STREAM_Q, G, d), (sum(runs), G * Hkv, d), dt)
+    out, t, l, starts = b.multi(runs, q)
+    check_close(out, b.oracle(q, t, l, starts), dt, "runs")
+
+
+@pytest.mark.parametrize("dt,B", [("bf16", 16), ("f32", 32)])
+def test_whole_prompts_long(dt, B):
+    """Prompt attention over 1000-2000 tokens: many chunks and many row tiles per (sequence, KV head)."""
+    lens = [1500, 2048, 1001]
+    b = Batch(lens, 32, 8, 128, B, dt, seed=21)
+    q = wl.draw_values(wl.rng_for(6, wl.STREAM_Q), (sum(lens), 32, 128), dt)
+    out, t, l, starts = b.multi(lens, q)
+    check_close(out, b.oracle(q, t, l, starts), dt, "whole prompts")
+
+
+@pytest.mark.parametrize("dt,B", [("bf16", 16), ("bf16", 32), ("f32", 16)])
+def test_prefix_cached_prompts_compute_only_their_tails(dt, B):
+    """Requests that share stems take their leading blocks from the prefix cache; the multi-query call over just
+    the uncached tokens gives the rows of each whole prompt's causal attention."""
+    import paged_kv_cache_physical_amd as pk
+    R, Hq, Hkv, d = 16, 32, 8, 128
+    pr = wl.PrefixRequests(seed=40 + B, num_requests=R, num_stems=3, stem_range=(100, 700), tail_range=(1, 120),
+                           num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, kv_dtype=dt)
+    lens = [len(pr.prompt(r)) for r in range(R)]
+    nb = sum(-(-n // B) for n in lens) + 16
+    order = wl.rng_for(8, wl.STREAM_PERM).permutation(nb).astype(np.int32)
+    pool = pk.Pool(nb, B, order)
+    caches = pk.empty_caches(nb, Hkv, B, d, dt)
+    ids, runs = [], []
+    for r in range(R):
+        ids_r = pr.prompt(r)
+        sid, hit = pool.create_prefixed(ids_r)
+        slots, pairs = pool.append([sid], [len(ids_r) - hit], token_ids=ids_r[hit:])
+        assert pairs.shape == (0, 2)
+        k, v = pr.kv(r)
+        pk.pkv_reshape_and_cache(to_dev(k[hit:], dt), to_dev(v[hit:], dt), *caches, torch.from_numpy(slots).cuda(), B)
+        ids.append(sid)
+        runs.append(len(ids_r) - hit)
+    assert sum(runs) < sum(lens) // 2, (sum(runs), sum(lens))
+    mb = max(-(-n // B) for n in lens)
+    t, l = pool.block_tables(ids, mb)
+    # one query per prompt position; the call gets only the uncached positions' rows
+    qfull = [wl.draw_values(wl.rng_for(9, wl.STREAM_Q, r), (lens[r], Hq, d), dt) for r in range(R)]
+    q = np.concatenate([qf[n - k:] for qf, n, k in zip(qfull, lens, runs)])
+    starts = np.concatenate([[0], np.cumsum(runs)]).astype(np.int32)
+    out = torch.full((q.shape[0], Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    pk.pkv_paged_attention_multi(out, to_dev(q, dt), *caches, torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(),
+                                 torch.from_numpy(starts).cuda(), int(l.max()), max(runs), 1.0 / np.sqrt(d))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    scale = np.float32(1.0 / np.sqrt(d))
+    ref = []
+    for r in range(R):  # each prompt's own contiguous K/V, never read through a cache
+        k, v = (oc.to_f64(x, dt) for x in pr.kv(r))
+        qq = oc.to_f64(qfull[r], dt)
+        for p in range(lens[r] - runs[r], lens[r]):
+            ref.append(oa.attention_contiguous(qq[p], k[:p + 1], v[:p + 1], scale))
+    check_close(out, np.stack(ref), dt, "prefix-cached tails")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_speculative_verify_rollback_decode(dt):
+    """Stage k drafted tokens, verify them with one multi-query call, keep a prefix, roll back the rest, write the
+    corrected token and decode: every step against the oracle, and the pool against the oracle pool."""
+    import paged_kv_cache_physical_amd as pk
+    B, Hq, Hkv, d, kdraft = 16, 32, 8, 128, 5
+    rng = wl.rng_for(77, 1)
+    base = [int(x) for x in rng.integers(20, 600, size=12)]
+    total = [n + kdraft for n in base]
+    b = Batch(total, Hq, Hkv, d, B, dt, seed=13, spare=32)
+    # the batch holds base + drafted tokens already; the drafts are the last kdraft positions
+    runs = [kdraft] * len(base)
+    q = wl.draw_values(wl.rng_for(14, wl.STREAM_Q), (sum(runs), Hq, d), dt)
+    out, t, l, starts = b.multi(runs, q)
+    check_close(out, b.oracle(q, t, l, starts), dt, "verify")
+    # keep a different number of drafts per sequence, drop the rest
+    keep = [int(x) for x in rng.integers(0, kdraft + 1, size=len(base))]
+    for i, (n, kk) in enumerate(zip(base, keep)):
+        b.pool.truncate(b.ids[i], n + kk)
+        b.opool.truncate(b.ids[i], n + kk)
+    b.pool.validate()
+    assert b.pool.free_list().tolist() == b.opool.free_list()
+    # the corrected token: new K/V at position n + keep
+    for i, (n, kk) in enumerate(zip(base, keep)):
+        b.k[i] = np.concatenate([b.k[i][:n + kk], wl.draw_values(wl.rng_for(15, i, 0), (1, Hkv, d), dt)])
+        b.v[i] = np.concatenate([b.v[i][:n + kk], wl.draw_values(wl.rng_for(15, i, 1), (1, Hkv, d), dt)])
+    b.write(list(range(len(base))), [n + kk for n, kk in zip(base, keep)], [1] * len(base))
+    t, l = b.tables()
+    assert l.tolist() == [n + kk + 1 for n, kk in zip(base, keep)]
+    qd = wl.draw_values(wl.rng_for(16, wl.STREAM_Q), (len(base), Hq, d), dt)
+    out, *_ = b.multi([1] * len(base), qd, tables=t, lens=l)
+    ref = oa.paged_attention(qd, *b.ocaches, t, l, np.float32(1.0 / np.sqrt(d)), dt)
+    check_close(out, ref, dt, "decode after rollback")
+    # the decode kernel agrees with the one-query runs
+    od = torch.empty((len(base), Hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(pk.pkv_attention_workspace_bytes(len(base), Hq, d, B, int(l.max()), 0), 1),
+                     dtype=torch.uint8, device="cuda")
+    pk.pkv_paged_attention_decode(od, to_dev(qd, dt), *b.caches, torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(),
+                                  int(l.max()), 1.0 / np.sqrt(d), 0, ws)
+    torch.cuda.synchronize()
+    check_close(od.cpu().numpy(), ref, dt, "decode kernel")
+
+
+def test_edge_cases():
+    """Empty runs, runs that cannot be computed (NaN rows), runs outside the rows (untouched), bad block ids."""
+    b = Batch([40, 33, 20, 64, 9], 8, 2, 64, 16, "f32", seed=3)
+    t, l = b.tables()
+    # sequence 1: empty run; sequence 2: a run longer than its context (NaN); sequence 4: longer than max_query_len
+    runs = [3, 0, 21, 2, 9]
+    T = sum(runs)
+    q = wl.draw_values(wl.rng_for(4, wl.STREAM_Q), (T, 8, 64), "f32")
+    starts = np.concatenate([[0], np.cumsum(runs)]).astype(np.int32)
+    sentinel = torch.full((T, 8, 64), 7.0, dtype=torch.float32, device="cuda")
+    out, *_ = b.multi(runs, q, tables=t, lens=l, query_start=starts, max_query_len=8, out=sentinel)
+    ref = b.oracle(q[:3], t[:1], l[:1], starts[:2])
+    check_close(out[:3], ref, "f32", "sequence 0")
+    assert np.all(np.isnan(out[3:3 + 8]))  # q_s > max_query_len and > n_s: the covered rows say so
+    assert np.all(out[3 + 8:24] == 7.0)  # rows past max_query_len are not written
+    ref3 = b.oracle(q[24:26], t[3:4], l[3:4], np.array([0, 2], np.int32))
+    check_close(out[24:26], ref3, "f32", "sequence 3")
+    assert np.all(np.isnan(out[26:26 + 8])) and np.all(out[26 + 8:] == 7.0)
+    # a bad block id poisons only its sequence; a run outside [0, T) is left alone
+    t2 = t.copy()
+    t2[3, 1] = b.nb + 5
+    starts2 = np.array([0, 3, 3, 3, 5, T + 4], np.int32)
+    runs2 = [3, 0, 0, 2, 1]
+    sentinel.fill_(7.0)
+    out, *_ = b.multi(runs2, q, tables=t2, lens=l, query_start=starts2, out=sentinel)
+    check_close(out[:3], ref, "f32", "sequence 0 again")
+    assert np.all(np.isnan(out[3:5])) and np.all(out[5:] == 7.0)
+    # an empty call does nothing
+    b.pk.pkv_paged_attention_multi(sentinel[:0], to_dev(q[:0], "f32"), *b.caches, torch.from_numpy(t).cuda(),
+                                   torch.from_numpy(l).cuda(), torch.zeros(6, dtype=torch.int32, device="cuda"),
+                                   64, 0, 0.125)
+    torch.cuda.synchronize()
+
+
+def test_full_size_verification_sampled():
+    """Speculative verification at the Llama-7B decode shape (64 sequences, 32 heads, d 128, bf16, lengths
+    uniform in [128, 2048]) with 4 drafted tokens per sequence; sampled sequences against the oracle."""
+    w = wl.named("llama7b_bf16", seed=0)
+    s = w.spec
+    runs = [4] * w.num_seqs
+    lens = [int(n) for n in w.context_lens]
+    b = Batch(lens, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, s.kv_dtype, seed=0, spare=64)
+    q = wl.draw_values(wl.rng_for(17, wl.STREAM_Q), (sum(runs), s.num_q_heads, s.head_dim), s.kv_dtype)
+    out, t, l, starts = b.multi(runs, q)
+    pick = [0, 9, 31, 63]
+    for i in pick:
+        ref = b.oracle(q[starts[i]:starts[i + 1]], t[i:i + 1], l[i:i + 1], np.array([0, 4], np.int32))
+        check_close(out[starts[i]:starts[i + 1]], ref, s.kv_dtype, f"sequence {i}")
