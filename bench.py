@@ -231,6 +231,7 @@ def cpu_baseline(w, budget_s=12.0):
                       f"{elapsed:.1f}s"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 HOST_LINK_PEAK_GBPS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes, 128b/130b coding
 
 
@@ -287,6 +288,72 @@ def measure_swap(stream, block_tokens=(1, 4, 16, 32), per_cache=256 << 20):
         del dk, dv, hk, hv, po, pi
         torch.cuda.empty_cache()
     return {"shape": "H_kv 32, d 128, bf16, both caches", "host_link_peak_gbps": HOST_LINK_PEAK_GBPS, **out}
+
+
+# Runs of causal queries (pkv_paged_attention_multi).  Each case: name -> (sequences, H_q, H_kv, context lengths
+# (lo, hi) uniform, or a constant, run length per sequence (an int, or "all" for the whole prompt)).
+MULTI_CASES = {
+    "verify4_llama7b_bf16": (64, 32, 32, (128, 2048), 4),
+    "verify4_gqa_bf16": (256, 64, 8, (128, 2048), 4),
+    "prefill2048_gqa_bf16": (16, 32, 8, 2048, "all"),
+    "prefix_tail256_gqa_bf16": (64, 32, 8, 1280, 256),
+}
+
+
+def measure_multi(stream, reps=20, case=None):
+    """pkv_paged_attention_multi on synthetic batches (bf16 caches, d 128, B 16, shuffled pool, every valid slot
+    N(0, 1)).  Verification runs are reported as KV GB/s (each sequence's K/V bytes counted once) against HBM
+    peak; prompt runs as matrix-core TFLOP/s (4 d flop per visible (query head, token) pair: QK and PV) against
+    the dense bf16 peak."""
+    import torch
+    import paged_kv_cache_physical_amd as pk
+    d, B = 128, 16
+    out = {}
+    for name, (S, Hq, Hkv, lens_spec, run) in MULTI_CASES.items():
+        if case is not None and name != case:
+            continue
+        rng = np.random.default_rng(1)
+        lens = (rng.integers(lens_spec[0], lens_spec[1], size=S, endpoint=True) if isinstance(lens_spec, tuple)
+                else np.full(S, lens_spec)).astype(np.int64)
+        runs = lens.copy() if run == "all" else np.full(S, run, dtype=np.int64)
+        nb = int(sum(-(-int(n) // B) for n in lens))
+        pool = pk.Pool(nb, B, rng.permutation(nb).astype(np.int32))
+        ids = [pool.create() for _ in range(S)]
+        pool.append(ids, lens.tolist())
+        tables, clens = pool.block_tables(ids, int(max(-(-int(n) // B) for n in lens)))
+        kc, vc = pk.empty_caches(nb, Hkv, B, d, "bf16", poison=False)
+        kc.normal_()
+        vc.normal_()
+        T = int(runs.sum())
+        q = torch.randn((T, Hq, d), device="cuda").to(torch.bfloat16)
+        o = torch.empty((T, Hq, d), dtype=torch.float32, device="cuda")
+        starts = torch.from_numpy(np.concatenate([[0], np.cumsum(runs)]).astype(np.int32)).cuda()
+        bt, cl = torch.from_numpy(tables).cuda(), torch.from_numpy(clens).cuda()
+        fn = lambda: pk.pkv_paged_attention_multi(o, q, kc, vc, bt, cl, starts, int(lens.max()), int(runs.max()),
+                                                  1.0 / np.sqrt(d), stream)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            t = time_launches(fn, reps, stream)
+        us = 1e3 * t[0]
+        visible = int(sum(int(r) * int(n) - int(r) * (int(r) - 1) // 2 for n, r in zip(lens, runs)))
+        flops = 4 * d * Hq * visible
+        kv_bytes = int(lens.sum()) * 2 * Hkv * d * 2
+        rec = {"sequences": S, "H_q": Hq, "H_kv": Hkv, "context_tokens": int(lens.sum()), "query_rows": T,
+               "launch_us": round(us, 2), "launch_us_median": round(1e3 * t[1], 2),
+               "kv_bytes": kv_bytes, "kv_gbps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+               "flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
+        if run == "all" or run > 16:
+            rec["roofline"] = {"bound": "mfma", "achieved": rec["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(rec["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
+        else:
+            rec["roofline"] = {"bound": "hbm", "achieved": rec["kv_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                               "frac": round(rec["kv_gbps"] / HBM_PEAK_GBPS, 4)}
+        out[name] = rec
+        log(f"[bench] multi {name}: {json.dumps(rec)}")
+        del kc, vc, q, o
+        torch.cuda.empty_cache()
+    return out
 
 
 def copy_probe(stream, nbytes=1 << 30):
@@ -364,6 +431,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other decode batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-swap", action="store_true", help="skip the device <-> host swap measurement")
+    ap.add_argument("--no-multi", action="store_true", help="skip the runs-of-queries measurement")
+    ap.add_argument("--multi-only", action="store_true", help="only the runs-of-queries measurement")
+    ap.add_argument("--multi-case", default=None, help="with --multi-only: one case of MULTI_CASES")
     ap.add_argument("--swap-only", action="store_true",
                     help="run only the swap measurement and print its JSON object (for profiling pkv_swap_blocks)")
     ap.add_argument("--partition", type=int, default=None, help="override the workload's partition size")
@@ -397,6 +467,9 @@ def main():
     if args.swap_only:
         print(json.dumps(measure_swap(stream)), flush=True)
         return
+    if args.multi_only:
+        print(json.dumps(measure_multi(stream, case=args.multi_case)), flush=True)
+        return
 
     over = {} if args.partition is None else {"partition_size": args.partition}
     w = wl.named(args.workload, seed=0, **over)
@@ -420,6 +493,7 @@ def main():
     ceiling = hbm_read_ceiling(stream)
     log(f"[bench] streaming-read probe {ceiling:.0f} GB/s")
     swap = None if args.no_swap else measure_swap(stream)
+    multi = None if args.no_multi else measure_multi(stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     if cpu:
         log(f"[bench] cpu baseline {json.dumps(cpu)}")
@@ -455,6 +529,7 @@ def main():
                      "launch_us": round(head["partition_kernel_us"]["mean"], 2)},
         "hbm_read_ceiling_gbps": round(ceiling, 1),
         "swap": swap,
+        "multi_query": multi,
         "cpu_baseline": cpu,
         "other_workloads": extra,
         "kernel_source_sha": kernel_sha(),

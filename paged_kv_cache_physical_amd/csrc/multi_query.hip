@@ -8,19 +8,23 @@
 // and rolls back KV positions; [P4] "Preemption": a whole prompt's KV is
 // computed in one parallel pass).
 //
-// Work unit: one wave per 16 rows of one (sequence, KV head), a row being a
-// (query, query head of the group) pair, query-major.  The wave walks the
-// sequence's tokens in 16-token chunks up to its last row's position:
-//   S = K Q^T on the matrix cores (A = 16 tokens x 32 or 16 dims straight from
-//       the 16-byte-piece key tile, B = the rows' queries held in registers),
+// Work unit: a workgroup of four waves per 64 rows of one (sequence, KV
+// head), a row being a (query, query head of the group) pair, query-major;
+// each wave owns 16 of the rows.  The workgroup walks the sequence's tokens in
+// chunks up to its last row's position.  Each chunk's keys and values
+// are loaded once per workgroup (every thread loads 16-byte pieces of the
+// tiles into registers, one chunk ahead) and parked in LDS, double-buffered
+// with one barrier per chunk (a chunk is 64 tokens, or 32 where 64 would not
+// fit two buffers in 64 KiB); every wave then reads its operands from LDS:
+//   S = K Q^T on the matrix cores (A = 16 tokens x 32 or 16 dims of the key
+//       pieces, B = the wave's queries held in registers),
 //   causal mask per row, online softmax per row in the exp2 domain,
-//   O += V P on the matrix cores (A = 16 dims x 4 tokens from the transposed
-//       value tile, B = the probabilities as QK left them in the lanes;
-//       for bf16 they enter as a high and a low bf16 term so the product keeps
-//       fp32 accuracy).
-// The next chunk's keys and values are loaded before the current chunk is
-// used; past the last chunk the loads go through a size-0 buffer resource, so
-// every path issues the same loads and the compiler's waits stay exact.
+//   O += V P on the matrix cores (A = 16 dims x 4 tokens of the transposed
+//       values, B = the probabilities as QK left them in the lanes; bf16 takes
+//       two sub-chunks per 16x16x32 step, and its probabilities enter as a
+//       high and a low bf16 term so the product keeps fp32 accuracy).
+// Past the last chunk the loads go through a size-0 buffer resource, so every
+// path issues the same loads and the compiler's waits stay exact.
 
 #include <type_traits>
 
@@ -41,7 +45,8 @@ __device__ __forceinline__ uint2 mq_load8(__amdgpu_buffer_rsrc_t r, int voff) {
   return make_uint2(v[0], v[1]);
 }
 
-constexpr int kMqMaxWaves = 4;
+constexpr int kMqWaves = 4;  // waves per workgroup
+constexpr int kXcds = 8;     // accelerator complex dies of an MI355X
 
 struct MultiArgs {
   float* out;
@@ -63,32 +68,41 @@ struct MultiArgs {
   float c;         // scale * log2(e)
 };
 
-template <class DT, int D>
-struct Chunk {
-  static constexpr bool kBF16 = std::is_same<DT, BF16>::value;
-  static constexpr int KS = D * DT::kItem / 64;  // QK k-steps: four 16-byte pieces each
-  static constexpr int NDT = D / 16;             // 16-dim tiles of the output
-  uint4 k[KS];
-  typename std::conditional<kBF16, uint2, uint4>::type v[NDT];  // 4 tokens of one dim
-};
-
 template <class DT, int D, int G>
-__global__ __launch_bounds__(kWave* kMqMaxWaves) void paged_multi_query_kernel(const MultiArgs a) {
-  using C = Chunk<DT, D>;
-  constexpr bool kBF16 = C::kBF16;
+__global__ __launch_bounds__(kWave* kMqWaves) void paged_multi_query_kernel(const MultiArgs a) {
+  constexpr bool kBF16 = std::is_same<DT, BF16>::value;
   constexpr int kItem = DT::kItem;
-  constexpr int KS = C::KS, NDT = C::NDT;
-  constexpr int kTileBytes16 = D * kItem;  // bytes of one token row; a tile is B of them
+  constexpr int KS = D * kItem / 64;  // QK k-steps: four 16-byte pieces each
+  constexpr int NDT = D / 16;         // 16-dim tiles of the output
+  constexpr int ITEMS = D * kItem;    // 16-byte pieces of 16 tokens' keys, and of their values
+  constexpr int kSubBytes = 16 * ITEMS;
+  // 16-token sub-chunks per chunk: as many as two buffers of keys and values fit in 64 KiB, at most 4.
+  constexpr int NSUB = (65536 / (4 * kSubBytes)) < 4 ? (65536 / (4 * kSubBytes)) : 4;
+  constexpr int CT = 16 * NSUB;  // tokens per chunk
+  constexpr int kThreads = kWave * kMqWaves;
+  constexpr int NIT = NSUB * ITEMS / kThreads;  // pieces per thread per cache per chunk
+  static_assert(NSUB >= 1 && (NSUB * ITEMS) % kThreads == 0 && ITEMS % kWave == 0, "staging shape");
+  // LDS per buffer and sub-chunk: keys [piece][16 tokens][16 B], then values
+  // [dim][16 tokens] with the row's four 4-token slots XOR-swizzled by the dim
+  // (slot t at t ^ ((dim >> 2) & 3) for bf16, t ^ ((dim >> 1) & 3) for fp32),
+  // so that the sixteen rows a value read touches fall in distinct banks.
+  __shared__ __attribute__((aligned(16))) char lds[2][NSUB][2 * kSubBytes];
 
-  const int lane = threadIdx.x % kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
   const int m16 = lane % 16, kq = lane / 16;
-  const int waves = blockDim.x / kWave;
-  const int s = blockIdx.x / a.wg_per_seq;
-  const int wg = a.wg_per_seq - 1 - blockIdx.x % a.wg_per_seq;  // rows with the most keys go first
-  const int g = blockIdx.y;
-  // The wave index is the same in every lane; saying so keeps the values
-  // derived from it (row tile, chunk count, buffer resources) scalar.
-  const int tile = wg * waves + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+  // The wave index is the same in every lane; saying so keeps what derives from it scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  // Workgroup ids are dealt to the 8 XCDs in turn (id mod 8), each XCD with its
+  // own L2.  Renumber them so that each XCD takes one contiguous run of
+  // (sequence, KV head, row block) units: the workgroups that read the same
+  // keys and values then share an L2.
+  const int nwg = gridDim.x, xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+  const int per = nwg / kXcds, extra = nwg % kXcds;
+  const int unit = xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k;
+  const int sg = unit / a.wg_per_seq;
+  const int wg = a.wg_per_seq - 1 - unit % a.wg_per_seq;  // rows with the most keys go first
+  const int s = sg / a.num_kv_heads, g = sg % a.num_kv_heads;
 
   const int q0 = mq_ld(a.query_start, s);
   const int qs = mq_ld(a.query_start, s + 1) - q0;
@@ -97,105 +111,125 @@ __global__ __launch_bounds__(kWave* kMqMaxWaves) void paged_multi_query_kernel(c
   const bool bad = n > a.max_context_len || static_cast<int64_t>(n) > static_cast<int64_t>(a.max_blocks) * a.block_size ||
                    qs > n || qs > a.max_query_len;
   const int nrows = min(qs, a.max_query_len) * G;
-  const int r0 = tile * 16;
-  if (r0 >= nrows) return;  // wave-uniform
+  const int R0 = wg * 16 * kMqWaves;
+  if (R0 >= nrows) return;  // the whole workgroup: no barrier is left waiting
 
+  const int r0 = R0 + 16 * wave;
+  const bool active = r0 < nrows;  // wave-uniform
   const int rr = r0 + m16;
   const bool vrow = rr < nrows;
   const int qi = vrow ? rr / G : 0;
   const int h = g * G + (vrow ? rr % G : 0);
   const int64_t row_elem = (static_cast<int64_t>(q0 + qi) * a.num_q_heads + h) * D;
+  float* orow = a.out + row_elem;
 
-  f32x4_t res[NDT];
-  if (bad) {
+  if (bad) {  // the same for every wave of the workgroup
+    if (vrow) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) res[dt] = f32x4_t{NAN, NAN, NAN, NAN};
-  } else {
-    const int B = a.block_size;
-    const int pos0 = n - qs;  // position of the run's first query
-    const int p_row = pos0 + qi;
-    const int p_max = pos0 + min(r0 + 15, nrows - 1) / G;
-    const int nc = p_max / 16 + 1;
-    const int tile_bytes = B * kTileBytes16;
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4_t*>(orow + 16 * dt + 4 * kq) = f32x4_t{NAN, NAN, NAN, NAN};
+    }
+    return;
+  }
 
-    uint4 qv[KS];
-    const char* qrow = static_cast<const char*>(a.q) + row_elem * kItem;
+  const int B = a.block_size;
+  const int pos0 = n - qs;  // position of the run's first query
+  const int p_row = pos0 + qi;
+  const int p_wave = pos0 + (active ? min(r0 + 15, nrows - 1) / G : 0);  // the wave's last position
+  const int nc = (pos0 + min(R0 + 16 * kMqWaves - 1, nrows - 1) / G) / CT + 1;  // chunks up to the last row
+  const int tile_bytes = B * D * kItem;
+
+  uint4 qv[KS];
+  const char* qrow = static_cast<const char*>(a.q) + row_elem * kItem;
 #pragma unroll
-    for (int st = 0; st < KS; ++st)
-      qv[st] = vrow ? *reinterpret_cast<const uint4*>(qrow + (st * 4 + kq) * 16) : make_uint4(0, 0, 0, 0);
+  for (int st = 0; st < KS; ++st)
+    qv[st] = vrow ? *reinterpret_cast<const uint4*>(qrow + (st * 4 + kq) * 16) : make_uint4(0, 0, 0, 0);
 
-    bool poison = false;
-    const int64_t table_row = static_cast<int64_t>(s) * a.max_blocks;
-    auto load = [&](int c, C& ch) __attribute__((always_inline)) {
-      const int t0 = 16 * c;
-      const bool in = c < nc;
+  // Staging: thread piece j of a chunk is i = tid + kThreads j, in sub-chunk
+  // i / ITEMS (the same for a whole wave); within it, key piece ii is (key
+  // piece ii / 16, token ii % 16) and value piece ii is (dim ii / kItem,
+  // tokens (ii % kItem) * 16 / kItem + 0 ..).
+  bool poison = false;
+  const int64_t table_row = static_cast<int64_t>(s) * a.max_blocks;
+  uint4 kr[NIT], vr[NIT];
+  auto stage = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int sub = (kWave * wave + kThreads * j) / ITEMS;  // wave-uniform
+      const int ii = tid + kThreads * j - sub * ITEMS;
+      const int t0 = CT * c + 16 * sub;
+      const bool in = c < nc && t0 < n;
       const int blk = in ? mq_ld(a.block_tables, table_row + t0 / B) : 0;
       const bool ok = blk >= 0 && blk < a.num_blocks;
       poison |= in && !ok;
       const int64_t off = ok ? (static_cast<int64_t>(blk) * a.num_kv_heads + g) * tile_bytes : 0;
       const int bytes = (in && ok) ? tile_bytes : 0;
-      const auto rk = make_rsrc(a.k_cache + off, bytes);
-      const auto rv = make_rsrc(a.v_cache + off, bytes);
       const int o = t0 % B;
+      kr[j] = mq_load16(make_rsrc(a.k_cache + off, bytes), ((ii >> 4) * B + o + (ii & 15)) * 16);
+      vr[j] = mq_load16(make_rsrc(a.v_cache + off, bytes), ((ii / kItem) * B + o + (ii % kItem) * (16 / kItem)) * kItem);
+    }
+  };
+  auto put = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int st = 0; st < KS; ++st) ch.k[st] = mq_load16(rk, ((st * 4 + kq) * B + o + m16) * 16);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int voff = ((16 * dt + m16) * B + o + 4 * kq) * kItem;
-        if constexpr (kBF16)
-          ch.v[dt] = mq_load8(rv, voff);
-        else
-          ch.v[dt] = mq_load16(rv, voff);
+    for (int j = 0; j < NIT; ++j) {
+      const int sub = (kWave * wave + kThreads * j) / ITEMS;
+      const int ii = tid + kThreads * j - sub * ITEMS;
+      *reinterpret_cast<uint4*>(&lds[buf][sub][16 * ii]) = kr[j];
+      const int dim = ii / kItem, part = ii % kItem;
+      if constexpr (kBF16) {
+        // Piece = 4-token slots 2 part and 2 part + 1 of the row; slot t sits at t ^ sw.
+        const int sw = (dim >> 2) & 3;
+        const uint4 v = (sw & 1) ? make_uint4(vr[j].z, vr[j].w, vr[j].x, vr[j].y) : vr[j];
+        *reinterpret_cast<uint4*>(&lds[buf][sub][kSubBytes + 32 * dim + 16 * (part ^ (sw >> 1))]) = v;
+      } else {
+        // Piece = 4-token slot `part` of the row; slot t sits at t ^ sw.
+        const int sw = (dim >> 1) & 3;
+        *reinterpret_cast<uint4*>(&lds[buf][sub][kSubBytes + 64 * dim + 16 * (part ^ sw)]) = vr[j];
       }
-    };
+    }
+  };
 
-    f32x4_t acc[NDT];
+  f32x4_t acc[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;
 
-    C cur, nxt;
-    load(0, cur);
-    for (int c = 0; c < nc; ++c) {
-      load(c + 1, nxt);
-      const int t0 = 16 * c;
-
-      // S[token 4 kq + r][row m16] on the matrix cores.
-      f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+  stage(0);
+  put(0);
+  stage(1);
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    if (active && CT * c <= p_wave) {
+      // S[token 16 sub + 4 kq + r][row m16] on the matrix cores, NSUB independent tiles.
+      f32x4_t sc[NSUB];
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const uint4 kv = cur.k[st], qq = qv[st];
-        if constexpr (kBF16) {
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qq), sc, 0, 0, 0);
-        } else {
-          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.x), __uint_as_float(qq.x), sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.y), __uint_as_float(qq.y), sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.z), __uint_as_float(qq.z), sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.w), __uint_as_float(qq.w), sc, 0, 0, 0);
+      for (int u = 0; u < NSUB; ++u) {
+        const char* kl = lds[c & 1][u];
+        sc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(kl + ((st * 4 + kq) * 16 + m16) * 16);
+          const uint4 qq = qv[st];
+          if constexpr (kBF16) {
+            sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qq), sc[u], 0, 0, 0);
+          } else {
+            sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.x), __uint_as_float(qq.x), sc[u], 0, 0, 0);
+            sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.y), __uint_as_float(qq.y), sc[u], 0, 0, 0);
+            sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.z), __uint_as_float(qq.z), sc[u], 0, 0, 0);
+            sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.w), __uint_as_float(qq.w), sc[u], 0, 0, 0);
+          }
         }
       }
       // Scaled logits; a token after the row's position (or past the
       // sequence, which is later still) gets -inf.
+      float gm = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = (t0 + 4 * kq + r <= p_row) ? sc[r] * a.c : -INFINITY;
-      if (t0 + 16 > n) {
-        // Values past the end may be anything (NaN poison included): zero them.
-        const int rel = n - t0 - 4 * kq;  // valid tokens among this lane's four
+      for (int u = 0; u < NSUB; ++u)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          if constexpr (kBF16) {
-            cur.v[dt].x &= (rel > 0 ? 0x0000ffffu : 0u) | (rel > 1 ? 0xffff0000u : 0u);
-            cur.v[dt].y &= (rel > 2 ? 0x0000ffffu : 0u) | (rel > 3 ? 0xffff0000u : 0u);
-          } else {
-            if (rel <= 0) cur.v[dt].x = 0u;
-            if (rel <= 1) cur.v[dt].y = 0u;
-            if (rel <= 2) cur.v[dt].z = 0u;
-            if (rel <= 3) cur.v[dt].w = 0u;
-          }
+        for (int r = 0; r < 4; ++r) {
+          sc[u][r] = (CT * c + 16 * u + 4 * kq + r <= p_row) ? sc[u][r] * a.c : -INFINITY;
+          gm = fmaxf(gm, sc[u][r]);
         }
-      }
       // Online softmax per row (lane column m16; the four lane groups hold its tokens).
-      float gm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       gm = max_xor32(max_xor16(gm));
       const float m_new = fmaxf(m_run, gm);  // finite from the first chunk on: token 0 is visible to every row
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -203,16 +237,50 @@ __global__ __launch_bounds__(kWave* kMqMaxWaves) void paged_multi_query_kernel(c
       for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
       l_run *= alpha;
       m_run = m_new;
-      float p[4];
+      // The lane's value columns of sub-chunk u: dims 16 dt + m16, tokens 4 kq .. 4 kq + 3
+      // (values past the end of the sequence may be anything, NaN poison included: zeroed).
+      auto values = [&](int u, auto (&vv)[NDT]) __attribute__((always_inline)) {
+        const int t0 = CT * c + 16 * u;
+        const char* vl = lds[c & 1][u] + kSubBytes;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
-        l_run += p[r];
-      }
-
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int dim = 16 * dt + m16;
+          if constexpr (kBF16)
+            vv[dt] = *reinterpret_cast<const uint2*>(vl + 32 * dim + 8 * (kq ^ ((dim >> 2) & 3)));
+          else
+            vv[dt] = *reinterpret_cast<const uint4*>(vl + 64 * dim + 16 * (kq ^ ((dim >> 1) & 3)));
+        }
+        if (t0 + 16 > n) {
+          const int rel = n - t0 - 4 * kq;  // valid tokens among this lane's four
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            if constexpr (kBF16) {
+              vv[dt].x &= (rel > 0 ? 0x0000ffffu : 0u) | (rel > 1 ? 0xffff0000u : 0u);
+              vv[dt].y &= (rel > 2 ? 0x0000ffffu : 0u) | (rel > 3 ? 0xffff0000u : 0u);
+            } else {
+              if (rel <= 0) vv[dt].x = 0u;
+              if (rel <= 1) vv[dt].y = 0u;
+              if (rel <= 2) vv[dt].z = 0u;
+              if (rel <= 3) vv[dt].w = 0u;
+            }
+          }
+        }
+      };
+      float p[NSUB][4];
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[u][r] = __builtin_amdgcn_exp2f(sc[u][r] - m_run);
+          l_run += p[u][r];
+        }
       // O[dim][row] += V[dim][token] P[token][row].
       if constexpr (kBF16) {
-        typedef short s4_t __attribute__((ext_vector_type(4)));
+        // Sub-chunks in pairs on 16x16x32 steps: lane (kq, m16) supplies k-slots
+        // 0-3 = tokens 4 kq + r of the first and 4-7 = the same of the second,
+        // for P (its QK registers) and V alike.  P enters as a high and a low
+        // bf16 term.
+        static_assert(NSUB % 2 == 0, "bf16 chunks hold pairs of sub-chunks");
         typedef float f2_t __attribute__((ext_vector_type(2)));
         typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
         auto hi_bits = [](float x) __attribute__((always_inline)) { return __float_as_uint(x) & 0xffff0000u; };
@@ -221,36 +289,52 @@ __global__ __launch_bounds__(kWave* kMqMaxWaves) void paged_multi_query_kernel(c
           const f2_t l = {x - __uint_as_float(hi_bits(x)), y - __uint_as_float(hi_bits(y))};
           return __builtin_bit_cast(uint32_t, __builtin_convertvector(l, b2_t));
         };
-        const u32x2_t ph = {pack_hi(p[0], p[1]), pack_hi(p[2], p[3])};
-        const u32x2_t pl = {pack_lo(p[0], p[1]), pack_lo(p[2], p[3])};
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const u32x2_t av = {cur.v[dt].x, cur.v[dt].y};
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, av),
-                                                              __builtin_bit_cast(s4_t, ph), acc[dt], 0, 0, 0);
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, av),
-                                                              __builtin_bit_cast(s4_t, pl), acc[dt], 0, 0, 0);
+        for (int u = 0; u < NSUB; u += 2) {
+          if (CT * c + 16 * u > p_wave) break;  // no row of the wave sees these tokens (wave-uniform)
+          uint2 va[NDT], vb[NDT];
+          values(u, va);
+          values(u + 1, vb);
+          const u32x4_t ph = {pack_hi(p[u][0], p[u][1]), pack_hi(p[u][2], p[u][3]), pack_hi(p[u + 1][0], p[u + 1][1]),
+                              pack_hi(p[u + 1][2], p[u + 1][3])};
+          const u32x4_t pl = {pack_lo(p[u][0], p[u][1]), pack_lo(p[u][2], p[u][3]), pack_lo(p[u + 1][0], p[u + 1][1]),
+                              pack_lo(p[u + 1][2], p[u + 1][3])};
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const u32x4_t av = {va[dt].x, va[dt].y, vb[dt].x, vb[dt].y};
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                              __builtin_bit_cast(bf16x8_t, ph), acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                              __builtin_bit_cast(bf16x8_t, pl), acc[dt], 0, 0, 0);
+          }
         }
       } else {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(cur.v[dt].x), p[0], acc[dt], 0, 0, 0);
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(cur.v[dt].y), p[1], acc[dt], 0, 0, 0);
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(cur.v[dt].z), p[2], acc[dt], 0, 0, 0);
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(cur.v[dt].w), p[3], acc[dt], 0, 0, 0);
+        for (int u = 0; u < NSUB; ++u) {
+          if (CT * c + 16 * u > p_wave) break;  // no row of the wave sees these tokens (wave-uniform)
+          uint4 vv[NDT];
+          values(u, vv);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].x), p[u][0], acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].y), p[u][1], acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].z), p[u][2], acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].w), p[u][3], acc[dt], 0, 0, 0);
+          }
         }
       }
-      cur = nxt;
     }
-    const float l_tot = sum_xor32(sum_xor16(l_run));
-    const float inv = poison ? NAN : 1.0f / l_tot;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) res[dt] = acc[dt] * inv;
+    // Chunk c + 1 into the other buffer (its last readers passed the previous
+    // barrier), then the loads of chunk c + 2.
+    put((c + 1) & 1);
+    stage(c + 2);
+    __syncthreads();
   }
+  const float l_tot = sum_xor32(sum_xor16(l_run));  // every lane takes part in the swaps
+  const float inv = poison ? NAN : 1.0f / l_tot;
   if (vrow) {
-    float* orow = a.out + row_elem;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4_t*>(orow + 16 * dt + 4 * kq) = res[dt];
+    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4_t*>(orow + 16 * dt + 4 * kq) = acc[dt] * inv;
   }
 }
 
@@ -302,10 +386,9 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
 
-  const int64_t tiles = (static_cast<int64_t>(max_query_len) * G + 15) / 16;  // 16-row wave tiles per (s, g)
-  const int waves = static_cast<int>(tiles < kMqMaxWaves ? tiles : kMqMaxWaves);
-  const int64_t wg_per_seq = (tiles + waves - 1) / waves;
-  if (wg_per_seq * num_seqs > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  const int64_t rows_per_wg = 16 * kMqWaves;
+  const int64_t wg_per_seq = (static_cast<int64_t>(max_query_len) * G + rows_per_wg - 1) / rows_per_wg;
+  if (wg_per_seq * num_seqs * num_kv_heads > INT32_MAX) return PKV_ERR_INVALID_ARG;
   MultiArgs a{};
   a.out = out;
   a.q = q;
@@ -324,8 +407,8 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   a.max_query_len = max_query_len;
   a.wg_per_seq = static_cast<int>(wg_per_seq);
   a.c = scale * 1.4426950408889634f;
-  const dim3 grid(static_cast<unsigned>(wg_per_seq * num_seqs), static_cast<unsigned>(num_kv_heads));
-  const dim3 block(static_cast<unsigned>(waves * kWave));
+  const dim3 grid(static_cast<unsigned>(wg_per_seq * num_seqs * num_kv_heads));
+  const dim3 block(static_cast<unsigned>(kMqWaves * kWave));
   const hipError_t err = kv_dtype == PKV_BF16 ? launch_multi<BF16>(a, head_dim, G, grid, block, stream)
                                               : launch_multi<F32>(a, head_dim, G, grid, block, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
