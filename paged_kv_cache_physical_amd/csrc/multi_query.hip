@@ -14,8 +14,8 @@
 // chunks up to its last row's position.  Each chunk's keys and values
 // are loaded once per workgroup (every thread loads 16-byte pieces of the
 // tiles into registers, one chunk ahead) and parked in LDS, double-buffered
-// with one barrier per chunk (a chunk is 64 tokens, or 32 where 64 would not
-// fit two buffers in 64 KiB); every wave then reads its operands from LDS:
+// with one barrier per chunk (a chunk is 32 tokens, 16 where 32 would not fit
+// two buffers in 64 KiB); every wave then reads its operands from LDS:
 //   S = K Q^T on the matrix cores (A = 16 tokens x 32 or 16 dims of the key
 //       pieces, B = the wave's queries held in registers),
 //   causal mask per row, online softmax per row in the exp2 domain,
@@ -69,15 +69,19 @@ struct MultiArgs {
 };
 
 template <class DT, int D, int G>
-__global__ __launch_bounds__(kWave* kMqWaves) void paged_multi_query_kernel(const MultiArgs a) {
+// Three workgroups per CU: at bf16/d = 128 the compiler then keeps the
+// accumulators in VGPRs (146, no AGPR copies, no scratch).
+__global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(const MultiArgs a) {
   constexpr bool kBF16 = std::is_same<DT, BF16>::value;
   constexpr int kItem = DT::kItem;
   constexpr int KS = D * kItem / 64;  // QK k-steps: four 16-byte pieces each
   constexpr int NDT = D / 16;         // 16-dim tiles of the output
   constexpr int ITEMS = D * kItem;    // 16-byte pieces of 16 tokens' keys, and of their values
   constexpr int kSubBytes = 16 * ITEMS;
-  // 16-token sub-chunks per chunk: as many as two buffers of keys and values fit in 64 KiB, at most 4.
-  constexpr int NSUB = (65536 / (4 * kSubBytes)) < 4 ? (65536 / (4 * kSubBytes)) : 4;
+  // 16-token sub-chunks per chunk: 2, or 1 where two buffers of keys and values
+  // would not fit in 64 KiB.  32-token chunks (32 KiB at bf16, d = 128) leave
+  // room for three workgroups per CU; 64-token chunks measured slower.
+  constexpr int NSUB = (65536 / (4 * kSubBytes)) < 2 ? (65536 / (4 * kSubBytes)) : 2;
   constexpr int CT = 16 * NSUB;  // tokens per chunk
   constexpr int kThreads = kWave * kMqWaves;
   constexpr int NIT = NSUB * ITEMS / kThreads;  // pieces per thread per cache per chunk
