@@ -182,6 +182,35 @@ def host_allocator_step_us(w, reps=20):
     return 1e6 * float(np.median(t))
 
 
+def measure_prefix_cache(requests=256, stems=8, block_size=16):
+    """Automatic prefix caching on the host pool: requests over a few shared stems (1000-2000 tokens, as a
+    system prompt or few-shot header) with their own tails (1-256 tokens) are admitted one by one
+    (pkv_seq_create_prefixed, then pkv_append_tokens of the uncached ids).  Reports the host time per admitted
+    request, the prompt tokens mapped from the cache instead of written, and the blocks in use against the same
+    requests with private blocks."""
+    import workloads as wl
+    from paged_kv_cache_physical_amd import Pool
+    pr = wl.PrefixRequests(seed=0, num_requests=requests, num_stems=stems, stem_range=(1000, 2000),
+                           tail_range=(1, 256), num_q_heads=32, num_kv_heads=8, head_dim=128, kv_dtype="bf16")
+    prompts = [np.asarray(pr.prompt(r), dtype=np.int32) for r in range(requests)]  # ids as the binding takes them
+    need = sum(-(-len(p) // block_size) for p in prompts)
+    pool = Pool(need, block_size, np.random.default_rng(0).permutation(need).astype(np.int32))
+    mapped, t = 0, []
+    for ids in prompts:
+        t0 = time.perf_counter()
+        sid, hit = pool.create_prefixed(ids)
+        pool.append([sid], [len(ids) - hit], token_ids=ids[hit:])
+        t.append(time.perf_counter() - t0)
+        mapped += hit
+    st = pool.stats()
+    total = sum(len(p) for p in prompts)
+    return {"requests": requests, "stems": stems, "prompt_tokens": total, "tokens_from_cache": mapped,
+            "fraction_from_cache": round(mapped / total, 4), "blocks_used": st["used_blocks"],
+            "blocks_private": need, "cached_blocks": st["cached_blocks"],
+            "host_us_per_request_median": round(1e6 * float(np.median(t)), 2),
+            "host_us_per_request_mean": round(1e6 * float(np.mean(t)), 2)}
+
+
 def hbm_read_ceiling(stream):
     """Practical HBM read rate of a plain streaming kernel over 4 GiB (context for the roofline)."""
     import torch
@@ -494,6 +523,8 @@ def main():
     log(f"[bench] streaming-read probe {ceiling:.0f} GB/s")
     swap = None if args.no_swap else measure_swap(stream)
     multi = None if args.no_multi else measure_multi(stream)
+    prefix = measure_prefix_cache()
+    log(f"[bench] prefix cache {json.dumps(prefix)}")
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     if cpu:
         log(f"[bench] cpu baseline {json.dumps(cpu)}")
@@ -530,6 +561,7 @@ def main():
         "hbm_read_ceiling_gbps": round(ceiling, 1),
         "swap": swap,
         "multi_query": multi,
+        "prefix_cache": prefix,
         "cpu_baseline": cpu,
         "other_workloads": extra,
         "kernel_source_sha": kernel_sha(),

@@ -270,3 +270,42 @@ def test_full_size_verification_sampled():
     for i in pick:
         ref = b.oracle(q[starts[i]:starts[i + 1]], t[i:i + 1], l[i:i + 1], np.array([0, 4], np.int32))
         check_close(out[starts[i]:starts[i + 1]], ref, s.kv_dtype, f"sequence {i}")
+
+
+def test_repeated_calls_and_graph_replays_are_bitwise_stable():
+    """Runs of queries give the same bits on every call, and as a captured HIP graph on every replay, with eager
+    work and synchronisations between the replays."""
+    import paged_kv_cache_physical_amd as pk
+    lens = [900, 1500, 37, 2048, 640]
+    runs = [300, 7, 37, 512, 1]
+    b = Batch(lens, 32, 8, 128, 16, "bf16", seed=29)
+    t, l = b.tables()
+    q = to_dev(wl.draw_values(wl.rng_for(30, wl.STREAM_Q), (sum(runs), 32, 128), "bf16"), "bf16")
+    starts = torch.from_numpy(np.concatenate([[0], np.cumsum(runs)]).astype(np.int32)).cuda()
+    bt, cl = torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda()
+    out = torch.empty((sum(runs), 32, 128), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    call = lambda: pk.pkv_paged_attention_multi(out, q, *b.caches, bt, cl, starts, int(l.max()), max(runs),
+                                                1.0 / np.sqrt(128), stream=s)
+    with torch.cuda.stream(s):
+        call()
+        torch.cuda.synchronize()
+        first = out.clone()
+        assert bool(torch.isfinite(first).all())
+        for i in range(6):
+            out.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+            assert torch.equal(out, first), i
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            call()
+        for i in range(4):
+            out.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, first), i
+            out.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+            assert torch.equal(out, first), i
