@@ -324,6 +324,7 @@ def measure_swap(stream, block_tokens=(1, 4, 16, 32), per_cache=256 << 20):
 MULTI_CASES = {
     "verify4_llama7b_bf16": (64, 32, 32, (128, 2048), 4),
     "verify4_gqa_bf16": (256, 64, 8, (128, 2048), 4),
+    "verify4_long_bf16": (8, 32, 8, 32768, 4),
     "prefill2048_gqa_bf16": (16, 32, 8, 2048, "all"),
     "prefix_tail256_gqa_bf16": (64, 32, 8, 1280, 256),
 }
@@ -358,8 +359,10 @@ def measure_multi(stream, reps=20, case=None):
         o = torch.empty((T, Hq, d), dtype=torch.float32, device="cuda")
         starts = torch.from_numpy(np.concatenate([[0], np.cumsum(runs)]).astype(np.int32)).cuda()
         bt, cl = torch.from_numpy(tables).cuda(), torch.from_numpy(clens).cuda()
+        wsb = pk.pkv_attention_multi_workspace_bytes(S, Hq, Hkv, d, int(lens.max()), int(runs.max()))
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
         fn = lambda: pk.pkv_paged_attention_multi(o, q, kc, vc, bt, cl, starts, int(lens.max()), int(runs.max()),
-                                                  1.0 / np.sqrt(d), stream)
+                                                  1.0 / np.sqrt(d), stream, workspace=ws)
         with torch.cuda.stream(stream):
             for _ in range(3):
                 fn()
@@ -369,6 +372,7 @@ def measure_multi(stream, reps=20, case=None):
         flops = 4 * d * Hq * visible
         kv_bytes = int(lens.sum()) * 2 * Hkv * d * 2
         rec = {"sequences": S, "H_q": Hq, "H_kv": Hkv, "context_tokens": int(lens.sum()), "query_rows": T,
+               "workspace_bytes": wsb,
                "launch_us": round(us, 2), "launch_us_median": round(1e3 * t[1], 2),
                "kv_bytes": kv_bytes, "kv_gbps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
                "flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
@@ -380,7 +384,7 @@ def measure_multi(stream, reps=20, case=None):
                                "frac": round(rec["kv_gbps"] / HBM_PEAK_GBPS, 4)}
         out[name] = rec
         log(f"[bench] multi {name}: {json.dumps(rec)}")
-        del kc, vc, q, o
+        del kc, vc, q, o, ws
         torch.cuda.empty_cache()
     return out
 

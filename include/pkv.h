@@ -405,21 +405,37 @@ pkv_status pkv_decode_step(const void* k_new, const void* v_new, float* out, con
  *   query_start: device int32 [num_seqs + 1], non-decreasing.
  *   block_tables, context_lens: as for pkv_paged_attention_decode.
  *   max_query_len: a bound on every q_s (it sizes the launch).
- * Rows of a run with q_s > n_s, q_s > max_query_len, n_s > max_context_len,
- * n_s > max_blocks * B, or a block id outside [0, num_blocks) are NaN (for
- * q_s > max_query_len, only its first max_query_len rows are written); a run
- * with query_start[s] < 0 or query_start[s+1] > num_query_rows is not
- * written.  Supported shapes and dtypes as for decode.  Arithmetic: fp32
- * accumulation, products on the matrix cores; bf16 probabilities enter the
- * value product as two bf16 terms.  Allocates nothing; needs no workspace.
- * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+ *   workspace: device memory of workspace_bytes >= the value of
+ *     pkv_attention_multi_workspace_bytes(...) for these sizes, 16-byte
+ *     aligned, or NULL; with it, long contexts of few (sequence, KV head)
+ *     pairs are split (see there).  Its contents are private.
+ * Rows of a run with q_s > n_s, q_s > max_query_len, n_s > max_context_len or
+ * n_s > max_blocks * B are NaN (for q_s > max_query_len, only its first
+ * max_query_len rows are written); a row that reads a block id outside
+ * [0, num_blocks) is NaN, and so may be the rows computed with it; a run with
+ * query_start[s] < 0 or query_start[s+1] > num_query_rows is not written.
+ * Supported shapes and dtypes as for decode.  Arithmetic: fp32 accumulation,
+ * products on the matrix cores; bf16 probabilities enter the value product as
+ * two bf16 terms.  Allocates nothing.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (too small or misaligned when a
+ * split is planned), HIP. */
 pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* block_tables, const int32_t* context_lens,
                                      const int32_t* query_start, int32_t num_seqs, int32_t num_query_rows,
                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                      int32_t block_size, int32_t num_blocks, int32_t max_blocks,
-                                     int32_t max_context_len, int32_t max_query_len, float scale, int32_t kv_dtype,
-                                     hipStream_t stream);
+                                     int32_t max_context_len, int32_t max_query_len, float scale, void* workspace,
+                                     size_t workspace_bytes, int32_t kv_dtype, hipStream_t stream);
+
+/* Bytes of workspace pkv_paged_attention_multi uses to split long contexts (0
+ * when it would not split them).  A context is split when every run's rows
+ * (max_query_len * H_q / H_kv) fit one 64-row block and the batch has too few
+ * (sequence, KV head) pairs to fill the GPU: each pair's context is cut into
+ * splits of at least 256 tokens, computed apart and combined with log-sum-exp
+ * weights (speculative verification over long contexts).  With no workspace
+ * the call does not split. */
+size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_context_len, int32_t max_query_len);
 
 /* The two stages of pkv_paged_attention_decode, for callers that schedule or
  * time them separately.  Same arguments and errors; issue `partitions` then

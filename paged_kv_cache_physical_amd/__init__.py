@@ -26,6 +26,7 @@ from ._lib import (PKV_BF16, PKV_ERR_INVALID_ARG, PKV_F32, InvalidArg, NoSuchSeq
 __all__ = [
     "pkv_pool_create", "pkv_pool_destroy", "pkv_seq_create", "pkv_seq_fork", "pkv_seq_free", "pkv_append_tokens",
     "pkv_seq_create_prefixed", "pkv_pool_cached_blocks", "pkv_seq_truncate", "pkv_paged_attention_multi",
+    "pkv_attention_multi_workspace_bytes",
     "pkv_block_tables", "pkv_seq_info", "pkv_pool_stats", "pkv_block_refcount", "pkv_pool_free_list",
     "pkv_pool_validate", "pkv_pool_set_host_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_seq_table",
     "pkv_host_block_refcount", "pkv_pool_host_free_list", "pkv_swap_blocks", "empty_host_caches", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_attention_workspace_bytes",
@@ -486,11 +487,19 @@ def pkv_decode_step(k_new, v_new, out, q, k_cache, v_cache, block_tables, contex
                partition_size, workspace, stream, new_kv=(k_new, v_new))
 
 
+def pkv_attention_multi_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                        max_query_len) -> int:
+    return int(lib().pkv_attention_multi_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                         max_context_len, max_query_len))
+
+
 def pkv_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
-                              max_context_len: int, max_query_len: int, scale: float, stream=None) -> None:
+                              max_context_len: int, max_query_len: int, scale: float, stream=None,
+                              workspace=None) -> None:
     """Runs of causal queries: out fp32 [T][H_q][d]; q [T][H_q][d] (cache dtype); query_start int32 [S+1]
     (rows of sequence s: its last query_start[s+1] - query_start[s] positions); block_tables int32
-    [S][max_blocks]; context_lens int32 [S]."""
+    [S][max_blocks]; context_lens int32 [S]; workspace: uint8 tensor of >= pkv_attention_multi_workspace_bytes
+    bytes, or None (no context split)."""
     torch = _torch()
     fn = "pkv_paged_attention_multi"
     if q.dim() != 3 or out.shape != q.shape or out.dtype != torch.float32:
@@ -513,7 +522,9 @@ def pkv_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_le
                                           _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
                                           _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), S, T,
                                           Hq, Hkv, d, B, nb, block_tables.shape[1], max_context_len, max_query_len,
-                                          scale, _dtype_code(q), _stream(stream)), fn)
+                                          scale, None if workspace is None else _dev(workspace, "workspace"),
+                                          0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                          _dtype_code(q), _stream(stream)), fn)
 
 
 def pkv_paged_attention_partitions(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,

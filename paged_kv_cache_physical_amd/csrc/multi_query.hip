@@ -64,9 +64,17 @@ struct MultiArgs {
   int max_blocks;
   int max_context_len;
   int max_query_len;
-  int wg_per_seq;  // workgroups per (sequence, KV head)
+  int wg_per_seq;  // row blocks per (sequence, KV head)
+  int nsplit;      // context splits per (sequence, KV head): 1, or several when its rows fit one block
+  int split_len;   // tokens per split (a multiple of the chunk), when nsplit > 1
+  float* ws_acc;   // split partials: [S][H_kv][nsplit][64 rows][d], un-normalised
+  float* ws_m;     // [S][H_kv][nsplit][64 rows], running max (exp2 domain)
+  float* ws_l;     // [S][H_kv][nsplit][64 rows], sum of weights
   float c;         // scale * log2(e)
 };
+
+constexpr int kMqRows = 16 * kMqWaves;  // rows per workgroup
+constexpr int kMqChunk = 32;            // tokens per chunk (every supported shape)
 
 template <class DT, int D, int G>
 // Three workgroups per CU: at bf16/d = 128 the compiler then keeps the
@@ -104,9 +112,12 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
   const int nwg = gridDim.x, xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
   const int per = nwg / kXcds, extra = nwg % kXcds;
   const int unit = xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k;
-  const int sg = unit / a.wg_per_seq;
-  const int wg = a.wg_per_seq - 1 - unit % a.wg_per_seq;  // rows with the most keys go first
+  const int per_sg = a.wg_per_seq * a.nsplit;
+  const int sg = unit / per_sg;
+  const int wg = a.wg_per_seq - 1 - (unit % per_sg) / a.nsplit;  // rows with the most keys go first
+  const int split = unit % a.nsplit;
   const int s = sg / a.num_kv_heads, g = sg % a.num_kv_heads;
+  static_assert(CT == kMqChunk, "split lengths are counted in chunks");
 
   const int q0 = mq_ld(a.query_start, s);
   const int qs = mq_ld(a.query_start, s + 1) - q0;
@@ -127,8 +138,8 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
   const int64_t row_elem = (static_cast<int64_t>(q0 + qi) * a.num_q_heads + h) * D;
   float* orow = a.out + row_elem;
 
-  if (bad) {  // the same for every wave of the workgroup
-    if (vrow) {
+  if (bad) {  // the same for every wave of the workgroup (the split combine skips such runs)
+    if (vrow && split == 0) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4_t*>(orow + 16 * dt + 4 * kq) = f32x4_t{NAN, NAN, NAN, NAN};
     }
@@ -139,8 +150,24 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
   const int pos0 = n - qs;  // position of the run's first query
   const int p_row = pos0 + qi;
   const int p_wave = pos0 + (active ? min(r0 + 15, nrows - 1) / G : 0);  // the wave's last position
-  const int nc = (pos0 + min(R0 + 16 * kMqWaves - 1, nrows - 1) / G) / CT + 1;  // chunks up to the last row
+  const int p_last = pos0 + min(R0 + 16 * kMqWaves - 1, nrows - 1) / G;  // the workgroup's last position
+  // Chunks [c_begin, nc): this split's tokens up to the last position.
+  const int c_begin = a.nsplit > 1 ? split * (a.split_len / CT) : 0;
+  const int nc = a.nsplit > 1 ? min((split + 1) * (a.split_len / CT), p_last / CT + 1) : p_last / CT + 1;
   const int tile_bytes = B * D * kItem;
+  const int64_t part = (static_cast<int64_t>(sg) * a.nsplit + split) * kMqRows + (rr - R0);  // split partial row
+  if (c_begin >= nc) {  // a split past every row's position: an empty partial
+    if (vrow) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4_t*>(a.ws_acc + part * D + 16 * dt + 4 * kq) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if (kq == 0) {
+        a.ws_m[part] = -INFINITY;
+        a.ws_l[part] = 0.0f;
+      }
+    }
+    return;  // the same for the whole workgroup
+  }
 
   uint4 qv[KS];
   const char* qrow = static_cast<const char*>(a.q) + row_elem * kItem;
@@ -197,11 +224,11 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  stage(0);
-  put(0);
-  stage(1);
+  stage(c_begin);
+  put(c_begin & 1);
+  stage(c_begin + 1);
   __syncthreads();
-  for (int c = 0; c < nc; ++c) {
+  for (int c = c_begin; c < nc; ++c) {
     if (active && CT * c <= p_wave) {
       // S[token 16 sub + 4 kq + r][row m16] on the matrix cores, NSUB independent tiles.
       f32x4_t sc[NSUB];
@@ -235,8 +262,11 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
         }
       // Online softmax per row (lane column m16; the four lane groups hold its tokens).
       gm = max_xor32(max_xor16(gm));
-      const float m_new = fmaxf(m_run, gm);  // finite from the first chunk on: token 0 is visible to every row
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_new = fmaxf(m_run, gm);
+      // -inf only for a row that has seen no token yet (in a split that starts after
+      // its position): then alpha and its weights are 0, never inf - inf.
+      const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
       l_run *= alpha;
@@ -275,7 +305,7 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
       for (int u = 0; u < NSUB; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[u][r] = __builtin_amdgcn_exp2f(sc[u][r] - m_run);
+          p[u][r] = __builtin_amdgcn_exp2f(sc[u][r] - m_ref);
           l_run += p[u][r];
         }
       // O[dim][row] += V[dim][token] P[token][row].
@@ -335,11 +365,103 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
     __syncthreads();
   }
   const float l_tot = sum_xor32(sum_xor16(l_run));  // every lane takes part in the swaps
+  if (a.nsplit > 1) {
+    // Split partial: un-normalised accumulator, max and sum (NaN if a block id was bad).
+    const float f = poison ? NAN : 1.0f;
+    if (vrow) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4_t*>(a.ws_acc + part * D + 16 * dt + 4 * kq) = acc[dt] * f;
+      if (kq == 0) {
+        a.ws_m[part] = m_run;
+        a.ws_l[part] = l_tot * f;
+      }
+    }
+    return;
+  }
   const float inv = poison ? NAN : 1.0f / l_tot;
   if (vrow) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4_t*>(orow + 16 * dt + 4 * kq) = acc[dt] * inv;
   }
+}
+
+// Log-sum-exp combination of the split partials of one (sequence, KV head):
+// out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k with M = max_k m_k; a
+// split that saw no token of a row has m = -inf and weighs nothing.  Runs the
+// attention kernel did not write, or wrote as NaN, are skipped.
+template <int D, int G>
+__global__ __launch_bounds__(256) void multi_combine_kernel(const MultiArgs a) {
+  const int sg = blockIdx.x;
+  const int s = sg / a.num_kv_heads, g = sg % a.num_kv_heads;
+  const int q0 = mq_ld(a.query_start, s);
+  const int qs = mq_ld(a.query_start, s + 1) - q0;
+  if (q0 < 0 || qs <= 0 || static_cast<int64_t>(q0) + qs > a.num_query_rows) return;
+  const int n = mq_ld(a.context_lens, s);
+  if (n > a.max_context_len || static_cast<int64_t>(n) > static_cast<int64_t>(a.max_blocks) * a.block_size ||
+      qs > n || qs > a.max_query_len)
+    return;
+  const int nrows = qs * G;  // at most kMqRows when the context is split
+  const int64_t base = static_cast<int64_t>(sg) * a.nsplit * kMqRows;
+  for (int idx = threadIdx.x; idx < nrows * (D / 4); idx += blockDim.x) {
+    const int rr = idx / (D / 4), quad = idx % (D / 4);
+    float M = -INFINITY;
+    for (int k = 0; k < a.nsplit; ++k) M = fmaxf(M, a.ws_m[base + k * kMqRows + rr]);
+    f32x4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
+    float den = 0.0f;
+    for (int k = 0; k < a.nsplit; ++k) {
+      const int64_t pr = base + k * kMqRows + rr;
+      const float mk = a.ws_m[pr];
+      const float w = mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk - M);
+      num += w * *reinterpret_cast<const f32x4_t*>(a.ws_acc + pr * D + 4 * quad);
+      den += w * a.ws_l[pr];
+    }
+    const int h = g * G + rr % G;
+    float* o = a.out + (static_cast<int64_t>(q0 + rr / G) * a.num_q_heads + h) * D + 4 * quad;
+    *reinterpret_cast<f32x4_t*>(o) = num / den;
+  }
+}
+
+template <int D>
+hipError_t launch_combine(const MultiArgs& a, int G, int units, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(units)), block(256);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((multi_combine_kernel<D, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((multi_combine_kernel<D, 2>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((multi_combine_kernel<D, 4>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((multi_combine_kernel<D, 8>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Split plan: a (sequence, KV head) whose rows fit one workgroup is cut into
+// enough context splits for about kMqSplitTarget workgroups in all, each at
+// least kMqMinSplit tokens, so that few long sequences still fill the chip.
+constexpr int kMqSplitTarget = 2048;
+constexpr int kMqMinSplit = 256;
+struct MultiPlan {
+  int nsplit = 1;
+  int split_len = 0;
+  size_t bytes = 0;
+};
+MultiPlan multi_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t G, int32_t head_dim, int32_t max_context_len,
+                     int32_t max_query_len) {
+  MultiPlan p;
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  if (units <= 0 || static_cast<int64_t>(max_query_len) * G > kMqRows || max_context_len < 2 * kMqMinSplit) return p;
+  int64_t ns = (kMqSplitTarget + units - 1) / units;
+  ns = ns < max_context_len / kMqMinSplit ? ns : max_context_len / kMqMinSplit;
+  if (ns <= 1) return p;
+  const int64_t len = ((max_context_len + ns - 1) / ns + kMqChunk - 1) / kMqChunk * kMqChunk;
+  p.nsplit = static_cast<int>((max_context_len + len - 1) / len);
+  if (p.nsplit <= 1) {
+    p.nsplit = 1;
+    return p;
+  }
+  p.split_len = static_cast<int>(len);
+  const int64_t rows = units * p.nsplit * kMqRows;
+  p.bytes = static_cast<size_t>(rows) * (head_dim + 2) * sizeof(float);
+  return p;
 }
 
 template <class DT, int D>
@@ -372,7 +494,8 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
                                                  int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads,
                                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                                  int32_t max_blocks, int32_t max_context_len, int32_t max_query_len,
-                                                 float scale, int32_t kv_dtype, hipStream_t stream) {
+                                                 float scale, void* workspace, size_t workspace_bytes,
+                                                 int32_t kv_dtype, hipStream_t stream) {
   if (item_size(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_query_rows < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks <= 0 || max_context_len < 0 || max_query_len < 0 || num_kv_heads > 65535)
@@ -390,9 +513,12 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
 
-  const int64_t rows_per_wg = 16 * kMqWaves;
-  const int64_t wg_per_seq = (static_cast<int64_t>(max_query_len) * G + rows_per_wg - 1) / rows_per_wg;
-  if (wg_per_seq * num_seqs * num_kv_heads > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  const int64_t wg_per_seq = (static_cast<int64_t>(max_query_len) * G + kMqRows - 1) / kMqRows;
+  // Split the context only when a workspace is given and the plan asks for it.
+  MultiPlan plan = multi_plan(num_seqs, num_kv_heads, G, head_dim, max_context_len, max_query_len);
+  if (!workspace) plan = MultiPlan{};
+  if (plan.nsplit > 1 && (workspace_bytes < plan.bytes || !aligned16(workspace))) return PKV_ERR_WORKSPACE;
+  if (wg_per_seq * plan.nsplit * num_seqs * num_kv_heads > INT32_MAX) return PKV_ERR_INVALID_ARG;
   MultiArgs a{};
   a.out = out;
   a.q = q;
@@ -410,10 +536,30 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   a.max_context_len = max_context_len;
   a.max_query_len = max_query_len;
   a.wg_per_seq = static_cast<int>(wg_per_seq);
+  a.nsplit = plan.nsplit;
+  a.split_len = plan.split_len;
+  if (plan.nsplit > 1) {
+    const int64_t rows = static_cast<int64_t>(num_seqs) * num_kv_heads * plan.nsplit * kMqRows;
+    a.ws_acc = static_cast<float*>(workspace);
+    a.ws_m = a.ws_acc + rows * head_dim;
+    a.ws_l = a.ws_m + rows;
+  }
   a.c = scale * 1.4426950408889634f;
-  const dim3 grid(static_cast<unsigned>(wg_per_seq * num_seqs * num_kv_heads));
+  const dim3 grid(static_cast<unsigned>(wg_per_seq * plan.nsplit * num_seqs * num_kv_heads));
   const dim3 block(static_cast<unsigned>(kMqWaves * kWave));
-  const hipError_t err = kv_dtype == PKV_BF16 ? launch_multi<BF16>(a, head_dim, G, grid, block, stream)
-                                              : launch_multi<F32>(a, head_dim, G, grid, block, stream);
+  hipError_t err = kv_dtype == PKV_BF16 ? launch_multi<BF16>(a, head_dim, G, grid, block, stream)
+                                        : launch_multi<F32>(a, head_dim, G, grid, block, stream);
+  if (err == hipSuccess && plan.nsplit > 1) {
+    const int units = num_seqs * num_kv_heads;
+    err = head_dim == 64 ? launch_combine<64>(a, G, units, stream) : launch_combine<128>(a, G, units, stream);
+  }
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                      int32_t head_dim, int32_t max_context_len, int32_t max_query_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 ||
+      max_context_len < 0 || max_query_len < 0)
+    return 0;
+  return multi_plan(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim, max_context_len, max_query_len).bytes;
 }

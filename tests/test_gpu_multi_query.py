@@ -91,15 +91,21 @@ class Batch:
         assert np.array_equal(t, ot) and np.array_equal(l, ol)
         return t, l
 
-    def multi(self, runs, q, tables=None, lens=None, query_start=None, max_query_len=None, out=None):
+    def multi(self, runs, q, tables=None, lens=None, query_start=None, max_query_len=None, out=None, split=False):
         t, l = self.tables() if tables is None else (tables, lens)
         starts = np.concatenate([[0], np.cumsum(runs)]).astype(np.int32) if query_start is None else query_start
         T = q.shape[0]
         out = torch.full((T, self.Hq, self.d), float("nan"), dtype=torch.float32, device="cuda") if out is None else out
+        mql = int(max(runs) if max_query_len is None else max_query_len)
+        ws = None
+        if split:
+            nbytes = self.pk.pkv_attention_multi_workspace_bytes(len(l), self.Hq, self.Hkv, self.d, int(max(l.max(), 1)),
+                                                                 mql)
+            assert nbytes > 0, "the plan does not split this batch"
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.pk.pkv_paged_attention_multi(out, to_dev(q, self.dt), *self.caches, torch.from_numpy(t).cuda(),
                                           torch.from_numpy(l).cuda(), torch.from_numpy(starts).cuda(),
-                                          int(max(l.max(), 1)), int(max(runs) if max_query_len is None else max_query_len),
-                                          1.0 / np.sqrt(self.d))
+                                          int(max(l.max(), 1)), mql, 1.0 / np.sqrt(self.d), workspace=ws)
         torch.cuda.synchronize()
         return out.cpu().numpy(), t, l, starts
 
@@ -309,3 +315,65 @@ def test_repeated_calls_and_graph_replays_are_bitwise_stable():
             call()
             torch.cuda.synchronize()
             assert torch.equal(out, first), i
+
+
+
+SPLIT_GRID = [(dt, G, B) for dt in ("f32", "bf16") for G in (1, 4, 8) for B in (16, 32)]
+
+
+@pytest.mark.parametrize("dt,G,B", SPLIT_GRID)
+def test_split_context_runs(dt, G, B):
+    """Few sequences with long contexts: each (sequence, KV head) is cut into context splits combined by
+    log-sum-exp weights.  Lengths put runs across split boundaries, inside the first split, and past every split
+    of shorter sequences; the split result matches the oracle and the unsplit call."""
+    rng = wl.rng_for(300 + G + B, 1)
+    lens = [2600, 1283, 770, 514, 257, 33, 1]
+    runs = [min(n, int(x)) for n, x in zip(lens, rng.integers(1, 64 // G + 1, size=len(lens)))]
+    Hkv = 2
+    say(f"case {dt} G={G} B={B}: lens={lens} runs={runs}")
+    b = Batch(lens, G * Hkv, Hkv, 128, B, dt, seed=40 + G + B)
+    q = wl.draw_values(wl.rng_for(41, wl.STREAM_Q, G, B), (sum(runs), G * Hkv, 128), dt)
+    out, t, l, starts = b.multi(runs, q, split=True)
+    ref = b.oracle(q, t, l, starts)
+    check_close(out, ref, dt, "split")
+    whole, *_ = b.multi(runs, q)
+    check_close(whole, ref, dt, "unsplit")
+    assert np.max(np.abs(out - whole)) <= (1e-5 if dt == "f32" else 1e-3)
+
+
+def test_split_context_long_verification():
+    """Verification of 4 drafted tokens over 8192-token contexts (4 sequences, 32/8 heads, bf16): 32 pairs of
+    (sequence, KV head), each cut into splits, against the oracle."""
+    lens = [8192, 8190, 6001, 8192]
+    runs = [4, 4, 4, 4]
+    b = Batch(lens, 32, 8, 128, 16, "bf16", seed=51)
+    q = wl.draw_values(wl.rng_for(52, wl.STREAM_Q), (16, 32, 128), "bf16")
+    out, t, l, starts = b.multi(runs, q, split=True)
+    check_close(out, b.oracle(q, t, l, starts), "bf16", "long verification, split")
+
+
+def test_split_context_edges():
+    import paged_kv_cache_physical_amd as pk
+    b = Batch([1500, 900, 700], 8, 2, 64, 16, "f32", seed=61)
+    t, l = b.tables()
+    runs = [3, 3, 3]
+    q = wl.draw_values(wl.rng_for(62, wl.STREAM_Q), (9, 8, 64), "f32")
+    starts = np.array([0, 3, 6, 9], np.int32)
+    nbytes = pk.pkv_attention_multi_workspace_bytes(3, 8, 2, 64, 1500, 3)
+    assert nbytes > 0
+    args = lambda ws: (torch.empty((9, 8, 64), dtype=torch.float32, device="cuda"), to_dev(q, "f32"), *b.caches,
+                       torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(), torch.from_numpy(starts).cuda(), 1500, 3,
+                       0.125)
+    with pytest.raises(pk.PkvError):  # a workspace too small for the planned split
+        pk.pkv_paged_attention_multi(*args(None), workspace=torch.empty(nbytes - 16, dtype=torch.uint8, device="cuda"))
+    # a bad block id in the middle of sequence 0, and sequence 2 made longer than its table (its extra tokens
+    # read the -1 padding): NaN rows for both, the rest exact
+    t2 = t.copy()
+    t2[0, 40] = b.nb + 3
+    l2 = l.copy()
+    l2[2] = 1501
+    sentinel = torch.full((9, 8, 64), 7.0, dtype=torch.float32, device="cuda")
+    out, *_ = b.multi(runs, q, tables=t2, lens=l2, out=sentinel, split=True)
+    assert np.all(np.isnan(out[0:3])) and np.all(np.isnan(out[6:9]))
+    ref = b.oracle(q[3:6], t[1:2], l[1:2], np.array([0, 3], np.int32))
+    check_close(out[3:6], ref, "f32", "sequence 1")
