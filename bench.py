@@ -172,14 +172,32 @@ def host_allocator_step_us(w, reps=20):
     seqs = np.asarray(sorted(ids), dtype=np.int32)
     ones = np.ones(len(seqs), dtype=np.int32)
     # table width sized once, with room for the appended tokens (a server keeps a fixed-width table)
-    mb = max(pool.info(int(i))[1] for i in seqs) + reps // w.spec.block_size + 1
+    mb = max(pool.info(int(i))[1] for i in seqs) + 2 * reps // w.spec.block_size + 2
     t = []
     for _ in range(reps):
         t0 = time.perf_counter()
         pool.append(seqs, ones)
         pool.block_tables(seqs, mb)
         t.append(time.perf_counter() - t0)
-    return 1e6 * float(np.median(t))
+    # the same two C calls with buffers allocated once, as a native serving loop makes them
+    import ctypes
+    from paged_kv_cache_physical_amd import _lib
+    L = _lib.lib()
+    n = len(seqs)
+    slots = np.empty(n, np.int64)
+    pairs = np.empty((n, 2), np.int32)
+    tables = np.empty((n, mb + reps // w.spec.block_size + 1), np.int32)
+    lens = np.empty(n, np.int32)
+    ncow = ctypes.c_int32()
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    ps, po, pslot, ppair, ptab, plen = P(seqs), P(ones), P(slots), P(pairs), P(tables), P(lens)
+    tc = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        L.pkv_append_tokens(pool.handle, ps, po, n, None, pslot, n, ppair, n, ctypes.byref(ncow))
+        L.pkv_block_tables(pool.handle, ps, n, tables.shape[1], ptab, plen)
+        tc.append(time.perf_counter() - t0)
+    return 1e6 * float(np.median(t)), 1e6 * float(np.median(tc))
 
 
 def measure_prefix_cache(requests=256, stems=8, block_size=16):
@@ -520,7 +538,7 @@ def main():
     if args.copy_probe:
         copy_probe(stream)
     try:
-        head["host_allocator_us_per_step"] = host_allocator_step_us(w)
+        head["host_allocator_us_per_step"], head["host_allocator_c_us_per_step"] = host_allocator_step_us(w)
     except Exception as e:  # a full pool cannot take another token per sequence
         log(f"[bench] host allocator step not timed: {e}")
     ceiling = hbm_read_ceiling(stream)
@@ -551,6 +569,7 @@ def main():
         "seq_steps_per_s": round(head["seq_steps_per_s"], 1),
         "pct_hbm_peak_step": round(100 * head["kv_gbps_step"] / HBM_PEAK_GBPS, 2),
         "host_allocator_us_per_step": round(head.get("host_allocator_us_per_step", float("nan")), 2),
+        "host_allocator_c_us_per_step": round(head.get("host_allocator_c_us_per_step", float("nan")), 2),
         "kernels_us": {"paged_decode_partitions": round(head["partition_kernel_us"]["mean"], 2),
                        "lse_reduce": round(head["reduce_kernel_us"], 2),
                        "reshape_and_cache": round(head["reshape_and_cache_us"], 2),

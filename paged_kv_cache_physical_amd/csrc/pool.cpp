@@ -121,6 +121,13 @@ struct pkv_pool {
   std::vector<char> keyed;
   std::vector<uint64_t> bkey, bparent;
   std::vector<int32_t> btokens;
+  // Scratch of pkv_append_tokens, kept between calls: a stamp per sequence id
+  // (listed in this batch), and per device block the copies earlier in the
+  // batch have taken from its refcount.
+  std::vector<uint32_t> seq_stamp;
+  uint32_t stamp = 0;
+  std::vector<int32_t> blk_drop;
+  std::vector<int32_t> blk_touched;
 
   Seq* get(int32_t id) {
     if (id < 0 || static_cast<size_t>(id) >= seqs.size() || !seqs[id].live) return nullptr;
@@ -290,10 +297,27 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
   const int64_t B = pool->block_size;
 
   // Pass 1: validate (argument errors first, then unknown ids), then count
-  // what the batch needs.
-  std::unordered_map<int32_t, int32_t> listed;
+  // what the batch needs.  Duplicates are found with the stamp of this call;
+  // ids that are not sequence ids of the pool are compared among themselves.
+  if (pool->seq_stamp.size() < pool->seqs.size()) pool->seq_stamp.resize(pool->seqs.size(), 0);
+  if (++pool->stamp == 0) {
+    std::fill(pool->seq_stamp.begin(), pool->seq_stamp.end(), 0);
+    pool->stamp = 1;
+  }
+  std::vector<int32_t> strays;
   for (int32_t i = 0; i < n; ++i) {
-    if (counts[i] < 0 || !listed.emplace(seqs[i], i).second) return PKV_ERR_INVALID_ARG;
+    if (counts[i] < 0) return PKV_ERR_INVALID_ARG;
+    const int32_t id = seqs[i];
+    if (id >= 0 && static_cast<size_t>(id) < pool->seq_stamp.size()) {
+      if (pool->seq_stamp[id] == pool->stamp) return PKV_ERR_INVALID_ARG;
+      pool->seq_stamp[id] = pool->stamp;
+    } else {
+      strays.push_back(id);
+    }
+  }
+  if (strays.size() > 1) {
+    std::sort(strays.begin(), strays.end());
+    if (std::adjacent_find(strays.begin(), strays.end()) != strays.end()) return PKV_ERR_INVALID_ARG;
   }
   for (int32_t i = 0; i < n; ++i) {
     if (!pool->get(seqs[i])) return PKV_ERR_NO_SUCH_SEQ;
@@ -301,7 +325,7 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
   for (int32_t i = 0; i < n; ++i) {
     if (pool->seqs[seqs[i]].on_host) return PKV_ERR_SWAPPED;
   }
-  std::unordered_map<int32_t, int32_t> dropped;  // refcount drops from copies earlier in the batch
+  if (pool->blk_drop.size() < static_cast<size_t>(pool->dev.num_blocks)) pool->blk_drop.assign(pool->dev.num_blocks, 0);
   int64_t total_slots = 0, need = 0;
   int32_t cows = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -311,16 +335,16 @@ pkv_status pkv_append_tokens(pkv_pool* pool, const int32_t* seqs, const int32_t*
     if (c == 0) continue;
     if (L % B != 0) {
       const int32_t last = s->table.back();
-      auto it = dropped.find(last);
-      const int32_t rc = pool->dev.refcount[last] - (it == dropped.end() ? 0 : it->second);
-      if (rc > 1) {
+      if (pool->dev.refcount[last] - pool->blk_drop[last] > 1) {  // net of copies earlier in the batch
         ++need;
         ++cows;
-        ++dropped[last];
+        if (pool->blk_drop[last]++ == 0) pool->blk_touched.push_back(last);
       }
     }
     need += ceil_div(L + c, B) - ceil_div(L, B);
   }
+  for (int32_t b : pool->blk_touched) pool->blk_drop[b] = 0;
+  pool->blk_touched.clear();
   if (total_slots > 0 && (!out_slots || slots_cap < total_slots)) return PKV_ERR_INVALID_ARG;
   if (cows > 0 && (!out_cow_pairs || cow_cap < cows)) {
     *out_n_cow = cows;

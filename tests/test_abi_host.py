@@ -501,3 +501,22 @@ def test_truncate_matches_oracle(libpkv):
                 else:
                     assert np.array_equal(c.swap_out(group) if out else c.swap_in(group), po)
             same_state(c, o)
+
+
+def test_duplicate_and_unknown_ids_in_one_append(libpkv):
+    """A sequence listed twice is an argument error before any unknown id is reported, whether or not the
+    id exists, on both pools."""
+    c, o = pk.Pool(8, 4), al.BlockPool(8, 4)
+    c.create(), o.create()
+    for seqs, err in (([99, 99], pk.InvalidArg), ([-3, -3], pk.InvalidArg), ([0, 0], pk.InvalidArg),
+                      ([99, -3], pk.NoSuchSeq), ([0, 7, 0], pk.InvalidArg)):
+        with pytest.raises({pk.InvalidArg: al.InvalidArg, pk.NoSuchSeq: al.NoSuchSeq}[err]):
+            o.append(seqs, [1] * len(seqs))
+        with pytest.raises(err):
+            c.append(seqs, [1] * len(seqs))
+        same_state(c, o)
+    # many calls in a row keep their duplicate checks separate
+    for _ in range(5):
+        c.append([0], [1])
+        o.append([0], [1])
+    same_state(c, o)
