@@ -385,45 +385,64 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
   }
 }
 
-// Log-sum-exp combination of the split partials of one (sequence, KV head):
-// out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k with M = max_k m_k; a
-// split that saw no token of a row has m = -inf and weighs nothing.  Runs the
-// attention kernel did not write, or wrote as NaN, are skipped.
+// Log-sum-exp combination of the split partials of one row of one (sequence,
+// KV head): out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k with
+// M = max_k m_k; a split that saw none of the row's tokens has m = -inf and
+// weighs nothing.  One workgroup per (pair, row slot): wave 0 turns the
+// splits' maxima and sums into weights (one split per lane), then every
+// thread sums a share of the splits for four dims and LDS adds the shares.
+// Runs the attention kernel did not write, or wrote as NaN, are skipped.
+constexpr int kMqMaxSplits = 64;  // one split per lane of the weighting wave
 template <int D, int G>
 __global__ __launch_bounds__(256) void multi_combine_kernel(const MultiArgs a) {
-  const int sg = blockIdx.x;
+  constexpr int NQ = D / 4;       // four-dim quads of a row
+  constexpr int KG = 256 / NQ;    // split groups: thread (kg, quad)
+  __shared__ float wsh[kMqMaxSplits];
+  __shared__ float inv_den;
+  __shared__ f32x4_t red[KG][NQ];
+  const int sg = blockIdx.x / kMqRows, rr = blockIdx.x % kMqRows;
   const int s = sg / a.num_kv_heads, g = sg % a.num_kv_heads;
   const int q0 = mq_ld(a.query_start, s);
   const int qs = mq_ld(a.query_start, s + 1) - q0;
   if (q0 < 0 || qs <= 0 || static_cast<int64_t>(q0) + qs > a.num_query_rows) return;
   const int n = mq_ld(a.context_lens, s);
   if (n > a.max_context_len || static_cast<int64_t>(n) > static_cast<int64_t>(a.max_blocks) * a.block_size ||
-      qs > n || qs > a.max_query_len)
+      qs > n || qs > a.max_query_len || rr >= qs * G)  // the same for the whole workgroup
     return;
-  const int nrows = qs * G;  // at most kMqRows when the context is split
-  const int64_t base = static_cast<int64_t>(sg) * a.nsplit * kMqRows;
-  for (int idx = threadIdx.x; idx < nrows * (D / 4); idx += blockDim.x) {
-    const int rr = idx / (D / 4), quad = idx % (D / 4);
-    float M = -INFINITY;
-    for (int k = 0; k < a.nsplit; ++k) M = fmaxf(M, a.ws_m[base + k * kMqRows + rr]);
-    f32x4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
-    float den = 0.0f;
-    for (int k = 0; k < a.nsplit; ++k) {
-      const int64_t pr = base + k * kMqRows + rr;
-      const float mk = a.ws_m[pr];
-      const float w = mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk - M);
-      num += w * *reinterpret_cast<const f32x4_t*>(a.ws_acc + pr * D + 4 * quad);
-      den += w * a.ws_l[pr];
-    }
+  const int64_t base = static_cast<int64_t>(sg) * a.nsplit * kMqRows + rr;  // split k's row: base + k * kMqRows
+  const int tid = threadIdx.x;
+  if (tid < kWave) {
+    const bool in = tid < a.nsplit;
+    const float m = in ? a.ws_m[base + tid * kMqRows] : -INFINITY;
+    const float l = in ? a.ws_l[base + tid * kMqRows] : 0.0f;
+    float M = m;
+    for (int o = kWave / 2; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float w = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    float den = w * l;
+    for (int o = kWave / 2; o > 0; o >>= 1) den += __shfl_xor(den, o);
+    if (in) wsh[tid] = w;
+    if (tid == 0) inv_den = 1.0f / den;
+  }
+  __syncthreads();
+  const int kg = tid / NQ, quad = tid % NQ;
+  f32x4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int k = kg; k < a.nsplit; k += KG)
+    sum += wsh[k] * *reinterpret_cast<const f32x4_t*>(a.ws_acc + (base + k * kMqRows) * D + 4 * quad);
+  red[kg][quad] = sum;
+  __syncthreads();
+  if (kg == 0) {
+#pragma unroll
+    for (int j = 1; j < KG; ++j) sum += red[j][quad];
     const int h = g * G + rr % G;
     float* o = a.out + (static_cast<int64_t>(q0 + rr / G) * a.num_q_heads + h) * D + 4 * quad;
-    *reinterpret_cast<f32x4_t*>(o) = num / den;
+    *reinterpret_cast<f32x4_t*>(o) = sum * inv_den;
   }
 }
 
 template <int D>
 hipError_t launch_combine(const MultiArgs& a, int G, int units, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(units)), block(256);
+  const dim3 grid(static_cast<unsigned>(units) * kMqRows), block(256);
   switch (G) {
     case 1: hipLaunchKernelGGL((multi_combine_kernel<D, 1>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((multi_combine_kernel<D, 2>), grid, block, 0, stream, a); break;
@@ -436,7 +455,8 @@ hipError_t launch_combine(const MultiArgs& a, int G, int units, hipStream_t stre
 
 // Split plan: a (sequence, KV head) whose rows fit one workgroup is cut into
 // enough context splits for about kMqSplitTarget workgroups in all, each at
-// least kMqMinSplit tokens, so that few long sequences still fill the chip.
+// least kMqMinSplit tokens and at most kMqMaxSplits of them, so that few long
+// sequences still fill the chip.
 constexpr int kMqSplitTarget = 2048;
 constexpr int kMqMinSplit = 256;
 struct MultiPlan {
@@ -451,6 +471,7 @@ MultiPlan multi_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t G, int32_t 
   if (units <= 0 || static_cast<int64_t>(max_query_len) * G > kMqRows || max_context_len < 2 * kMqMinSplit) return p;
   int64_t ns = (kMqSplitTarget + units - 1) / units;
   ns = ns < max_context_len / kMqMinSplit ? ns : max_context_len / kMqMinSplit;
+  ns = ns < kMqMaxSplits ? ns : kMqMaxSplits;
   if (ns <= 1) return p;
   const int64_t len = ((max_context_len + ns - 1) / ns + kMqChunk - 1) / kMqChunk * kMqChunk;
   p.nsplit = static_cast<int>((max_context_len + len - 1) / len);
