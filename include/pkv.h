@@ -284,6 +284,11 @@ pkv_status pkv_pool_host_free_list(const pkv_pool* pool, int32_t* out, int32_t c
  * Device calls (HIP, gfx950).  All pointers are device memory owned by the
  * caller, 16-byte aligned (pkv_swap_blocks also takes page-locked host
  * memory); `stream` may be NULL (the default stream).
+ *
+ * Debug mode: with the environment variable PKV_DEBUG set to anything but ""
+ * or "0" (read once per process), pkv_reshape_and_cache and pkv_copy_blocks
+ * also copy their slots / pairs to the host, wait for the stream, and return
+ * INVALID_ARG when two of them would write the same slot / block.
  * ------------------------------------------------------------------------- */
 
 /* Write token i's key and value (k_new, v_new: [num_tokens][H_kv][d], the
@@ -292,7 +297,7 @@ pkv_status pkv_pool_host_free_list(const pkv_pool* pool, int32_t* out, int32_t c
  * ([P4] KV-cache introduction; [P2] core idea item 3).
  * slots: device int64[num_tokens]; a slot of -1 is skipped, a slot at or past
  * num_blocks * B is skipped as well.  Slots must be distinct within a call
- * (two writers of one slot race).
+ * (two writers of one slot race; checked in debug mode).
  * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
 pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                  const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
@@ -302,8 +307,9 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_c
 /* Copy whole blocks (every head and slot of both caches) src -> dst for each
  * pair: the device half of copy-on-write ([P3] section 3).
  * pairs: device int32[n_pairs][2] as returned by pkv_append_tokens.  The dst
- * blocks must be distinct and no dst may be another pair's src (the pool never
- * produces either).  Pairs with an id out of [0, num_blocks) are skipped.
+ * blocks must be distinct (checked in debug mode) and no dst may be another
+ * pair's src (the pool never produces either).  Pairs with an id out of
+ * [0, num_blocks) are skipped.
  * block_bytes: bytes of one block in one cache, H_kv * B * d * scalar size.
  * Errors: INVALID_ARG (block_bytes not a positive multiple of 16), HIP. */
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,

@@ -3,6 +3,10 @@
 // swapping between device and host memory, and a plain streaming-read probe
 // used to measure the HBM read ceiling.
 
+#include <algorithm>
+#include <cstdlib>
+#include <vector>
+
 #include "device_common.h"
 
 namespace pkv {
@@ -183,6 +187,35 @@ hipError_t launch_write_last_token(const void* k_new, const void* v_new, void* k
 
 using namespace pkv;
 
+namespace {
+// Debug validation, on when the environment variable PKV_DEBUG is set to
+// anything but "" or "0" (read once): the write targets of one call are copied
+// to the host (the call then waits for its stream) and must be distinct, since
+// two writers of one slot or one block would race.
+bool debug_checks() {
+  static const bool on = [] {
+    const char* v = std::getenv("PKV_DEBUG");
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+  }();
+  return on;
+}
+
+template <class T>
+bool fetch(std::vector<T>& host, const T* dev, size_t count, hipStream_t stream) {
+  host.resize(count);
+  return hipMemcpyAsync(host.data(), dev, count * sizeof(T), hipMemcpyDeviceToHost, stream) == hipSuccess &&
+         hipStreamSynchronize(stream) == hipSuccess;
+}
+
+// Distinct values among those in [0, limit) (others are skipped by the kernels).
+template <class T>
+bool distinct_in_range(std::vector<T> v, int64_t limit) {
+  v.erase(std::remove_if(v.begin(), v.end(), [&](T x) { return x < 0 || x >= limit; }), v.end());
+  std::sort(v.begin(), v.end());
+  return std::adjacent_find(v.begin(), v.end()) == v.end();
+}
+}  // namespace
+
 extern "C" {
 
 pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -196,6 +229,11 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_c
   if (!k_new || !v_new || !k_cache || !v_cache || !slots) return PKV_ERR_INVALID_ARG;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_ERR_INVALID_ARG;
+  if (debug_checks()) {
+    std::vector<int64_t> h;
+    if (!fetch(h, slots, static_cast<size_t>(num_tokens), stream)) return PKV_ERR_HIP;
+    if (!distinct_in_range(h, static_cast<int64_t>(num_blocks) * block_size)) return PKV_ERR_INVALID_ARG;
+  }
   const int64_t waves = static_cast<int64_t>(num_tokens) * num_kv_heads;  // one per (token, head)
   const int64_t grid = ceil_div64(waves, 4);
   if (grid > 0x7fffffff) return PKV_ERR_INVALID_ARG;
@@ -212,6 +250,15 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
   if (n_pairs < 0 || num_blocks <= 0 || block_bytes <= 0 || block_bytes % 16) return PKV_ERR_INVALID_ARG;
   if (n_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !pairs || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
+  if (debug_checks()) {
+    std::vector<int32_t> h;
+    if (!fetch(h, pairs, 2 * static_cast<size_t>(n_pairs), stream)) return PKV_ERR_HIP;
+    std::vector<int32_t> dst;
+    for (int32_t i = 0; i < n_pairs; ++i) {
+      if (h[2 * i] >= 0 && h[2 * i] < num_blocks) dst.push_back(h[2 * i + 1]);  // pairs the kernel copies
+    }
+    if (!distinct_in_range(dst, num_blocks)) return PKV_ERR_INVALID_ARG;
+  }
   const int64_t n16 = block_bytes / 16;
   const int64_t splits = ceil_div64(n16, 256);
   const unsigned z = static_cast<unsigned>(splits < 16 ? splits : 16);

@@ -145,3 +145,44 @@ def test_swap_blocks_refuses_memory_the_gpu_cannot_reach(libpkv):
     assert call(kd, hk, 4, 4096, pairs) == _lib.PKV_ERR_INVALID_ARG  # past the host allocation
     assert call(kd, hk, 1 << 20, 4, pairs) == _lib.PKV_ERR_INVALID_ARG  # past the device allocation
     torch.cuda.synchronize()
+
+
+DEBUG_CHILD = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import paged_kv_cache_physical_amd as pk
+kc, vc = pk.empty_caches(8, 2, 16, 64, "bf16")
+k = torch.randn(3, 2, 64, device="cuda").to(torch.bfloat16)
+v = torch.randn(3, 2, 64, device="cuda").to(torch.bfloat16)
+def refused(fn):
+    try:
+        fn()
+    except pk.InvalidArg:
+        return True
+    return False
+# two writers of slot 5 are refused; a skipped (-1) or out-of-range slot may repeat
+assert refused(lambda: pk.pkv_reshape_and_cache(k, v, kc, vc, torch.tensor([5, 7, 5], device="cuda"), 16))
+pk.pkv_reshape_and_cache(k, v, kc, vc, torch.tensor([5, -1, -1], device="cuda"), 16)
+pk.pkv_reshape_and_cache(k, v, kc, vc, torch.tensor([1, 999, 999], device="cuda"), 16)
+torch.cuda.synchronize()
+assert torch.equal(kc.view(8, 2, 8, 16, 8)[0, :, :, 5, :].reshape(2, 64), k[0])
+# two copies into block 3 are refused; distinct targets pass
+assert refused(lambda: pk.pkv_copy_blocks(kc, vc, torch.tensor([[0, 3], [1, 3]], dtype=torch.int32, device="cuda")))
+pk.pkv_copy_blocks(kc, vc, torch.tensor([[0, 3], [1, 4], [9, 4]], dtype=torch.int32, device="cuda"))
+torch.cuda.synchronize()
+assert torch.equal(kc[3].view(torch.int16), kc[0].view(torch.int16))
+print("debug checks ok", flush=True)
+"""
+
+
+def test_debug_mode_refuses_duplicate_write_targets():
+    """With PKV_DEBUG set, reshape_and_cache and copy_blocks refuse two writers of one slot / block before
+    launching (a child process: the setting is read once per process)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PKV_DEBUG="1")
+    r = subprocess.run([sys.executable, "-c", DEBUG_CHILD, root], capture_output=True, text=True, timeout=240, env=env)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-3000:])
+    assert "debug checks ok" in r.stdout
