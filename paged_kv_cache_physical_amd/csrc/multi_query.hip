@@ -25,6 +25,13 @@
 //       high and a low bf16 term so the product keeps fp32 accuracy).
 // Past the last chunk the loads go through a size-0 buffer resource, so every
 // path issues the same loads and the compiler's waits stay exact.
+//
+// Workgroups are renumbered so that each XCD (each with its own L2) takes one
+// contiguous run of (sequence, KV head, row block) units.  When the batch has
+// few (sequence, KV head) pairs whose rows fit one workgroup (verification of
+// a few drafted tokens over long contexts), a caller-provided workspace lets
+// each pair's context be cut into splits computed apart; multi_combine_kernel
+// then merges the split partials with log-sum-exp weights.
 
 #include <type_traits>
 
@@ -39,10 +46,6 @@ __device__ __forceinline__ int32_t mq_ld(const int32_t* p, int64_t i) { return (
 __device__ __forceinline__ uint4 mq_load16(__amdgpu_buffer_rsrc_t r, int voff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ uint2 mq_load8(__amdgpu_buffer_rsrc_t r, int voff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
-  return make_uint2(v[0], v[1]);
 }
 
 constexpr int kMqWaves = 4;  // waves per workgroup
