@@ -377,3 +377,66 @@ def test_split_context_edges():
     assert np.all(np.isnan(out[0:3])) and np.all(np.isnan(out[6:9]))
     ref = b.oracle(q[3:6], t[1:2], l[1:2], np.array([0, 3], np.int32))
     check_close(out[3:6], ref, "f32", "sequence 1")
+
+
+def test_preemption_by_recomputation_through_the_prefix_cache():
+    """Preemption by recomputation ([P4] "Preemption"): a request's blocks are freed; while it waits, other
+    requests take some of them (evicting their keys); on re-admission the prompt maps what the prefix cache still
+    holds, only the lost positions' K/V are written again and their rows recomputed (runs of queries), and the
+    next decode step equals the oracle and the step before preemption."""
+    import paged_kv_cache_physical_amd as pk
+    B, Hq, Hkv, d, dt = 16, 32, 8, 128, "bf16"
+    pr = wl.PrefixRequests(seed=71, num_requests=6, num_stems=2, stem_range=(300, 600), tail_range=(40, 120),
+                           num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, kv_dtype=dt)
+    lens = [len(pr.prompt(r)) for r in range(6)]
+    nb = 67  # sized so that the waiting request's tail blocks are taken while its stem stays cached
+    pool = pk.Pool(nb, B, wl.rng_for(72, wl.STREAM_PERM).permutation(nb).astype(np.int32))
+    caches = pk.empty_caches(nb, Hkv, B, d, dt)
+    scale = 1.0 / np.sqrt(d)
+
+    def admit(r):
+        ids = pr.prompt(r)
+        sid, hit = pool.create_prefixed(ids)
+        slots, pairs = pool.append([sid], [len(ids) - hit], token_ids=ids[hit:])
+        assert pairs.shape == (0, 2)
+        k, v = pr.kv(r)
+        pk.pkv_reshape_and_cache(to_dev(k[hit:], dt), to_dev(v[hit:], dt), *caches, torch.from_numpy(slots).cuda(), B)
+        return sid, hit
+
+    def decode(sid, q):
+        t, l = pool.block_tables([sid], max(-(-n // B) for n in lens))
+        out = torch.empty((1, Hq, d), dtype=torch.float32, device="cuda")
+        pk.pkv_paged_attention_multi(out, to_dev(q, dt), *caches, torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(),
+                                     torch.tensor([0, 1], dtype=torch.int32, device="cuda"), int(l.max()), 1, scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    victim = 0
+    sid, _ = admit(victim)
+    q = wl.draw_values(wl.rng_for(73, wl.STREAM_Q), (1, Hq, d), dt)
+    before = decode(sid, q)
+    pool.free_seq(sid)  # preempted: its blocks wait at the tail of the free queue, still keyed
+    sharer, shared = admit(2)  # request 2 has the same stem: it maps the waiting stem blocks
+    assert shared == 320
+    other, _ = admit(1)  # request 1 drains the queue into the victim's tail blocks, evicting their keys
+    pool.free_seq(other)  # and finishes
+    sid2, hit = admit(victim)  # re-admission: the stem (held by request 2) is mapped, the rest is written again
+    n = lens[victim]
+    assert 0 < hit < n, (hit, n)  # part of the prompt survived, part was evicted
+    say(f"  re-admission mapped {hit} of {n} prompt tokens")
+    # the recomputed positions' own attention rows (the prefill of what was lost), against the oracle
+    t, l = pool.block_tables([sid2], max(-(-m // B) for m in lens))
+    qrun = wl.draw_values(wl.rng_for(74, wl.STREAM_Q), (n - hit, Hq, d), dt)
+    out = torch.empty((n - hit, Hq, d), dtype=torch.float32, device="cuda")
+    pk.pkv_paged_attention_multi(out, to_dev(qrun, dt), *caches, torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(),
+                                 torch.tensor([0, n - hit], dtype=torch.int32, device="cuda"), int(l.max()), n - hit, scale)
+    torch.cuda.synchronize()
+    k, v = (oc.to_f64(x, dt) for x in pr.kv(victim))
+    ref = np.stack([oa.attention_contiguous(oc.to_f64(qrun[i], dt), k[:hit + i + 1], v[:hit + i + 1], np.float32(scale))
+                    for i in range(n - hit)])
+    check_close(out.cpu().numpy(), ref, dt, "recomputed rows")
+    after = decode(sid2, q)
+    check_close(after, oa.attention_contiguous(oc.to_f64(q[0], dt), k, v, np.float32(scale))[None], dt, "decode after")
+    assert np.array_equal(after, before)  # the same tokens in other blocks: the same bits
+    pool.validate()
+    pool.free_seq(sharer)
