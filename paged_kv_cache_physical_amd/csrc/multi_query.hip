@@ -391,7 +391,7 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
 // Log-sum-exp combination of the split partials of one row of one (sequence,
 // KV head): out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k with
 // M = max_k m_k; a split that saw none of the row's tokens has m = -inf and
-// weighs nothing.  One workgroup per (pair, row slot): wave 0 turns the
+// weighs nothing.  One workgroup per (pair, row of the longest run): wave 0 turns the
 // splits' maxima and sums into weights (one split per lane), then every
 // thread sums a share of the splits for four dims and LDS adds the shares.
 // Runs the attention kernel did not write, or wrote as NaN, are skipped.
@@ -403,7 +403,8 @@ __global__ __launch_bounds__(256) void multi_combine_kernel(const MultiArgs a) {
   __shared__ float wsh[kMqMaxSplits];
   __shared__ float inv_den;
   __shared__ f32x4_t red[KG][NQ];
-  const int sg = blockIdx.x / kMqRows, rr = blockIdx.x % kMqRows;
+  const int row_slots = a.max_query_len * G;  // rows a pair can have (at most kMqRows when split)
+  const int sg = blockIdx.x / row_slots, rr = blockIdx.x % row_slots;
   const int s = sg / a.num_kv_heads, g = sg % a.num_kv_heads;
   const int q0 = mq_ld(a.query_start, s);
   const int qs = mq_ld(a.query_start, s + 1) - q0;
@@ -445,7 +446,7 @@ __global__ __launch_bounds__(256) void multi_combine_kernel(const MultiArgs a) {
 
 template <int D>
 hipError_t launch_combine(const MultiArgs& a, int G, int units, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(units) * kMqRows), block(256);
+  const dim3 grid(static_cast<unsigned>(units) * static_cast<unsigned>(a.max_query_len * G)), block(256);
   switch (G) {
     case 1: hipLaunchKernelGGL((multi_combine_kernel<D, 1>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((multi_combine_kernel<D, 2>), grid, block, 0, stream, a); break;
