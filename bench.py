@@ -379,8 +379,10 @@ def measure_multi(stream, reps=20, case=None):
         bt, cl = torch.from_numpy(tables).cuda(), torch.from_numpy(clens).cuda()
         wsb = pk.pkv_attention_multi_workspace_bytes(S, Hq, Hkv, d, int(lens.max()), int(runs.max()))
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+        # longest first: the order a scheduler that knows the lengths hands over
+        order = torch.from_numpy(np.argsort(-lens, kind="stable").astype(np.int32)).cuda()
         fn = lambda: pk.pkv_paged_attention_multi(o, q, kc, vc, bt, cl, starts, int(lens.max()), int(runs.max()),
-                                                  1.0 / np.sqrt(d), stream, workspace=ws)
+                                                  1.0 / np.sqrt(d), stream, workspace=ws, seq_order=order)
         with torch.cuda.stream(stream):
             for _ in range(3):
                 fn()
@@ -402,7 +404,7 @@ def measure_multi(stream, reps=20, case=None):
                                "frac": round(rec["kv_gbps"] / HBM_PEAK_GBPS, 4)}
         out[name] = rec
         log(f"[bench] multi {name}: {json.dumps(rec)}")
-        del kc, vc, q, o, ws
+        del kc, vc, q, o, ws, order
         torch.cuda.empty_cache()
     return out
 

@@ -410,6 +410,12 @@ pkv_status pkv_decode_step(const void* k_new, const void* v_new, float* out, con
  *     cache's scalar type.
  *   query_start: device int32 [num_seqs + 1], non-decreasing.
  *   block_tables, context_lens: as for pkv_paged_attention_decode.
+ *   seq_order: device int32 [num_seqs], a permutation of the sequences giving
+ *     the order in which their work starts (longest first evens out the end
+ *     of a ragged batch), or NULL for 0, 1, 2, ...  It changes scheduling
+ *     only, never the results.  An entry outside [0, num_seqs) is skipped;
+ *     a sequence the order leaves out is not computed (its rows are left as
+ *     they were, or unspecified when the call splits contexts).
  *   max_query_len: a bound on every q_s (it sizes the launch).
  *   workspace: device memory of workspace_bytes >= the value of
  *     pkv_attention_multi_workspace_bytes(...) for these sizes, 16-byte
@@ -427,7 +433,8 @@ pkv_status pkv_decode_step(const void* k_new, const void* v_new, float* out, con
  * split is planned), HIP. */
 pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* block_tables, const int32_t* context_lens,
-                                     const int32_t* query_start, int32_t num_seqs, int32_t num_query_rows,
+                                     const int32_t* query_start, const int32_t* seq_order, int32_t num_seqs,
+                                     int32_t num_query_rows,
                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                      int32_t block_size, int32_t num_blocks, int32_t max_blocks,
                                      int32_t max_context_len, int32_t max_query_len, float scale, void* workspace,

@@ -495,11 +495,12 @@ def pkv_attention_multi_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, hea
 
 def pkv_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
                               max_context_len: int, max_query_len: int, scale: float, stream=None,
-                              workspace=None) -> None:
+                              workspace=None, seq_order=None) -> None:
     """Runs of causal queries: out fp32 [T][H_q][d]; q [T][H_q][d] (cache dtype); query_start int32 [S+1]
     (rows of sequence s: its last query_start[s+1] - query_start[s] positions); block_tables int32
     [S][max_blocks]; context_lens int32 [S]; workspace: uint8 tensor of >= pkv_attention_multi_workspace_bytes
-    bytes, or None (no context split)."""
+    bytes, or None (no context split); seq_order: int32 [S] on the GPU, the order to start the sequences in
+    (e.g. longest first), or None."""
     torch = _torch()
     fn = "pkv_paged_attention_multi"
     if q.dim() != 3 or out.shape != q.shape or out.dtype != torch.float32:
@@ -518,9 +519,12 @@ def pkv_paged_attention_multi(out, q, k_cache, v_cache, block_tables, context_le
             raise InvalidArg(-1, fn, f"{name} must be int32" + (f" of shape {shape}" if shape else ""))
     if block_tables.dim() != 2 or block_tables.shape[0] != S:
         raise InvalidArg(-1, fn, "block_tables must be [S][max_blocks]")
+    if seq_order is not None and (seq_order.dtype != torch.int32 or tuple(seq_order.shape) != (S,)):
+        raise InvalidArg(-1, fn, "seq_order must be int32 [S]")
     check(lib().pkv_paged_attention_multi(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
                                           _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
-                                          _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), S, T,
+                                          _dev(context_lens, "context_lens"), _dev(query_start, "query_start"),
+                                          None if seq_order is None else _dev(seq_order, "seq_order"), S, T,
                                           Hq, Hkv, d, B, nb, block_tables.shape[1], max_context_len, max_query_len,
                                           scale, None if workspace is None else _dev(workspace, "workspace"),
                                           0 if workspace is None else workspace.numel() * workspace.element_size(),

@@ -59,6 +59,8 @@ struct MultiArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* query_start;
+  const int32_t* seq_order;  // optional: the order in which to start the sequences
+  int num_seqs;
   int num_query_rows;
   int num_q_heads;
   int num_kv_heads;
@@ -112,14 +114,24 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
   // own L2.  Renumber them so that each XCD takes one contiguous run of
   // (sequence, KV head, row block) units: the workgroups that read the same
   // keys and values then share an L2.
+  // Only row blocks of one pair share keys and values; with one workgroup per
+  // pair (verification, or context splits, which read disjoint ranges) the
+  // hardware's round-robin is kept, so that a longest-first order is spread
+  // over the XCDs instead of piling the longest pairs onto one.
   const int nwg = gridDim.x, xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
   const int per = nwg / kXcds, extra = nwg % kXcds;
-  const int unit = xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k;
+  const int unit = a.wg_per_seq == 1 ? static_cast<int>(blockIdx.x)
+                 : xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k;
   const int per_sg = a.wg_per_seq * a.nsplit;
   const int sg = unit / per_sg;
   const int wg = a.wg_per_seq - 1 - (unit % per_sg) / a.nsplit;  // rows with the most keys go first
   const int split = unit % a.nsplit;
-  const int s = sg / a.num_kv_heads, g = sg % a.num_kv_heads;
+  const int g = sg % a.num_kv_heads;
+  int s = sg / a.num_kv_heads;
+  if (a.seq_order) {
+    s = mq_ld(a.seq_order, s);
+    if (s < 0 || s >= a.num_seqs) return;  // not a sequence: nothing to do
+  }
   static_assert(CT == kMqChunk, "split lengths are counted in chunks");
 
   const int q0 = mq_ld(a.query_start, s);
@@ -158,7 +170,8 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
   const int c_begin = a.nsplit > 1 ? split * (a.split_len / CT) : 0;
   const int nc = a.nsplit > 1 ? min((split + 1) * (a.split_len / CT), p_last / CT + 1) : p_last / CT + 1;
   const int tile_bytes = B * D * kItem;
-  const int64_t part = (static_cast<int64_t>(sg) * a.nsplit + split) * kMqRows + (rr - R0);  // split partial row
+  // Split partial row, indexed by the pair itself (not by its place in the order).
+  const int64_t part = ((static_cast<int64_t>(s) * a.num_kv_heads + g) * a.nsplit + split) * kMqRows + (rr - R0);
   if (c_begin >= nc) {  // a split past every row's position: an empty partial
     if (vrow) {
 #pragma unroll
@@ -515,7 +528,8 @@ using namespace pkv;
 
 extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_cache, const void* v_cache,
                                                  const int32_t* block_tables, const int32_t* context_lens,
-                                                 const int32_t* query_start, int32_t num_seqs,
+                                                 const int32_t* query_start, const int32_t* seq_order,
+                                                 int32_t num_seqs,
                                                  int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads,
                                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                                  int32_t max_blocks, int32_t max_context_len, int32_t max_query_len,
@@ -552,6 +566,8 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start = query_start;
+  a.seq_order = seq_order;
+  a.num_seqs = num_seqs;
   a.num_query_rows = num_query_rows;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;

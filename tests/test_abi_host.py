@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(libpkv):
     assert len(syms) >= 18
     missing = [s for s in syms if not hasattr(libpkv, s)]
     assert missing == []
-    assert pk.pkv_abi_version() == 8
+    assert pk.pkv_abi_version() == 9
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert libpkv.pkv_status_string(code) != b"unknown status"
     assert libpkv.pkv_status_string(-9) == b"unknown status"
