@@ -246,25 +246,30 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
   __syncthreads();
   for (int c = c_begin; c < nc; ++c) {
     if (active && CT * c <= p_wave) {
-      // S[token 16 sub + 4 kq + r][row m16] on the matrix cores, NSUB independent tiles.
-      f32x4_t sc[NSUB];
+      // S[token 16 sub + 4 kq + r][row m16] on the matrix cores: NSUB tiles, each
+      // summed in two halves (even and odd k-steps) so that more independent
+      // chains overlap in the matrix pipeline.
+      f32x4_t sc[NSUB], sc2[NSUB];
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
         const char* kl = lds[c & 1][u];
         sc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        sc2[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
           const uint4 kv = *reinterpret_cast<const uint4*>(kl + ((st * 4 + kq) * 16 + m16) * 16);
           const uint4 qq = qv[st];
+          f32x4_t& acc_s = (st & 1) ? sc2[u] : sc[u];
           if constexpr (kBF16) {
-            sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qq), sc[u], 0, 0, 0);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qq), acc_s, 0, 0, 0);
           } else {
-            sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.x), __uint_as_float(qq.x), sc[u], 0, 0, 0);
-            sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.y), __uint_as_float(qq.y), sc[u], 0, 0, 0);
-            sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.z), __uint_as_float(qq.z), sc[u], 0, 0, 0);
-            sc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.w), __uint_as_float(qq.w), sc[u], 0, 0, 0);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.x), __uint_as_float(qq.x), acc_s, 0, 0, 0);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.y), __uint_as_float(qq.y), acc_s, 0, 0, 0);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.z), __uint_as_float(qq.z), acc_s, 0, 0, 0);
+            acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.w), __uint_as_float(qq.w), acc_s, 0, 0, 0);
           }
         }
+        sc[u] += sc2[u];
       }
       // Scaled logits; a token after the row's position (or past the
       // sequence, which is later still) gets -inf.
@@ -282,11 +287,13 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
       // -inf only for a row that has seen no token yet (in a split that starts after
       // its position): then alpha and its weights are 0, never inf - inf.
       const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      if (__ballot(m_new > m_run)) {  // some row's maximum grew: rescale (wave-uniform branch)
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
       // The lane's value columns of sub-chunk u: dims 16 dt + m16, tokens 4 kq .. 4 kq + 3
       // (values past the end of the sequence may be anything, NaN poison included: zeroed).
       auto values = [&](int u, auto (&vv)[NDT]) __attribute__((always_inline)) {
