@@ -81,10 +81,12 @@ struct MultiArgs {
 constexpr int kMqRows = 16 * kMqWaves;  // rows per workgroup
 constexpr int kMqChunk = 32;            // tokens per chunk (every supported shape)
 
-template <class DT, int D, int G>
-// Three workgroups per CU: at bf16/d = 128 the compiler then keeps the
-// accumulators in VGPRs (146, no AGPR copies, no scratch).
-__global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(const MultiArgs a) {
+// T: 16-row tiles per wave (1, or 2 for prompts: two independent chains per
+// wave, each K/V operand read from LDS once for both).  With one tile, three
+// workgroups per CU: at bf16/d = 128 the compiler then keeps the accumulators
+// in VGPRs (146, no AGPR copies, no scratch); with two, two per CU.
+template <class DT, int D, int G, int T>
+__global__ __launch_bounds__(kWave* kMqWaves, T == 1 ? 3 : 2) void paged_multi_query_kernel(const MultiArgs a) {
   constexpr bool kBF16 = std::is_same<DT, BF16>::value;
   constexpr int kItem = DT::kItem;
   constexpr int KS = D * kItem / 64;  // QK k-steps: four 16-byte pieces each
@@ -141,39 +143,55 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
   const bool bad = n > a.max_context_len || static_cast<int64_t>(n) > static_cast<int64_t>(a.max_blocks) * a.block_size ||
                    qs > n || qs > a.max_query_len;
   const int nrows = min(qs, a.max_query_len) * G;
-  const int R0 = wg * 16 * kMqWaves;
+  const int R0 = wg * 16 * kMqWaves * T;
   if (R0 >= nrows) return;  // the whole workgroup: no barrier is left waiting
 
-  const int r0 = R0 + 16 * wave;
-  const bool active = r0 < nrows;  // wave-uniform
-  const int rr = r0 + m16;
-  const bool vrow = rr < nrows;
-  const int qi = vrow ? rr / G : 0;
-  const int h = g * G + (vrow ? rr % G : 0);
-  const int64_t row_elem = (static_cast<int64_t>(q0 + qi) * a.num_q_heads + h) * D;
-  float* orow = a.out + row_elem;
+  // Tile t of wave w holds rows R0 + 16 (w + kMqWaves t) + m16, so every wave has
+  // rows from each part of the block.
+  int r0[T], rr[T], qi[T];
+  bool active[T], vrow[T];
+  int64_t row_elem[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    r0[t] = R0 + 16 * (wave + kMqWaves * t);
+    active[t] = r0[t] < nrows;  // wave-uniform
+    rr[t] = r0[t] + m16;
+    vrow[t] = rr[t] < nrows;
+    qi[t] = vrow[t] ? rr[t] / G : 0;
+    const int h = g * G + (vrow[t] ? rr[t] % G : 0);
+    row_elem[t] = (static_cast<int64_t>(q0 + qi[t]) * a.num_q_heads + h) * D;
+  }
 
   if (bad) {  // the same for every wave of the workgroup (the split combine skips such runs)
-    if (vrow && split == 0) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4_t*>(orow + 16 * dt + 4 * kq) = f32x4_t{NAN, NAN, NAN, NAN};
-    }
+    for (int t = 0; t < T; ++t)
+      if (vrow[t] && split == 0) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<f32x4_t*>(a.out + row_elem[t] + 16 * dt + 4 * kq) = f32x4_t{NAN, NAN, NAN, NAN};
+      }
     return;
   }
 
   const int B = a.block_size;
   const int pos0 = n - qs;  // position of the run's first query
-  const int p_row = pos0 + qi;
-  const int p_wave = pos0 + (active ? min(r0 + 15, nrows - 1) / G : 0);  // the wave's last position
-  const int p_last = pos0 + min(R0 + 16 * kMqWaves - 1, nrows - 1) / G;  // the workgroup's last position
+  int p_row[T];
+  int p_wave = -1;  // the wave's last position (-1: no rows)
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    p_row[t] = pos0 + qi[t];
+    if (active[t]) p_wave = max(p_wave, pos0 + min(r0[t] + 15, nrows - 1) / G);
+  }
+  const int p_last = pos0 + min(R0 + 16 * kMqWaves * T - 1, nrows - 1) / G;  // the workgroup's last position
   // Chunks [c_begin, nc): this split's tokens up to the last position.
   const int c_begin = a.nsplit > 1 ? split * (a.split_len / CT) : 0;
   const int nc = a.nsplit > 1 ? min((split + 1) * (a.split_len / CT), p_last / CT + 1) : p_last / CT + 1;
   const int tile_bytes = B * D * kItem;
-  // Split partial row, indexed by the pair itself (not by its place in the order).
-  const int64_t part = ((static_cast<int64_t>(s) * a.num_kv_heads + g) * a.nsplit + split) * kMqRows + (rr - R0);
+  // Split partial row, indexed by the pair itself (not by its place in the order);
+  // context splits are planned only for one tile per wave, rows < kMqRows.
+  const int64_t part = ((static_cast<int64_t>(s) * a.num_kv_heads + g) * a.nsplit + split) * kMqRows + (rr[0] - R0);
   if (c_begin >= nc) {  // a split past every row's position: an empty partial
-    if (vrow) {
+    if (vrow[0]) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         *reinterpret_cast<f32x4_t*>(a.ws_acc + part * D + 16 * dt + 4 * kq) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -185,11 +203,14 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
     return;  // the same for the whole workgroup
   }
 
-  uint4 qv[KS];
-  const char* qrow = static_cast<const char*>(a.q) + row_elem * kItem;
+  uint4 qv[T][KS];
 #pragma unroll
-  for (int st = 0; st < KS; ++st)
-    qv[st] = vrow ? *reinterpret_cast<const uint4*>(qrow + (st * 4 + kq) * 16) : make_uint4(0, 0, 0, 0);
+  for (int t = 0; t < T; ++t) {
+    const char* qrow = static_cast<const char*>(a.q) + row_elem[t] * kItem;
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      qv[t][st] = vrow[t] ? *reinterpret_cast<const uint4*>(qrow + (st * 4 + kq) * 16) : make_uint4(0, 0, 0, 0);
+  }
 
   // Staging: thread piece j of a chunk is i = tid + kThreads j, in sub-chunk
   // i / ITEMS (the same for a whole wave); within it, key piece ii is (key
@@ -235,64 +256,82 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
     }
   };
 
-  f32x4_t acc[NDT];
+  f32x4_t acc[T][NDT];
+  float m_run[T], l_run[T];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int t = 0; t < T; ++t) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[t][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.0f;
+  }
 
   stage(c_begin);
   put(c_begin & 1);
   stage(c_begin + 1);
   __syncthreads();
   for (int c = c_begin; c < nc; ++c) {
-    if (active && CT * c <= p_wave) {
-      // S[token 16 sub + 4 kq + r][row m16] on the matrix cores: NSUB tiles, each
-      // summed in two halves (even and odd k-steps) so that more independent
-      // chains overlap in the matrix pipeline.
-      f32x4_t sc[NSUB], sc2[NSUB];
+    if (CT * c <= p_wave) {  // some row of the wave sees this chunk (wave-uniform)
+      // S[token 16 sub + 4 kq + r][row m16] on the matrix cores: NSUB tiles per
+      // row tile, each summed in two halves (even and odd k-steps) so that more
+      // independent chains overlap in the matrix pipeline; a key operand read
+      // from LDS serves every row tile.
+      f32x4_t sc[T][NSUB], sc2[T][NSUB];
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
         const char* kl = lds[c & 1][u];
-        sc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        sc2[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          sc[t][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          sc2[t][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
           const uint4 kv = *reinterpret_cast<const uint4*>(kl + ((st * 4 + kq) * 16 + m16) * 16);
-          const uint4 qq = qv[st];
-          f32x4_t& acc_s = (st & 1) ? sc2[u] : sc[u];
-          if constexpr (kBF16) {
-            acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qq), acc_s, 0, 0, 0);
-          } else {
-            acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.x), __uint_as_float(qq.x), acc_s, 0, 0, 0);
-            acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.y), __uint_as_float(qq.y), acc_s, 0, 0, 0);
-            acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.z), __uint_as_float(qq.z), acc_s, 0, 0, 0);
-            acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.w), __uint_as_float(qq.w), acc_s, 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const uint4 qq = qv[t][st];
+            f32x4_t& acc_s = (st & 1) ? sc2[t][u] : sc[t][u];
+            if constexpr (kBF16) {
+              acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qq), acc_s, 0, 0, 0);
+            } else {
+              acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.x), __uint_as_float(qq.x), acc_s, 0, 0, 0);
+              acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.y), __uint_as_float(qq.y), acc_s, 0, 0, 0);
+              acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.z), __uint_as_float(qq.z), acc_s, 0, 0, 0);
+              acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.w), __uint_as_float(qq.w), acc_s, 0, 0, 0);
+            }
           }
         }
-        sc[u] += sc2[u];
+#pragma unroll
+        for (int t = 0; t < T; ++t) sc[t][u] += sc2[t][u];
       }
-      // Scaled logits; a token after the row's position (or past the
-      // sequence, which is later still) gets -inf.
-      float gm = -INFINITY;
+      float m_ref[T];
 #pragma unroll
-      for (int u = 0; u < NSUB; ++u)
+      for (int t = 0; t < T; ++t) {
+        // Scaled logits; a token after the row's position (or past the
+        // sequence, which is later still) gets -inf.
+        float gm = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc[u][r] = (CT * c + 16 * u + 4 * kq + r <= p_row) ? sc[u][r] * a.c : -INFINITY;
-          gm = fmaxf(gm, sc[u][r]);
+        for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sc[t][u][r] = (CT * c + 16 * u + 4 * kq + r <= p_row[t]) ? sc[t][u][r] * a.c : -INFINITY;
+            gm = fmaxf(gm, sc[t][u][r]);
+          }
+        // Online softmax per row (lane column m16; the four lane groups hold its tokens).
+        gm = max_xor32(max_xor16(gm));
+        const float m_new = fmaxf(m_run[t], gm);
+        // -inf only for a row that has seen no token yet (in a split that starts
+        // after its position, or a tile past the run): then alpha and its weights
+        // are 0, never inf - inf.
+        m_ref[t] = m_new == -INFINITY ? 0.0f : m_new;
+        if (__ballot(m_new > m_run[t])) {  // some row's maximum grew: rescale (wave-uniform branch)
+          const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_ref[t]);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[t][dt] *= alpha;
+          l_run[t] *= alpha;
+          m_run[t] = m_new;
         }
-      // Online softmax per row (lane column m16; the four lane groups hold its tokens).
-      gm = max_xor32(max_xor16(gm));
-      const float m_new = fmaxf(m_run, gm);
-      // -inf only for a row that has seen no token yet (in a split that starts after
-      // its position): then alpha and its weights are 0, never inf - inf.
-      const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
-      if (__ballot(m_new > m_run)) {  // some row's maximum grew: rescale (wave-uniform branch)
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
       }
       // The lane's value columns of sub-chunk u: dims 16 dt + m16, tokens 4 kq .. 4 kq + 3
       // (values past the end of the sequence may be anything, NaN poison included: zeroed).
@@ -323,14 +362,16 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
           }
         }
       };
-      float p[NSUB][4];
+      float p[T][NSUB][4];
 #pragma unroll
-      for (int u = 0; u < NSUB; ++u)
+      for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[u][r] = __builtin_amdgcn_exp2f(sc[u][r] - m_ref);
-          l_run += p[u][r];
-        }
+        for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[t][u][r] = __builtin_amdgcn_exp2f(sc[t][u][r] - m_ref[t]);
+            l_run[t] += p[t][u][r];
+          }
       // O[dim][row] += V[dim][token] P[token][row].
       if constexpr (kBF16) {
         // Sub-chunks in pairs on 16x16x32 steps: lane (kq, m16) supplies k-slots
@@ -352,17 +393,24 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
           uint2 va[NDT], vb[NDT];
           values(u, va);
           values(u + 1, vb);
-          const u32x4_t ph = {pack_hi(p[u][0], p[u][1]), pack_hi(p[u][2], p[u][3]), pack_hi(p[u + 1][0], p[u + 1][1]),
-                              pack_hi(p[u + 1][2], p[u + 1][3])};
-          const u32x4_t pl = {pack_lo(p[u][0], p[u][1]), pack_lo(p[u][2], p[u][3]), pack_lo(p[u + 1][0], p[u + 1][1]),
-                              pack_lo(p[u + 1][2], p[u + 1][3])};
+          u32x4_t ph[T], pl[T];
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            ph[t] = u32x4_t{pack_hi(p[t][u][0], p[t][u][1]), pack_hi(p[t][u][2], p[t][u][3]),
+                            pack_hi(p[t][u + 1][0], p[t][u + 1][1]), pack_hi(p[t][u + 1][2], p[t][u + 1][3])};
+            pl[t] = u32x4_t{pack_lo(p[t][u][0], p[t][u][1]), pack_lo(p[t][u][2], p[t][u][3]),
+                            pack_lo(p[t][u + 1][0], p[t][u + 1][1]), pack_lo(p[t][u + 1][2], p[t][u + 1][3])};
+          }
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
             const u32x4_t av = {va[dt].x, va[dt].y, vb[dt].x, vb[dt].y};
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                              __builtin_bit_cast(bf16x8_t, ph), acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                              __builtin_bit_cast(bf16x8_t, pl), acc[dt], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                   __builtin_bit_cast(bf16x8_t, ph[t]), acc[t][dt], 0, 0, 0);
+              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                   __builtin_bit_cast(bf16x8_t, pl[t]), acc[t][dt], 0, 0, 0);
+            }
           }
         }
       } else {
@@ -372,12 +420,14 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
           uint4 vv[NDT];
           values(u, vv);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].x), p[u][0], acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].y), p[u][1], acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].z), p[u][2], acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].w), p[u][3], acc[dt], 0, 0, 0);
-          }
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].x), p[t][u][0], acc[t][dt], 0, 0, 0);
+              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].y), p[t][u][1], acc[t][dt], 0, 0, 0);
+              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].z), p[t][u][2], acc[t][dt], 0, 0, 0);
+              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].w), p[t][u][3], acc[t][dt], 0, 0, 0);
+            }
         }
       }
     }
@@ -387,24 +437,31 @@ __global__ __launch_bounds__(kWave* kMqWaves, 3) void paged_multi_query_kernel(c
     stage(c + 2);
     __syncthreads();
   }
-  const float l_tot = sum_xor32(sum_xor16(l_run));  // every lane takes part in the swaps
+  float l_tot[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) l_tot[t] = sum_xor32(sum_xor16(l_run[t]));  // every lane takes part in the swaps
   if (a.nsplit > 1) {
     // Split partial: un-normalised accumulator, max and sum (NaN if a block id was bad).
     const float f = poison ? NAN : 1.0f;
-    if (vrow) {
+    if (vrow[0]) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4_t*>(a.ws_acc + part * D + 16 * dt + 4 * kq) = acc[dt] * f;
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4_t*>(a.ws_acc + part * D + 16 * dt + 4 * kq) = acc[0][dt] * f;
       if (kq == 0) {
-        a.ws_m[part] = m_run;
-        a.ws_l[part] = l_tot * f;
+        a.ws_m[part] = m_run[0];
+        a.ws_l[part] = l_tot[0] * f;
       }
     }
     return;
   }
-  const float inv = poison ? NAN : 1.0f / l_tot;
-  if (vrow) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4_t*>(orow + 16 * dt + 4 * kq) = acc[dt] * inv;
+  for (int t = 0; t < T; ++t) {
+    const float inv = poison ? NAN : 1.0f / l_tot[t];
+    if (vrow[t]) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4_t*>(a.out + row_elem[t] + 16 * dt + 4 * kq) = acc[t][dt] * inv;
+    }
   }
 }
 
@@ -509,22 +566,27 @@ MultiPlan multi_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t G, int32_t 
   return p;
 }
 
-template <class DT, int D>
-hipError_t launch_multi_d(const MultiArgs& a, int G, dim3 grid, dim3 block, hipStream_t stream) {
+template <class DT, int D, int T>
+hipError_t launch_multi_t(const MultiArgs& a, int G, dim3 grid, dim3 block, hipStream_t stream) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((paged_multi_query_kernel<DT, D, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((paged_multi_query_kernel<DT, D, 2>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((paged_multi_query_kernel<DT, D, 4>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((paged_multi_query_kernel<DT, D, 8>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((paged_multi_query_kernel<DT, D, 1, T>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((paged_multi_query_kernel<DT, D, 2, T>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((paged_multi_query_kernel<DT, D, 4, T>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((paged_multi_query_kernel<DT, D, 8, T>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <class DT, int D>
+hipError_t launch_multi_d(const MultiArgs& a, int G, int T, dim3 grid, dim3 block, hipStream_t stream) {
+  return T == 2 ? launch_multi_t<DT, D, 2>(a, G, grid, block, stream) : launch_multi_t<DT, D, 1>(a, G, grid, block, stream);
+}
+
 template <class DT>
-hipError_t launch_multi(const MultiArgs& a, int D, int G, dim3 grid, dim3 block, hipStream_t stream) {
-  if (D == 64) return launch_multi_d<DT, 64>(a, G, grid, block, stream);
-  if (D == 128) return launch_multi_d<DT, 128>(a, G, grid, block, stream);
+hipError_t launch_multi(const MultiArgs& a, int D, int G, int T, dim3 grid, dim3 block, hipStream_t stream) {
+  if (D == 64) return launch_multi_d<DT, 64>(a, G, T, grid, block, stream);
+  if (D == 128) return launch_multi_d<DT, 128>(a, G, T, grid, block, stream);
   return hipErrorInvalidValue;
 }
 
@@ -559,7 +621,10 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
 
-  const int64_t wg_per_seq = (static_cast<int64_t>(max_query_len) * G + kMqRows - 1) / kMqRows;
+  // Two row tiles per wave when a pair has more rows than one workgroup of one-tile waves holds.
+  const int T = static_cast<int64_t>(max_query_len) * G > kMqRows ? 2 : 1;
+  const int64_t rows_per_wg = static_cast<int64_t>(kMqRows) * T;
+  const int64_t wg_per_seq = (static_cast<int64_t>(max_query_len) * G + rows_per_wg - 1) / rows_per_wg;
   // Split the context only when a workspace is given and the plan asks for it.
   MultiPlan plan = multi_plan(num_seqs, num_kv_heads, G, head_dim, max_context_len, max_query_len);
   if (!workspace) plan = MultiPlan{};
@@ -595,8 +660,8 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   a.c = scale * 1.4426950408889634f;
   const dim3 grid(static_cast<unsigned>(wg_per_seq * plan.nsplit * num_seqs * num_kv_heads));
   const dim3 block(static_cast<unsigned>(kMqWaves * kWave));
-  hipError_t err = kv_dtype == PKV_BF16 ? launch_multi<BF16>(a, head_dim, G, grid, block, stream)
-                                        : launch_multi<F32>(a, head_dim, G, grid, block, stream);
+  hipError_t err = kv_dtype == PKV_BF16 ? launch_multi<BF16>(a, head_dim, G, T, grid, block, stream)
+                                        : launch_multi<F32>(a, head_dim, G, T, grid, block, stream);
   if (err == hipSuccess && plan.nsplit > 1) {
     const int units = num_seqs * num_kv_heads;
     err = head_dim == 64 ? launch_combine<64>(a, G, units, stream) : launch_combine<128>(a, G, units, stream);
