@@ -1,5 +1,8 @@
-"""paged_kv_cache_physical_amd — Python binding of libpkv, the paged KV-cache decode
-path for AMD MI355X (gfx950).
+"""paged_kv_cache_physical_amd — Python binding of libpkv, the paged KV-cache
+attention path for AMD MI355X (gfx950): a host block pool (refcounted sharing,
+copy-on-write, swapping, prefix caching, rollback), decode attention, runs of
+causal queries (prefill, prefix-cached tails, speculative verification) and the
+cache writes and block copies around them.
 
 Argument marshalling only: every call below forwards to the C function of the
 same name in ``libpkv.so`` (declared in ``include/pkv.h``); host arrays are
