@@ -520,3 +520,38 @@ def test_duplicate_and_unknown_ids_in_one_append(libpkv):
         c.append([0], [1])
         o.append([0], [1])
     same_state(c, o)
+
+
+def test_runs_of_queries_host_checks_and_split_plan(libpkv):
+    """pkv_paged_attention_multi rejects bad arguments before any device work, and the split workspace follows
+    the plan: >= 256-token splits for about 2048 workgroups, at most 64, only when a pair's rows fit 64."""
+    L = libpkv
+    vp = ctypes.c_void_p
+    # (num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len) -> bytes
+    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 32768, 4) == 64 * 32 * 64 * 130 * 4
+    assert pk.pkv_attention_multi_workspace_bytes(3, 8, 2, 64, 600, 5) == 6 * 2 * 64 * 66 * 4
+    assert pk.pkv_attention_multi_workspace_bytes(1, 8, 8, 128, 1 << 20, 1) == 8 * 64 * 64 * 130 * 4  # capped
+    assert pk.pkv_attention_multi_workspace_bytes(64, 32, 32, 128, 2048, 4) == 0  # enough pairs already
+    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 32768, 17) == 0  # 68 rows: no split
+    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 500, 4) == 0  # too short to split
+    assert pk.pkv_attention_multi_workspace_bytes(8, 30, 8, 128, 32768, 4) == 0  # H_q % H_kv != 0
+
+    def call(out=None, q=None, k=None, v=None, bt=None, cl=None, qs=None, order=None, S=2, T=8, Hq=8, Hkv=8, d=128,
+             B=16, nb=10, mb=4, mctx=64, mq=4, scale=1.0, ws=None, wsb=0, dt=1):
+        return L.pkv_paged_attention_multi(out, q, k, v, bt, cl, qs, order, S, T, Hq, Hkv, d, B, nb, mb, mctx, mq,
+                                           scale, ws, wsb, dt, None)
+    assert call(dt=7) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(Hq=6, Hkv=4) == _lib.PKV_ERR_INVALID_ARG
+    assert call(Hq=48, Hkv=4) == _lib.PKV_ERR_UNSUPPORTED  # G = 12
+    assert call(d=96) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(B=24) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == _lib.PKV_ERR_INVALID_ARG
+    assert call(mq=-1) == _lib.PKV_ERR_INVALID_ARG
+    assert call(S=0) == _lib.PKV_OK and call(mq=0) == _lib.PKV_OK and call(T=0) == _lib.PKV_OK  # nothing to do
+    assert call() == _lib.PKV_ERR_INVALID_ARG  # NULL buffers
+    buf = [vp(4096)] * 7  # aligned stand-ins: every call below is rejected before any device work
+    assert call(*buf[:2], vp(4104), *buf[3:]) == _lib.PKV_ERR_INVALID_ARG  # misaligned key cache
+    need = pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 32768, 4)
+    split = dict(S=8, Hq=32, Hkv=8, mctx=32768, mb=2048, nb=16384)
+    assert call(*buf, **split, ws=vp(4096), wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
+    assert call(*buf, **split, ws=vp(4104), wsb=need) == _lib.PKV_ERR_WORKSPACE  # misaligned workspace
