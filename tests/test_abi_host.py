@@ -555,3 +555,19 @@ def test_runs_of_queries_host_checks_and_split_plan(libpkv):
     split = dict(S=8, Hq=32, Hkv=8, mctx=32768, mb=2048, nb=16384)
     assert call(*buf, **split, ws=vp(4096), wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
     assert call(*buf, **split, ws=vp(4104), wsb=need) == _lib.PKV_ERR_WORKSPACE  # misaligned workspace
+
+
+def test_freed_blocks_wait_out_every_earlier_free_block(libpkv):
+    """The C pool hands a freed block out again only after every block that was free before it (FIFO)."""
+    c = pk.Pool(12, 4)
+    a, b = c.create(), c.create()
+    c.append([a], [16])  # blocks 0-3
+    c.append([b], [8])   # blocks 4-5
+    c.free_seq(a)        # 0-3 join the tail, behind 6-11
+    assert list(c.free_list()) == [6, 7, 8, 9, 10, 11, 0, 1, 2, 3]
+    x = c.create()
+    slots, _ = c.append([x], [24])  # six blocks: every never-used one first
+    assert sorted(set((slots // 4).tolist())) == [6, 7, 8, 9, 10, 11]
+    y = c.create()
+    slots, _ = c.append([y], [5])
+    assert (slots // 4).tolist() == [0, 0, 0, 0, 1]  # then the oldest freed, in release order

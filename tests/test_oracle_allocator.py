@@ -478,3 +478,36 @@ def test_prefix_cache_random_operations():
             for key, b in pool.cached.items():  # registered keys name live or queued device blocks
                 assert pool.block_keys[b][0] == key
                 assert pool.refcount[b] > 0 or b in pool.free
+
+
+def test_freed_blocks_wait_out_every_earlier_free_block():
+    """The address non-reuse window the pages ask to test: a freed block is handed out again only after every
+    block that was free when it was released (FIFO), so its old contents stay addressable that long."""
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        nb, B = int(rng.integers(8, 40)), int(rng.choice([1, 4, 16]))
+        pool = al.BlockPool(nb, B, rng.permutation(nb))
+        released = {}  # block -> number of blocks that must be popped before it
+        pops = 0
+        for _ in range(60):
+            if pool.seqs and rng.random() < 0.35:
+                sid = int(rng.choice(list(pool.seqs)))
+                before = len(pool.free_list())
+                table = pool.table(sid)
+                pool.free_seq(sid)
+                for i, b in enumerate(t for t in table if pool.refcount[t] == 0):
+                    released[b] = pops + before + i
+            else:
+                sid = pool.create()
+                n = int(rng.integers(1, 3 * B))
+                free_before = pool.free_list()
+                try:
+                    pool.append([sid], [n])
+                except al.OutOfBlocks:
+                    pool.free_seq(sid)
+                    continue
+                taken = free_before[:len(free_before) - len(pool.free_list())]
+                for b in taken:
+                    if b in released:
+                        assert pops >= released.pop(b), (b, pops)
+                    pops += 1

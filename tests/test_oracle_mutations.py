@@ -142,6 +142,7 @@ def test_lifo_reuse_is_caught(monkeypatch):
 
     monkeypatch.setattr(al.BlockPool, "free_seq", lifo_free)
     assert _fails_some([t_alloc.test_fifo_slots_by_hand, t_alloc.test_free_order_after_fork_free])
+    assert _fails_some([t_alloc.test_freed_blocks_wait_out_every_earlier_free_block])
 
 
 def test_cow_without_decrement_is_caught(monkeypatch):
