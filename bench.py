@@ -345,6 +345,8 @@ MULTI_CASES = {
     "verify4_long_bf16": (8, 32, 8, 32768, 4),
     "prefill2048_gqa_bf16": (16, 32, 8, 2048, "all"),
     "prefix_tail256_gqa_bf16": (64, 32, 8, 1280, 256),
+    # one continuous-batching step: 4 sequences take a 512-token prompt chunk, 60 decode one token
+    "mixed4x512_plus60_gqa_bf16": (64, 32, 8, (640, 2048), ("mixed", 4, 512)),
 }
 
 
@@ -363,7 +365,13 @@ def measure_multi(stream, reps=20, case=None):
         rng = np.random.default_rng(1)
         lens = (rng.integers(lens_spec[0], lens_spec[1], size=S, endpoint=True) if isinstance(lens_spec, tuple)
                 else np.full(S, lens_spec)).astype(np.int64)
-        runs = lens.copy() if run == "all" else np.full(S, run, dtype=np.int64)
+        if run == "all":
+            runs = lens.copy()
+        elif isinstance(run, tuple):  # ("mixed", k, chunk): k sequences run `chunk` queries, the rest one
+            runs = np.ones(S, dtype=np.int64)
+            runs[:run[1]] = run[2]
+        else:
+            runs = np.full(S, run, dtype=np.int64)
         nb = int(sum(-(-int(n) // B) for n in lens))
         pool = pk.Pool(nb, B, rng.permutation(nb).astype(np.int32))
         ids = [pool.create() for _ in range(S)]
@@ -396,7 +404,12 @@ def measure_multi(stream, reps=20, case=None):
                "launch_us": round(us, 2), "launch_us_median": round(1e3 * t[1], 2),
                "kv_bytes": kv_bytes, "kv_gbps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
                "flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
-        if run == "all" or run > 16:
+        if isinstance(run, tuple):  # mixed work: both fractions, neither bound alone
+            rec["hbm_frac"] = round(rec["kv_gbps"] / HBM_PEAK_GBPS, 4)
+            rec["mfma_frac"] = round(rec["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+            rec["roofline"] = {"bound": "mixed", "achieved": rec["kv_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                               "frac": rec["hbm_frac"]}
+        elif run == "all" or run > 16:
             rec["roofline"] = {"bound": "mfma", "achieved": rec["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
                                "unit": "TFLOP/s", "frac": round(rec["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
         else:

@@ -70,6 +70,8 @@ struct MultiArgs {
   int max_context_len;
   int max_query_len;
   int wg_per_seq;  // row blocks per (sequence, KV head)
+  int num_pairs;   // (sequence, KV head) pairs
+  int pair_slots;  // with several row blocks per pair: ceil(num_pairs / 8), the pairs per XCD
   int nsplit;      // context splits per (sequence, KV head): 1, or several when its rows fit one block
   int split_len;   // tokens per split (a multiple of the chunk), when nsplit > 1
   float* ws_acc;   // split partials: [S][H_kv][nsplit][64 rows][d], un-normalised
@@ -113,9 +115,9 @@ __global__ __launch_bounds__(kWave* kMqWaves, T == 1 ? 3 : 2) void paged_multi_q
   // The wave index is the same in every lane; saying so keeps what derives from it scalar.
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   // Workgroup ids are dealt to the 8 XCDs in turn (id mod 8), each XCD with its
-  // own L2.  Renumber them so that each XCD takes one contiguous run of
-  // (sequence, KV head, row block) units: the workgroups that read the same
-  // keys and values then share an L2.
+  // own L2.  With several row blocks per pair, renumber them so that each XCD
+  // takes one contiguous run of units (below): the workgroups that read the
+  // same keys and values then share an L2.
   // Only row blocks of one pair share keys and values; with one workgroup per
   // pair (verification, or context splits, which read disjoint ranges) the
   // hardware's round-robin is kept, so that a longest-first order is spread
@@ -125,7 +127,15 @@ __global__ __launch_bounds__(kWave* kMqWaves, T == 1 ? 3 : 2) void paged_multi_q
   const int unit = a.wg_per_seq == 1 ? static_cast<int>(blockIdx.x)
                  : xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k;
   const int per_sg = a.wg_per_seq * a.nsplit;
-  const int sg = unit / per_sg;
+  int sg = unit / per_sg;
+  if (a.wg_per_seq > 1) {
+    // XCD x holds pair slots [x m, (x + 1) m) (m = pair_slots); slot j is pair
+    // 8 (j mod m) + j div m, so XCD x serves pairs x, x + 8, x + 16, ...: a pair's
+    // row blocks share an L2 while the pairs, in their given order, are dealt
+    // across the XCDs.  Slots past the last pair have nothing to do.
+    sg = kXcds * (sg % a.pair_slots) + sg / a.pair_slots;
+    if (sg >= a.num_pairs) return;
+  }
   const int wg = a.wg_per_seq - 1 - (unit % per_sg) / a.nsplit;  // rows with the most keys go first
   const int split = unit % a.nsplit;
   const int g = sg % a.num_kv_heads;
@@ -621,15 +631,28 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
 
-  // Two row tiles per wave when a pair has more rows than one workgroup of one-tile waves holds.
-  const int T = static_cast<int64_t>(max_query_len) * G > kMqRows ? 2 : 1;
+  // Two row tiles per wave when a pair has more rows than one workgroup of
+  // one-tile waves holds, and the batch's rows (num_query_rows * G in all, the
+  // host's only measure of the work) make at least one full round of
+  // two-tile workgroups (two fit a CU); otherwise one tile per wave gives
+  // twice the workgroups to spread a few long prompts over.
+  int T = 1;
+  if (static_cast<int64_t>(max_query_len) * G > kMqRows) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t blocks2 = (static_cast<int64_t>(num_query_rows) * G + 2 * kMqRows - 1) / (2 * kMqRows);
+    if (blocks2 >= 2 * static_cast<int64_t>(cus)) T = 2;
+  }
   const int64_t rows_per_wg = static_cast<int64_t>(kMqRows) * T;
   const int64_t wg_per_seq = (static_cast<int64_t>(max_query_len) * G + rows_per_wg - 1) / rows_per_wg;
   // Split the context only when a workspace is given and the plan asks for it.
   MultiPlan plan = multi_plan(num_seqs, num_kv_heads, G, head_dim, max_context_len, max_query_len);
   if (!workspace) plan = MultiPlan{};
   if (plan.nsplit > 1 && (workspace_bytes < plan.bytes || !aligned16(workspace))) return PKV_ERR_WORKSPACE;
-  if (wg_per_seq * plan.nsplit * num_seqs * num_kv_heads > INT32_MAX) return PKV_ERR_INVALID_ARG;
+  const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  const int64_t pair_slots = (pairs + kXcds - 1) / kXcds;
+  const int64_t grid_pairs = wg_per_seq > 1 ? kXcds * pair_slots : pairs;  // whole XCD runs when renumbering
+  if (wg_per_seq * plan.nsplit * grid_pairs > INT32_MAX) return PKV_ERR_INVALID_ARG;
   MultiArgs a{};
   a.out = out;
   a.q = q;
@@ -649,6 +672,8 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   a.max_context_len = max_context_len;
   a.max_query_len = max_query_len;
   a.wg_per_seq = static_cast<int>(wg_per_seq);
+  a.num_pairs = static_cast<int>(pairs);
+  a.pair_slots = static_cast<int>(pair_slots);
   a.nsplit = plan.nsplit;
   a.split_len = plan.split_len;
   if (plan.nsplit > 1) {
@@ -658,7 +683,7 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
     a.ws_l = a.ws_m + rows;
   }
   a.c = scale * 1.4426950408889634f;
-  const dim3 grid(static_cast<unsigned>(wg_per_seq * plan.nsplit * num_seqs * num_kv_heads));
+  const dim3 grid(static_cast<unsigned>(wg_per_seq * plan.nsplit * grid_pairs));
   const dim3 block(static_cast<unsigned>(kMqWaves * kWave));
   hipError_t err = kv_dtype == PKV_BF16 ? launch_multi<BF16>(a, head_dim, G, T, grid, block, stream)
                                         : launch_multi<F32>(a, head_dim, G, T, grid, block, stream);
