@@ -429,6 +429,10 @@ pkv_status pkv_decode_step(const void* k_new, const void* v_new, float* out, con
  * Supported shapes and dtypes as for decode.  Arithmetic: fp32 accumulation,
  * products on the matrix cores; bf16 probabilities enter the value product as
  * two bf16 terms.  Allocates nothing.
+ * Tuning: where a pair has more than 64 rows, a workgroup serves 128 rows
+ * (two row tiles per wave) when the batch's rows fill the GPU, else 64; the
+ * environment variable PKV_MULTI_TILES set to "1" or "2" (read at each call)
+ * forces the choice.  Both give the same rows.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (too small or misaligned when a
  * split is planned), HIP. */
 pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_cache, const void* v_cache,

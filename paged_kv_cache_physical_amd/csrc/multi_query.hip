@@ -33,6 +33,8 @@
 // each pair's context be cut into splits computed apart; multi_combine_kernel
 // then merges the split partials with log-sum-exp weights.
 
+#include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -555,6 +557,21 @@ struct MultiPlan {
   int split_len = 0;
   size_t bytes = 0;
 };
+
+// Compute units of the current device, cached per device (256 if the query fails).
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    cache[dev] = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0 ? cus : 256;
+  }
+  return cache[dev];
+}
+
 MultiPlan multi_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t G, int32_t head_dim, int32_t max_context_len,
                      int32_t max_query_len) {
   MultiPlan p;
@@ -636,12 +653,17 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   // host's only measure of the work) make at least one full round of
   // two-tile workgroups (two fit a CU); otherwise one tile per wave gives
   // twice the workgroups to spread a few long prompts over.
+  // PKV_MULTI_TILES=1 or 2 (read at each call) forces the choice; both kernels
+  // give the same rows.
   int T = 1;
   if (static_cast<int64_t>(max_query_len) * G > kMqRows) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int64_t blocks2 = (static_cast<int64_t>(num_query_rows) * G + 2 * kMqRows - 1) / (2 * kMqRows);
-    if (blocks2 >= 2 * static_cast<int64_t>(cus)) T = 2;
+    const char* force = std::getenv("PKV_MULTI_TILES");
+    if (force && (force[0] == '1' || force[0] == '2') && force[1] == 0) {
+      T = force[0] - '0';
+    } else {
+      const int64_t blocks2 = (static_cast<int64_t>(num_query_rows) * G + 2 * kMqRows - 1) / (2 * kMqRows);
+      if (blocks2 >= 2 * static_cast<int64_t>(device_cus())) T = 2;
+    }
   }
   const int64_t rows_per_wg = static_cast<int64_t>(kMqRows) * T;
   const int64_t wg_per_seq = (static_cast<int64_t>(max_query_len) * G + rows_per_wg - 1) / rows_per_wg;

@@ -119,14 +119,19 @@ class Batch:
 GRID = [(dt, d, G, B) for dt in ("f32", "bf16") for d in (64, 128) for G in (1, 2, 4, 8) for B in (16, 32)]
 
 
+@pytest.mark.parametrize("tiles", ["auto", "2"])
 @pytest.mark.parametrize("dt,d,G,B", GRID)
-def test_runs_grid(dt, d, G, B):
+def test_runs_grid(dt, d, G, B, tiles, monkeypatch):
+    """Every supported shape; "2" forces two row tiles per wave (PKV_MULTI_TILES), which these small batches would
+    not choose, so both kernels of each shape are checked."""
+    if tiles != "auto":
+        monkeypatch.setenv("PKV_MULTI_TILES", tiles)
     rng = wl.rng_for(G * 100 + d + B, 99)
     lens = [int(x) for x in rng.integers(1, 300, size=6)] + [1, 17]
     runs = [n if i % 3 == 0 else int(rng.integers(1, min(n, 40) + 1)) for i, n in enumerate(lens)]
     runs[-1] = 17  # a whole 17-token prompt
     Hkv = 2
-    say(f"case {dt} d={d} G={G} B={B}: lens={lens} runs={runs}")
+    say(f"case {dt} d={d} G={G} B={B} tiles={tiles}: lens={lens} runs={runs}")
     b = Batch(lens, G * Hkv, Hkv, d, B, dt, seed=G + d + B)
     q = wl.draw_values(wl.rng_for(5, wl.STREAM_Q, G, d), (sum(runs), G * Hkv, d), dt)
     out, t, l, starts = b.multi(runs, q)
@@ -263,6 +268,27 @@ def test_edge_cases():
                                    torch.from_numpy(l).cuda(), torch.zeros(6, dtype=torch.int32, device="cuda"),
                                    64, 0, 0.125)
     torch.cuda.synchronize()
+
+
+def test_full_size_prefill_sampled(monkeypatch):
+    """Whole prompts at the prefill shape (16 prompts x 2048 tokens, 32/8 heads, d 128, bf16, B 16): the batch's
+    rows fill the GPU, so the call takes two row tiles per wave.  Sampled rows (chunk and tile edges, first and last
+    positions) against the oracle on each prompt's own K/V; forcing one tile per wave gives the same rows."""
+    S, L, Hq, Hkv, d = 16, 2048, 32, 8, 128
+    monkeypatch.delenv("PKV_MULTI_TILES", raising=False)
+    b = Batch([L] * S, Hq, Hkv, d, 16, "bf16", seed=23)
+    q = wl.draw_values(wl.rng_for(24, wl.STREAM_Q), (S * L, Hq, d), "bf16")
+    out2, t, l, starts = b.multi([L] * S, q)
+    scale = np.float32(1.0 / np.sqrt(d))
+    for i in (0, 7, 15):
+        k, v = oc.to_f64(b.k[i], "bf16"), oc.to_f64(b.v[i], "bf16")
+        qq = oc.to_f64(q[starts[i]:starts[i + 1]], "bf16")
+        pos = [0, 1, 31, 32, 127, 128, 1000, 1023, 1024, 2046, 2047]
+        ref = np.stack([oa.attention_contiguous(qq[p], k[:p + 1], v[:p + 1], scale) for p in pos])
+        check_close(out2[starts[i] + np.array(pos)], ref, "bf16", f"prompt {i}")
+    monkeypatch.setenv("PKV_MULTI_TILES", "1")
+    out1, _, _, _ = b.multi([L] * S, q)
+    assert np.array_equal(out1, out2), float(np.max(np.abs(out1 - out2)))
 
 
 def test_full_size_verification_sampled():
