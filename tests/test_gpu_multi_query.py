@@ -307,6 +307,32 @@ def test_full_size_verification_sampled():
         check_close(out[starts[i]:starts[i + 1]], ref, s.kv_dtype, f"sequence {i}")
 
 
+def test_full_size_mixed_step_sampled():
+    """One continuous-batching step at full size, launched as timed: 64 sequences with contexts uniform in
+    [640, 2048], 32/8 heads, d 128, bf16, B 16; 4 of them take a 512-query prompt chunk and 60 decode one token, in
+    longest-first order.  Sampled rows of every chunk and a set of decodes against the oracle."""
+    rng = wl.rng_for(31, 0)
+    S, Hq, Hkv, d = 64, 32, 8, 128
+    lens = [int(x) for x in rng.integers(640, 2048, size=S, endpoint=True)]
+    runs = [512] * 4 + [1] * (S - 4)
+    b = Batch(lens, Hq, Hkv, d, 16, "bf16", seed=31)
+    q = wl.draw_values(wl.rng_for(32, wl.STREAM_Q), (sum(runs), Hq, d), "bf16")
+    order = np.argsort(-np.array(lens), kind="stable").astype(np.int32)
+    out, t, l, starts = b.multi(runs, q, order=order)
+    scale = np.float32(1.0 / np.sqrt(d))
+    for i in range(4):  # the prompt chunks: rows at its start, chunk and tile edges, and its end
+        k, v = oc.to_f64(b.k[i], "bf16"), oc.to_f64(b.v[i], "bf16")
+        rows = np.array([0, 1, 15, 16, 63, 64, 255, 256, 510, 511])
+        pos = lens[i] - 512 + rows
+        qq = oc.to_f64(q[starts[i] + rows], "bf16")
+        ref = np.stack([oa.attention_contiguous(qq[j], k[:p + 1], v[:p + 1], scale) for j, p in enumerate(pos)])
+        check_close(out[starts[i] + rows], ref, "bf16", f"chunk of sequence {i}")
+    dec = [4, 5, 17, 40, 63, int(np.argmax(lens[4:])) + 4]
+    ref = np.stack([b.oracle(q[starts[i]:starts[i] + 1], t[i:i + 1], l[i:i + 1], np.array([0, 1], np.int32))[0]
+                    for i in dec])
+    check_close(out[[starts[i] for i in dec]], ref, "bf16", "decodes")
+
+
 def test_repeated_calls_and_graph_replays_are_bitwise_stable():
     """Runs of queries give the same bits on every call, and as a captured HIP graph on every replay, with eager
     work and synchronisations between the replays."""
