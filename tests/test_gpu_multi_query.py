@@ -270,6 +270,34 @@ def test_edge_cases():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("tiles", ["1", "2"])
+def test_edge_cases_wide_runs(tiles, monkeypatch):
+    """The edge cases with more than 64 rows per (sequence, KV head), in both kernels: runs longer than
+    max_query_len or than their context give NaN on the rows the launch covers and leave the rest alone, an empty
+    run writes nothing, and a bad block id poisons only the rows of its own sequence."""
+    monkeypatch.setenv("PKV_MULTI_TILES", tiles)
+    b = Batch([40, 33, 20, 64, 90], 8, 2, 64, 16, "f32", seed=3)  # G = 4: max_query_len 20 makes 80 rows
+    t, l = b.tables()
+    runs = [30, 0, 21, 2, 20]
+    T = sum(runs)
+    q = wl.draw_values(wl.rng_for(41, wl.STREAM_Q), (T, 8, 64), "f32")
+    starts = np.concatenate([[0], np.cumsum(runs)]).astype(np.int32)
+    sentinel = torch.full((T, 8, 64), 7.0, dtype=torch.float32, device="cuda")
+    out, *_ = b.multi(runs, q, tables=t, lens=l, query_start=starts, max_query_len=20, out=sentinel)
+    assert np.all(np.isnan(out[0:20])) and np.all(out[20:30] == 7.0)  # 30 > max_query_len
+    assert np.all(np.isnan(out[30:50])) and np.all(out[50] == 7.0)  # 21 > its 20-token context
+    ref3 = b.oracle(q[51:53], t[3:4], l[3:4], np.array([0, 2], np.int32))
+    ref4 = b.oracle(q[53:73], t[4:5], l[4:5], np.array([0, 20], np.int32))
+    check_close(out[51:53], ref3, "f32", f"sequence 3, tiles {tiles}")
+    check_close(out[53:73], ref4, "f32", f"sequence 4, tiles {tiles}")
+    t2 = t.copy()
+    t2[4, 2] = b.nb + 5  # tokens 32-47 of sequence 4: every one of its rows sees them
+    sentinel.fill_(7.0)
+    out, *_ = b.multi(runs, q, tables=t2, lens=l, query_start=starts, max_query_len=20, out=sentinel)
+    check_close(out[51:53], ref3, "f32", f"sequence 3 beside a bad id, tiles {tiles}")
+    assert np.all(np.isnan(out[53:73]))
+
+
 def test_full_size_prefill_sampled(monkeypatch):
     """Whole prompts at the prefill shape (16 prompts x 2048 tokens, 32/8 heads, d 128, bf16, B 16): the batch's
     rows fill the GPU, so the call takes two row tiles per wave.  Sampled rows (chunk and tile edges, first and last
