@@ -348,9 +348,13 @@ MULTI_CASES = {
     # one continuous-batching step: 4 sequences take a 512-token prompt chunk, 60 decode one token
     "mixed4x512_plus60_gqa_bf16": (64, 32, 8, (640, 2048), ("mixed", 4, 512)),
 }
+# --multi-sweep: the verification batches with 1, 2, 4 or 8 drafted tokens per sequence (how the cost of a run
+# grows with its length, against the decode kernel on the same kind of batch).
+SWEEP_CASES = {f"verify{k}_llama7b_bf16": (64, 32, 32, (128, 2048), k) for k in (1, 2, 4, 8)}
+SWEEP_CASES.update({f"verify{k}_gqa_bf16": (256, 64, 8, (128, 2048), k) for k in (1, 4)})
 
 
-def measure_multi(stream, reps=20, case=None):
+def measure_multi(stream, reps=20, case=None, cases=None):
     """pkv_paged_attention_multi on synthetic batches (bf16 caches, d 128, B 16, shuffled pool, every valid slot
     N(0, 1)).  Verification runs are reported as KV GB/s (each sequence's K/V bytes counted once) against HBM
     peak; prompt runs as matrix-core TFLOP/s (4 d flop per visible (query head, token) pair: QK and PV) against
@@ -359,7 +363,7 @@ def measure_multi(stream, reps=20, case=None):
     import paged_kv_cache_physical_amd as pk
     d, B = 128, 16
     out = {}
-    for name, (S, Hq, Hkv, lens_spec, run) in MULTI_CASES.items():
+    for name, (S, Hq, Hkv, lens_spec, run) in (MULTI_CASES if cases is None else cases).items():
         if case is not None and name != case:
             continue
         rng = np.random.default_rng(1)
@@ -500,6 +504,8 @@ def main():
     ap.add_argument("--no-multi", action="store_true", help="skip the runs-of-queries measurement")
     ap.add_argument("--multi-only", action="store_true", help="only the runs-of-queries measurement")
     ap.add_argument("--multi-case", default=None, help="with --multi-only: one case of MULTI_CASES")
+    ap.add_argument("--multi-sweep", action="store_true",
+                    help="only the verification batches with 1, 2, 4 and 8 drafted tokens (SWEEP_CASES)")
     ap.add_argument("--swap-only", action="store_true",
                     help="run only the swap measurement and print its JSON object (for profiling pkv_swap_blocks)")
     ap.add_argument("--partition", type=int, default=None, help="override the workload's partition size")
@@ -532,6 +538,9 @@ def main():
     stream = torch.cuda.Stream()  # default priority
     if args.swap_only:
         print(json.dumps(measure_swap(stream)), flush=True)
+        return
+    if args.multi_sweep:
+        print(json.dumps(measure_multi(stream, cases=SWEEP_CASES)), flush=True)
         return
     if args.multi_only:
         print(json.dumps(measure_multi(stream, case=args.multi_case)), flush=True)
