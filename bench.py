@@ -124,6 +124,7 @@ def measure(w, steps, warmup, stream):
         rc = time_launches(lambda: gb.write_decode_token(stream=stream), n_k, stream)
         attn = time_launches(lambda: gb.attention(stream=stream), n_k, stream)
         sep = time_launches(lambda: gb.step_separate(stream=stream), n_k, stream)
+        stp = time_launches(lambda: gb.step(stream=stream), n_k, stream)  # per-step spread
     res = {
         "ms_per_step": ms_step,
         "wall_ms_per_step": 1e3 * wall / steps,
@@ -131,6 +132,7 @@ def measure(w, steps, warmup, stream):
         "seq_steps_per_s": w.num_seqs / (ms_step * 1e-3),
         "partition_kernel_us": {"mean": 1e3 * part[0], "median": 1e3 * part[1], "p10": 1e3 * part[2],
                                 "p90": 1e3 * part[3]},
+        "step_us": {"mean": 1e3 * stp[0], "median": 1e3 * stp[1], "p10": 1e3 * stp[2], "p90": 1e3 * stp[3]},
         "reduce_kernel_us": 1e3 * red[0],
         "reshape_and_cache_us": 1e3 * rc[0],
         "attention_us": 1e3 * attn[0],
@@ -599,6 +601,8 @@ def main():
                        "reshape_and_cache": round(head["reshape_and_cache_us"], 2),
                        "attention_call": round(head["attention_us"], 2),
                        "step_as_separate_calls": round(head["separate_calls_step_us"], 2)},
+        "timing_us": {"step_each_launch": {k: round(v, 2) for k, v in head["step_us"].items()},
+                      "partition_pass": {k: round(v, 2) for k, v in head["partition_kernel_us"].items()}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(w.spec.name),
