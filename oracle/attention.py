@@ -132,12 +132,15 @@ def paged_attention_multi(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarra
     (``q`` is ``[T][H_q][d]`` in the cache's storage dtype); they are its last
     q_s positions n_s - q_s .. n_s - 1, and row i of the run (position
     p = n_s - q_s + i) attends to tokens 0 .. p of the sequence, read through
-    its block table.  Written out as that definition: gather, then one
-    contiguous attention per query over its visible prefix.
+    its block table.  Written out as that definition in matrix form: gather,
+    then per query head the scores of every query of the run against every
+    token (one matrix product), -inf where t > p, a softmax along each row with
+    its maximum subtracted, and the weighted sum of the values.
     """
     T, Hq, d = q.shape
     out = np.full((T, Hq, d), np.nan)
     starts = [int(x) for x in query_start]
+    sc = float(np.float64(scale))
     for s in range(len(starts) - 1):
         n = int(context_lens[s])
         qs = starts[s + 1] - starts[s]
@@ -148,8 +151,17 @@ def paged_attention_multi(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarra
         k, v = _cache.gather(k_cache, v_cache, block_tables[s], n)
         k = _cache.to_f64(k, kv_dtype)
         v = _cache.to_f64(v, kv_dtype)
-        for i in range(qs):
-            p = n - qs + i
-            row = starts[s] + i
-            out[row] = attention_contiguous(_cache.to_f64(q[row], kv_dtype), k[:p + 1], v[:p + 1], scale)
+        Hkv = k.shape[1]
+        if Hq % Hkv:
+            raise ValueError("H_q must be a multiple of H_kv")
+        G = Hq // Hkv
+        rows = slice(starts[s], starts[s + 1])
+        qq = _cache.to_f64(q[rows], kv_dtype)  # [q_s][H_q][d]
+        pos = np.arange(n - qs, n)  # the run's positions
+        visible = np.arange(n)[None, :] <= pos[:, None]  # [q_s][n]: token t is seen at position p iff t <= p
+        for h in range(Hq):
+            g = h // G
+            sco = np.where(visible, sc * (qq[:, h, :] @ k[:, g, :].T), -np.inf)
+            w = np.exp(sco - sco.max(axis=1, keepdims=True))
+            out[rows, h] = (w @ v[:, g, :]) / w.sum(axis=1, keepdims=True)
     return out
