@@ -86,11 +86,15 @@ constexpr int kMqRows = 16 * kMqWaves;  // rows per workgroup
 constexpr int kMqChunk = 32;            // tokens per chunk (every supported shape)
 
 // T: 16-row tiles per wave (1, or 2 for prompts: two independent chains per
-// wave, each K/V operand read from LDS once for both).  With one tile, three
-// workgroups per CU: at bf16/d = 128 the compiler then keeps the accumulators
-// in VGPRs (146, no AGPR copies, no scratch); with two, two per CU.
+// wave, each K/V operand read from LDS once for both).  One tile: three
+// workgroups per CU, and at bf16/d = 128 the compiler then keeps the
+// accumulators in VGPRs (146, no AGPR copies, no scratch).  Two tiles, and
+// fp32 at d = 128 (32-token chunks of fp32 keys and values fill 64 KiB of LDS
+// per workgroup, so no third fits the CU's 160 KiB), two per CU.
+template <class DT, int D>
+constexpr int mq_min_blocks(int T) { return (T == 1 && !(std::is_same<DT, F32>::value && D == 128)) ? 3 : 2; }
 template <class DT, int D, int G, int T>
-__global__ __launch_bounds__(kWave* kMqWaves, T == 1 ? 3 : 2) void paged_multi_query_kernel(const MultiArgs a) {
+__global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void paged_multi_query_kernel(const MultiArgs a) {
   constexpr bool kBF16 = std::is_same<DT, BF16>::value;
   constexpr int kItem = DT::kItem;
   constexpr int KS = D * kItem / 64;  // QK k-steps: four 16-byte pieces each
@@ -228,7 +232,12 @@ __global__ __launch_bounds__(kWave* kMqWaves, T == 1 ? 3 : 2) void paged_multi_q
   // i / ITEMS (the same for a whole wave); within it, key piece ii is (key
   // piece ii / 16, token ii % 16) and value piece ii is (dim ii / kItem,
   // tokens (ii % kItem) * 16 / kItem + 0 ..).
+  // A bad block id is seen only by the threads that stage its tile; the flag
+  // is combined over the workgroup after the chunk loop, since every wave's
+  // rows read the whole chunk from LDS.
   bool poison = false;
+  __shared__ int poison_any;
+  if (tid == 0) poison_any = 0;  // ordered before any write of 1 by the barriers below
   const int64_t table_row = static_cast<int64_t>(s) * a.max_blocks;
   uint4 kr[NIT], vr[NIT];
   auto stage = [&](int c) __attribute__((always_inline)) {
@@ -449,6 +458,9 @@ __global__ __launch_bounds__(kWave* kMqWaves, T == 1 ? 3 : 2) void paged_multi_q
     stage(c + 2);
     __syncthreads();
   }
+  if (__ballot(poison) != 0 && lane == 0) poison_any = 1;
+  __syncthreads();
+  poison = poison_any != 0;
   float l_tot[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) l_tot[t] = sum_xor32(sum_xor16(l_run[t]));  // every lane takes part in the swaps
