@@ -298,30 +298,49 @@ def test_edge_cases_wide_runs(tiles, monkeypatch):
     assert np.all(np.isnan(out[53:73]))
 
 
-def test_full_size_prefill_sampled(monkeypatch):
+@pytest.mark.parametrize("split", [False, True])
+def test_bad_block_id_in_the_second_half_of_a_chunk(split):
+    """bf16, d = 64, B = 16: a 32-token chunk is staged by two halves of the workgroup, waves 0-1 loading tokens
+    0-15 and waves 2-3 tokens 16-31, while every wave reads the whole chunk from LDS.  A bad block id in tokens
+    16-31 must make the rows that saw it NaN even when all of them sit in wave 0 (3 queries x G = 4 rows), with
+    and without context splits; the other sequence stays exact."""
+    lens = [1200, 700]
+    runs = [3, 3]
+    b = Batch(lens, 8, 2, 64, 16, "bf16", seed=51)
+    t, l = b.tables()
+    q = wl.draw_values(wl.rng_for(52, wl.STREAM_Q), (sum(runs), 8, 64), "bf16")
+    out, _, _, starts = b.multi(runs, q, tables=t, lens=l, split=split)
+    ref = b.oracle(q, t, l, starts)
+    check_close(out, ref, "bf16", f"both sequences, split={split}")
+    t2 = t.copy()
+    t2[0, 1] = b.nb + 5  # block 1 of sequence 0: tokens 16-31, the second half of its first chunk
+    out, *_ = b.multi(runs, q, tables=t2, lens=l, split=split)
+    assert np.all(np.isnan(out[:3])), "rows that read a bad block id"
+    check_close(out[3:], ref[3:], "bf16", f"the sequence beside it, split={split}")
+
+
+def test_full_size_prefill(monkeypatch):
     """Whole prompts at the prefill shape (16 prompts x 2048 tokens, 32/8 heads, d 128, bf16, B 16): the batch's
-    rows fill the GPU, so the call takes two row tiles per wave.  Sampled rows (chunk and tile edges, first and last
-    positions) against the oracle on each prompt's own K/V; forcing one tile per wave gives the same rows."""
+    rows fill the GPU, so the call takes two row tiles per wave.  Every row of four whole prompts (first, last and
+    two between) against the float64 oracle over the oracle pool's own caches; forcing one tile per wave gives the
+    same bits for the whole batch."""
     S, L, Hq, Hkv, d = 16, 2048, 32, 8, 128
     monkeypatch.delenv("PKV_MULTI_TILES", raising=False)
     b = Batch([L] * S, Hq, Hkv, d, 16, "bf16", seed=23)
     q = wl.draw_values(wl.rng_for(24, wl.STREAM_Q), (S * L, Hq, d), "bf16")
     out2, t, l, starts = b.multi([L] * S, q)
-    scale = np.float32(1.0 / np.sqrt(d))
-    for i in (0, 7, 15):
-        k, v = oc.to_f64(b.k[i], "bf16"), oc.to_f64(b.v[i], "bf16")
-        qq = oc.to_f64(q[starts[i]:starts[i + 1]], "bf16")
-        pos = [0, 1, 31, 32, 127, 128, 1000, 1023, 1024, 2046, 2047]
-        ref = np.stack([oa.attention_contiguous(qq[p], k[:p + 1], v[:p + 1], scale) for p in pos])
-        check_close(out2[starts[i] + np.array(pos)], ref, "bf16", f"prompt {i}")
+    for i in (0, 5, 10, 15):
+        rows = slice(starts[i], starts[i + 1])
+        ref = b.oracle(q[rows], t[i:i + 1], l[i:i + 1], np.array([0, L], np.int32))
+        check_close(out2[rows], ref, "bf16", f"prompt {i}, all {L} rows")
     monkeypatch.setenv("PKV_MULTI_TILES", "1")
     out1, _, _, _ = b.multi([L] * S, q)
     assert np.array_equal(out1, out2), float(np.max(np.abs(out1 - out2)))
 
 
-def test_full_size_verification_sampled():
+def test_full_size_verification():
     """Speculative verification at the Llama-7B decode shape (64 sequences, 32 heads, d 128, bf16, lengths
-    uniform in [128, 2048]) with 4 drafted tokens per sequence; sampled sequences against the oracle."""
+    uniform in [128, 2048]) with 4 drafted tokens per sequence: every row of the batch against the oracle."""
     w = wl.named("llama7b_bf16", seed=0)
     s = w.spec
     runs = [4] * w.num_seqs
@@ -329,16 +348,13 @@ def test_full_size_verification_sampled():
     b = Batch(lens, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, s.kv_dtype, seed=0, spare=64)
     q = wl.draw_values(wl.rng_for(17, wl.STREAM_Q), (sum(runs), s.num_q_heads, s.head_dim), s.kv_dtype)
     out, t, l, starts = b.multi(runs, q)
-    pick = [0, 9, 31, 63]
-    for i in pick:
-        ref = b.oracle(q[starts[i]:starts[i + 1]], t[i:i + 1], l[i:i + 1], np.array([0, 4], np.int32))
-        check_close(out[starts[i]:starts[i + 1]], ref, s.kv_dtype, f"sequence {i}")
+    check_close(out, b.oracle(q, t, l, starts), s.kv_dtype, f"all {len(runs)} runs")
 
 
-def test_full_size_mixed_step_sampled():
+def test_full_size_mixed_step():
     """One continuous-batching step at full size, launched as timed: 64 sequences with contexts uniform in
     [640, 2048], 32/8 heads, d 128, bf16, B 16; 4 of them take a 512-query prompt chunk and 60 decode one token, in
-    longest-first order.  Sampled rows of every chunk and a set of decodes against the oracle."""
+    longest-first order.  Every row (the four chunks and the 60 decodes) against the oracle."""
     rng = wl.rng_for(31, 0)
     S, Hq, Hkv, d = 64, 32, 8, 128
     lens = [int(x) for x in rng.integers(640, 2048, size=S, endpoint=True)]
@@ -347,18 +363,9 @@ def test_full_size_mixed_step_sampled():
     q = wl.draw_values(wl.rng_for(32, wl.STREAM_Q), (sum(runs), Hq, d), "bf16")
     order = np.argsort(-np.array(lens), kind="stable").astype(np.int32)
     out, t, l, starts = b.multi(runs, q, order=order)
-    scale = np.float32(1.0 / np.sqrt(d))
-    for i in range(4):  # the prompt chunks: rows at its start, chunk and tile edges, and its end
-        k, v = oc.to_f64(b.k[i], "bf16"), oc.to_f64(b.v[i], "bf16")
-        rows = np.array([0, 1, 15, 16, 63, 64, 255, 256, 510, 511])
-        pos = lens[i] - 512 + rows
-        qq = oc.to_f64(q[starts[i] + rows], "bf16")
-        ref = np.stack([oa.attention_contiguous(qq[j], k[:p + 1], v[:p + 1], scale) for j, p in enumerate(pos)])
-        check_close(out[starts[i] + rows], ref, "bf16", f"chunk of sequence {i}")
-    dec = [4, 5, 17, 40, 63, int(np.argmax(lens[4:])) + 4]
-    ref = np.stack([b.oracle(q[starts[i]:starts[i] + 1], t[i:i + 1], l[i:i + 1], np.array([0, 1], np.int32))[0]
-                    for i in dec])
-    check_close(out[[starts[i] for i in dec]], ref, "bf16", "decodes")
+    ref = b.oracle(q, t, l, starts)
+    check_close(out[:4 * 512], ref[:4 * 512], "bf16", "the four prompt chunks, all rows")
+    check_close(out[4 * 512:], ref[4 * 512:], "bf16", "the 60 decodes")
 
 
 def test_repeated_calls_and_graph_replays_are_bitwise_stable():

@@ -61,16 +61,6 @@ def check_close(out, ref, kv_dtype, what=""):
     assert rl2 <= 1e-4, (what, rl2)
 
 
-def oracle_rows(w, seqs):
-    s = w.spec
-    ref = {}
-    for i in seqs:
-        k, v = w.token_kv(i)
-        ref[i] = oa.attention_contiguous(oc.to_f64(w.q[i], s.kv_dtype), oc.to_f64(k, s.kv_dtype),
-                                         oc.to_f64(v, s.kv_dtype), w.scale)
-    return ref
-
-
 def full_parity(w, partitions):
     GpuBatch = runner()
     s = w.spec
@@ -158,36 +148,32 @@ def test_more_sequences_than_the_item_list_holds():
     full_parity(w, [0, 16])
 
 
-@pytest.mark.parametrize("name,nsample", [("llama7b_bf16", 12), ("gqa_bf16_b16", 12), ("gqa_bf16_b32", 12),
-                                          ("beam_cow_bf16", 16), ("long_bf16", 3)])
-def test_named_full_size(name, nsample):
+@pytest.mark.parametrize("name", ["llama7b_bf16", "gqa_bf16_b16", "gqa_bf16_b32", "beam_cow_bf16", "long_bf16"])
+def test_named_full_size(name):
+    """A full-size workload, every output row against the float64 oracle (the contiguous-KV baseline of the
+    guide's verification protocol): block tables and lengths equal the oracle pool's, both whole caches equal the
+    oracle's own scatter bit for bit (unwritten slots' NaN poison included), and the attention output over all
+    S x H_q x d elements meets the bars at the workload's partition size and unsplit, as does the decode step
+    (token write plus attention), which is also idempotent."""
     GpuBatch = runner()
     w = wl.named(name, seed=0)
     s = w.spec
     say(f"case {name}: S={w.num_seqs} tokens={w.total_tokens} pool={w.num_blocks}")
     gb = GpuBatch(w)
-    rp = orun.replay(w, with_cache=False)
+    rp = orun.replay(w)
     assert np.array_equal(gb.tables_host[:, :rp.tables.shape[1]], rp.tables)
+    assert np.all(gb.tables_host[:, rp.tables.shape[1]:] == -1)
     assert np.array_equal(gb.lens_host, rp.context_lens)
-    rng = np.random.default_rng(1)
-    lens = w.context_lens
-    picks = set(rng.choice(w.num_seqs, size=min(nsample, w.num_seqs), replace=False).tolist())
-    picks |= {int(np.argmax(lens)), int(np.argmin(lens))}
-    picks = sorted(picks)
-    # cache bytes of the sampled sequences, read back through their tables
-    kc, vc = host_bits(gb.k_cache), host_bits(gb.v_cache)
-    for i in picks:
-        kg, vg = oc.gather(kc, vc, rp.tables[i], int(lens[i]))
-        kt, vt = w.token_kv(i)
-        assert same_bits(kg, kt) and same_bits(vg, vt), f"cache bytes of sequence {i}"
-    del kc, vc
-    ref = oracle_rows(w, picks)
+    assert same_bits(host_bits(gb.k_cache), rp.k_cache), "key cache bytes"
+    assert same_bits(host_bits(gb.v_cache), rp.v_cache), "value cache bytes"
+    ref = oa.paged_attention(w.q, rp.k_cache, rp.v_cache, rp.tables, rp.context_lens, w.scale, s.kv_dtype)
+    del rp
+    say(f"  oracle: {ref.shape[0]} sequences x {ref.shape[1]} heads x {ref.shape[2]} dims")
     for P in sorted({s.partition_size, 0}):
         out = gb.attention(P).cpu().numpy()
-        check_close(np.stack([out[i] for i in picks]), np.stack([ref[i] for i in picks]), s.kv_dtype,
-                    f"{name} P={P}")
-    # the decode step (K/V write + attention) is idempotent
+        check_close(out, ref, s.kv_dtype, f"{name} P={P}, all rows")
     out1 = gb.step().cpu().numpy()
+    check_close(out1, ref, s.kv_dtype, f"{name} decode step, all rows")
     out2 = gb.step().cpu().numpy()
     assert np.array_equal(out1, out2)
 
