@@ -32,10 +32,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 METRIC = "decode-attention KV GB/s (% of HBM peak) and seq-steps/sec at 1 MI355X"
-HEADLINE = "llama7b_bf16"
-EXTRA = ["gqa_bf16_b16", "gqa_bf16_b32", "long_bf16", "beam_cow_bf16"]
-KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_physical_amd", "csrc", f)
-               for f in ("attention.hip", "device_common.h")]
+# The headline: the largest single-GPU decode batch (256 sequences, GQA 64/8 heads, lognormal contexts).
+HEADLINE = "gqa_bf16_b16"
+EXTRA = ["llama7b_bf16", "gqa_bf16_b32", "long_bf16", "beam_cow_bf16"]
+_CSRC = os.path.join(ROOT, "paged_kv_cache_physical_amd", "csrc")
+# Source files of each kernel family; a profile-derived number is used only while its family's hash matches.
+KERNEL_FAMILIES = {
+    "decode": ("attention.hip", "device_common.h"),
+    "multi_query": ("multi_query.hip", "device_common.h"),
+    "cache_ops": ("cache_ops.hip", "device_common.h"),
+}
 
 
 def log(*a):
@@ -49,13 +55,17 @@ def code_text(src: str) -> str:
     return "\n".join(line for line in lines if line.strip())
 
 
-def kernel_sha() -> str:
-    """Hash of the attention kernel's code (ties profile-derived numbers to the code they measured)."""
+def kernel_sha(family: str = "decode") -> str:
+    """Hash of one kernel family's code (ties profile-derived numbers to the code they measured)."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, encoding="utf-8") as f:
+    for name in KERNEL_FAMILIES[family]:
+        with open(os.path.join(_CSRC, name), encoding="utf-8") as f:
             h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
+
+
+def source_shas() -> dict:
+    return {fam: kernel_sha(fam) for fam in KERNEL_FAMILIES}
 
 
 def describe(w) -> dict:
@@ -616,6 +626,7 @@ def main():
         "cpu_baseline": cpu,
         "other_workloads": extra,
         "kernel_source_sha": kernel_sha(),
+        "source_shas": source_shas(),
     }
     print(json.dumps(line), flush=True)
 

@@ -118,11 +118,14 @@ int32_t pkv_abi_version(void);
 pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
                            pkv_pool** out);
 
-/* Destroy a pool and every sequence in it.  NULL is ignored. */
+/* Destroy a pool and every sequence in it.  NULL is ignored.  A utility with
+ * no passage of its own: it releases the host metadata the pool owns. */
 void pkv_pool_destroy(pkv_pool* pool);
 
-/* Create an empty sequence (0 tokens, 0 blocks).  Ids are 0, 1, 2, ... in
- * creation order (forks included) and are never reused. */
+/* Create an empty sequence (0 tokens, 0 blocks): a new request holds no
+ * block until it grows onto one ([P2] core idea item 4 and [P1] core method,
+ * allocation on demand).  Ids are 0, 1, 2, ... in creation
+ * order (forks included) and are never reused. */
 pkv_status pkv_seq_create(pkv_pool* pool, int32_t* out_seq);
 
 /* Create a child that shares every block of parent: the child's table is a copy
@@ -220,7 +223,9 @@ pkv_status pkv_seq_info(const pkv_pool* pool, int32_t seq, int32_t* out_len, int
 /* Pool counters ([P3] Eq. (2)-(3) and section 6's accounting categories). */
 pkv_status pkv_pool_stats(const pkv_pool* pool, pkv_stats* out);
 
-/* Refcount of one physical block, or -1 for an id out of range. */
+/* Refcount of one physical block, or -1 for an id out of range: the number
+ * of block tables that map it ([P3] section 3: a shared block's lifetime is
+ * tied to a reference count; [P4] beam-search sharing). */
 int32_t pkv_block_refcount(const pkv_pool* pool, int32_t block);
 
 /* Copy the free queue, head first, into host out[cap]; *out_n = its length.
@@ -306,9 +311,10 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, void* k_c
 
 /* Copy whole blocks (every head and slot of both caches) src -> dst for each
  * pair: the device half of copy-on-write ([P3] section 3).
- * pairs: device int32[n_pairs][2] as returned by pkv_append_tokens.  The dst
- * blocks must be distinct (checked in debug mode) and no dst may be another
- * pair's src (the pool never produces either).  Pairs with an id out of
+ * pairs: device int32[n_pairs][2] as returned by pkv_append_tokens.  Every pair
+ * is copied at once, so the dst blocks must be distinct and no dst may also
+ * be a src in the same call, its own pair's included (the pool never produces
+ * either; debug mode refuses both with INVALID_ARG).  Pairs with an id out of
  * [0, num_blocks) are skipped.
  * block_bytes: bytes of one block in one cache, H_kv * B * d * scalar size.
  * Errors: INVALID_ARG (block_bytes not a positive multiple of 16), HIP. */
@@ -335,7 +341,10 @@ pkv_status pkv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, vo
                            hipStream_t stream);
 
 /* Bytes of workspace pkv_paged_attention_decode needs for these sizes (0 when
- * no sequence can span more than one partition). */
+ * no sequence can span more than one partition).  A utility with no passage
+ * of its own: the pages describe no split of a context; splitting long
+ * contexts across workgroups and combining them by log-sum-exp weights is
+ * this library's way to fill the GPU with few sequences. */
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                      int32_t block_size, int32_t max_context_len,
                                      int32_t partition_size);

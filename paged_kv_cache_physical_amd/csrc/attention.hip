@@ -1,8 +1,11 @@
 // Paged decode attention for gfx950: one query token per sequence, keys and
-// values read through block tables, split-context partitions combined by a
-// log-sum-exp reduction (PagedAttention, "PagedAttention" section and its
-// figure of the per-block computation; the split follows the decoding page's
-// partitioned reduction).
+// values read through block tables.  [P1] (lain42.top reading note), summary
+// section 2, core method: one custom kernel fuses the table lookup, the fetch
+// of scattered blocks and the attention; [P2] (aiplusplus.yigather.com
+// explainer), key technical point 1: the kernel reads each sequence's blocks
+// through its block table.  The pages do not describe cutting one context
+// across workgroups: the split context and its log-sum-exp combination are
+// this library's own, so that a few long sequences still fill the GPU.
 //
 // Unit of work: an item = the tokens of one sequence that a workgroup computes
 // for one KV head: a segment of its run of the cost-ordered work (up to 4096

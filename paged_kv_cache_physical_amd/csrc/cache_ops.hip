@@ -254,10 +254,17 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
     std::vector<int32_t> h;
     if (!fetch(h, pairs, 2 * static_cast<size_t>(n_pairs), stream)) return PKV_ERR_HIP;
     std::vector<int32_t> dst;
+    std::vector<char> is_src(static_cast<size_t>(num_blocks), 0);
     for (int32_t i = 0; i < n_pairs; ++i) {
-      if (h[2 * i] >= 0 && h[2 * i] < num_blocks) dst.push_back(h[2 * i + 1]);  // pairs the kernel copies
+      const int32_t src = h[2 * i], d = h[2 * i + 1];
+      if (src < 0 || src >= num_blocks || d < 0 || d >= num_blocks) continue;  // pairs the kernel skips
+      dst.push_back(d);
+      is_src[static_cast<size_t>(src)] = 1;
     }
     if (!distinct_in_range(dst, num_blocks)) return PKV_ERR_INVALID_ARG;
+    // all pairs run at once: a block that is read and written in one call races
+    for (const int32_t d : dst)
+      if (is_src[static_cast<size_t>(d)]) return PKV_ERR_INVALID_ARG;
   }
   const int64_t n16 = block_bytes / 16;
   const int64_t splits = ceil_div64(n16, 256);
