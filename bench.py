@@ -3,12 +3,14 @@
 
 A step is one pass of the decode hot path over a synthetic batch already
 resident in HBM: write each sequence's new K/V token into its slot, then
-paged decode attention over every context (the partition kernel plus, when a
-context spans several partitions, the log-sum-exp reduce).  The step is one
-pkv_decode_step call, whose partition kernel writes the new tokens in its
-set-up; the same step as two calls (reshape_and_cache, then attention) is
-timed beside it.  The block pool, tables and the rest of the context are
-built once before timing by the library's own allocator and kernels.
+paged decode attention over every context, with the log-sum-exp combination
+of contexts cut between workgroups.  The step is one pkv_decode_step call, one
+kernel launch for up to 4096 sequences: the kernel writes the new tokens in
+its set-up and combines cut sequences at the end.  The same step as two calls
+(reshape_and_cache, then attention) and the two-stage attention (partition
+pass, then a separate combination) are timed beside it.  The block pool,
+tables and the rest of the context are built once before timing by the
+library's own allocator and kernels.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -149,6 +151,7 @@ def measure(w, steps, warmup, stream):
         "separate_calls_step_us": 1e3 * sep[0],
         "kv_gbps_partition_kernel": w.kv_bytes / (part[0] * 1e-3) / 1e9,
         "kv_gbps_attention": w.kv_bytes / (attn[0] * 1e-3) / 1e9,
+        "kv_gbps_step_launch": w.kv_bytes / (stp[0] * 1e-3) / 1e9,
     }
     pairs = [p for p in gb.pairs if len(p)]
     if pairs:  # copy-on-write copies made while building the batch, re-issued: idempotent
@@ -452,17 +455,21 @@ def copy_probe(stream, nbytes=1 << 30):
     torch.cuda.empty_cache()
 
 
-def is_partition_pass(kernel_name: str) -> bool:
-    """The plain partition kernel; its last template flag is set only in the decode step's variant, which also
-    writes the new tokens."""
+def decode_kernel_flags(kernel_name: str):
+    """(LIST, WRITE, FUSED) template flags of a paged_decode_kernel name, or None for another kernel."""
     if "paged_decode_kernel<" not in kernel_name:
-        return False
-    flags = kernel_name.split("paged_decode_kernel<", 1)[1].split(">", 1)[0].split(",")
-    return flags[-1].strip() == "false"
+        return None
+    args = [x.strip() for x in kernel_name.split("paged_decode_kernel<", 1)[1].split(">", 1)[0].split(",")]
+    return tuple(x == "true" for x in args[-3:])
+
+
+def is_step_kernel(kernel_name: str) -> bool:
+    """The decode step's kernel: item list, token write and in-kernel combination."""
+    return decode_kernel_flags(kernel_name) == (True, True, True)
 
 
 def traffic_summary(pmc_dirs, workload: str, nbytes=1 << 30):
-    """HBM bytes per partition-kernel dispatch from rocprofv3 --pmc CSVs (one run with FETCH_SIZE, one with
+    """HBM bytes per decode-step kernel dispatch from rocprofv3 --pmc CSVs (one run with FETCH_SIZE, one with
     WRITE_SIZE), each counter scaled by its reading on the copy probe of nbytes."""
     import csv
     import glob
@@ -471,7 +478,7 @@ def traffic_summary(pmc_dirs, workload: str, nbytes=1 << 30):
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 name, ctr = r["Kernel_Name"], r["Counter_Name"]
-                kind = ("decode" if is_partition_pass(name) else
+                kind = ("decode" if is_step_kernel(name) else
                         "copy" if "copy" in name.lower() else None)
                 if kind is None:
                     continue
@@ -587,7 +594,7 @@ def main():
     if cpu:
         log(f"[bench] cpu baseline {json.dumps(cpu)}")
 
-    achieved = head["kv_gbps_partition_kernel"]
+    achieved = head["kv_gbps_step_launch"]
     line = {
         "metric": METRIC,
         "value": round(head["kv_gbps_step"], 2),
@@ -606,8 +613,9 @@ def main():
         "pct_hbm_peak_step": round(100 * head["kv_gbps_step"] / HBM_PEAK_GBPS, 2),
         "host_allocator_us_per_step": round(head.get("host_allocator_us_per_step", float("nan")), 2),
         "host_allocator_c_us_per_step": round(head.get("host_allocator_c_us_per_step", float("nan")), 2),
-        "kernels_us": {"paged_decode_partitions": round(head["partition_kernel_us"]["mean"], 2),
-                       "lse_reduce": round(head["reduce_kernel_us"], 2),
+        "kernels_us": {"decode_step_kernel": round(head["step_us"]["mean"], 2),
+                       "two_stage_partition_pass": round(head["partition_kernel_us"]["mean"], 2),
+                       "two_stage_reduce": round(head["reduce_kernel_us"], 2),
                        "reshape_and_cache": round(head["reshape_and_cache_us"], 2),
                        "attention_call": round(head["attention_us"], 2),
                        "step_as_separate_calls": round(head["separate_calls_step_us"], 2)},
@@ -616,9 +624,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_from_profiles(w.spec.name),
-                     "kernel": "paged_decode_kernel (partition pass)",
+                     "kernel": "paged_decode_kernel, decode-step variant (token write, attention, in-kernel "
+                               "combination: the step's only launch)",
                      "bytes_per_launch": w.kv_bytes,
-                     "launch_us": round(head["partition_kernel_us"]["mean"], 2)},
+                     "launch_us": round(head["step_us"]["mean"], 2)},
         "hbm_read_ceiling_gbps": round(ceiling, 1),
         "swap": swap,
         "multi_query": multi,

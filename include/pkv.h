@@ -340,13 +340,20 @@ pkv_status pkv_swap_blocks(const void* src_k, const void* src_v, void* dst_k, vo
                            int32_t n_pairs, int32_t src_blocks, int32_t dst_blocks, int64_t block_bytes,
                            hipStream_t stream);
 
-/* Bytes of workspace pkv_paged_attention_decode needs for these sizes (0 when
- * no sequence can span more than one partition).  A utility with no passage
- * of its own: the pages describe no split of a context; splitting long
- * contexts across workgroups and combining them by log-sum-exp weights is
- * this library's way to fill the GPU with few sequences. */
-size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                     int32_t block_size, int32_t max_context_len,
+/* Bytes of workspace pkv_paged_attention_decode, pkv_decode_step and the
+ * two-stage calls need for these sizes (0 when no sequence can span more than
+ * one partition, i.e. partition_size == 0 or max_context_len <= it).  A
+ * utility with no passage of its own: the pages describe no split of a
+ * context; splitting long contexts across workgroups and combining them by
+ * log-sum-exp weights is this library's way to fill the GPU with few
+ * sequences.  With up to 4096 sequences the workspace holds two records per
+ * workgroup of the persistent grid (at most 2048 workgroups): about
+ * 2 * min(2048, sequences * H_kv * partitions) * ((H_q / H_kv) * (d + 2) * 4 + 32)
+ * bytes whatever the lengths (17 MB at most for 64/8 heads and d 128); above
+ * 4096 sequences it holds one slot per (sequence, query head, partition).
+ * Errors: 0 for invalid sizes. */
+size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                      int32_t partition_size);
 
 /* Decode attention, one query token per sequence, reading K/V through block
@@ -364,12 +371,21 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int3
  *     n_s > max_blocks * B, or a block id outside [0, num_blocks) gives NaN.
  *   scale: any finite value (negative and zero included).
  *   partition_size: tokens per context partition (a multiple of B), or 0 for
- *     one partition per sequence.  The work is split at partition boundaries:
- *     a sequence is computed as one or more segments of consecutive
- *     partitions, and the segments' partial results are combined by a
- *     log-sum-exp reduction (split context); that needs `workspace` (device,
- *     workspace_bytes >= pkv_attention_workspace_bytes(...)) whenever a
- *     sequence can span more than one partition.  Its contents are private.
+ *     one partition per sequence.  The work is split at partition boundaries
+ *     (or inside a partition when every workgroup has plenty of work): a
+ *     sequence is computed as one or more segments, and the segments' partial
+ *     results are combined by log-sum-exp weights (split context).  With up
+ *     to 4096 sequences the combination happens in the same kernel: the
+ *     workgroup that computes a sequence's last segment waits for the others'
+ *     partials and combines them in token order; above that, a second kernel
+ *     does.  Splitting needs `workspace` (device, workspace_bytes >=
+ *     pkv_attention_workspace_bytes(...), 16-byte aligned) whenever a
+ *     sequence can span more than one partition.  Its contents are private
+ *     and need no initialisation (the hand-over between workgroups matches a
+ *     64-bit value derived from what the previous call left, so stale or
+ *     arbitrary contents do not leak into results, except with probability
+ *     2^-64 per record); one workspace serves one call at a time, so calls
+ *     in flight on different streams need different workspaces.
  * Arithmetic: fp32 accumulation; bf16 inputs are multiplied exactly and summed
  * in fp32 (probabilities enter the value product as two bf16 terms whose sum
  * is within 2^-16 of the fp32 value).  Errors: INVALID_ARG, UNSUPPORTED,
@@ -463,13 +479,14 @@ pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_ca
 size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t max_context_len, int32_t max_query_len);
 
-/* The two stages of pkv_paged_attention_decode, for callers that schedule or
- * time them separately.  Same arguments and errors; issue `partitions` then
- * `reduce` on one stream.
+/* pkv_paged_attention_decode as two launches, for callers that schedule or
+ * time the combination separately.  Same arguments and errors; issue
+ * `partitions` then `reduce` on one stream, with the same workspace; the
+ * output has the same bits as the one-call path.
  * pkv_paged_attention_partitions: one pass over every (sequence, KV head,
- *   segment of consecutive partitions); writes the final rows of sequences
- *   computed in one segment, and the (acc, max, sum) of every other segment
- *   with its extent into the workspace.
+ *   segment); writes the final rows of sequences computed in one segment, and
+ *   the (acc, max, sum) of every other segment with its extent into the
+ *   workspace.
  * pkv_paged_attention_reduce: combines the segments of every sequence that
  *   has more than one (log-sum-exp weights); a no-op when none has. */
 pkv_status pkv_paged_attention_partitions(float* out, const void* q, const void* k_cache, const void* v_cache,

@@ -437,10 +437,10 @@ def pkv_hbm_read_probe(buf, sink, stream=None) -> None:
           "pkv_hbm_read_probe")
 
 
-def pkv_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size, max_context_len,
+def pkv_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
                                   partition_size) -> int:
-    return int(lib().pkv_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, block_size, max_context_len,
-                                                   partition_size))
+    return int(lib().pkv_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                   max_context_len, partition_size))
 
 
 def _attention(fn: str, out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int, scale: float,

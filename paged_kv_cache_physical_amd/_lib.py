@@ -89,7 +89,7 @@ _SIGS = {
     "pkv_swap_blocks": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp]),
     "pkv_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
     "pkv_copy_blocks": (i32, [vp, vp, vp, i32, i32, i64, vp]),
-    "pkv_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
+    "pkv_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
     "pkv_hbm_read_probe": (i32, [vp, i64, vp, vp]),
     "pkv_paged_attention_decode": (i32, _ATTN),
     "pkv_paged_attention_partitions": (i32, _ATTN),

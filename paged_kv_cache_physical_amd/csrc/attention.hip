@@ -61,11 +61,19 @@ struct AttnArgs {
   const int32_t* context_lens;
   const void* k_new;  // decode step: the new token of each sequence [S][H_kv][d], written to the caches
   const void* v_new;  // (nullptr: no write)
-  float* ws_acc;  // [S][H_kv][max_parts][G][d]  one item's partials are one contiguous run
-  float* ws_m;    // [S][H_kv][max_parts][G]     maximum logit, exp2 domain (scaled)
-  float* ws_l;    // [S][H_kv][max_parts][G]     sum of exp2(logit - max)
-  int32_t* ws_seg;  // [S][H_kv][max_parts]      at a segment's slot: the slot of the sequence's next
+  // Workspace.  Item list (LIST): two records per workgroup b, record 2 b + j:
+  //   j = 1: the run's last segment when the run ends inside a sequence (an
+  //          empty segment for a run with no tokens that starts and ends there),
+  //   j = 0: the run's first segment when it is the last one of a sequence that
+  //          began in an earlier run (its "owner", which combines the sequence).
+  // Partition items (not LIST): one slot per (sequence, KV head, partition).
+  float* ws_acc;  // LIST [2 grid][G][d]; else [S][H_kv][max_parts][G][d]: un-normalised sums
+  float* ws_m;    // LIST [2 grid][G];    else [S][H_kv][max_parts][G]: maximum logit, exp2 domain (scaled)
+  float* ws_l;    // LIST [2 grid][G];    else [S][H_kv][max_parts][G]: sum of exp2(logit - max)
+  int32_t* ws_seg;  // not LIST [S][H_kv][max_parts]: at a segment's slot, the slot of the sequence's next
                     // segment (num partitions after the last); at slot 0 of a sequence written whole: -1
+  int32_t* ws_hdr;  // LIST [2 grid][4]: (sequence, first token, end token, 1 if record 0 of an owner)
+  uint64_t* ws_tag; // LIST [2 grid][2]: (turn, flag) of each record, see tag_next
   int32_t num_seqs;
   int32_t num_kv_heads;
   int32_t block_size;
@@ -77,6 +85,49 @@ struct AttnArgs {
   int32_t total_items;     // max_parts * num_seqs * num_kv_heads
   float c;                 // scale * log2(e): the softmax runs on u = c * (q . k) in the exp2 domain
 };
+
+// Hand-over of a record between workgroups of one launch, with no contract on
+// what the workspace holds beforehand.  Each record has a pair (turn, flag).
+// The writer of a record stores its data, makes it visible to the device,
+// then sets flag = tag_next(turn); the reader waits for exactly that value,
+// reads the data, and sets turn = tag_next(turn), which leaves flag == turn.
+// Visibility across the XCDs (each with its own L2) comes from the device
+// scope of the accesses themselves, not from fences: every store of a record
+// and of its pair has the device-scope bit (sc1), so it writes through the
+// L2, and every load of them has it too, so it misses in any cache that is
+// not coherent across the device; each writing wave waits for its stores to
+// complete (vmcnt(0)) before the flag is stored.  (A device-scope release or
+// acquire fence instead writes back or invalidates the XCD's whole L2 on
+// gfx950; done at every hand-over it made the pass 60% slower.)
+// tag_next is a bijection of 64-bit words (the output function of
+// SplitMix64, Steele, Lea and Flood), so from any state that ended a hand-over
+// (flag == turn) the next one needs a fresh write, and a pair that holds
+// unrelated data matches tag_next by chance with probability 2^-64.  The
+// pairs are indexed by record, whose position depends on the launch, so every
+// hand-over reads its own turn instead of a value passed in: replays of a
+// captured graph work the same way.
+__device__ __forceinline__ uint64_t tag_next(uint64_t x) {
+  x += 0x9e3779b97f4a7c15ull;
+  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+  return x ^ (x >> 31);
+}
+constexpr int kMaxPolls = 1 << 20;  // about a second of polling: a record that never comes gives NaN rows
+constexpr int kScopeDevice = 16;    // buffer-access cache policy: sc1, device scope (through L2)
+
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Device-scope loads through a wave-uniform resource at a per-lane byte
+// offset (an offset past the resource, such as kNowhere, reads zeros).
+__device__ __forceinline__ f32x4_t load_dev4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kScopeDevice));
+}
+__device__ __forceinline__ float load_dev(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kScopeDevice));
+}
+__device__ __forceinline__ int4 load_dev_i4(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kScopeDevice);
+  return make_int4(static_cast<int>(v[0]), static_cast<int>(v[1]), static_cast<int>(v[2]), static_cast<int>(v[3]));
+}
 
 // Number of partitions of a sequence of n_raw tokens (1 for an empty or
 // invalid one); sets *bad for invalid lengths.
@@ -162,11 +213,95 @@ struct Shared {
     float wl[kWaves][G];                         // per-wave sum of probabilities
   } mb[2];  // alternate items use alternate buffers: one barrier per item
   uint32_t csum[LIST ? kMaxListedSeqs + 1 : 1];  // prefix sums of sequence costs
+  int chain_first;  // combine: the first run holding a segment of the owner's sequence
+  int chain_ok;     // combine: every segment arrived and belongs to the sequence
 };
 
 // Cost of a partition in the work split: its groups plus a fixed charge for
 // an item's start-up and merge.
 constexpr int kItemCharge = 2;
+
+// Log-sum-exp combination of one sequence's segments for one KV head: the
+// segments sit in record 1 of runs first .. last - 1 and record 0 of run last,
+// in token order, and
+//   out = sum_r 2^(m_r - M) acc_r / sum_r 2^(m_r - M) l_r,   M = max_r m_r,
+// summed in that order (an empty segment has m = -inf and weighs nothing).
+// Explicit fmaf keeps the rounding identical wherever this is inlined, so the
+// fused and the two-stage paths give the same bits.  ok == false: NaN rows.
+template <int G, int D>
+__device__ __forceinline__ void combine_runs(const AttnArgs& a, int seq, int kvh, int first, int last, bool ok,
+                                             int tid) {
+  constexpr int NC = D / 4;  // float4 chunks of one head's row
+  constexpr int ITERS = (G * NC + kThreads - 1) / kThreads;
+  const int Hkv = a.num_kv_heads;
+  float* out = a.out + (static_cast<size_t>(seq) * Hkv + kvh) * G * D;
+  auto rec_of = [&](int L) __attribute__((always_inline)) { return 2 * (L * Hkv + kvh) + (L == last ? 0 : 1); };
+  // the launch's records: 2 per workgroup (at most 2 * 2048 * 8 * 128 * 4 bytes of sums)
+  const int recs = 2 * static_cast<int>(gridDim.x);
+  const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(a.ws_acc, recs * G * D * 4);
+  const __amdgpu_buffer_rsrc_t r_m = make_rsrc(a.ws_m, recs * G * 4);
+  const __amdgpu_buffer_rsrc_t r_l = make_rsrc(a.ws_l, recs * G * 4);
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int cidx = tid + it * kThreads;
+    if (cidx >= G * NC) break;
+    const int h = cidx / NC, d4 = (cidx % NC) * 4;
+    f32x4_t o = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    if (ok) {
+      // Records in groups of kGroup whose loads are all in flight at once (a
+      // record past the last one reads zeros, at an offset past the resource,
+      // and weighs nothing).  Up to kGroup records take one round of loads;
+      // more take a first round for the maximum.
+      constexpr int kGroup = 8;
+      float mv[kGroup], lv[kGroup];
+      f32x4_t av[kGroup];
+      auto load_group = [&](int L0, bool sums) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          const int r = rec_of(L0 + j) * G + h;
+          const bool in = L0 + j <= last;
+          mv[j] = load_dev(r_m, in ? r * 4 : kNowhere);
+          if (sums) {
+            lv[j] = load_dev(r_l, in ? r * 4 : kNowhere);
+            av[j] = load_dev4(r_acc, in ? (r * D + d4) * 4 : kNowhere);
+          }
+        }
+      };
+      float M = -INFINITY;
+      f32x4_t sa = {0.0f, 0.0f, 0.0f, 0.0f};
+      float sl = 0.0f;
+      auto add_group = [&](int L0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          const float w = L0 + j <= last ? __builtin_amdgcn_exp2f(mv[j] - M) : 0.0f;
+          sa.x = fmaf(w, av[j].x, sa.x);
+          sa.y = fmaf(w, av[j].y, sa.y);
+          sa.z = fmaf(w, av[j].z, sa.z);
+          sa.w = fmaf(w, av[j].w, sa.w);
+          sl = fmaf(w, lv[j], sl);
+        }
+      };
+      if (last - first < kGroup) {
+        load_group(first, true);
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) M = fmaxf(M, first + j <= last ? mv[j] : -INFINITY);
+        add_group(first);
+      } else {
+        for (int L0 = first; L0 <= last; L0 += kGroup) {
+          load_group(L0, false);
+#pragma unroll
+          for (int j = 0; j < kGroup; ++j) M = fmaxf(M, L0 + j <= last ? mv[j] : -INFINITY);
+        }
+        for (int L0 = first; L0 <= last; L0 += kGroup) {
+          load_group(L0, true);
+          add_group(L0);
+        }
+      }
+      o = f32x4_t{sa.x / sl, sa.y / sl, sa.z / sl, sa.w / sl};
+    }
+    *reinterpret_cast<f32x4_t*>(out + h * D + d4) = o;
+  }
+}
 
 // Workgroup b serves KV head b % H_kv (the grid is a multiple of H_kv), so the
 // H_kv workgroups of lane b / H_kv read the adjacent head tiles of the same
@@ -182,7 +317,13 @@ constexpr int kItemCharge = 2;
 // max_parts, dealt round-robin to the lanes, the empty ones (partition past
 // the sequence's end) skipped.  WRITE (LIST only): the decode step's variant,
 // which also stores each sequence's new token before reading.
-template <class DT, int D, int G, int B, bool LIST, bool WRITE>
+// FUSED (LIST only): the workgroup whose run starts with the last segment of a
+// sequence cut between runs (its owner) combines that sequence's segments at
+// the end of its run, once the earlier runs have handed their records over;
+// without it, list_reduce_kernel does the same work as a second launch.  An
+// owner waits only for runs of lower index, which never wait on it, and it
+// waits after its own work is done, so every run's work proceeds.
+template <class DT, int D, int G, int B, bool LIST, bool WRITE, bool FUSED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_decode_kernel(AttnArgs a) {
   using Gm = Geo<DT, D, B>;
@@ -244,24 +385,13 @@ void paged_decode_kernel(AttnArgs a) {
   };
   const uint64_t C = LIST ? uni64(sh.csum[S]) : 0;
   const bool fine = C >= static_cast<uint64_t>(4) * lanes * full_cost;
-  auto cut_at = [&](uint64_t T) __attribute__((always_inline)) {
+  // The cut inside sequence lo, where csum[lo] = base <= T < csum[lo + 1].
+  auto cut_in = [&](int lo, uint64_t T, uint64_t base) __attribute__((always_inline)) {
     Cut c{S, 0};
-    if (T >= C) return c;
-    // csum[lo] <= T < csum[lo + 1]: csum rises strictly, so the lanes of a wave
-    // test 64 evenly spaced candidates and narrow the range 64-fold per round
-    // (two rounds for up to 4096 sequences).
-    int lo = 0, span = S;
-    while (span > 1) {
-      const int step = (span + kWave - 1) / kWave, end = lo + span;
-      const int idx = lo + lane * step;
-      const uint64_t below = __ballot(idx < end && sh.csum[idx] <= T);
-      lo += (__popcll(below) - 1) * step;
-      span = min(step, end - lo);
-    }
     const int n = ld_const(a.context_lens, lo);
     bool bad;
     const int np = seq_parts(a, n, &bad);
-    const uint64_t rel = T - uni64(sh.csum[lo]);
+    const uint64_t rel = T - base;
     if (bad || n == 0) {  // no tokens: the sequence starts the run that holds its first cost unit
       c.seq = rel == 0 ? lo : lo + 1;
       return c;
@@ -278,6 +408,34 @@ void paged_decode_kernel(AttnArgs a) {
     c.seq = tok >= n ? lo + 1 : lo;
     c.tok = tok >= n ? 0 : tok;
     return c;
+  };
+  auto cut_at = [&](uint64_t T) __attribute__((always_inline)) {
+    if (T >= C) return Cut{S, 0};
+    // csum[lo] <= T < csum[lo + 1]: csum rises strictly, so the lanes of a wave
+    // test 64 evenly spaced candidates and narrow the range 64-fold per round
+    // (two rounds for up to 4096 sequences).
+    int lo = 0, span = S;
+    while (span > 1) {
+      const int step = (span + kWave - 1) / kWave, end = lo + span;
+      const int idx = lo + lane * step;
+      const uint64_t below = __ballot(idx < end && sh.csum[idx] <= T);
+      lo += (__popcll(below) - 1) * step;
+      span = min(step, end - lo);
+    }
+    return cut_in(lo, T, uni64(sh.csum[lo]));
+  };
+  // The same cut found by one lane alone (a binary search), for a different T per lane.
+  auto cut_at_lane = [&](uint64_t T) __attribute__((always_inline)) {
+    if (T >= C) return Cut{S, 0};
+    int lo = 0, hi = S;  // csum[lo] <= T < csum[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sh.csum[mid] <= T)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return cut_in(lo, T, sh.csum[lo]);
   };
   // Not LIST: first non-empty partition item at or after k in this workgroup's stride.
   const int total = a.total_items;
@@ -317,7 +475,7 @@ void paged_decode_kernel(AttnArgs a) {
     bool bad;
     if constexpr (LIST) {
       it.seq = k;
-      it.next = k + 1;
+      it.next = k - 1;  // a run is walked backwards, see below
       n = ld_const(a.context_lens, it.seq);
       nparts = seq_parts(a, n, &bad);
       it.tok_begin = k == run_begin.seq ? run_begin.tok : 0;
@@ -347,6 +505,47 @@ void paged_decode_kernel(AttnArgs a) {
     return it;
   };
 
+  // LIST: a run that starts inside a sequence and ends after it owns that
+  // sequence's combination; a run that ends inside a sequence leaves record 1.
+  bool owner = false;
+  const bool split_ws = a.max_parts > 1;  // the workspace exists (otherwise no sequence is cut)
+  // Hands record rec over once every wave's stores of it have completed (every thread calls it).
+  auto publish = [&](int rec) __attribute__((always_inline)) {
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t* tg = a.ws_tag + 2 * static_cast<size_t>(rec);
+      const uint64_t turn = __hip_atomic_load(tg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(tg + 1, tag_next(turn), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  if constexpr (LIST) {
+    owner = split_ws && run_begin.tok > 0 && run_begin.seq < run_end.seq;
+    if constexpr (!FUSED) {
+      // the two-stage reduction finds the owners from these marks
+      if (split_ws && tid == 0)
+        *reinterpret_cast<int4*>(a.ws_hdr + 8 * static_cast<size_t>(blockIdx.x)) =
+            make_int4(run_begin.seq, run_begin.tok, 0, owner ? 1 : 0);
+    }
+    if (k_first >= k_end && split_ws && run_end.tok > 0) {
+      // No tokens, inside a sequence: an empty segment (m = -inf, l = 0, acc = 0) keeps the runs between the
+      // sequence's first and its owner a contiguous chain of records.
+      const int rec = 2 * static_cast<int>(blockIdx.x) + 1;
+      const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(a.ws_acc + static_cast<size_t>(rec) * G * D, G * D * 4);
+      for (int i = tid; i < G * D / 4; i += kThreads)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, r_acc, 16 * i, 0, kScopeDevice);
+      const __amdgpu_buffer_rsrc_t r_m = make_rsrc(a.ws_m + static_cast<size_t>(rec) * G, G * 4);
+      const __amdgpu_buffer_rsrc_t r_l = make_rsrc(a.ws_l + static_cast<size_t>(rec) * G, G * 4);
+      const __amdgpu_buffer_rsrc_t r_hdr = make_rsrc(a.ws_hdr + 4 * static_cast<size_t>(rec), 16);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), r_m, tid < G ? 4 * tid : kNowhere, 0,
+                                            kScopeDevice);
+      __builtin_amdgcn_raw_buffer_store_b32(0u, r_l, tid < G ? 4 * tid : kNowhere, 0, kScopeDevice);
+      const u32x4_t hdr = {static_cast<uint32_t>(run_end.seq), static_cast<uint32_t>(run_end.tok),
+                           static_cast<uint32_t>(run_end.tok), 0u};
+      __builtin_amdgcn_raw_buffer_store_b128(hdr, r_hdr, tid == 0 ? 0 : kNowhere, 0, kScopeDevice);
+      if constexpr (FUSED) publish(rec);
+    }
+  }
   if (k_first >= k_end) return;
   if constexpr (LIST && WRITE) {
     // The decode step's new tokens.  The run holds the last token of every
@@ -377,9 +576,14 @@ void paged_decode_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have reached the cache hierarchy
     __syncthreads();
   }
-  Item cur = decode(k_first);
+  // LIST walks its run backwards, last sequence first: the run's last segment,
+  // which a later run's owner combines, is computed and handed over first, and
+  // an owner's own segment (the run's first) comes last, when the segments
+  // before it have long been handed over.  Partition items go forwards.
+  auto live = [&](int k) __attribute__((always_inline)) { return LIST ? k >= k_first : k < k_end; };
+  Item cur = decode(LIST ? k_end - 1 : k_first);
   Item nxt = cur;
-  if (cur.next < k_end) nxt = decode(cur.next);
+  if (live(cur.next)) nxt = decode(cur.next);
   nxt.k = cur.next;
 
   // ---- loads ---------------------------------------------------------------
@@ -472,7 +676,7 @@ void paged_decode_kernel(AttnArgs a) {
   constexpr bool kPrefetchQ = NQ <= 4;
   uint4 q_cur[NQ], q_nxt[kPrefetchQ ? NQ : 1];
   load_query(q_cur, cur);
-  if constexpr (kPrefetchQ) load_query(q_nxt, nxt.k < k_end ? nxt : cur);
+  if constexpr (kPrefetchQ) load_query(q_nxt, live(nxt.k) ? nxt : cur);
 
   uint4 kb[NBUF][NT][KS];
   uint32_t vb[NBUF][NDT][VW];
@@ -487,7 +691,7 @@ void paged_decode_kernel(AttnArgs a) {
     load_values(vb[s], T);
   }
   // The block id of the next refill target is fetched one step ahead.
-  int pend_id = table_entry(where(NBUF, nxt.k < k_end));
+  int pend_id = table_entry(where(NBUF, live(nxt.k)));
 
   const float c = a.c;
   int parity = 0;  // LDS merge buffer of the current item
@@ -496,7 +700,7 @@ void paged_decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;
-    const bool has_next = nxt.k < k_end;
+    const bool has_next = live(nxt.k);
 
     for (int i0 = 0; i0 < cur.npad; i0 += NBUF) {
 #pragma unroll
@@ -686,17 +890,30 @@ void paged_decode_kernel(AttnArgs a) {
       // partition, with its length.
       const bool direct = cur.flags & kDirect;
       const size_t head0 = static_cast<size_t>(cur.seq) * Hkv * G + static_cast<size_t>(cur.kvh) * G;
-      const size_t prow = (static_cast<size_t>(cur.seq) * Hkv + cur.kvh) * a.max_parts + cur.part;
-      const bool split = a.max_parts > 1;  // the workspace exists
+      // The partials' slot: LIST, record 0 of an owner's first item or record 1
+      // of a run's last item; otherwise the segment's partition slot.
+      const int rec = 2 * static_cast<int>(blockIdx.x) + ((owner && cur.k == k_first) ? 0 : 1);
+      const size_t prow =
+          LIST ? static_cast<size_t>(rec) : (static_cast<size_t>(cur.seq) * Hkv + cur.kvh) * a.max_parts + cur.part;
+      const bool split = split_ws;
       const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + head0 * D, direct ? G * D * 4 : 0);
       const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(split ? a.ws_acc + prow * G * D : a.out, direct ? 0 : G * D * 4);
       const __amdgpu_buffer_rsrc_t r_m = make_rsrc(split ? a.ws_m + prow * G : a.out, direct ? 0 : G * 4);
       const __amdgpu_buffer_rsrc_t r_l = make_rsrc(split ? a.ws_l + prow * G : a.out, direct ? 0 : G * 4);
-      const bool seg_store = split && (!direct || (cur.flags & kSplitSeq));
-      const __amdgpu_buffer_rsrc_t r_seg =
-          make_rsrc(split ? static_cast<const void*>(a.ws_seg + prow) : static_cast<const void*>(a.out), seg_store ? 4 : 0);
-      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(direct ? -1 : cur.part_next), r_seg,
-                                            tid == 0 ? 0 : kNowhere, 0, 0);
+      if constexpr (LIST) {
+        const __amdgpu_buffer_rsrc_t r_hdr =
+            make_rsrc(split ? static_cast<const void*>(a.ws_hdr + 4 * prow) : static_cast<const void*>(a.out),
+                      direct ? 0 : 16);
+        const u32x4_t hdr = {static_cast<uint32_t>(cur.seq), static_cast<uint32_t>(cur.tok_begin),
+                             static_cast<uint32_t>(cur.tok_end), (rec & 1) ? 0u : 1u};
+        __builtin_amdgcn_raw_buffer_store_b128(hdr, r_hdr, tid == 0 ? 0 : kNowhere, 0, kScopeDevice);
+      } else {
+        const bool seg_store = split && (!direct || (cur.flags & kSplitSeq));
+        const __amdgpu_buffer_rsrc_t r_seg = make_rsrc(
+            split ? static_cast<const void*>(a.ws_seg + prow) : static_cast<const void*>(a.out), seg_store ? 4 : 0);
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(direct ? -1 : cur.part_next), r_seg,
+                                              tid == 0 ? 0 : kNowhere, 0, 0);
+      }
       constexpr int NC = D / 4;  // float4 chunks of one head's row
       constexpr int ITERS = (G * NC + kThreads - 1) / kThreads;
       const float fill = (cur.flags & kBad) ? __builtin_nanf("") : 0.0f;
@@ -720,10 +937,15 @@ void paged_decode_kernel(AttnArgs a) {
         const int voff = live ? (h * D + d4) * 4 : kNowhere;
         const int soff = live && d4 == 0 ? h * 4 : kNowhere;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), r_out, voff, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sa), r_acc, voff, 0, kLoadNT);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), r_m, soff, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sl), r_l, soff, 0, 0);
+        // item-list records are read by another workgroup, maybe on another XCD: device scope
+        constexpr int kRecAux = LIST ? kScopeDevice : 0;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sa), r_acc, voff, 0, kRecAux | kLoadNT);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), r_m, soff, 0, kRecAux);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sl), r_l, soff, 0, kRecAux);
       }
+      // FUSED: a run's last segment that a later run's owner combines is handed over.
+      if constexpr (LIST && FUSED)
+        if (!direct && (rec & 1)) publish(rec);
     }
     parity ^= 1;
 
@@ -741,15 +963,107 @@ void paged_decode_kernel(AttnArgs a) {
     {
       const int kn = cur.next;
       nxt = cur;
-      if (kn < k_end) nxt = decode(kn);
+      if (live(kn)) nxt = decode(kn);
       nxt.k = kn;
     }
-    if constexpr (kPrefetchQ) load_query(q_nxt, nxt.k < k_end ? nxt : cur);
+    if constexpr (kPrefetchQ) load_query(q_nxt, live(nxt.k) ? nxt : cur);
     // Ring position NBUF of the new item: when the item has only NBUF
     // positions it is the following item's first group, which the old item's
     // look-ahead could not know.
-    pend_id = table_entry(where(NBUF, nxt.k < k_end));
+    pend_id = table_entry(where(NBUF, live(nxt.k)));
   }
+
+  if constexpr (LIST && FUSED) {
+    if (owner) {
+      // Combine the owned sequence: its segments lie in record 1 of the runs
+      // that start inside it, going down from this one, and of the run before
+      // them (which holds its token 0), and in this run's record 0.
+      const int seq = run_begin.seq;
+      wait_stores();  // this run's record 0 is complete
+      __syncthreads();
+      if (wave == 0) {
+        // first: the highest run below this one that does not start inside the
+        // sequence (it holds token 0); 64 runs tested at once, one per lane.
+        int first = -1;
+        for (int top = lane_b - 1; first < 0; top -= kWave) {
+          const int L = top - lane;
+          bool inside = false;
+          if (L >= 0) {
+            const Cut c = cut_at_lane((static_cast<uint64_t>(L) * C + lanes - 1) / lanes);
+            inside = c.seq == seq && c.tok > 0;
+          }
+          const uint64_t outside = __ballot(!inside);  // bit i: run top - i; run 0 never starts inside
+          if (outside) first = top - (__ffsll(static_cast<unsigned long long>(outside)) - 1);
+        }
+        // Take the records of runs first .. lane_b - 1 over, 64 at a time, lane i
+        // waiting for run first + i (also after a time-out, so that a late write
+        // leaves flag == turn); their headers must tile the sequence's tokens
+        // [0, this run's first token).
+        bool ok = true;
+        int carry = 0;  // where the next record must start
+        for (int L0 = first; L0 < lane_b; L0 += kWave) {
+          const int L = L0 + lane, count = min(kWave, lane_b - L0);
+          int4 h = make_int4(seq, 0, 0, 0);
+          bool good = true;
+          if (L < lane_b) {
+            const int rec = 2 * (L * Hkv + kvh_b) + 1;
+            uint64_t* tg = a.ws_tag + 2 * static_cast<size_t>(rec);
+            const uint64_t want = tag_next(__hip_atomic_load(tg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            int polls = 0;
+            while (__hip_atomic_load(tg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want && polls < kMaxPolls) {
+              __builtin_amdgcn_s_sleep(1);
+              ++polls;
+            }
+            __hip_atomic_store(tg, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            h = load_dev_i4(make_rsrc(a.ws_hdr, 2 * static_cast<int>(gridDim.x) * 16), 16 * rec);
+            good = polls < kMaxPolls && h.x == seq && h.z >= h.y;
+          }
+          const int before = __shfl(h.z, lane > 0 ? lane - 1 : 0);
+          if (L < lane_b) good = good && h.y == (lane == 0 ? carry : before);
+          ok = ok && __ballot(!good) == 0;
+          carry = __shfl(h.z, count - 1);
+        }
+        if (lane == 0) {
+          sh.chain_first = first;
+          sh.chain_ok = ok && carry == run_begin.tok;
+        }
+      }
+      __syncthreads();
+      combine_runs<G, D>(a, seq, kvh_b, sh.chain_first, lane_b, sh.chain_ok != 0, tid);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The two-stage path's combination (item list): one workgroup per workgroup
+// of the partition pass, same grid.  An owner (marked in its record 0) walks
+// down the records 1 of the runs before it while they start inside its
+// sequence, then combines them as the fused kernel does.
+// ---------------------------------------------------------------------------
+template <int G, int D>
+__global__ __launch_bounds__(kThreads) void list_reduce_kernel(AttnArgs a) {
+  const int b = blockIdx.x, Hkv = a.num_kv_heads, kvh = b % Hkv, lane_b = b / Hkv;
+  const int4 mark = *reinterpret_cast<const int4*>(a.ws_hdr + 8 * static_cast<size_t>(b));
+  if (mark.w != 1) return;
+  __shared__ int first_sh, ok_sh;
+  if (threadIdx.x == 0) {
+    // The walk moves down and stops at run 0, so it ends whatever the workspace holds.
+    int first = lane_b - 1, expect = mark.y;
+    bool ok = true;
+    for (; first >= 0; --first) {
+      const int4 h = *reinterpret_cast<const int4*>(a.ws_hdr + 4 * (2 * static_cast<size_t>(first * Hkv + kvh) + 1));
+      if (h.x != mark.x || h.z != expect || h.y > h.z) {
+        ok = false;
+        break;
+      }
+      if (h.y == 0) break;
+      expect = h.y;
+    }
+    first_sh = first < 0 ? 0 : first;
+    ok_sh = ok && first >= 0;
+  }
+  __syncthreads();
+  combine_runs<G, D>(a, mark.x, kvh, first_sh, lane_b, ok_sh != 0, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -806,25 +1120,45 @@ bool use_list(int32_t num_seqs, int32_t max_context_len, int32_t max_parts) {
   return num_seqs <= kMaxListedSeqs && static_cast<uint64_t>(num_seqs) * seq_cost_bound < (1ull << 32);
 }
 
+// The persistent grid never exceeds this many workgroups (an MI355X holds 512
+// to 768 of this kernel at once); it bounds the item list's records.
+constexpr int kMaxGrid = 2048;
+
 struct Plan {
   int32_t P;          // effective partition size
   int32_t max_parts;  // partitions of the longest sequence
-  size_t off_m, off_l, off_seg, bytes;
+  bool list;          // item list (records per workgroup), else a slot per partition
+  int32_t grid_cap;   // the largest grid a launch uses (a multiple of H_kv)
+  size_t off_m, off_l, off_seg, off_hdr, off_tag, bytes;
 };
 
-Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t block_size, int32_t max_context_len,
-               int32_t partition_size) {
+Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+               int32_t max_context_len, int32_t partition_size) {
   Plan p{};
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
   p.P = partition_size > 0 ? partition_size : static_cast<int32_t>(ceil_div64(ctx, block_size) * block_size);
   p.max_parts = static_cast<int32_t>(ceil_div64(ctx, p.P));
-  if (p.max_parts <= 1) return p;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * p.max_parts;
+  p.list = use_list(num_seqs, max_context_len, p.max_parts);
+  const int64_t items = static_cast<int64_t>(p.max_parts) * num_seqs * num_kv_heads;
+  const int64_t want = items < kMaxGrid ? items : kMaxGrid;
+  p.grid_cap = static_cast<int32_t>(want >= num_kv_heads ? want / num_kv_heads * num_kv_heads : num_kv_heads);
+  if (p.max_parts <= 1 || num_seqs <= 0) return p;
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  p.off_m = up(rows * head_dim * sizeof(float));
-  p.off_l = p.off_m + up(rows * sizeof(float));
-  p.off_seg = p.off_l + up(rows * sizeof(float));
-  p.bytes = p.off_seg + up(rows * sizeof(int32_t));
+  const size_t G = static_cast<size_t>(num_q_heads / num_kv_heads);
+  if (p.list) {
+    const size_t recs = 2 * static_cast<size_t>(p.grid_cap);
+    p.off_m = up(recs * G * head_dim * sizeof(float));
+    p.off_l = p.off_m + up(recs * G * sizeof(float));
+    p.off_hdr = p.off_l + up(recs * G * sizeof(float));
+    p.off_tag = p.off_hdr + up(recs * 4 * sizeof(int32_t));
+    p.bytes = p.off_tag + up(recs * 2 * sizeof(uint64_t));
+  } else {
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * p.max_parts;
+    p.off_m = up(rows * head_dim * sizeof(float));
+    p.off_l = p.off_m + up(rows * sizeof(float));
+    p.off_seg = p.off_l + up(rows * sizeof(float));
+    p.bytes = p.off_seg + up(rows * sizeof(int32_t));
+  }
   return p;
 }
 
@@ -846,49 +1180,77 @@ int resident_workgroups() {
   return cache[dev];
 }
 
-template <class DT, int D, int G, int B, bool LIST, bool WRITE = false>
-hipError_t launch_kernel(const AttnArgs& a, hipStream_t stream) {
+// The persistent grid: as many workgroups as fit at once, at most one per
+// item and at most kMaxGrid, rounded to a multiple of H_kv: with the KV head
+// varying fastest in the item order, workgroup b always serves head b % H_kv
+// and the workgroups of all heads of one partition run side by side, reading
+// adjacent tiles of the same blocks (and, for shared prefixes, the same
+// blocks).
+template <class DT, int D, int G, int B, bool LIST, bool WRITE, bool FUSED>
+int grid_for(const AttnArgs& a) {
   using K = void (*)(AttnArgs);
-  constexpr K kernel = paged_decode_kernel<DT, D, G, B, LIST, WRITE>;
+  constexpr K kernel = paged_decode_kernel<DT, D, G, B, LIST, WRITE, FUSED>;
   const int fill = resident_workgroups<K, kernel>();
-  if (fill <= 0) return hipErrorInvalidValue;
-  // A multiple of H_kv: with the KV head varying fastest in the item order,
-  // workgroup b always serves head b % H_kv and the workgroups of all heads
-  // of one partition run side by side, reading adjacent tiles of the same
-  // blocks (and, for shared prefixes, the same blocks).
-  const int want = a.total_items < fill ? a.total_items : fill;
-  const int grid = want >= a.num_kv_heads ? want / a.num_kv_heads * a.num_kv_heads : a.num_kv_heads;
-  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, a);
+  if (fill <= 0) return 0;
+  int want = a.total_items < fill ? a.total_items : fill;
+  if (want > kMaxGrid) want = kMaxGrid;
+  return want >= a.num_kv_heads ? want / a.num_kv_heads * a.num_kv_heads : a.num_kv_heads;
+}
+
+template <class DT, int D, int G, int B, bool LIST, bool WRITE, bool FUSED>
+hipError_t launch_kernel(const AttnArgs& a, hipStream_t stream) {
+  const int grid = grid_for<DT, D, G, B, LIST, WRITE, FUSED>(a);
+  if (grid <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, B, LIST, WRITE, FUSED>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <class DT, int D, int G>
-hipError_t launch_attention_g(const AttnArgs& a, hipStream_t stream) {
-  // k_new is set only where the listed split applies (attention_stages)
-  const bool list = use_list(a.num_seqs, a.max_context_len, a.max_parts);
-  if (a.block_size == 16) {
-    if (!list) return launch_kernel<DT, D, G, 16, false>(a, stream);
-    return a.k_new ? launch_kernel<DT, D, G, 16, true, true>(a, stream) : launch_kernel<DT, D, G, 16, true>(a, stream);
+// What one launch does.  kPass: the partition pass alone (the two-stage path,
+// or partition items); kFused: the item list with the combination inside;
+// kWriteFused: the same, storing each sequence's new token first;
+// kListReduce: the two-stage path's combination for the item list.
+enum class Op { kPass, kFused, kWriteFused, kListReduce };
+
+template <class DT, int D, int G, int B>
+hipError_t launch_op_b(const AttnArgs& a, bool list, Op op, hipStream_t stream) {
+  if (!list) return launch_kernel<DT, D, G, B, false, false, false>(a, stream);
+  switch (op) {
+    case Op::kPass: return launch_kernel<DT, D, G, B, true, false, false>(a, stream);
+    case Op::kFused: return launch_kernel<DT, D, G, B, true, false, true>(a, stream);
+    case Op::kWriteFused: return launch_kernel<DT, D, G, B, true, true, true>(a, stream);
+    case Op::kListReduce: {
+      // the same grid as the two-stage path's partition pass, whose records it reads
+      const int grid = grid_for<DT, D, G, B, true, false, false>(a);
+      if (grid <= 0) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((list_reduce_kernel<G, D>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    }
   }
-  if (!list) return launch_kernel<DT, D, G, 32, false>(a, stream);
-  return a.k_new ? launch_kernel<DT, D, G, 32, true, true>(a, stream) : launch_kernel<DT, D, G, 32, true>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+template <class DT, int D, int G>
+hipError_t launch_op_g(const AttnArgs& a, bool list, Op op, hipStream_t stream) {
+  return a.block_size == 16 ? launch_op_b<DT, D, G, 16>(a, list, op, stream)
+                            : launch_op_b<DT, D, G, 32>(a, list, op, stream);
 }
 
 template <class DT, int D>
-hipError_t launch_attention_d(const AttnArgs& a, int G, hipStream_t stream) {
+hipError_t launch_op_d(const AttnArgs& a, int G, bool list, Op op, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_attention_g<DT, D, 1>(a, stream);
-    case 2: return launch_attention_g<DT, D, 2>(a, stream);
-    case 4: return launch_attention_g<DT, D, 4>(a, stream);
-    case 8: return launch_attention_g<DT, D, 8>(a, stream);
+    case 1: return launch_op_g<DT, D, 1>(a, list, op, stream);
+    case 2: return launch_op_g<DT, D, 2>(a, list, op, stream);
+    case 4: return launch_op_g<DT, D, 4>(a, list, op, stream);
+    case 8: return launch_op_g<DT, D, 8>(a, list, op, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class DT>
-hipError_t launch_attention(const AttnArgs& a, int D, int G, hipStream_t stream) {
-  if (D == 64) return launch_attention_d<DT, 64>(a, G, stream);
-  if (D == 128) return launch_attention_d<DT, 128>(a, G, stream);
+hipError_t launch_op(const AttnArgs& a, int D, int G, bool list, Op op, hipStream_t stream) {
+  if (D == 64) return launch_op_d<DT, 64>(a, G, list, op, stream);
+  if (D == 128) return launch_op_d<DT, 128>(a, G, list, op, stream);
   return hipErrorInvalidValue;
 }
 
@@ -918,7 +1280,8 @@ pkv_status attention_stages(int stages, const void* k_new, const void* v_new, fl
   if ((k_new != nullptr) != (v_new != nullptr)) return PKV_ERR_INVALID_ARG;
   if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_INVALID_ARG;
 
-  const Plan plan = make_plan(num_seqs, num_q_heads, head_dim, block_size, max_context_len, partition_size);
+  const Plan plan =
+      make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size);
   const int64_t items = static_cast<int64_t>(plan.max_parts) * num_seqs * num_kv_heads;
   if (items > INT32_MAX / 2) return PKV_ERR_INVALID_ARG;
   AttnArgs a{};
@@ -934,7 +1297,12 @@ pkv_status attention_stages(int stages, const void* k_new, const void* v_new, fl
     a.ws_acc = reinterpret_cast<float*>(ws);
     a.ws_m = reinterpret_cast<float*>(ws + plan.off_m);
     a.ws_l = reinterpret_cast<float*>(ws + plan.off_l);
-    a.ws_seg = reinterpret_cast<int32_t*>(ws + plan.off_seg);
+    if (plan.list) {
+      a.ws_hdr = reinterpret_cast<int32_t*>(ws + plan.off_hdr);
+      a.ws_tag = reinterpret_cast<uint64_t*>(ws + plan.off_tag);
+    } else {
+      a.ws_seg = reinterpret_cast<int32_t*>(ws + plan.off_seg);
+    }
   }
   a.num_seqs = num_seqs;
   a.num_kv_heads = num_kv_heads;
@@ -949,11 +1317,16 @@ pkv_status attention_stages(int stages, const void* k_new, const void* v_new, fl
   // zero scale gives equal weights).
   a.c = scale * 1.4426950408889634f;
 
+  auto run = [&](Op op) {
+    return kv_dtype == PKV_BF16 ? launch_op<BF16>(a, head_dim, G, plan.list, op, stream)
+                                : launch_op<F32>(a, head_dim, G, plan.list, op, stream);
+  };
+  const bool both = (stages & kStagePartitions) && (stages & kStageReduce);
   if (stages & kStagePartitions) {
     if (k_new) {
-      // The listed split writes the new tokens inside the attention kernel;
+      // The item list writes the new tokens inside the attention kernel;
       // partition items take a separate write first.
-      if (use_list(num_seqs, max_context_len, plan.max_parts)) {
+      if (plan.list) {
         a.k_new = k_new;
         a.v_new = v_new;
       } else if (launch_write_last_token(k_new, v_new, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
@@ -962,17 +1335,20 @@ pkv_status attention_stages(int stages, const void* k_new, const void* v_new, fl
         return PKV_ERR_HIP;
       }
     }
-    const hipError_t err = kv_dtype == PKV_BF16 ? launch_attention<BF16>(a, head_dim, G, stream)
-                                                : launch_attention<F32>(a, head_dim, G, stream);
-    if (err != hipSuccess) return PKV_ERR_HIP;
+    const Op op = !plan.list ? Op::kPass : k_new ? Op::kWriteFused : both ? Op::kFused : Op::kPass;
+    if (run(op) != hipSuccess) return PKV_ERR_HIP;
   }
   if ((stages & kStageReduce) && plan.max_parts > 1) {
-    const dim3 rg(static_cast<unsigned>(num_seqs) * num_kv_heads);
-    if (head_dim == 64)
-      hipLaunchKernelGGL((lse_reduce_kernel<64>), rg, dim3(kThreads), 0, stream, a, num_q_heads);
-    else
-      hipLaunchKernelGGL((lse_reduce_kernel<128>), rg, dim3(kThreads), 0, stream, a, num_q_heads);
-    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+    if (!plan.list) {
+      const dim3 rg(static_cast<unsigned>(num_seqs) * num_kv_heads);
+      if (head_dim == 64)
+        hipLaunchKernelGGL((lse_reduce_kernel<64>), rg, dim3(kThreads), 0, stream, a, num_q_heads);
+      else
+        hipLaunchKernelGGL((lse_reduce_kernel<128>), rg, dim3(kThreads), 0, stream, a, num_q_heads);
+      if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+    } else if (!both) {
+      if (run(Op::kListReduce) != hipSuccess) return PKV_ERR_HIP;
+    }
   }
   return PKV_OK;
 }
@@ -984,12 +1360,12 @@ using namespace pkv;
 
 extern "C" {
 
-size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t block_size,
-                                     int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_context_len < 0 ||
-      partition_size < 0)
+size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 ||
+      block_size <= 0 || max_context_len < 0 || partition_size < 0)
     return 0;
-  return make_plan(num_seqs, num_q_heads, head_dim, block_size, max_context_len, partition_size).bytes;
+  return make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, partition_size).bytes;
 }
 
 #define PKV_ATTN_PARAMS                                                                                          \

@@ -85,8 +85,8 @@ class GpuBatch:
     def workspace(self, partition_size: int):
         import torch
         s = self.workload.spec
-        nbytes = pkv_attention_workspace_bytes(self.q.shape[0], s.num_q_heads, s.head_dim, s.block_size,
-                                               self.max_context_len, partition_size)
+        nbytes = pkv_attention_workspace_bytes(self.q.shape[0], s.num_q_heads, s.num_kv_heads, s.head_dim,
+                                               s.block_size, self.max_context_len, partition_size)
         if nbytes == 0:
             return None
         ws = self._ws.get(nbytes)

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(libpkv):
     assert len(syms) >= 18
     missing = [s for s in syms if not hasattr(libpkv, s)]
     assert missing == []
-    assert pk.pkv_abi_version() == 9
+    assert pk.pkv_abi_version() == 10
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert libpkv.pkv_status_string(code) != b"unknown status"
     assert libpkv.pkv_status_string(-9) == b"unknown status"
@@ -263,11 +263,22 @@ def test_cow_capacity_error_reports_need(libpkv):
 
 def test_workspace_size_and_device_arg_checks(libpkv):
     # sizes are host arithmetic: 0 when one partition holds every sequence
-    assert pk.pkv_attention_workspace_bytes(8, 32, 128, 16, 32768, 0) == 0
-    assert pk.pkv_attention_workspace_bytes(8, 32, 128, 16, 512, 512) == 0
-    nbytes = pk.pkv_attention_workspace_bytes(8, 32, 128, 16, 32768, 512)
-    rows = 8 * 32 * 64
-    assert nbytes >= rows * (128 + 2) * 4
+    assert pk.pkv_attention_workspace_bytes(8, 32, 8, 128, 16, 32768, 0) == 0
+    assert pk.pkv_attention_workspace_bytes(8, 32, 8, 128, 16, 512, 512) == 0
+    assert pk.pkv_attention_workspace_bytes(8, 32, 6, 128, 16, 32768, 512) == 0  # 32 % 6 != 0
+    # up to 4096 sequences: two records per workgroup of a grid of at most 2048
+    # (here 8 x 8 heads x 64 partitions = 4096 items), each G x (d + 2) floats
+    # plus a 16-byte header and a 16-byte hand-over pair
+    nbytes = pk.pkv_attention_workspace_bytes(8, 32, 8, 128, 16, 32768, 512)
+    recs = 2 * 2048
+    assert recs * (4 * (128 + 2) * 4 + 32) <= nbytes <= recs * (4 * (128 + 2) * 4 + 32) + 5 * 256
+    # few items: the grid, and so the records, shrink with them (2 x 8 heads x 2 partitions)
+    small = pk.pkv_attention_workspace_bytes(2, 32, 8, 128, 16, 1024, 512)
+    assert 2 * 32 * (4 * 130 * 4 + 32) <= small <= 2 * 32 * (4 * 130 * 4 + 32) + 5 * 256
+    # above 4096 sequences: one slot per (sequence, query head, partition)
+    big = pk.pkv_attention_workspace_bytes(5000, 8, 2, 64, 16, 1024, 512)
+    rows = 5000 * 8 * 2
+    assert rows * (64 + 3) * 4 <= big <= rows * (64 + 3) * 4 + 4 * 256
     # argument errors are returned before anything touches a GPU
     L = libpkv
     vp = ctypes.c_void_p

@@ -5,8 +5,9 @@ import os
 
 import bench
 
-PLAIN = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, false>(pkv::AttnArgs)"
-STEP = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, true>(pkv::AttnArgs)"
+PASS = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, false, false>(pkv::AttnArgs)"
+FUSED = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, false, true>(pkv::AttnArgs)"
+STEP = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, true, true>(pkv::AttnArgs)"
 COPY = "void pkv::(anonymous namespace)::copy_probe_kernel(uint4 const*, uint4*, long)"
 
 
@@ -19,20 +20,21 @@ def write_csv(path, rows):
             w.writerow({"Kernel_Name": name, "Counter_Name": ctr, "Counter_Value": val, "Grid_Size": 512})
 
 
-def test_partition_pass_name():
-    assert bench.is_partition_pass(PLAIN)
-    assert not bench.is_partition_pass(STEP)
-    assert bench.is_partition_pass(PLAIN.replace("true, false", "false, false"))
-    assert not bench.is_partition_pass("void pkv::(anonymous namespace)::lse_reduce_kernel<128>(pkv::AttnArgs)")
+def test_step_kernel_name():
+    assert bench.is_step_kernel(STEP)
+    assert not bench.is_step_kernel(PASS) and not bench.is_step_kernel(FUSED)
+    assert bench.decode_kernel_flags(PASS) == (True, False, False)
+    assert bench.decode_kernel_flags(PASS.replace("true, false, false", "false, false, false")) == (False, False, False)
+    assert bench.decode_kernel_flags("void pkv::(anonymous namespace)::lse_reduce_kernel<128>(pkv::AttnArgs)") is None
 
 
-def test_traffic_summary_scales_by_the_copy_and_skips_the_step_variant(tmp_path):
+def test_traffic_summary_scales_by_the_copy_and_takes_the_step_kernel(tmp_path):
     gib = 1 << 30
     # the copy reads 1 GiB but its counter reads half of that: a scale of 2; writes read true
-    fetch = [(COPY, "FETCH_SIZE", gib / 2 / 1024)] * 3 + [(PLAIN, "FETCH_SIZE", 1000.0)] * 5 + \
-            [(STEP, "FETCH_SIZE", 9999.0)] * 9
-    write = [(COPY, "WRITE_SIZE", gib / 1024)] * 3 + [(PLAIN, "WRITE_SIZE", 10.0)] * 5 + \
-            [(STEP, "WRITE_SIZE", 9999.0)] * 9
+    fetch = [(COPY, "FETCH_SIZE", gib / 2 / 1024)] * 3 + [(STEP, "FETCH_SIZE", 1000.0)] * 5 + \
+            [(PASS, "FETCH_SIZE", 9999.0)] * 9 + [(FUSED, "FETCH_SIZE", 7777.0)] * 4
+    write = [(COPY, "WRITE_SIZE", gib / 1024)] * 3 + [(STEP, "WRITE_SIZE", 10.0)] * 5 + \
+            [(PASS, "WRITE_SIZE", 9999.0)] * 9 + [(FUSED, "WRITE_SIZE", 7777.0)] * 4
     write_csv(str(tmp_path / "f" / "p_counter_collection.csv"), fetch)
     write_csv(str(tmp_path / "w" / "p_counter_collection.csv"), write)
     out = bench.traffic_summary([str(tmp_path / "f"), str(tmp_path / "w")], "llama7b_bf16")

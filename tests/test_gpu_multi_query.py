@@ -228,7 +228,7 @@ def test_speculative_verify_rollback_decode(dt):
     check_close(out, ref, dt, "decode after rollback")
     # the decode kernel agrees with the one-query runs
     od = torch.empty((len(base), Hq, d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(pk.pkv_attention_workspace_bytes(len(base), Hq, d, B, int(l.max()), 0), 1),
+    ws = torch.empty(max(pk.pkv_attention_workspace_bytes(len(base), Hq, Hkv, d, B, int(l.max()), 0), 1),
                      dtype=torch.uint8, device="cuda")
     pk.pkv_paged_attention_decode(od, to_dev(qd, dt), *b.caches, torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(),
                                   int(l.max()), 1.0 / np.sqrt(d), 0, ws)

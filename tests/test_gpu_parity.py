@@ -263,6 +263,61 @@ def test_two_stage_equals_fused_with_stale_workspace(nseq, lens, P):
         assert torch.equal(gb.out, fused), fill
 
 
+@pytest.mark.parametrize("nseq,lens,P", [(300, (100, 2000), 256), (6, (200, 1500), 48), (8, (20000, 32768), 512)])
+def test_fused_combine_needs_no_clean_workspace(nseq, lens, P):
+    # The one-call path combines a cut sequence inside the kernel: the owner
+    # waits for the earlier runs' records through (turn, flag) pairs in the
+    # workspace.  Starting from zeros, 0xFF bytes, random bytes, consecutive
+    # int64 values (equal neighbours off by one), and a workspace last used by
+    # a batch of another shape, every call gives the two-stage path's bits,
+    # on repeated calls too; the last case spans each sequence over dozens of
+    # runs (long chains of records, empty runs inside them).
+    import paged_kv_cache_physical_amd as pk
+    GpuBatch = runner()
+    w = wl.small_decode(nseq, lens, 8, 2, 128, 16, "bf16", seed=19)
+    gb = GpuBatch(w)
+    ws = gb.workspace(P)
+    assert ws is not None
+    gb.out.fill_(float("nan"))
+    gb.attention_partitions(P)
+    gb.attention_reduce(P)
+    torch.cuda.synchronize()
+    ref = gb.out.clone()
+    assert bool(torch.isfinite(ref).all())
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    fills = {"zeros": lambda: ws.zero_(), "0xff": lambda: ws.fill_(0xFF),
+             "random": lambda: ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda",
+                                                      generator=gen)),
+             "count": lambda: ws.view(torch.int64).copy_(torch.arange(ws.numel() // 8, device="cuda"))}
+    for name, fill in fills.items():
+        fill()
+        for rep in range(3):
+            gb.out.fill_(float("nan"))
+            gb.attention(P)
+            torch.cuda.synchronize()
+            assert torch.equal(gb.out, ref), (name, rep)
+    # the same buffer for a batch of another shape (G = 4 over 8 KV heads, d = 64, B = 32), then back
+    w2 = wl.small_decode(50, (10, 3000), 32, 8, 64, 32, "bf16", seed=20)
+    g2 = GpuBatch(w2)
+    P2 = 64
+    need = pk.pkv_attention_workspace_bytes(w2.num_seqs, 32, 8, 64, 32, g2.max_context_len, P2)
+    ws2 = ws if need <= ws.numel() else torch.zeros(need, dtype=torch.uint8, device="cuda")
+    g2.attention_partitions(P2)
+    g2.attention_reduce(P2)
+    torch.cuda.synchronize()
+    ref2 = g2.out.clone()
+    for rep in range(2):
+        g2.out.fill_(float("nan"))
+        pk.pkv_paged_attention_decode(g2.out, g2.q, g2.k_cache, g2.v_cache, g2.block_tables, g2.context_lens,
+                                      g2.max_context_len, float(w2.scale), P2, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(g2.out, ref2), rep
+        gb.out.fill_(float("nan"))
+        gb.attention(P)
+        torch.cuda.synchronize()
+        assert torch.equal(gb.out, ref), rep
+
+
 @pytest.mark.parametrize("name", ["gqa_bf16_b16", "long_bf16"])
 def test_repeated_calls_are_bitwise_stable(name):
     # the same inputs give the same bits on every call

@@ -44,7 +44,7 @@ def bits(t):
 def attention(pk, caches, tables, lens, q_dev, B, P):
     S, Hq, d = q_dev.shape
     max_n = int(lens.max())
-    ws_bytes = pk.pkv_attention_workspace_bytes(S, Hq, d, B, max_n, P)
+    ws_bytes = pk.pkv_attention_workspace_bytes(S, Hq, caches[1].shape[1], d, B, max_n, P)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     out = torch.full((S, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
     pk.pkv_paged_attention_decode(out, q_dev, caches[0], caches[1], torch.from_numpy(tables).cuda(),
