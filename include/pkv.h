@@ -419,6 +419,25 @@ pkv_status pkv_decode_step(const void* k_new, const void* v_new, float* out, con
                            float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                            int32_t kv_dtype, hipStream_t stream);
 
+/* pkv_decode_step for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid it): the same
+ * kernels and results, with the split-context workspace taken from a static
+ * device array of the library (18 MiB, one per GPU, held until the process
+ * ends) instead of a caller argument.  It covers every batch of up to 4096
+ * sequences with at most 2048 KV heads (whose workspace is at most about
+ * 17 MB); a batch that needs more returns WORKSPACE before any device work.
+ * The array needs no clearing between calls, but every call on one GPU uses
+ * it: calls that overlap on one GPU (different streams, threads or
+ * processes' streams on the same device) race and must be serialised.  No
+ * hipMalloc, hipFree or other allocation happens inside.  Other errors as
+ * pkv_decode_step. */
+pkv_status pkv_decode_step_static(const void* k_new, const void* v_new, float* out, const void* q,
+                                  const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t max_blocks, int32_t max_context_len, float scale, int32_t partition_size,
+                                  int32_t kv_dtype, hipStream_t stream);
+
 /* Runs of causal queries over the paged cache ([P3] section 5: blockwise
  * attention composes with paging, and speculative decoding stages KV positions
  * that verification keeps or rolls back; [P4] "Preemption": a whole prompt's

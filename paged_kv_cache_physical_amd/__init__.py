@@ -34,7 +34,7 @@ __all__ = [
     "pkv_pool_validate", "pkv_pool_set_host_blocks", "pkv_swap_out", "pkv_swap_in", "pkv_seq_table",
     "pkv_host_block_refcount", "pkv_pool_host_free_list", "pkv_swap_blocks", "empty_host_caches", "pkv_reshape_and_cache", "pkv_copy_blocks", "pkv_attention_workspace_bytes",
     "pkv_paged_attention_decode", "pkv_paged_attention_partitions", "pkv_paged_attention_reduce",
-    "pkv_decode_step", "pkv_abi_version", "pkv_hbm_read_probe", "Pool", "cache_shapes", "empty_caches", "PkvError",
+    "pkv_decode_step", "pkv_decode_step_static", "pkv_abi_version", "pkv_hbm_read_probe", "Pool", "cache_shapes", "empty_caches", "PkvError",
     "OutOfBlocks", "NoSuchSeq", "InvalidArg", "WrongTier",
 ]
 
@@ -444,7 +444,7 @@ def pkv_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
 
 
 def _attention(fn: str, out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int, scale: float,
-               partition_size: int = 0, workspace=None, stream=None, new_kv=None) -> None:
+               partition_size: int = 0, workspace=None, stream=None, new_kv=None, static_scratch=False) -> None:
     torch = _torch()
     S, Hq, d = q.shape
     nb, Hkv, d2, B = v_cache.shape
@@ -467,10 +467,11 @@ def _attention(fn: str, out, q, k_cache, v_cache, block_tables, context_lens, ma
                 k_new.dtype != q.dtype or v_new.dtype != q.dtype:
             raise InvalidArg(-1, fn, "new token shape or dtype mismatch")
         lead = [_dev(k_new, "k_new"), _dev(v_new, "v_new")]
+    ws_args = [] if static_scratch else [ws_ptr, ws_bytes]
     check(getattr(lib(), fn)(*lead, _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
                              _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
                              _dev(context_lens, "context_lens"), S, Hq, Hkv, d, B, nb, max_blocks,
-                             int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
+                             int(max_context_len), float(scale), int(partition_size), *ws_args,
                              _dtype_code(q), _stream(stream)), fn)
 
 
@@ -488,6 +489,14 @@ def pkv_decode_step(k_new, v_new, out, q, k_cache, v_cache, block_tables, contex
     sequence) into the caches through the block tables, then pkv_paged_attention_decode (same arguments)."""
     _attention("pkv_decode_step", out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                partition_size, workspace, stream, new_kv=(k_new, v_new))
+
+
+def pkv_decode_step_static(k_new, v_new, out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                           scale: float, partition_size: int = 0, stream=None) -> None:
+    """pkv_decode_step with the library's static device scratch instead of a workspace (for callers that cannot
+    allocate); calls that overlap on one GPU race."""
+    _attention("pkv_decode_step_static", out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+               scale, partition_size, None, stream, new_kv=(k_new, v_new), static_scratch=True)
 
 
 def pkv_attention_multi_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,

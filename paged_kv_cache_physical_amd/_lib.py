@@ -95,6 +95,7 @@ _SIGS = {
     "pkv_paged_attention_partitions": (i32, _ATTN),
     "pkv_paged_attention_reduce": (i32, _ATTN),
     "pkv_decode_step": (i32, [vp, vp] + _ATTN),
+    "pkv_decode_step_static": (i32, [vp, vp] + _ATTN[:16] + [i32, vp]),
     "pkv_paged_attention_multi": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                         i32, i32, f32, vp, sz, i32, vp]),
     "pkv_attention_multi_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),

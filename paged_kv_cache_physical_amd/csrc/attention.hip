@@ -1353,6 +1353,33 @@ pkv_status attention_stages(int stages, const void* k_new, const void* v_new, fl
   return PKV_OK;
 }
 
+// The decode step's workspace for callers that cannot allocate: a
+// file-scope device array, one per GPU the library runs on (the code object
+// holds it until the process ends).  Its device address is looked up once per
+// device, with that device current; the array's name is only a host-side
+// stand-in and is never passed to a kernel.  Every call on one GPU shares it
+// (the hand-over pairs need no clearing: see tag_next), so calls that overlap
+// on one GPU race.
+constexpr size_t kScratchBytes = size_t{18} << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+void* scratch_address() {
+  static std::mutex mu;
+  static void* cache[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    cache[dev] = p;
+  }
+  return cache[dev];
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -1393,6 +1420,34 @@ pkv_status pkv_paged_attention_reduce(PKV_ATTN_PARAMS) {
 pkv_status pkv_decode_step(const void* k_new, const void* v_new, PKV_ATTN_PARAMS) {
   if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
   return attention_stages(kStagePartitions | kStageReduce, k_new, v_new, PKV_ATTN_ARGS);
+}
+
+pkv_status pkv_decode_step_static(const void* k_new, const void* v_new, float* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t max_blocks, int32_t max_context_len,
+                                  float scale, int32_t partition_size, int32_t kv_dtype, hipStream_t stream) {
+  // Shapes the kernels take; anything else goes straight to pkv_decode_step,
+  // which refuses it before any device work.
+  const int G = num_kv_heads > 0 && num_q_heads > 0 && num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
+  if (num_seqs > 0 && (G == 1 || G == 2 || G == 4 || G == 8) && (head_dim == 64 || head_dim == 128) &&
+      (block_size == 16 || block_size == 32) && item_size(kv_dtype) != 0 && max_context_len >= 0 &&
+      partition_size >= 0 && partition_size % block_size == 0) {
+    const size_t need = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                                  partition_size).bytes;
+    if (need > kScratchBytes) return PKV_ERR_WORKSPACE;
+    if (need > 0) {
+      void* ws = scratch_address();
+      if (!ws) return PKV_ERR_HIP;
+      return pkv_decode_step(k_new, v_new, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks,
+                             max_context_len, scale, partition_size, ws, kScratchBytes, kv_dtype, stream);
+    }
+  }
+  // no workspace needed, or arguments that pkv_decode_step refuses
+  return pkv_decode_step(k_new, v_new, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                         num_kv_heads, head_dim, block_size, num_blocks, max_blocks, max_context_len, scale,
+                         partition_size, nullptr, 0, kv_dtype, stream);
 }
 
 #undef PKV_ATTN_PARAMS

@@ -196,7 +196,7 @@ const char* pkv_status_string(pkv_status s) {
   }
 }
 
-int32_t pkv_abi_version(void) { return 10; }
+int32_t pkv_abi_version(void) { return 11; }
 
 pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
                            pkv_pool** out) {

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(libpkv):
     assert len(syms) >= 18
     missing = [s for s in syms if not hasattr(libpkv, s)]
     assert missing == []
-    assert pk.pkv_abi_version() == 10
+    assert pk.pkv_abi_version() == 11
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert libpkv.pkv_status_string(code) != b"unknown status"
     assert libpkv.pkv_status_string(-9) == b"unknown status"
@@ -279,6 +279,10 @@ def test_workspace_size_and_device_arg_checks(libpkv):
     big = pk.pkv_attention_workspace_bytes(5000, 8, 2, 64, 16, 1024, 512)
     rows = 5000 * 8 * 2
     assert rows * (64 + 3) * 4 <= big <= rows * (64 + 3) * 4 + 4 * 256
+    # the static-scratch decode step refuses a batch whose workspace exceeds its 18 MiB before any device work
+    # (5000 sequences take one slot per sequence, head and partition)
+    assert libpkv.pkv_decode_step_static(None, None, None, None, None, None, None, None, 5000, 64, 8, 128, 16, 100000,
+                                         128, 2048, ctypes.c_float(1.0), 16, 1, None) == _lib.PKV_ERR_WORKSPACE
     # argument errors are returned before anything touches a GPU
     L = libpkv
     vp = ctypes.c_void_p
