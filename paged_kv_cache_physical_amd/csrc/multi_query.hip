@@ -109,11 +109,23 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
   constexpr int kThreads = kWave * kMqWaves;
   constexpr int NIT = NSUB * ITEMS / kThreads;  // pieces per thread per cache per chunk
   static_assert(NSUB >= 1 && (NSUB * ITEMS) % kThreads == 0 && ITEMS % kWave == 0, "staging shape");
-  // LDS per buffer and sub-chunk: keys [piece][16 tokens][16 B], then values
-  // [dim][16 tokens] with the row's four 4-token slots XOR-swizzled by the dim
-  // (slot t at t ^ ((dim >> 2) & 3) for bf16, t ^ ((dim >> 1) & 3) for fp32),
-  // so that the sixteen rows a value read touches fall in distinct banks.
-  __shared__ __attribute__((aligned(16))) char lds[2][NSUB][2 * kSubBytes];
+  // LDS per buffer: the keys of each sub-chunk u at u kSubBytes, laid out
+  // [piece][16 tokens][16 B]; then the values.  bf16: one region for the
+  // chunk, [dim][slot][16 B], where slot s holds tokens 4 s .. 4 s + 3 of sub-
+  // chunk 0 and then of sub-chunk 1, exactly the 16 bytes one lane feeds a
+  // 16x16x32 step; fp32: per sub-chunk, [dim][16 tokens].  The slots of a row
+  // sit XOR-swizzled by the dim (slot s at s ^ vswz(dim)), so that the rows
+  // one value read touches fall in distinct banks.
+  // bf16: three buffers, the scores of chunk c + 1 issued while chunk c's
+  // softmax runs (below); fp32 (twice the bytes per chunk): two.
+  constexpr bool kAhead = kBF16;
+  constexpr int NBUF = kAhead ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) char lds[NBUF][2 * NSUB * kSubBytes];
+  // The buffer of chunk c + k, given b = the buffer of chunk c (0 <= k < NBUF).
+  auto buf_add = [](int b, int k) __attribute__((always_inline)) { return b + k >= NBUF ? b + k - NBUF : b + k; };
+  auto vswz = [](int dim) __attribute__((always_inline)) {
+    return kBF16 ? ((dim >> 1) ^ (dim >> 2)) & 3 : (dim >> 1) & 3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -219,13 +231,24 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
     return;  // the same for the whole workgroup
   }
 
+  // The softmax runs on logits c s (s = q . k) in the exp2 domain as
+  // p = exp2(fma(s, c', -c' m)) with c' = |c| and m a per-row reference: with a
+  // negative scale the queries enter with their sign bits flipped (exact), so
+  // that c s = c' s' and the row maximum of the raw scores s' is the maximum
+  // of the logits.  A zero scale is taken as the smallest normal float, which
+  // leaves every exp2 argument within 2^-25 of 0 (weights exactly 1) and keeps
+  // -inf * c' = -inf for masked tokens.
+  const uint32_t qflip = a.c < 0.0f ? (kBF16 ? 0x80008000u : 0x80000000u) : 0u;
+  const float cs = fmaxf(fabsf(a.c), FLT_MIN);
   uint4 qv[T][KS];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const char* qrow = static_cast<const char*>(a.q) + row_elem[t] * kItem;
 #pragma unroll
-    for (int st = 0; st < KS; ++st)
-      qv[t][st] = vrow[t] ? *reinterpret_cast<const uint4*>(qrow + (st * 4 + kq) * 16) : make_uint4(0, 0, 0, 0);
+    for (int st = 0; st < KS; ++st) {
+      const uint4 v = vrow[t] ? *reinterpret_cast<const uint4*>(qrow + (st * 4 + kq) * 16) : make_uint4(0, 0, 0, 0);
+      qv[t][st] = make_uint4(v.x ^ qflip, v.y ^ qflip, v.z ^ qflip, v.w ^ qflip);
+    }
   }
 
   // Staging: thread piece j of a chunk is i = tid + kThreads j, in sub-chunk
@@ -239,223 +262,327 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
   __shared__ int poison_any;
   if (tid == 0) poison_any = 0;  // ordered before any write of 1 by the barriers below
   const int64_t table_row = static_cast<int64_t>(s) * a.max_blocks;
+  // Block sizes are 16 or 32 (checked by the host): shifts, not divisions.
+  const int lgB = B == 16 ? 4 : 5;
+  const int last_blk = (n - 1) >> lgB;  // n >= qs >= 1 here
+  // Address parts fixed for the whole loop: a block's tile of this KV head
+  // starts at cache + (head 0 of the KV head's tiles) + id * kstride
+  // (kstride = H_kv tiles < 2^32 bytes, as H_kv <= 65535 and a tile <= 16 KiB),
+  // and each thread's pieces sit at fixed offsets in the tiles.
+  const uint32_t kstride = static_cast<uint32_t>(a.num_kv_heads) * static_cast<uint32_t>(tile_bytes);
+  const char* kbase = a.k_cache + static_cast<int64_t>(g) * tile_bytes;
+  const char* vbase = a.v_cache + static_cast<int64_t>(g) * tile_bytes;
+  int koff[NIT], voff[NIT];
+#pragma unroll
+  for (int j = 0; j < NIT; ++j) {
+    const int sub = (kWave * wave + kThreads * j) / ITEMS;  // wave-uniform
+    const int ii = tid + kThreads * j - sub * ITEMS;
+    const int o = (16 * sub) & (B - 1);  // the sub-chunk's first row in its block (chunks start at block starts)
+    koff[j] = ((ii >> 4) * B + o + (ii & 15)) * 16;
+    voff[j] = ((ii / kItem) * B + o + (ii % kItem) * (16 / kItem)) * kItem;
+  }
+  // Block ids of chunk c's sub-chunks, read one iteration before they are
+  // used (scalar loads; the index is clamped to the sequence's last block,
+  // which matters only for sub-chunks past its end, which load nothing).
+  auto chunk_ids = [&](int c, int (&ids)[NSUB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) ids[u] = mq_ld(a.block_tables, table_row + min((CT * c + 16 * u) >> lgB, last_blk));
+  };
   uint4 kr[NIT], vr[NIT];
-  auto stage = [&](int c) __attribute__((always_inline)) {
+  auto stage = [&](int c, const int (&ids)[NSUB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NIT; ++j) {
       const int sub = (kWave * wave + kThreads * j) / ITEMS;  // wave-uniform
-      const int ii = tid + kThreads * j - sub * ITEMS;
-      const int t0 = CT * c + 16 * sub;
-      const bool in = c < nc && t0 < n;
-      const int blk = in ? mq_ld(a.block_tables, table_row + t0 / B) : 0;
-      const bool ok = blk >= 0 && blk < a.num_blocks;
+      const bool in = c < nc && CT * c + 16 * sub < n;
+      const int blk = ids[sub];
+      const bool ok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
       poison |= in && !ok;
-      const int64_t off = ok ? (static_cast<int64_t>(blk) * a.num_kv_heads + g) * tile_bytes : 0;
+      const uint64_t off = ok ? static_cast<uint64_t>(static_cast<uint32_t>(blk)) * kstride : 0;
       const int bytes = (in && ok) ? tile_bytes : 0;
-      const int o = t0 % B;
-      kr[j] = mq_load16(make_rsrc(a.k_cache + off, bytes), ((ii >> 4) * B + o + (ii & 15)) * 16);
-      vr[j] = mq_load16(make_rsrc(a.v_cache + off, bytes), ((ii / kItem) * B + o + (ii % kItem) * (16 / kItem)) * kItem);
+      kr[j] = mq_load16(make_rsrc(kbase + off, bytes), koff[j]);
+      vr[j] = mq_load16(make_rsrc(vbase + off, bytes), voff[j]);
     }
   };
-  auto put = [&](int buf) __attribute__((always_inline)) {
+  // Parks the staged chunk c in its buffer.  Values of tokens past the end of
+  // the sequence (the cache may hold anything there, NaN poison included) are
+  // parked as zeros, so that their zero weights give exact zeros; their keys'
+  // scores are masked.
+  auto put = [&](int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NIT; ++j) {
       const int sub = (kWave * wave + kThreads * j) / ITEMS;
       const int ii = tid + kThreads * j - sub * ITEMS;
-      *reinterpret_cast<uint4*>(&lds[buf][sub][16 * ii]) = kr[j];
+      *reinterpret_cast<uint4*>(&lds[buf][sub * kSubBytes + 16 * ii]) = kr[j];
       const int dim = ii / kItem, part = ii % kItem;
+      if (CT * c + 16 * sub + 16 > n) {  // wave-uniform
+        // valid tokens among the piece's: bf16 8 (two per dword), fp32 4
+        const int rel = n - CT * c - 16 * sub - part * (16 / kItem);
+        uint32_t* w = reinterpret_cast<uint32_t*>(&vr[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (kBF16)
+            w[e] &= (2 * e < rel ? 0x0000ffffu : 0u) | (2 * e + 1 < rel ? 0xffff0000u : 0u);
+          else if (e >= rel)
+            w[e] = 0u;
+        }
+      }
+      char* vreg = &lds[buf][NSUB * kSubBytes];
       if constexpr (kBF16) {
-        // Piece = 4-token slots 2 part and 2 part + 1 of the row; slot t sits at t ^ sw.
-        const int sw = (dim >> 2) & 3;
-        const uint4 v = (sw & 1) ? make_uint4(vr[j].z, vr[j].w, vr[j].x, vr[j].y) : vr[j];
-        *reinterpret_cast<uint4*>(&lds[buf][sub][kSubBytes + 32 * dim + 16 * (part ^ (sw >> 1))]) = v;
+        // Piece = tokens 8 part .. 8 part + 7 of the row: the sub-chunk's halves of slots 2 part and 2 part + 1.
+        *reinterpret_cast<uint2*>(vreg + 64 * dim + 16 * ((2 * part) ^ vswz(dim)) + 8 * (sub & 1)) =
+            make_uint2(vr[j].x, vr[j].y);
+        *reinterpret_cast<uint2*>(vreg + 64 * dim + 16 * ((2 * part + 1) ^ vswz(dim)) + 8 * (sub & 1)) =
+            make_uint2(vr[j].z, vr[j].w);
       } else {
-        // Piece = 4-token slot `part` of the row; slot t sits at t ^ sw.
-        const int sw = (dim >> 1) & 3;
-        *reinterpret_cast<uint4*>(&lds[buf][sub][kSubBytes + 64 * dim + 16 * (part ^ sw)]) = vr[j];
+        // Piece = 4-token slot `part` of the row.
+        *reinterpret_cast<uint4*>(vreg + sub * kSubBytes + 64 * dim + 16 * (part ^ vswz(dim))) = vr[j];
       }
     }
   };
 
+  // Row state: acc and l are relative to the reference m_ref (a raw score; -inf
+  // until the row sees a token).  The reference moves lazily: only when some
+  // row's maximum exceeds it by more than kLazy in the exp2 domain, so weights
+  // stay below 2^kLazy and the accumulators are rarely rescaled.
+  constexpr float kLazy = 8.0f;
   f32x4_t acc[T][NDT];
-  float m_run[T], l_run[T];
+  float m_ref[T], l_run[T];
+  int p_first[T];  // the tile's first row position: chunks past it need the causal mask
 #pragma unroll
   for (int t = 0; t < T; ++t) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[t][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    m_run[t] = -INFINITY;
+    m_ref[t] = -INFINITY;
     l_run[t] = 0.0f;
+    p_first[t] = pos0 + r0[t] / G;
   }
 
-  stage(c_begin);
-  put(c_begin & 1);
-  stage(c_begin + 1);
-  __syncthreads();
-  for (int c = c_begin; c < nc; ++c) {
-    if (CT * c <= p_wave) {  // some row of the wave sees this chunk (wave-uniform)
-      // S[token 16 sub + 4 kq + r][row m16] on the matrix cores: NSUB tiles per
-      // row tile, each summed in two halves (even and odd k-steps) so that more
-      // independent chains overlap in the matrix pipeline; a key operand read
-      // from LDS serves every row tile.
-      f32x4_t sc[T][NSUB], sc2[T][NSUB];
+  // S[token 16 u + 4 kq + r][row m16] of chunk c on the matrix cores: T x NSUB
+  // independent chains; a key operand read from LDS serves every row tile.
+  auto qk = [&](int buf, f32x4_t (&sc)[T][NSUB]) __attribute__((always_inline)) {
+    const char* kl = &lds[buf][0];
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
-        const char* kl = lds[c & 1][u];
+        const uint4 kv = *reinterpret_cast<const uint4*>(kl + u * kSubBytes + ((st * 4 + kq) * 16 + m16) * 16);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          sc[t][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          sc2[t][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-#pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(kl + ((st * 4 + kq) * 16 + m16) * 16);
-#pragma unroll
-          for (int t = 0; t < T; ++t) {
-            const uint4 qq = qv[t][st];
-            f32x4_t& acc_s = (st & 1) ? sc2[t][u] : sc[t][u];
-            if constexpr (kBF16) {
-              acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qq), acc_s, 0, 0, 0);
-            } else {
-              acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.x), __uint_as_float(qq.x), acc_s, 0, 0, 0);
-              acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.y), __uint_as_float(qq.y), acc_s, 0, 0, 0);
-              acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.z), __uint_as_float(qq.z), acc_s, 0, 0, 0);
-              acc_s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.w), __uint_as_float(qq.w), acc_s, 0, 0, 0);
-            }
+          const uint4 qq = qv[t][st];
+          const f32x4_t prev = st == 0 ? f32x4_t{0.0f, 0.0f, 0.0f, 0.0f} : sc[t][u];
+          if constexpr (kBF16) {
+            sc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qq), prev, 0, 0, 0);
+          } else {
+            f32x4_t x = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.x), __uint_as_float(qq.x), prev, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.y), __uint_as_float(qq.y), x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.z), __uint_as_float(qq.z), x, 0, 0, 0);
+            sc[t][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kv.w), __uint_as_float(qq.w), x, 0, 0, 0);
           }
-        }
-#pragma unroll
-        for (int t = 0; t < T; ++t) sc[t][u] += sc2[t][u];
-      }
-      float m_ref[T];
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        // Scaled logits; a token after the row's position (or past the
-        // sequence, which is later still) gets -inf.
-        float gm = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < NSUB; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sc[t][u][r] = (CT * c + 16 * u + 4 * kq + r <= p_row[t]) ? sc[t][u][r] * a.c : -INFINITY;
-            gm = fmaxf(gm, sc[t][u][r]);
-          }
-        // Online softmax per row (lane column m16; the four lane groups hold its tokens).
-        gm = max_xor32(max_xor16(gm));
-        const float m_new = fmaxf(m_run[t], gm);
-        // -inf only for a row that has seen no token yet (in a split that starts
-        // after its position, or a tile past the run): then alpha and its weights
-        // are 0, never inf - inf.
-        m_ref[t] = m_new == -INFINITY ? 0.0f : m_new;
-        if (__ballot(m_new > m_run[t])) {  // some row's maximum grew: rescale (wave-uniform branch)
-          const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_ref[t]);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) acc[t][dt] *= alpha;
-          l_run[t] *= alpha;
-          m_run[t] = m_new;
-        }
-      }
-      // The lane's value columns of sub-chunk u: dims 16 dt + m16, tokens 4 kq .. 4 kq + 3
-      // (values past the end of the sequence may be anything, NaN poison included: zeroed).
-      auto values = [&](int u, auto (&vv)[NDT]) __attribute__((always_inline)) {
-        const int t0 = CT * c + 16 * u;
-        const char* vl = lds[c & 1][u] + kSubBytes;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int dim = 16 * dt + m16;
-          if constexpr (kBF16)
-            vv[dt] = *reinterpret_cast<const uint2*>(vl + 32 * dim + 8 * (kq ^ ((dim >> 2) & 3)));
-          else
-            vv[dt] = *reinterpret_cast<const uint4*>(vl + 64 * dim + 16 * (kq ^ ((dim >> 1) & 3)));
-        }
-        if (t0 + 16 > n) {
-          const int rel = n - t0 - 4 * kq;  // valid tokens among this lane's four
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            if constexpr (kBF16) {
-              vv[dt].x &= (rel > 0 ? 0x0000ffffu : 0u) | (rel > 1 ? 0xffff0000u : 0u);
-              vv[dt].y &= (rel > 2 ? 0x0000ffffu : 0u) | (rel > 3 ? 0xffff0000u : 0u);
-            } else {
-              if (rel <= 0) vv[dt].x = 0u;
-              if (rel <= 1) vv[dt].y = 0u;
-              if (rel <= 2) vv[dt].z = 0u;
-              if (rel <= 3) vv[dt].w = 0u;
-            }
-          }
-        }
-      };
-      float p[T][NSUB][4];
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int u = 0; u < NSUB; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[t][u][r] = __builtin_amdgcn_exp2f(sc[t][u][r] - m_ref[t]);
-            l_run[t] += p[t][u][r];
-          }
-      // O[dim][row] += V[dim][token] P[token][row].
-      if constexpr (kBF16) {
-        // Sub-chunks in pairs on 16x16x32 steps: lane (kq, m16) supplies k-slots
-        // 0-3 = tokens 4 kq + r of the first and 4-7 = the same of the second,
-        // for P (its QK registers) and V alike.  P enters as a high and a low
-        // bf16 term.
-        static_assert(NSUB % 2 == 0, "bf16 chunks hold pairs of sub-chunks");
-        typedef float f2_t __attribute__((ext_vector_type(2)));
-        typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
-        auto hi_bits = [](float x) __attribute__((always_inline)) { return __float_as_uint(x) & 0xffff0000u; };
-        auto pack_hi = [&](float x, float y) __attribute__((always_inline)) { return (hi_bits(x) >> 16) | hi_bits(y); };
-        auto pack_lo = [&](float x, float y) __attribute__((always_inline)) {
-          const f2_t l = {x - __uint_as_float(hi_bits(x)), y - __uint_as_float(hi_bits(y))};
-          return __builtin_bit_cast(uint32_t, __builtin_convertvector(l, b2_t));
-        };
-#pragma unroll
-        for (int u = 0; u < NSUB; u += 2) {
-          if (CT * c + 16 * u > p_wave) break;  // no row of the wave sees these tokens (wave-uniform)
-          uint2 va[NDT], vb[NDT];
-          values(u, va);
-          values(u + 1, vb);
-          u32x4_t ph[T], pl[T];
-#pragma unroll
-          for (int t = 0; t < T; ++t) {
-            ph[t] = u32x4_t{pack_hi(p[t][u][0], p[t][u][1]), pack_hi(p[t][u][2], p[t][u][3]),
-                            pack_hi(p[t][u + 1][0], p[t][u + 1][1]), pack_hi(p[t][u + 1][2], p[t][u + 1][3])};
-            pl[t] = u32x4_t{pack_lo(p[t][u][0], p[t][u][1]), pack_lo(p[t][u][2], p[t][u][3]),
-                            pack_lo(p[t][u + 1][0], p[t][u + 1][1]), pack_lo(p[t][u + 1][2], p[t][u + 1][3])};
-          }
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const u32x4_t av = {va[dt].x, va[dt].y, vb[dt].x, vb[dt].y};
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                                   __builtin_bit_cast(bf16x8_t, ph[t]), acc[t][dt], 0, 0, 0);
-              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                                   __builtin_bit_cast(bf16x8_t, pl[t]), acc[t][dt], 0, 0, 0);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < NSUB; ++u) {
-          if (CT * c + 16 * u > p_wave) break;  // no row of the wave sees these tokens (wave-uniform)
-          uint4 vv[NDT];
-          values(u, vv);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].x), p[t][u][0], acc[t][dt], 0, 0, 0);
-              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].y), p[t][u][1], acc[t][dt], 0, 0, 0);
-              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].z), p[t][u][2], acc[t][dt], 0, 0, 0);
-              acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].w), p[t][u][3], acc[t][dt], 0, 0, 0);
-            }
         }
       }
     }
-    // Chunk c + 1 into the other buffer (its last readers passed the previous
-    // barrier), then the loads of chunk c + 2.
-    put((c + 1) & 1);
-    stage(c + 2);
+  };
+
+  // Causal mask of chunk c's scores (a token after the row's position, or past
+  // the sequence, gets -inf: the lane's tokens 16 u + r past lim), then the
+  // row maxima gm[t] of the chunk (lane column m16; the four lane groups hold
+  // its tokens), NaN-propagating: no quieting steps, and a NaN score (garbage
+  // in the cache) makes its row NaN.  Chunks that end before the tile's first
+  // row need no mask.
+  auto mask_max = [&](int c, f32x4_t (&x)[T][NSUB], float (&gm)[T]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (CT * c + CT - 1 > p_first[t]) {
+        const int lim = p_row[t] - CT * c - 4 * kq;
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[t][u][r] = 16 * u + r > lim ? -INFINITY : x[t][u][r];
+      }
+      float m = x[t][0][0];
+#pragma unroll
+      for (int i = 1; i < 4 * NSUB; i += 2) {
+        const float y0 = x[t][i / 4][i % 4];
+        const float y1 = i + 1 < 4 * NSUB ? x[t][(i + 1) / 4][(i + 1) % 4] : y0;
+        m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, y0), y1);
+      }
+      gm[t] = nmax_xor32(nmax_xor16(m));
+    }
+  };
+  // The lazy reference: when some row's maximum exceeds its reference by more
+  // than kLazy (cs (m_new - m_ref) is +inf from an empty start and NaN for a
+  // row still empty), every row whose maximum grew moves to it and its
+  // accumulators are rescaled.
+  auto update = [&](const float (&gm)[T]) __attribute__((always_inline)) {
+    float m_new[T];
+    bool far = false;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      m_new[t] = __builtin_elementwise_maximum(m_ref[t], gm[t]);
+      far = far || cs * (m_new[t] - m_ref[t]) > kLazy;
+    }
+    if (__ballot(far)) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float alpha = m_new[t] == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(cs * (m_ref[t] - m_new[t]));
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[t][dt] *= alpha;
+        l_run[t] *= alpha;
+        m_ref[t] = m_new[t];
+      }
+    }
+  };
+  // Probabilities p[t][u][r] of token 16 u + 4 kq + r for row m16 of tile t; a
+  // row whose reference is still -inf (it has seen no token: a split that
+  // starts after its position, or a tile past the run) gets weights 0.
+  auto probs = [&](const f32x4_t (&x)[T][NSUB], float (&p)[T][NSUB][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float bias = m_ref[t] == -INFINITY ? 0.0f : cs * m_ref[t];
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[t][u][r] = __builtin_amdgcn_exp2f(fmaf(x[t][u][r], cs, -bias));
+          l_run[t] += p[t][u][r];
+        }
+    }
+  };
+  // O[dim][row] += V[dim][token] P[token][row] for the chunk in buffer buf.
+  auto pv = [&](int buf, const float (&p)[T][NSUB][4], int c) __attribute__((always_inline)) {
+    const char* vreg = &lds[buf][NSUB * kSubBytes];
+    if constexpr (kBF16) {
+      // Sub-chunks in pairs on 16x16x32 steps: lane (kq, m16) supplies k-slots
+      // 0-3 = tokens 4 kq + r of the first and 4-7 = the same of the second,
+      // for P (its QK registers) and V (one 16-byte slot) alike.  P enters as
+      // hi + lo: hi = p truncated to bf16 (the upper halves of two floats, one
+      // byte permutation), lo = bf16_rne(p - hi), so |p - hi - lo| <= 2^-16 p.
+      static_assert(NSUB == 2, "bf16 chunks are one pair of sub-chunks");
+      typedef float f2_t __attribute__((ext_vector_type(2)));
+      typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+      auto pack_hi = [](float x, float y) __attribute__((always_inline)) {
+        return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+      };
+      auto pack_lo = [](float x, float y) __attribute__((always_inline)) {
+        const f2_t l = {x - __uint_as_float(__float_as_uint(x) & 0xffff0000u),
+                        y - __uint_as_float(__float_as_uint(y) & 0xffff0000u)};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(l, b2_t));
+      };
+      u32x4_t vv[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int dim = 16 * dt + m16;
+        vv[dt] = *reinterpret_cast<const u32x4_t*>(vreg + 64 * dim + 16 * (kq ^ vswz(dim)));
+      }
+      u32x4_t ph[T], pl[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        ph[t] = u32x4_t{pack_hi(p[t][0][0], p[t][0][1]), pack_hi(p[t][0][2], p[t][0][3]),
+                        pack_hi(p[t][1][0], p[t][1][1]), pack_hi(p[t][1][2], p[t][1][3])};
+        pl[t] = u32x4_t{pack_lo(p[t][0][0], p[t][0][1]), pack_lo(p[t][0][2], p[t][0][3]),
+                        pack_lo(p[t][1][0], p[t][1][1]), pack_lo(p[t][1][2], p[t][1][3])};
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv[dt]),
+                                                               __builtin_bit_cast(bf16x8_t, ph[t]), acc[t][dt], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv[dt]),
+                                                               __builtin_bit_cast(bf16x8_t, pl[t]), acc[t][dt], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) {
+        if (CT * c + 16 * u > p_wave) break;  // no row of the wave sees these tokens (wave-uniform)
+        uint4 vv[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int dim = 16 * dt + m16;
+          vv[dt] = *reinterpret_cast<const uint4*>(vreg + u * kSubBytes + 64 * dim + 16 * (kq ^ vswz(dim)));
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].x), p[t][u][0], acc[t][dt], 0, 0, 0);
+            acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].y), p[t][u][1], acc[t][dt], 0, 0, 0);
+            acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].z), p[t][u][2], acc[t][dt], 0, 0, 0);
+            acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vv[dt].w), p[t][u][3], acc[t][dt], 0, 0, 0);
+          }
+      }
+    }
+  };
+
+  // Chunk c sits in LDS buffer (c - c_begin) mod NBUF.  bf16: iteration c
+  // runs chunk c's mask and maxima, then computes chunk c + 1's scores beside
+  // chunk c's exponentials and packing (matrix cores beside vector units),
+  // then chunk c's value product, and parks chunk c + 2, whose buffer chunk
+  // c - 1 left before the previous barrier.  fp32: scores, softmax and value
+  // product of chunk c in turn, and chunk c + 1 parked in the other buffer.
+  constexpr int kLead = kAhead ? 2 : 1;  // chunks parked ahead of the one computed
+  int ids[NSUB];
+  chunk_ids(c_begin, ids);
+  stage(c_begin, ids);
+  put(c_begin, 0);
+  if constexpr (kAhead) {
+    chunk_ids(c_begin + 1, ids);
+    stage(c_begin + 1, ids);
+    put(c_begin + 1, 1);
+  }
+  chunk_ids(c_begin + kLead, ids);
+  stage(c_begin + kLead, ids);
+  __syncthreads();
+  f32x4_t sc[T][NSUB];
+  if constexpr (kAhead) {
+    if (CT * c_begin <= p_wave) qk(0, sc);
+  }
+  int b_cur = 0;  // the buffer of chunk c
+  for (int c = c_begin; c < nc; ++c) {
+    // The block ids staged at the end of this iteration, read at its start:
+    // an outstanding scalar load makes every LDS wait a full one, and the
+    // barrier waits for it.
+    chunk_ids(c + kLead + 1, ids);
+    if (CT * c <= p_wave) {  // some row of the wave sees this chunk (wave-uniform)
+      float p[T][NSUB][4];
+      float gm[T];
+      if constexpr (kAhead) {
+        mask_max(c, sc, gm);
+        update(gm);
+        // Past the last chunk (or the wave's) the next chunk's scores read a
+        // stale buffer and are discarded.
+        f32x4_t sc_next[T][NSUB];
+        qk(buf_add(b_cur, 1), sc_next);
+        probs(sc, p);
+        pv(b_cur, p, c);
+        // Issue order for this block: the LDS reads first, then each score
+        // step followed by a share of the exponentials and packing, then the
+        // value product.
+        __builtin_amdgcn_sched_group_barrier(0x100, KS * NSUB + NDT, 0);  // DS reads
+#pragma unroll
+        for (int i = 0; i < KS * NSUB * T; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int u = 0; u < NSUB; ++u) sc[t][u] = sc_next[t][u];
+      } else {
+        qk(b_cur, sc);
+        mask_max(c, sc, gm);
+        update(gm);
+        probs(sc, p);
+        pv(b_cur, p, c);
+      }
+    }
+    // Chunk c + kLead into its buffer (whose last readers passed the previous
+    // barrier), then the loads of chunk c + kLead + 1.
+    put(c + kLead, buf_add(b_cur, kLead));
+    b_cur = buf_add(b_cur, 1);
+    stage(c + kLead + 1, ids);
     __syncthreads();
   }
   if (__ballot(poison) != 0 && lane == 0) poison_any = 1;
@@ -472,7 +599,7 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
       for (int dt = 0; dt < NDT; ++dt)
         *reinterpret_cast<f32x4_t*>(a.ws_acc + part * D + 16 * dt + 4 * kq) = acc[0][dt] * f;
       if (kq == 0) {
-        a.ws_m[part] = m_run[0];
+        a.ws_m[part] = m_ref[0] == -INFINITY ? -INFINITY : cs * m_ref[0];  // the reference, exp2 domain
         a.ws_l[part] = l_tot[0] * f;
       }
     }

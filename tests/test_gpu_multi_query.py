@@ -92,7 +92,7 @@ class Batch:
         return t, l
 
     def multi(self, runs, q, tables=None, lens=None, query_start=None, max_query_len=None, out=None, split=False,
-              order=None):
+              order=None, scale=None):
         t, l = self.tables() if tables is None else (tables, lens)
         starts = np.concatenate([[0], np.cumsum(runs)]).astype(np.int32) if query_start is None else query_start
         T = q.shape[0]
@@ -106,14 +106,16 @@ class Batch:
             ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.pk.pkv_paged_attention_multi(out, to_dev(q, self.dt), *self.caches, torch.from_numpy(t).cuda(),
                                           torch.from_numpy(l).cuda(), torch.from_numpy(starts).cuda(),
-                                          int(max(l.max(), 1)), mql, 1.0 / np.sqrt(self.d), workspace=ws,
+                                          int(max(l.max(), 1)), mql,
+                                          1.0 / np.sqrt(self.d) if scale is None else scale, workspace=ws,
                                           seq_order=None if order is None else torch.tensor(order, dtype=torch.int32,
                                                                                             device="cuda"))
         torch.cuda.synchronize()
         return out.cpu().numpy(), t, l, starts
 
-    def oracle(self, q, t, l, starts):
-        return oa.paged_attention_multi(q, *self.ocaches, t, l, starts, np.float32(1.0 / np.sqrt(self.d)), self.dt)
+    def oracle(self, q, t, l, starts, scale=None):
+        sc = np.float32(1.0 / np.sqrt(self.d) if scale is None else scale)
+        return oa.paged_attention_multi(q, *self.ocaches, t, l, starts, sc, self.dt)
 
 
 GRID = [(dt, d, G, B) for dt in ("f32", "bf16") for d in (64, 128) for G in (1, 2, 4, 8) for B in (16, 32)]
@@ -136,6 +138,25 @@ def test_runs_grid(dt, d, G, B, tiles, monkeypatch):
     q = wl.draw_values(wl.rng_for(5, wl.STREAM_Q, G, d), (sum(runs), G * Hkv, d), dt)
     out, t, l, starts = b.multi(runs, q)
     check_close(out, b.oracle(q, t, l, starts), dt, "runs")
+
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("dt,scale", [(dt, x) for dt in ("bf16", "f32") for x in (-0.125, 0.0, 0.3)] +
+                         [("bf16", 0.6), ("bf16", -1.5)])
+def test_scale_sign_and_size(dt, scale, split):
+    """Any finite scale: a negative one (the queries enter with flipped signs), zero (equal weights over the visible
+    tokens) and larger ones, whose logits spread over tens of exp2 units, so that the row references move many
+    times and the weights of a chunk reach up to 2^8 between moves; with and without context splits.  (fp32 keeps
+    to scales whose logits' float32 rounding stays inside its 1e-5 bound.)"""
+    if split:
+        lens, runs = [1200, 700, 64], [3, 2, 1]  # few rows per pair over long contexts: the plan splits them
+    else:
+        lens, runs = [300, 47, 513, 96], [300, 5, 200, 1]
+    b = Batch(lens, 8, 2, 128, 16, dt, seed=77)
+    q = wl.draw_values(wl.rng_for(11, wl.STREAM_Q), (sum(runs), 8, 128), dt)
+    say(f"case {dt} scale={scale} split={split}")
+    out, t, l, starts = b.multi(runs, q, split=split, scale=scale)
+    check_close(out, b.oracle(q, t, l, starts, scale=scale), dt, f"scale {scale}")
 
 
 @pytest.mark.parametrize("dt,B", [("bf16", 16), ("f32", 32)])
