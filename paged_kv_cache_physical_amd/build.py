@@ -5,6 +5,7 @@ Usage: ``python -m paged_kv_cache_physical_amd.build`` (or ``build()``).
 
 from __future__ import annotations
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -41,6 +42,12 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{out}")
     if verbose and out.strip():
         print(out, flush=True)
+    # A kernel whose host-side launch stub failed to generate leaves an
+    # undefined symbol that only a load shows: load it now, resolving every symbol.
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

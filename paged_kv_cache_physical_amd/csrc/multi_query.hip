@@ -50,6 +50,13 @@ __device__ __forceinline__ uint4 mq_load16(__amdgpu_buffer_rsrc_t r, int voff) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16-byte load of each lane straight into LDS: lane L's bytes land at
+// dst + 16 L (dst: the wave's LDS block, the same for every lane).
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, char* dst, int voff) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+
 constexpr int kMqWaves = 4;  // waves per workgroup
 constexpr int kXcds = 8;     // accelerator complex dies of an MI355X
 
@@ -107,25 +114,41 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
   constexpr int NSUB = (65536 / (4 * kSubBytes)) < 2 ? (65536 / (4 * kSubBytes)) : 2;
   constexpr int CT = 16 * NSUB;  // tokens per chunk
   constexpr int kThreads = kWave * kMqWaves;
-  constexpr int NIT = NSUB * ITEMS / kThreads;  // pieces per thread per cache per chunk
-  static_assert(NSUB >= 1 && (NSUB * ITEMS) % kThreads == 0 && ITEMS % kWave == 0, "staging shape");
-  // LDS per buffer: the keys of each sub-chunk u at u kSubBytes, laid out
-  // [piece][16 tokens][16 B]; then the values.  bf16: one region for the
-  // chunk, [dim][slot][16 B], where slot s holds tokens 4 s .. 4 s + 3 of sub-
-  // chunk 0 and then of sub-chunk 1, exactly the 16 bytes one lane feeds a
-  // 16x16x32 step; fp32: per sub-chunk, [dim][16 tokens].  The slots of a row
-  // sit XOR-swizzled by the dim (slot s at s ^ vswz(dim)), so that the rows
-  // one value read touches fall in distinct banks.
-  // bf16: three buffers, the scores of chunk c + 1 issued while chunk c's
-  // softmax runs (below); fp32 (twice the bytes per chunk): two.
-  constexpr bool kAhead = kBF16;
-  constexpr int NBUF = kAhead ? 3 : 2;
-  __shared__ __attribute__((aligned(16))) char lds[NBUF][2 * NSUB * kSubBytes];
-  // The buffer of chunk c + k, given b = the buffer of chunk c (0 <= k < NBUF).
-  auto buf_add = [](int b, int k) __attribute__((always_inline)) { return b + k >= NBUF ? b + k - NBUF : b + k; };
-  auto vswz = [](int dim) __attribute__((always_inline)) {
-    return kBF16 ? ((dim >> 1) ^ (dim >> 2)) & 3 : (dim >> 1) & 3;
+  // Chunks move straight from HBM into LDS: a wave's 16-byte load lands lane L's
+  // bytes at its 1 KiB block's base + 16 L, so the layout is set by which source
+  // unit each lane fetches.  Per buffer, NBLK blocks of keys then NBLK of values:
+  //   keys: sub-chunk u at u kSubBytes, [piece][16 positions][16 B]; bf16 token
+  //     t of the sub-chunk sits at position t ^ 4 (t >> 3) ^ 4 u, so that the
+  //     sixteen rows of a score tile (below) fall in distinct banks.
+  //   values, bf16: sub-chunk u at u kSubBytes, 1 KiB per 32 dims, the dim's
+  //     two 8-token units at 2 (dim & 31) + (half ^ vflip(dim)); fp32: sub-chunk
+  //     u at u kSubBytes, [dim][4-token slot ^ vswz(dim)][16 B].
+  // bf16 score tiles take the chunk's tokens permuted: row r of tile u is token
+  // 8 (r / 4) + 4 u + r % 4, so that lane (kq, m16) ends up holding the scores
+  // of tokens 8 kq .. 8 kq + 7, the k-slots it feeds a 16x16x32 value step, and
+  // its value operand is one 8-token unit.
+  constexpr int NBLK = NSUB * kSubBytes / 1024;  // 1 KiB blocks of one cache per chunk
+  constexpr int NB = NBLK / kMqWaves;           // blocks per wave per cache per chunk
+  constexpr int BPS = kSubBytes / 1024;         // blocks per sub-chunk
+  static_assert(NSUB >= 1 && NBLK % kMqWaves == 0 && kSubBytes % 1024 == 0, "staging shape");
+  // Three buffers where they fit in 48 KiB (two chunks of loads in flight while
+  // a third is computed), else two.
+  // The buffers are separate LDS objects, indexed by compile-time constants
+  // (the chunk loop below is unrolled over them), so that the compiler can
+  // tell a read of one buffer from a load still landing in another and waits
+  // only where a read needs its own wave's load.
+  constexpr int NBUF = 3 * 2 * NSUB * kSubBytes <= 49152 ? 3 : 2;
+  constexpr int kBufBytes = 2 * NSUB * kSubBytes;
+  __shared__ __attribute__((aligned(1024))) char lds0[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char lds2[NBUF == 3 ? kBufBytes : 16];
+  auto lds_buf = [&](auto b) __attribute__((always_inline)) -> char* {
+    constexpr int k = decltype(b)::value % NBUF;
+    return k == 0 ? lds0 : k == 1 ? lds1 : lds2;
   };
+  auto vswz = [](int dim) __attribute__((always_inline)) { return (dim >> 1) & 3; };
+  auto vflip = [](int dim) __attribute__((always_inline)) { return ((dim >> 2) ^ (dim >> 3)) & 1; };
+  auto kpos = [](int t, int u) __attribute__((always_inline)) { return kBF16 ? t ^ (4 * (t >> 3)) ^ (4 * u) : t; };
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -251,13 +274,10 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
     }
   }
 
-  // Staging: thread piece j of a chunk is i = tid + kThreads j, in sub-chunk
-  // i / ITEMS (the same for a whole wave); within it, key piece ii is (key
-  // piece ii / 16, token ii % 16) and value piece ii is (dim ii / kItem,
-  // tokens (ii % kItem) * 16 / kItem + 0 ..).
-  // A bad block id is seen only by the threads that stage its tile; the flag
-  // is combined over the workgroup after the chunk loop, since every wave's
-  // rows read the whole chunk from LDS.
+  // Wave w moves blocks w + 4 j (j < NB) of each cache per chunk.  A bad block
+  // id is seen only by the waves that load its tiles; the flag is combined
+  // over the workgroup after the chunk loop, since every wave's rows read the
+  // whole chunk.
   bool poison = false;
   __shared__ int poison_any;
   if (tid == 0) poison_any = 0;  // ordered before any write of 1 by the barriers below
@@ -268,19 +288,33 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
   // Address parts fixed for the whole loop: a block's tile of this KV head
   // starts at cache + (head 0 of the KV head's tiles) + id * kstride
   // (kstride = H_kv tiles < 2^32 bytes, as H_kv <= 65535 and a tile <= 16 KiB),
-  // and each thread's pieces sit at fixed offsets in the tiles.
+  // and each lane's source units sit at fixed offsets in the tiles.
   const uint32_t kstride = static_cast<uint32_t>(a.num_kv_heads) * static_cast<uint32_t>(tile_bytes);
   const char* kbase = a.k_cache + static_cast<int64_t>(g) * tile_bytes;
   const char* vbase = a.v_cache + static_cast<int64_t>(g) * tile_bytes;
-  int koff[NIT], voff[NIT];
-#pragma unroll
-  for (int j = 0; j < NIT; ++j) {
-    const int sub = (kWave * wave + kThreads * j) / ITEMS;  // wave-uniform
-    const int ii = tid + kThreads * j - sub * ITEMS;
+  // Lane parts of block j's source units, recomputed where used (cheaper than
+  // holding them in registers): key offset, value offset, and the value
+  // unit's first token in its sub-chunk.
+  struct Src {
+    int k, v, vtok;
+  };
+  auto unit_src = [&](int j) __attribute__((always_inline)) {
+    const int blk = wave + kMqWaves * j, sub = blk / BPS, pg = blk % BPS;
     const int o = (16 * sub) & (B - 1);  // the sub-chunk's first row in its block (chunks start at block starts)
-    koff[j] = ((ii >> 4) * B + o + (ii & 15)) * 16;
-    voff[j] = ((ii / kItem) * B + o + (ii % kItem) * (16 / kItem)) * kItem;
-  }
+    const int piece = 4 * pg + (lane >> 4);
+    Src r;
+    r.k = (piece * B + o + kpos(lane & 15, sub & 1)) * 16;
+    if constexpr (kBF16) {
+      const int dim = 32 * pg + (lane >> 1), half = (lane & 1) ^ vflip(32 * pg + (lane >> 1));
+      r.v = (dim * B + o + 8 * half) * 2;
+      r.vtok = 8 * half;
+    } else {
+      const int dim = 16 * pg + (lane >> 2), slot = (lane & 3) ^ vswz(16 * pg + (lane >> 2));
+      r.v = (dim * B + o + 4 * slot) * 4;
+      r.vtok = 4 * slot;
+    }
+    return r;
+  };
   // Block ids of chunk c's sub-chunks, read one iteration before they are
   // used (scalar loads; the index is clamped to the sequence's last block,
   // which matters only for sub-chunks past its end, which load nothing).
@@ -288,36 +322,37 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
 #pragma unroll
     for (int u = 0; u < NSUB; ++u) ids[u] = mq_ld(a.block_tables, table_row + min((CT * c + 16 * u) >> lgB, last_blk));
   };
-  uint4 kr[NIT], vr[NIT];
-  auto stage = [&](int c, const int (&ids)[NSUB]) __attribute__((always_inline)) {
+  // Loads chunk c into buffer buf; sub-chunks past the sequence (and past the
+  // last chunk) go through size-0 resources and land as zeros.
+  auto issue = [&](int c, auto buf, const int (&ids)[NSUB]) __attribute__((always_inline)) {
+    char* const lb = lds_buf(buf);
 #pragma unroll
-    for (int j = 0; j < NIT; ++j) {
-      const int sub = (kWave * wave + kThreads * j) / ITEMS;  // wave-uniform
+    for (int j = 0; j < NB; ++j) {
+      const int blk_idx = wave + kMqWaves * j, sub = blk_idx / BPS;  // wave-uniform
       const bool in = c < nc && CT * c + 16 * sub < n;
       const int blk = ids[sub];
       const bool ok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
       poison |= in && !ok;
       const uint64_t off = ok ? static_cast<uint64_t>(static_cast<uint32_t>(blk)) * kstride : 0;
       const int bytes = (in && ok) ? tile_bytes : 0;
-      kr[j] = mq_load16(make_rsrc(kbase + off, bytes), koff[j]);
-      vr[j] = mq_load16(make_rsrc(vbase + off, bytes), voff[j]);
+      const Src src = unit_src(j);
+      load_to_lds16(make_rsrc(kbase + off, bytes), lb + 1024 * blk_idx, src.k);
+      load_to_lds16(make_rsrc(vbase + off, bytes), lb + 1024 * (NBLK + blk_idx), src.v);
     }
   };
-  // Parks the staged chunk c in its buffer.  Values of tokens past the end of
-  // the sequence (the cache may hold anything there, NaN poison included) are
-  // parked as zeros, so that their zero weights give exact zeros; their keys'
-  // scores are masked.
-  auto put = [&](int c, int buf) __attribute__((always_inline)) {
+  // Values of tokens past the end of the sequence (the cache may hold anything
+  // there, NaN poison included) become zeros once this wave's loads of chunk c
+  // have landed, so that their zero weights give exact zeros; their keys'
+  // scores are masked.  Each wave fixes the units it loaded.
+  auto fix_tail = [&](int c, auto buf) __attribute__((always_inline)) {
+    if (CT * c + CT <= n) return;  // wave-uniform
 #pragma unroll
-    for (int j = 0; j < NIT; ++j) {
-      const int sub = (kWave * wave + kThreads * j) / ITEMS;
-      const int ii = tid + kThreads * j - sub * ITEMS;
-      *reinterpret_cast<uint4*>(&lds[buf][sub * kSubBytes + 16 * ii]) = kr[j];
-      const int dim = ii / kItem, part = ii % kItem;
-      if (CT * c + 16 * sub + 16 > n) {  // wave-uniform
-        // valid tokens among the piece's: bf16 8 (two per dword), fp32 4
-        const int rel = n - CT * c - 16 * sub - part * (16 / kItem);
-        uint32_t* w = reinterpret_cast<uint32_t*>(&vr[j]);
+    for (int j = 0; j < NB; ++j) {
+      const int blk_idx = wave + kMqWaves * j, sub = blk_idx / BPS;
+      const int rel = n - (CT * c + 16 * sub + unit_src(j).vtok);  // valid tokens of the unit (8 bf16 or 4 fp32)
+      if (rel < (kBF16 ? 8 : 4)) {
+        uint32_t* unit = reinterpret_cast<uint32_t*>(lds_buf(buf) + 1024 * (NBLK + blk_idx) + 16 * lane);
+        u32x4_t w = *reinterpret_cast<u32x4_t*>(unit);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (kBF16)
@@ -325,17 +360,7 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
           else if (e >= rel)
             w[e] = 0u;
         }
-      }
-      char* vreg = &lds[buf][NSUB * kSubBytes];
-      if constexpr (kBF16) {
-        // Piece = tokens 8 part .. 8 part + 7 of the row: the sub-chunk's halves of slots 2 part and 2 part + 1.
-        *reinterpret_cast<uint2*>(vreg + 64 * dim + 16 * ((2 * part) ^ vswz(dim)) + 8 * (sub & 1)) =
-            make_uint2(vr[j].x, vr[j].y);
-        *reinterpret_cast<uint2*>(vreg + 64 * dim + 16 * ((2 * part + 1) ^ vswz(dim)) + 8 * (sub & 1)) =
-            make_uint2(vr[j].z, vr[j].w);
-      } else {
-        // Piece = 4-token slot `part` of the row.
-        *reinterpret_cast<uint4*>(vreg + sub * kSubBytes + 64 * dim + 16 * (part ^ vswz(dim))) = vr[j];
+        *reinterpret_cast<u32x4_t*>(unit) = w;
       }
     }
   };
@@ -357,15 +382,21 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
     p_first[t] = pos0 + r0[t] / G;
   }
 
-  // S[token 16 u + 4 kq + r][row m16] of chunk c on the matrix cores: T x NSUB
+  // Scores of chunk c on the matrix cores, S[token][row m16] for the tokens of
+  // score tile u (bf16: 8 (r / 4) + 4 u + r % 4 for tile row r; fp32: sub-chunk
+  // u); lane (kq, m16) receives tile rows 4 kq .. 4 kq + 3.  T x NSUB
   // independent chains; a key operand read from LDS serves every row tile.
-  auto qk = [&](int buf, f32x4_t (&sc)[T][NSUB]) __attribute__((always_inline)) {
-    const char* kl = &lds[buf][0];
+  auto qk = [&](auto buf, f32x4_t (&sc)[T][NSUB]) __attribute__((always_inline)) {
+    const char* kl = lds_buf(buf);
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(kl + u * kSubBytes + ((st * 4 + kq) * 16 + m16) * 16);
+        // the key row this lane feeds: token tt of sub-chunk su
+        const int tok = kBF16 ? 8 * (m16 >> 2) + 4 * u + (m16 & 3) : 16 * u + m16;
+        const int su = tok >> 4, tt = tok & 15;
+        const uint4 kv =
+            *reinterpret_cast<const uint4*>(kl + su * kSubBytes + ((st * 4 + kq) * 16 + kpos(tt, su)) * 16);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const uint4 qq = qv[t][st];
@@ -384,7 +415,7 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
   };
 
   // Causal mask of chunk c's scores (a token after the row's position, or past
-  // the sequence, gets -inf: the lane's tokens 16 u + r past lim), then the
+  // the sequence, gets -inf), then the
   // row maxima gm[t] of the chunk (lane column m16; the four lane groups hold
   // its tokens), NaN-propagating: no quieting steps, and a NaN score (garbage
   // in the cache) makes its row NaN.  Chunks that end before the tile's first
@@ -393,11 +424,12 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (CT * c + CT - 1 > p_first[t]) {
-        const int lim = p_row[t] - CT * c - 4 * kq;
+        // the lane's tokens: bf16 8 kq + 4 u + r, fp32 16 u + 4 kq + r
+        const int lim = p_row[t] - CT * c - (kBF16 ? 8 : 4) * kq;
 #pragma unroll
         for (int u = 0; u < NSUB; ++u)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[t][u][r] = 16 * u + r > lim ? -INFINITY : x[t][u][r];
+          for (int r = 0; r < 4; ++r) x[t][u][r] = (kBF16 ? 4 : 16) * u + r > lim ? -INFINITY : x[t][u][r];
       }
       float m = x[t][0][0];
 #pragma unroll
@@ -432,7 +464,7 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
       }
     }
   };
-  // Probabilities p[t][u][r] of token 16 u + 4 kq + r for row m16 of tile t; a
+  // Probabilities p[t][u][r] for the scores sc[t][u][r] of row m16 of tile t; a
   // row whose reference is still -inf (it has seen no token: a split that
   // starts after its position, or a tile past the run) gets weights 0.
   auto probs = [&](const f32x4_t (&x)[T][NSUB], float (&p)[T][NSUB][4]) __attribute__((always_inline)) {
@@ -449,14 +481,15 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
     }
   };
   // O[dim][row] += V[dim][token] P[token][row] for the chunk in buffer buf.
-  auto pv = [&](int buf, const float (&p)[T][NSUB][4], int c) __attribute__((always_inline)) {
-    const char* vreg = &lds[buf][NSUB * kSubBytes];
+  auto pv = [&](auto buf, const float (&p)[T][NSUB][4], int c) __attribute__((always_inline)) {
+    const char* vreg = lds_buf(buf) + 1024 * NBLK;
     if constexpr (kBF16) {
-      // Sub-chunks in pairs on 16x16x32 steps: lane (kq, m16) supplies k-slots
-      // 0-3 = tokens 4 kq + r of the first and 4-7 = the same of the second,
-      // for P (its QK registers) and V (one 16-byte slot) alike.  P enters as
-      // hi + lo: hi = p truncated to bf16 (the upper halves of two floats, one
-      // byte permutation), lo = bf16_rne(p - hi), so |p - hi - lo| <= 2^-16 p.
+      // One 16x16x32 step per dim tile: lane (kq, m16) supplies k-slots
+      // 8 kq .. 8 kq + 7 = tokens 8 kq .. 8 kq + 7 of the chunk, for P (its
+      // score registers of tiles 0 and 1) and V (one 8-token unit) alike.  P
+      // enters as hi + lo: hi = p truncated to bf16 (the upper halves of two
+      // floats, one byte permutation), lo = bf16_rne(p - hi), so
+      // |p - hi - lo| <= 2^-16 p.
       static_assert(NSUB == 2, "bf16 chunks are one pair of sub-chunks");
       typedef float f2_t __attribute__((ext_vector_type(2)));
       typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
@@ -472,7 +505,8 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int dim = 16 * dt + m16;
-        vv[dt] = *reinterpret_cast<const u32x4_t*>(vreg + 64 * dim + 16 * (kq ^ vswz(dim)));
+        vv[dt] = *reinterpret_cast<const u32x4_t*>(vreg + (kq >> 1) * kSubBytes + 1024 * (dim >> 5) +
+                                                   16 * (2 * (dim & 31) + ((kq & 1) ^ vflip(dim))));
       }
       u32x4_t ph[T], pl[T];
 #pragma unroll
@@ -516,74 +550,57 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
     }
   };
 
-  // Chunk c sits in LDS buffer (c - c_begin) mod NBUF.  bf16: iteration c
-  // runs chunk c's mask and maxima, then computes chunk c + 1's scores beside
-  // chunk c's exponentials and packing (matrix cores beside vector units),
-  // then chunk c's value product, and parks chunk c + 2, whose buffer chunk
-  // c - 1 left before the previous barrier.  fp32: scores, softmax and value
-  // product of chunk c in turn, and chunk c + 1 parked in the other buffer.
-  constexpr int kLead = kAhead ? 2 : 1;  // chunks parked ahead of the one computed
+  // Chunk c sits in LDS buffer (c - c_begin) mod NBUF.  Iteration c starts the
+  // loads of chunk c + NBUF - 1 into the buffer chunk c - 1 left before the
+  // previous barrier, computes chunk c (scores, softmax, value product), then
+  // waits for this wave's loads of chunk c + 1 (issued at least one iteration
+  // earlier), fixes its tail, and meets the other waves at the barrier.  The
+  // barrier is a plain s_barrier after explicit waits: a workgroup fence there
+  // would also wait for the loads still in flight.
+  constexpr int NL = 2 * NB;  // loads per lane per chunk
+  auto barrier_after_loads = [](auto keep) __attribute__((always_inline)) {
+    // vmcnt(keep): at most `keep` of this wave's loads still outstanding; lgkmcnt(0): its LDS accesses done
+    static_assert(decltype(keep)::value < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0070 | decltype(keep)::value);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  using Keep = std::integral_constant<int, (NBUF - 2) * NL>;
   int ids[NSUB];
   chunk_ids(c_begin, ids);
-  stage(c_begin, ids);
-  put(c_begin, 0);
-  if constexpr (kAhead) {
+  issue(c_begin, std::integral_constant<int, 0>{}, ids);
+  if constexpr (NBUF == 3) {
     chunk_ids(c_begin + 1, ids);
-    stage(c_begin + 1, ids);
-    put(c_begin + 1, 1);
+    issue(c_begin + 1, std::integral_constant<int, 1>{}, ids);
   }
-  chunk_ids(c_begin + kLead, ids);
-  stage(c_begin + kLead, ids);
-  __syncthreads();
-  f32x4_t sc[T][NSUB];
-  if constexpr (kAhead) {
-    if (CT * c_begin <= p_wave) qk(0, sc);
-  }
-  int b_cur = 0;  // the buffer of chunk c
-  for (int c = c_begin; c < nc; ++c) {
-    // The block ids staged at the end of this iteration, read at its start:
-    // an outstanding scalar load makes every LDS wait a full one, and the
-    // barrier waits for it.
-    chunk_ids(c + kLead + 1, ids);
-    if (CT * c <= p_wave) {  // some row of the wave sees this chunk (wave-uniform)
-      float p[T][NSUB][4];
-      float gm[T];
-      if constexpr (kAhead) {
-        mask_max(c, sc, gm);
-        update(gm);
-        // Past the last chunk (or the wave's) the next chunk's scores read a
-        // stale buffer and are discarded.
-        f32x4_t sc_next[T][NSUB];
-        qk(buf_add(b_cur, 1), sc_next);
-        probs(sc, p);
-        pv(b_cur, p, c);
-        // Issue order for this block: the LDS reads first, then each score
-        // step followed by a share of the exponentials and packing, then the
-        // value product.
-        __builtin_amdgcn_sched_group_barrier(0x100, KS * NSUB + NDT, 0);  // DS reads
-#pragma unroll
-        for (int i = 0; i < KS * NSUB * T; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
-        }
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-          for (int u = 0; u < NSUB; ++u) sc[t][u] = sc_next[t][u];
-      } else {
-        qk(b_cur, sc);
-        mask_max(c, sc, gm);
-        update(gm);
-        probs(sc, p);
-        pv(b_cur, p, c);
-      }
+  chunk_ids(c_begin + NBUF - 1, ids);  // for the first iteration
+  __builtin_amdgcn_s_waitcnt(0x0070 | Keep::value);
+  fix_tail(c_begin, std::integral_constant<int, 0>{});
+  barrier_after_loads(Keep{});
+  // One iteration, for chunk c in buffer `buf` (a compile-time constant).
+  auto step = [&](int c, auto buf) __attribute__((always_inline)) {
+    constexpr int b = decltype(buf)::value;
+    issue(c + NBUF - 1, std::integral_constant<int, (b + NBUF - 1) % NBUF>{}, ids);
+    chunk_ids(c + NBUF, ids);  // for the next iteration
+    if (c < nc && CT * c <= p_wave) {  // a chunk of this split that some row of the wave sees (wave-uniform)
+      f32x4_t sc[T][NSUB];
+      float gm[T], p[T][NSUB][4];
+      qk(buf, sc);
+      mask_max(c, sc, gm);
+      update(gm);
+      probs(sc, p);
+      pv(buf, p, c);
     }
-    // Chunk c + kLead into its buffer (whose last readers passed the previous
-    // barrier), then the loads of chunk c + kLead + 1.
-    put(c + kLead, buf_add(b_cur, kLead));
-    b_cur = buf_add(b_cur, 1);
-    stage(c + kLead + 1, ids);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0070 | Keep::value);
+    fix_tail(c + 1, std::integral_constant<int, (b + 1) % NBUF>{});
+    barrier_after_loads(Keep{});
+  };
+  // Whole rounds of NBUF steps: a step past the last chunk loads zeros and
+  // computes nothing, and the steps need no branch between them (which keeps
+  // the compiler's tracking of the loads in flight per buffer exact).
+  for (int c = c_begin; c < nc; c += NBUF) {
+    step(c, std::integral_constant<int, 0>{});
+    step(c + 1, std::integral_constant<int, 1>{});
+    if constexpr (NBUF == 3) step(c + 2, std::integral_constant<int, 2>{});
   }
   if (__ballot(poison) != 0 && lane == 0) poison_any = 1;
   __syncthreads();
