@@ -473,12 +473,21 @@ pkv_status pkv_decode_step_static(const void* k_new, const void* v_new, float* o
  * Supported shapes and dtypes as for decode.  Arithmetic: fp32 accumulation,
  * products on the matrix cores; bf16 probabilities enter the value product as
  * two bf16 terms.  Allocates nothing.
+ * Paths: runs of at most 16 / G queries (max_query_len * H_q / H_kv <= 16;
+ * speculative verification) with at most 4096 sequences go to the decode
+ * kernel's listed pass, the queries of a run as further matrix-core columns of
+ * one persistent, cost-balanced pass over 512-token partitions; that path
+ * needs the workspace when a context exceeds 512 tokens, and without one the
+ * call uses the runs kernel, unsplit.  Other batches use the runs kernel.  The
+ * environment variable PKV_MULTI_PATH set to "runs" (read at each call) keeps
+ * every batch on the runs kernel.  Both paths meet the same contract and
+ * tolerances; their rows differ in rounding.
  * Tuning: where a pair has more than 64 rows, a workgroup serves 128 rows
  * (two row tiles per wave) when the batch's rows fill the GPU, else 64; the
  * environment variable PKV_MULTI_TILES set to "1" or "2" (read at each call)
  * forces the choice.  Both give the same rows.
- * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (too small or misaligned when a
- * split is planned), HIP. */
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE (given but smaller than
+ * pkv_attention_multi_workspace_bytes for these sizes, or misaligned), HIP. */
 pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* block_tables, const int32_t* context_lens,
                                      const int32_t* query_start, const int32_t* seq_order, int32_t num_seqs,
@@ -489,12 +498,14 @@ pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_ca
                                      size_t workspace_bytes, int32_t kv_dtype, hipStream_t stream);
 
 /* Bytes of workspace pkv_paged_attention_multi uses to split long contexts (0
- * when it would not split them).  A context is split when every run's rows
- * (max_query_len * H_q / H_kv) fit one 64-row block and the batch has too few
- * (sequence, KV head) pairs to fill the GPU: each pair's context is cut into
- * splits of at least 256 tokens, computed apart and combined with log-sum-exp
- * weights (speculative verification over long contexts).  With no workspace
- * the call does not split. */
+ * when it would not split them): the larger of the two paths' needs.  The
+ * decode kernel's path (short runs, see there) cuts contexts into 512-token
+ * partitions and between workgroups, with records per workgroup.  On the runs
+ * kernel a context is split when every run's rows (max_query_len * H_q / H_kv)
+ * fit one 64-row block and the batch has too few (sequence, KV head) pairs to
+ * fill the GPU: each pair's context is cut into splits of at least 256 tokens,
+ * computed apart and combined with log-sum-exp weights.  With no workspace the
+ * call does not split. */
 size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t max_context_len, int32_t max_query_len);
 

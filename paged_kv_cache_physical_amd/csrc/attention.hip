@@ -84,6 +84,13 @@ struct AttnArgs {
   int32_t max_parts;
   int32_t total_items;     // max_parts * num_seqs * num_kv_heads
   float c;                 // scale * log2(e): the softmax runs on u = c * (q . k) in the exp2 domain
+  // Runs of queries (kernels with QR > 1 queries per item): sequence s owns the
+  // query rows query_start[s] .. query_start[s + 1] - 1 of q and out, which are
+  // [num_query_rows][num_q_heads][d]; decode (QR = 1) has one row per sequence.
+  const int32_t* query_start;
+  int32_t num_q_heads;
+  int32_t num_query_rows;
+  int32_t max_query_len;
 };
 
 // Hand-over of a record between workgroups of one launch, with no contract on
@@ -153,6 +160,42 @@ __device__ __forceinline__ int32_t ld_const(const int32_t* p, size_t i) {
   return ((const_i32_ptr)p)[i];
 }
 
+// A sequence's query rows (its run): rows q0 .. q0 + nq - 1 of q and out, at
+// positions n - nq .. n - 1 of its context.  Decode: the sequence's own row.
+// A run can also be (as the runs kernel takes it): outside the rows (nothing
+// is written), or impossible (longer than its context or than the batch's
+// longest run: NaN rows, at most max_query_len of them).
+struct RunRows {
+  int q0, nq;
+  bool bad;
+};
+template <int QR>
+__device__ __forceinline__ RunRows run_rows(const AttnArgs& a, int s, int n) {
+  if constexpr (QR == 1) {
+    return RunRows{s, 1, false};
+  } else {
+    const int q0 = ld_const(a.query_start, s);
+    const int qs = ld_const(a.query_start, s + 1) - q0;
+    const bool rows = q0 >= 0 && qs > 0 && static_cast<int64_t>(q0) + qs <= a.num_query_rows;
+    return RunRows{q0, rows ? min(qs, a.max_query_len) : 0, rows && (qs > n || qs > a.max_query_len)};
+  }
+}
+// Partitions of sequence s (1 when it has no tokens to read: *special), with
+// *bad for NaN rows.
+template <int QR>
+__device__ __forceinline__ int seq_state(const AttnArgs& a, int s, int n, bool* special, bool* bad) {
+  const int np = seq_parts(a, n, bad);
+  if constexpr (QR == 1) {
+    *special = *bad || n == 0;
+    return np;
+  } else {
+    const RunRows r = run_rows<QR>(a, s, n);
+    *bad = r.nq > 0 && (*bad || r.bad);
+    *special = *bad || n == 0 || r.nq == 0;
+    return *special ? 1 : np;
+  }
+}
+
 // voff: the lane's offset; soff: a wave-uniform offset added to it.  A load
 // stays inside its tile, and a size-0 resource rejects every load, so the
 // result does not depend on whether the range check includes soff.
@@ -199,19 +242,24 @@ struct Item {
   int nk;     // groups of this wave
   int npad;   // ring positions of this wave: nk rounded up to NBUF, at least NBUF
   int flags;  // kDirect | kSplitSeq | kSpecial | kBad
+  int n;      // the sequence's length
+  int q0, nq; // its query rows (see run_rows)
 };
 constexpr int kDirect = 1;    // the segment covers the whole sequence: write the output rows
 constexpr int kSplitSeq = 2;  // the sequence has several partitions
 constexpr int kSpecial = 4;   // empty or invalid sequence: no groups, fill the rows
 constexpr int kBad = 8;       // invalid length: fill with NaN
 
-template <int G, int D, bool LIST>
+// C: matrix-core columns in use, a (query, head) pair each (decode: the G
+// heads).  Up to 8 columns the items alternate between two merge buffers (one
+// barrier per item); 16 columns take one buffer and a second barrier.
+template <int C, int D, bool LIST>
 struct Shared {
   struct Merge {
-    alignas(16) float region[kWaves][G][D + 4];  // per-wave partial output (padded rows)
-    float wm[kWaves][G];                         // per-wave running maximum (exp2 domain, scaled)
-    float wl[kWaves][G];                         // per-wave sum of probabilities
-  } mb[2];  // alternate items use alternate buffers: one barrier per item
+    alignas(16) float region[kWaves][C][D + 4];  // per-wave partial output (padded rows)
+    float wm[kWaves][C];                         // per-wave running maximum (exp2 domain, scaled)
+    float wl[kWaves][C];                         // per-wave sum of probabilities
+  } mb[C > 8 ? 1 : 2];
   uint32_t csum[LIST ? kMaxListedSeqs + 1 : 1];  // prefix sums of sequence costs
   int chain_first;  // combine: the first run holding a segment of the owner's sequence
   int chain_ok;     // combine: every segment arrived and belongs to the sequence
@@ -228,24 +276,29 @@ constexpr int kItemCharge = 2;
 // summed in that order (an empty segment has m = -inf and weighs nothing).
 // Explicit fmaf keeps the rounding identical wherever this is inlined, so the
 // fused and the two-stage paths give the same bits.  ok == false: NaN rows.
-template <int G, int D>
+// Column h of a record is query h / G of the run, head h % G of the KV head.
+template <int G, int QR, int D>
 __device__ __forceinline__ void combine_runs(const AttnArgs& a, int seq, int kvh, int first, int last, bool ok,
                                              int tid) {
+  constexpr int C = QR * G;
   constexpr int NC = D / 4;  // float4 chunks of one head's row
-  constexpr int ITERS = (G * NC + kThreads - 1) / kThreads;
+  constexpr int ITERS = (C * NC + kThreads - 1) / kThreads;
   const int Hkv = a.num_kv_heads;
-  float* out = a.out + (static_cast<size_t>(seq) * Hkv + kvh) * G * D;
+  const RunRows run = run_rows<QR>(a, seq, 0);
+  const int Hq = Hkv * G;
+  float* out = a.out + (static_cast<size_t>(run.q0) * Hq + static_cast<size_t>(kvh) * G) * D;
   auto rec_of = [&](int L) __attribute__((always_inline)) { return 2 * (L * Hkv + kvh) + (L == last ? 0 : 1); };
-  // the launch's records: 2 per workgroup (at most 2 * 2048 * 8 * 128 * 4 bytes of sums)
+  // the launch's records: 2 per workgroup (at most 2 * 2048 * 16 * 128 * 4 bytes of sums)
   const int recs = 2 * static_cast<int>(gridDim.x);
-  const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(a.ws_acc, recs * G * D * 4);
-  const __amdgpu_buffer_rsrc_t r_m = make_rsrc(a.ws_m, recs * G * 4);
-  const __amdgpu_buffer_rsrc_t r_l = make_rsrc(a.ws_l, recs * G * 4);
+  const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(a.ws_acc, recs * C * D * 4);
+  const __amdgpu_buffer_rsrc_t r_m = make_rsrc(a.ws_m, recs * C * 4);
+  const __amdgpu_buffer_rsrc_t r_l = make_rsrc(a.ws_l, recs * C * 4);
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int cidx = tid + it * kThreads;
-    if (cidx >= G * NC) break;
+    if (cidx >= C * NC) break;
     const int h = cidx / NC, d4 = (cidx % NC) * 4;
+    if (h / G >= run.nq) break;  // columns past the run's queries (cidx grows with h)
     f32x4_t o = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     if (ok) {
       // Records in groups of kGroup whose loads are all in flight at once (a
@@ -258,7 +311,7 @@ __device__ __forceinline__ void combine_runs(const AttnArgs& a, int seq, int kvh
       auto load_group = [&](int L0, bool sums) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) {
-          const int r = rec_of(L0 + j) * G + h;
+          const int r = rec_of(L0 + j) * C + h;
           const bool in = L0 + j <= last;
           mv[j] = load_dev(r_m, in ? r * 4 : kNowhere);
           if (sums) {
@@ -299,7 +352,7 @@ __device__ __forceinline__ void combine_runs(const AttnArgs& a, int seq, int kvh
       }
       o = f32x4_t{sa.x / sl, sa.y / sl, sa.z / sl, sa.w / sl};
     }
-    *reinterpret_cast<f32x4_t*>(out + h * D + d4) = o;
+    *reinterpret_cast<f32x4_t*>(out + (static_cast<size_t>(h / G) * Hq + h % G) * D + d4) = o;
   }
 }
 
@@ -323,14 +376,20 @@ __device__ __forceinline__ void combine_runs(const AttnArgs& a, int seq, int kvh
 // without it, list_reduce_kernel does the same work as a second launch.  An
 // owner waits only for runs of lower index, which never wait on it, and it
 // waits after its own work is done, so every run's work proceeds.
-template <class DT, int D, int G, int B, bool LIST, bool WRITE, bool FUSED>
+// QR > 1 (runs of queries, LIST and FUSED only): each item carries up to QR
+// queries of its sequence (its last positions), C = QR G columns of the
+// matrix-core tiles, column h being query h / G and head h % G; query i of a
+// run of nq sees the tokens up to position n - nq + i.
+template <class DT, int D, int G, int B, bool LIST, bool WRITE, bool FUSED, int QR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_decode_kernel(AttnArgs a) {
   using Gm = Geo<DT, D, B>;
   constexpr int GT = Gm::GT, NT = Gm::NT, KS = Gm::KS, NDT = Gm::NDT, VW = Gm::VW, NQ = Gm::NQ;
   constexpr int NBUF = Gm::NBUF, R = Gm::R, TILE = Gm::TILE;
   constexpr bool kBF16 = Gm::kBF16;
-  __shared__ Shared<G, D, LIST> sh;
+  constexpr int NCOL = QR * G;  // columns in use
+  static_assert(NCOL <= 16 && (QR == 1 || (LIST && FUSED && !WRITE)), "runs: 16 columns, listed and fused");
+  __shared__ Shared<NCOL, D, LIST> sh;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = uni(tid / kWave);
@@ -346,10 +405,10 @@ void paged_decode_kernel(AttnArgs a) {
   const int lane_b = static_cast<int>(blockIdx.x) / Hkv;
   if constexpr (LIST) {
     for (int s = tid; s < S; s += kThreads) {
-      bool bad;
+      bool bad, special;
       const int n = ld_const(a.context_lens, s);
-      const int np = seq_parts(a, n, &bad);
-      const int last = (bad || n == 0) ? 0 : n - (np - 1) * P;  // tokens of the last partition
+      const int np = seq_state<QR>(a, s, n, &special, &bad);
+      const int last = special ? 0 : n - (np - 1) * P;  // tokens of the last partition
       sh.csum[s + 1] = static_cast<uint32_t>(np - 1) * full_cost + (last + GT - 1) / GT + kItemCharge;
     }
     __syncthreads();
@@ -389,10 +448,10 @@ void paged_decode_kernel(AttnArgs a) {
   auto cut_in = [&](int lo, uint64_t T, uint64_t base) __attribute__((always_inline)) {
     Cut c{S, 0};
     const int n = ld_const(a.context_lens, lo);
-    bool bad;
-    const int np = seq_parts(a, n, &bad);
+    bool bad, special;
+    const int np = seq_state<QR>(a, lo, n, &special, &bad);
     const uint64_t rel = T - base;
-    if (bad || n == 0) {  // no tokens: the sequence starts the run that holds its first cost unit
+    if (special) {  // no tokens: the sequence starts the run that holds its first cost unit
       c.seq = rel == 0 ? lo : lo + 1;
       return c;
     }
@@ -473,11 +532,12 @@ void paged_decode_kernel(AttnArgs a) {
     it.kvh = kvh_b;
     int n, nparts;
     bool bad;
+    bool special;
     if constexpr (LIST) {
       it.seq = k;
       it.next = k - 1;  // a run is walked backwards, see below
       n = ld_const(a.context_lens, it.seq);
-      nparts = seq_parts(a, n, &bad);
+      nparts = seq_state<QR>(a, it.seq, n, &special, &bad);
       it.tok_begin = k == run_begin.seq ? run_begin.tok : 0;
       it.tok_end = k == run_end.seq ? run_end.tok : n;
     } else {
@@ -487,10 +547,16 @@ void paged_decode_kernel(AttnArgs a) {
       it.next = seek(k + grid);
       n = ld_const(a.context_lens, it.seq);
       nparts = seq_parts(a, n, &bad);
+      special = bad || n == 0;
       it.tok_begin = part * P;
       it.tok_end = min(n, it.tok_begin + P);
     }
-    const bool special = bad || n == 0;
+    {
+      const RunRows run = run_rows<QR>(a, it.seq, n);
+      it.n = n;
+      it.q0 = run.q0;
+      it.nq = run.nq;
+    }
     if (special) {
       it.tok_begin = 0;
       it.tok_end = 0;
@@ -531,15 +597,15 @@ void paged_decode_kernel(AttnArgs a) {
       // No tokens, inside a sequence: an empty segment (m = -inf, l = 0, acc = 0) keeps the runs between the
       // sequence's first and its owner a contiguous chain of records.
       const int rec = 2 * static_cast<int>(blockIdx.x) + 1;
-      const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(a.ws_acc + static_cast<size_t>(rec) * G * D, G * D * 4);
-      for (int i = tid; i < G * D / 4; i += kThreads)
+      const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(a.ws_acc + static_cast<size_t>(rec) * NCOL * D, NCOL * D * 4);
+      for (int i = tid; i < NCOL * D / 4; i += kThreads)
         __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, r_acc, 16 * i, 0, kScopeDevice);
-      const __amdgpu_buffer_rsrc_t r_m = make_rsrc(a.ws_m + static_cast<size_t>(rec) * G, G * 4);
-      const __amdgpu_buffer_rsrc_t r_l = make_rsrc(a.ws_l + static_cast<size_t>(rec) * G, G * 4);
+      const __amdgpu_buffer_rsrc_t r_m = make_rsrc(a.ws_m + static_cast<size_t>(rec) * NCOL, NCOL * 4);
+      const __amdgpu_buffer_rsrc_t r_l = make_rsrc(a.ws_l + static_cast<size_t>(rec) * NCOL, NCOL * 4);
       const __amdgpu_buffer_rsrc_t r_hdr = make_rsrc(a.ws_hdr + 4 * static_cast<size_t>(rec), 16);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), r_m, tid < G ? 4 * tid : kNowhere, 0,
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), r_m, tid < NCOL ? 4 * tid : kNowhere, 0,
                                             kScopeDevice);
-      __builtin_amdgcn_raw_buffer_store_b32(0u, r_l, tid < G ? 4 * tid : kNowhere, 0, kScopeDevice);
+      __builtin_amdgcn_raw_buffer_store_b32(0u, r_l, tid < NCOL ? 4 * tid : kNowhere, 0, kScopeDevice);
       const u32x4_t hdr = {static_cast<uint32_t>(run_end.seq), static_cast<uint32_t>(run_end.tok),
                            static_cast<uint32_t>(run_end.tok), 0u};
       __builtin_amdgcn_raw_buffer_store_b128(hdr, r_hdr, tid == 0 ? 0 : kNowhere, 0, kScopeDevice);
@@ -591,14 +657,19 @@ void paged_decode_kernel(AttnArgs a) {
   const char* vcache = static_cast<const char*>(a.v_cache);
 
   // Query rows of the item's KV head as the QK B operand: lane (m16, kq) holds
-  // bytes [64 s + 16 kq, +16) of head m16 (zeros for heads >= G).
+  // bytes [64 s + 16 kq, +16) of column m16, that is head m16 % G of query
+  // m16 / G of the run (zeros for columns past the run's).
   auto load_query = [&](uint4 (&q)[NQ], const Item& it) __attribute__((always_inline)) {
-    const char* base =
-        static_cast<const char*>(a.q) + (static_cast<size_t>(it.seq) * Hkv * G + static_cast<size_t>(it.kvh) * G) * R;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(base, G * R);
+    const char* base = static_cast<const char*>(a.q) +
+                       (static_cast<size_t>(it.q0) * Hkv * G + static_cast<size_t>(it.kvh) * G) * R;
+    // the run's rows from its first query's head 0 of this KV head on
+    const int span = QR == 1 ? G * R : ((it.nq - 1) * Hkv * G + G) * R;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(base, it.nq > 0 ? span : 0);
+    const int row = QR == 1 ? m16 : (m16 / G) * Hkv * G + m16 % G;
+    const int off = m16 < it.nq * G ? row * R + 16 * kq : kNowhere;
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
-      q[s] = bload16<0>(rq, m16 * R + 16 * kq, 64 * s);
+      q[s] = bload16<0>(rq, off, 64 * s);
     }
   };
 
@@ -771,7 +842,20 @@ void paged_decode_kernel(AttnArgs a) {
                   if (4 * kq + w >= rel) vb[s][dt][w] = 0u;
             }
           }
-          // Online softmax, per head (lane column m16).
+          if constexpr (QR > 1) {
+            // Runs: query m16 / G, at position n - nq + m16 / G, sees the tokens up to
+            // its position; only the run's last nq - 1 tokens are hidden from some.
+            const int first_hidden = cur.n - cur.nq + 1;  // the first token hidden from query 0
+            if (t_first + GT > first_hidden) {
+              const int lim = first_hidden - 1 + m16 / G - t_first;  // the column's last visible token, in the group
+#pragma unroll
+              for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (16 * t + 4 * kq + r > lim) sc[t][r] = -INFINITY;
+            }
+          }
+          // Online softmax, per column (lane column m16).
           float gm = -INFINITY;
 #pragma unroll
           for (int t = 0; t < NT; ++t) gm = fmaxf(gm, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
@@ -784,11 +868,14 @@ void paged_decode_kernel(AttnArgs a) {
             l_run *= alpha;
             m_run = m_new;
           }
+          // (runs: a column that has seen no token yet, its tokens all after its
+          // query, keeps m = -inf and gets weights exp2(-inf - 0) = 0)
+          const float m_use = (QR > 1 && m_run == -INFINITY) ? 0.0f : m_run;
 #pragma unroll
           for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              sc[t][r] = __builtin_amdgcn_exp2f(sc[t][r] - m_run);
+              sc[t][r] = __builtin_amdgcn_exp2f(sc[t][r] - m_use);
               l_run += sc[t][r];
             }
 
@@ -863,8 +950,10 @@ void paged_decode_kernel(AttnArgs a) {
     // buffers alternate between items, so the next item's barrier is what
     // orders the reuse of this one.
     const float l_tot = sum_xor32(sum_xor16(l_run));  // over the four token rows of each head
-    auto& mb = sh.mb[parity];
-    if (m16 < G) {
+    auto& mb = sh.mb[NCOL > 8 ? 0 : parity];
+    // columns in use: decode, the G heads; runs, those of the run's queries
+    const int ncol = QR == 1 ? G : cur.nq * G;
+    if (m16 < ncol) {
       float* reg = &mb.region[wave][m16][0];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -889,17 +978,20 @@ void paged_decode_kernel(AttnArgs a) {
       // reduction); any other segment writes its partials at its first
       // partition, with its length.
       const bool direct = cur.flags & kDirect;
-      const size_t head0 = static_cast<size_t>(cur.seq) * Hkv * G + static_cast<size_t>(cur.kvh) * G;
+      // the item's output rows: decode, the G heads of its KV head; runs, those
+      // of each query of the run, Hq rows apart
+      const size_t head0 = static_cast<size_t>(cur.q0) * Hkv * G + static_cast<size_t>(cur.kvh) * G;
+      const int out_rows = QR == 1 ? G : (cur.nq > 0 ? (cur.nq - 1) * Hkv * G + G : 0);
       // The partials' slot: LIST, record 0 of an owner's first item or record 1
       // of a run's last item; otherwise the segment's partition slot.
       const int rec = 2 * static_cast<int>(blockIdx.x) + ((owner && cur.k == k_first) ? 0 : 1);
       const size_t prow =
           LIST ? static_cast<size_t>(rec) : (static_cast<size_t>(cur.seq) * Hkv + cur.kvh) * a.max_parts + cur.part;
       const bool split = split_ws;
-      const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + head0 * D, direct ? G * D * 4 : 0);
-      const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(split ? a.ws_acc + prow * G * D : a.out, direct ? 0 : G * D * 4);
-      const __amdgpu_buffer_rsrc_t r_m = make_rsrc(split ? a.ws_m + prow * G : a.out, direct ? 0 : G * 4);
-      const __amdgpu_buffer_rsrc_t r_l = make_rsrc(split ? a.ws_l + prow * G : a.out, direct ? 0 : G * 4);
+      const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + head0 * D, direct ? out_rows * D * 4 : 0);
+      const __amdgpu_buffer_rsrc_t r_acc = make_rsrc(split ? a.ws_acc + prow * NCOL * D : a.out, direct ? 0 : NCOL * D * 4);
+      const __amdgpu_buffer_rsrc_t r_m = make_rsrc(split ? a.ws_m + prow * NCOL : a.out, direct ? 0 : NCOL * 4);
+      const __amdgpu_buffer_rsrc_t r_l = make_rsrc(split ? a.ws_l + prow * NCOL : a.out, direct ? 0 : NCOL * 4);
       if constexpr (LIST) {
         const __amdgpu_buffer_rsrc_t r_hdr =
             make_rsrc(split ? static_cast<const void*>(a.ws_hdr + 4 * prow) : static_cast<const void*>(a.out),
@@ -914,13 +1006,13 @@ void paged_decode_kernel(AttnArgs a) {
         __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(direct ? -1 : cur.part_next), r_seg,
                                               tid == 0 ? 0 : kNowhere, 0, 0);
       }
-      constexpr int NC = D / 4;  // float4 chunks of one head's row
-      constexpr int ITERS = (G * NC + kThreads - 1) / kThreads;
+      constexpr int NC = D / 4;  // float4 chunks of one column's row
+      constexpr int ITERS = (NCOL * NC + kThreads - 1) / kThreads;
       const float fill = (cur.flags & kBad) ? __builtin_nanf("") : 0.0f;
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
         const int cidx = tid + it * kThreads;
-        const bool live = cidx < G * NC;
+        const bool live = cidx < ncol * NC;  // columns past those in use store nothing
         const int h = live ? cidx / NC : 0, d4 = live ? (cidx % NC) * 4 : 0;
         float M = -INFINITY;
 #pragma unroll
@@ -929,14 +1021,16 @@ void paged_decode_kernel(AttnArgs a) {
         float sl = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float wt = __builtin_amdgcn_exp2f(mb.wm[w][h] - M);  // 0 for a wave that saw no token
+          // 0 for a wave that saw no token (runs: also when no wave saw one, M = -inf)
+          const float wt = (QR > 1 && M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mb.wm[w][h] - M);
           sa += wt * *reinterpret_cast<const f32x4_t*>(&mb.region[w][h][d4]);
           sl = fmaf(wt, mb.wl[w][h], sl);
         }
         const f32x4_t o = (cur.flags & kSpecial) ? f32x4_t{fill, fill, fill, fill} : sa / sl;
         const int voff = live ? (h * D + d4) * 4 : kNowhere;
         const int soff = live && d4 == 0 ? h * 4 : kNowhere;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), r_out, voff, 0, 0);
+        const int ooff = QR == 1 ? voff : live && h / G < cur.nq ? (((h / G) * Hkv * G + h % G) * D + d4) * 4 : kNowhere;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), r_out, ooff, 0, 0);
         // item-list records are read by another workgroup, maybe on another XCD: device scope
         constexpr int kRecAux = LIST ? kScopeDevice : 0;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sa), r_acc, voff, 0, kRecAux | kLoadNT);
@@ -947,6 +1041,7 @@ void paged_decode_kernel(AttnArgs a) {
       if constexpr (LIST && FUSED)
         if (!direct && (rec & 1)) publish(rec);
     }
+    if constexpr (NCOL > 8) __syncthreads();  // one merge buffer: every thread has read it before the next item writes
     parity ^= 1;
 
     if (!has_next) break;
@@ -1029,7 +1124,7 @@ void paged_decode_kernel(AttnArgs a) {
         }
       }
       __syncthreads();
-      combine_runs<G, D>(a, seq, kvh_b, sh.chain_first, lane_b, sh.chain_ok != 0, tid);
+      combine_runs<G, QR, D>(a, seq, kvh_b, sh.chain_first, lane_b, sh.chain_ok != 0, tid);
     }
   }
 }
@@ -1063,7 +1158,7 @@ __global__ __launch_bounds__(kThreads) void list_reduce_kernel(AttnArgs a) {
     ok_sh = ok && first >= 0;
   }
   __syncthreads();
-  combine_runs<G, D>(a, mark.x, kvh, first_sh, lane_b, ok_sh != 0, threadIdx.x);
+  combine_runs<G, 1, D>(a, mark.x, kvh, first_sh, lane_b, ok_sh != 0, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1132,8 +1227,9 @@ struct Plan {
   size_t off_m, off_l, off_seg, off_hdr, off_tag, bytes;
 };
 
+// cols: matrix-core columns per item (decode G; runs of queries 16).
 Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-               int32_t max_context_len, int32_t partition_size) {
+               int32_t max_context_len, int32_t partition_size, int32_t cols = 0) {
   Plan p{};
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
   p.P = partition_size > 0 ? partition_size : static_cast<int32_t>(ceil_div64(ctx, block_size) * block_size);
@@ -1144,7 +1240,7 @@ Plan make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int3
   p.grid_cap = static_cast<int32_t>(want >= num_kv_heads ? want / num_kv_heads * num_kv_heads : num_kv_heads);
   if (p.max_parts <= 1 || num_seqs <= 0) return p;
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  const size_t G = static_cast<size_t>(num_q_heads / num_kv_heads);
+  const size_t G = static_cast<size_t>(cols > 0 ? cols : num_q_heads / num_kv_heads);
   if (p.list) {
     const size_t recs = 2 * static_cast<size_t>(p.grid_cap);
     p.off_m = up(recs * G * head_dim * sizeof(float));
@@ -1186,10 +1282,10 @@ int resident_workgroups() {
 // and the workgroups of all heads of one partition run side by side, reading
 // adjacent tiles of the same blocks (and, for shared prefixes, the same
 // blocks).
-template <class DT, int D, int G, int B, bool LIST, bool WRITE, bool FUSED>
+template <class DT, int D, int G, int B, bool LIST, bool WRITE, bool FUSED, int QR = 1>
 int grid_for(const AttnArgs& a) {
   using K = void (*)(AttnArgs);
-  constexpr K kernel = paged_decode_kernel<DT, D, G, B, LIST, WRITE, FUSED>;
+  constexpr K kernel = paged_decode_kernel<DT, D, G, B, LIST, WRITE, FUSED, QR>;
   const int fill = resident_workgroups<K, kernel>();
   if (fill <= 0) return 0;
   int want = a.total_items < fill ? a.total_items : fill;
@@ -1197,11 +1293,11 @@ int grid_for(const AttnArgs& a) {
   return want >= a.num_kv_heads ? want / a.num_kv_heads * a.num_kv_heads : a.num_kv_heads;
 }
 
-template <class DT, int D, int G, int B, bool LIST, bool WRITE, bool FUSED>
+template <class DT, int D, int G, int B, bool LIST, bool WRITE, bool FUSED, int QR = 1>
 hipError_t launch_kernel(const AttnArgs& a, hipStream_t stream) {
-  const int grid = grid_for<DT, D, G, B, LIST, WRITE, FUSED>(a);
+  const int grid = grid_for<DT, D, G, B, LIST, WRITE, FUSED, QR>(a);
   if (grid <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, B, LIST, WRITE, FUSED>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((paged_decode_kernel<DT, D, G, B, LIST, WRITE, FUSED, QR>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -1251,6 +1347,29 @@ template <class DT>
 hipError_t launch_op(const AttnArgs& a, int D, int G, bool list, Op op, hipStream_t stream) {
   if (D == 64) return launch_op_d<DT, 64>(a, G, list, op, stream);
   if (D == 128) return launch_op_d<DT, 128>(a, G, list, op, stream);
+  return hipErrorInvalidValue;
+}
+
+// Runs of queries: the listed, fused kernel with 16 / G queries per item.
+template <class DT, int D, int G>
+hipError_t launch_runs_g(const AttnArgs& a, hipStream_t stream) {
+  return a.block_size == 16 ? launch_kernel<DT, D, G, 16, true, false, true, 16 / G>(a, stream)
+                            : launch_kernel<DT, D, G, 32, true, false, true, 16 / G>(a, stream);
+}
+template <class DT, int D>
+hipError_t launch_runs_d(const AttnArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_runs_g<DT, D, 1>(a, stream);
+    case 2: return launch_runs_g<DT, D, 2>(a, stream);
+    case 4: return launch_runs_g<DT, D, 4>(a, stream);
+    case 8: return launch_runs_g<DT, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <class DT>
+hipError_t launch_runs(const AttnArgs& a, int D, int G, hipStream_t stream) {
+  if (D == 64) return launch_runs_d<DT, 64>(a, G, stream);
+  if (D == 128) return launch_runs_d<DT, 128>(a, G, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1316,6 +1435,10 @@ pkv_status attention_stages(int stages, const void* k_new, const void* v_new, fl
   // Softmax of scale * (q . k), run in the exp2 domain (any sign of scale; a
   // zero scale gives equal weights).
   a.c = scale * 1.4426950408889634f;
+  a.query_start = nullptr;  // decode: one query row per sequence
+  a.num_q_heads = num_q_heads;
+  a.num_query_rows = num_seqs;
+  a.max_query_len = 1;
 
   auto run = [&](Op op) {
     return kv_dtype == PKV_BF16 ? launch_op<BF16>(a, head_dim, G, plan.list, op, stream)
@@ -1381,6 +1504,83 @@ void* scratch_address() {
 }
 
 }  // namespace
+
+// Runs of at most 16 / G queries per sequence (the verification of drafted
+// tokens) on the decode kernel: its persistent, cost-balanced item list with
+// the queries of a run as further matrix-core columns.  The partition size is
+// 512 tokens.  Arguments as pkv_paged_attention_multi takes them, already
+// checked; PKV_ERR_UNSUPPORTED when the batch does not fit this path (too
+// many sequences, runs too long, or no workspace where the split needs one),
+// and the caller then uses the runs kernel; PKV_ERR_WORKSPACE for a workspace
+// too small.
+constexpr int32_t kRunsPartition = 512;
+
+bool runs_listed_fits(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t max_context_len, int32_t max_query_len) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return false;
+  const int G = num_q_heads / num_kv_heads;
+  if (max_query_len < 1 || static_cast<int64_t>(max_query_len) * G > 16) return false;
+  const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, 16, max_context_len, kRunsPartition, 16);
+  // the output offsets of one run stay within 32 bits
+  return plan.list && static_cast<int64_t>(max_query_len) * num_q_heads * head_dim * 4 < (int64_t{1} << 31);
+}
+
+size_t runs_listed_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t max_query_len) {
+  if (!runs_listed_fits(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len)) return 0;
+  return make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, 16, max_context_len, kRunsPartition, 16).bytes;
+}
+
+pkv_status runs_listed(float* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+                       int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks, int32_t max_context_len,
+                       int32_t max_query_len, float scale, void* workspace, size_t workspace_bytes, int32_t kv_dtype,
+                       hipStream_t stream) {
+  if (!runs_listed_fits(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len))
+    return PKV_ERR_UNSUPPORTED;
+  const int G = num_q_heads / num_kv_heads;
+  const Plan plan =
+      make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kRunsPartition, 16);
+  const int64_t items = static_cast<int64_t>(plan.max_parts) * num_seqs * num_kv_heads;
+  if (items > INT32_MAX / 2) return PKV_ERR_UNSUPPORTED;
+  AttnArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  if (plan.max_parts > 1) {
+    // no workspace: the caller takes the runs kernel, which needs none; one too small is an error
+    if (!workspace) return PKV_ERR_UNSUPPORTED;
+    if (workspace_bytes < plan.bytes || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    a.ws_acc = reinterpret_cast<float*>(ws);
+    a.ws_m = reinterpret_cast<float*>(ws + plan.off_m);
+    a.ws_l = reinterpret_cast<float*>(ws + plan.off_l);
+    a.ws_hdr = reinterpret_cast<int32_t*>(ws + plan.off_hdr);
+    a.ws_tag = reinterpret_cast<uint64_t*>(ws + plan.off_tag);
+  }
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks;
+  a.max_context_len = max_context_len;
+  a.partition_size = plan.P;
+  a.max_parts = plan.max_parts;
+  a.total_items = static_cast<int32_t>(items);
+  a.c = scale * 1.4426950408889634f;
+  a.query_start = query_start;
+  a.num_q_heads = num_q_heads;
+  a.num_query_rows = num_query_rows;
+  a.max_query_len = max_query_len;
+  const hipError_t err = kv_dtype == PKV_BF16 ? launch_runs<BF16>(a, head_dim, G, stream)
+                                              : launch_runs<F32>(a, head_dim, G, stream);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 }  // namespace pkv
 
 using namespace pkv;

@@ -34,6 +34,7 @@
 // then merges the split partials with log-sum-exp weights.
 
 #include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <type_traits>
 
@@ -778,6 +779,9 @@ hipError_t launch_multi(const MultiArgs& a, int D, int G, int T, dim3 grid, dim3
 
 using namespace pkv;
 
+extern "C" size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                      int32_t head_dim, int32_t max_context_len, int32_t max_query_len);
+
 extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_cache, const void* v_cache,
                                                  const int32_t* block_tables, const int32_t* context_lens,
                                                  const int32_t* query_start, const int32_t* seq_order,
@@ -803,6 +807,27 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
+  // A workspace, when given, has at least the advertised size for these sizes (whichever path the call takes).
+  if (workspace) {
+    const size_t need = pkv_attention_multi_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                            max_context_len, max_query_len);
+    if (need > 0 && (workspace_bytes < need || !aligned16(workspace))) return PKV_ERR_WORKSPACE;
+  }
+
+  // Runs of at most 16 / G queries (verification of drafted tokens) go to the
+  // decode kernel's listed path, where the queries of a run are further
+  // matrix-core columns of one persistent, cost-balanced pass (seq_order does
+  // not apply there); PKV_MULTI_PATH=runs (read at each call) keeps them here.
+  {
+    const char* path = std::getenv("PKV_MULTI_PATH");
+    if (!(path && std::strcmp(path, "runs") == 0)) {
+      const pkv_status st = runs_listed(out, q, k_cache, v_cache, block_tables, context_lens, query_start, num_seqs,
+                                        num_query_rows, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                        max_blocks, max_context_len, max_query_len, scale, workspace, workspace_bytes,
+                                        kv_dtype, stream);
+      if (st != PKV_ERR_UNSUPPORTED) return st;
+    }
+  }
 
   // Two row tiles per wave when a pair has more rows than one workgroup of
   // one-tile waves holds, and the batch's rows (num_query_rows * G in all, the
@@ -877,5 +902,9 @@ extern "C" size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t 
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 ||
       max_context_len < 0 || max_query_len < 0)
     return 0;
-  return multi_plan(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim, max_context_len, max_query_len).bytes;
+  const size_t split = multi_plan(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim, max_context_len,
+                                  max_query_len).bytes;
+  const size_t listed =
+      runs_listed_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len);
+  return split > listed ? split : listed;
 }

@@ -537,16 +537,38 @@ def test_duplicate_and_unknown_ids_in_one_append(libpkv):
     same_state(c, o)
 
 
+def listed_runs_bytes(S, Hq, Hkv, d, ctx, mq):
+    """The decode kernel's path for short runs (mq * G <= 16): records of 16 columns for two per workgroup of a
+    grid of at most 2048 (a multiple of H_kv), over 512-token partitions; 0 when no context is cut."""
+    G = Hq // Hkv
+    if mq * G > 16:
+        return 0
+    parts = -(-max(ctx, 1) // 512)
+    if parts <= 1:
+        return 0
+    items = parts * S * Hkv
+    grid = min(items, 2048) // Hkv * Hkv
+    up = lambda x: (x + 255) // 256 * 256
+    recs = 2 * grid
+    return up(recs * 16 * d * 4) + 2 * up(recs * 16 * 4) + up(recs * 16) + up(recs * 16)
+
+
 def test_runs_of_queries_host_checks_and_split_plan(libpkv):
-    """pkv_paged_attention_multi rejects bad arguments before any device work, and the split workspace follows
-    the plan: >= 256-token splits for about 2048 workgroups, at most 64, only when a pair's rows fit 64."""
+    """pkv_paged_attention_multi rejects bad arguments before any device work, and the workspace is the larger of
+    the two paths' needs: the runs kernel's split plan (>= 256-token splits for about 2048 workgroups, at most 64,
+    only when a pair's rows fit 64) and the decode kernel's records for short runs (16 / G queries at most)."""
     L = libpkv
     vp = ctypes.c_void_p
     # (num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len) -> bytes
-    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 32768, 4) == 64 * 32 * 64 * 130 * 4
-    assert pk.pkv_attention_multi_workspace_bytes(3, 8, 2, 64, 600, 5) == 6 * 2 * 64 * 66 * 4
-    assert pk.pkv_attention_multi_workspace_bytes(1, 8, 8, 128, 1 << 20, 1) == 8 * 64 * 64 * 130 * 4  # capped
-    assert pk.pkv_attention_multi_workspace_bytes(64, 32, 32, 128, 2048, 4) == 0  # enough pairs already
+    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 32768, 4) == max(
+        64 * 32 * 64 * 130 * 4, listed_runs_bytes(8, 32, 8, 128, 32768, 4))
+    assert pk.pkv_attention_multi_workspace_bytes(3, 8, 2, 64, 600, 5) == 6 * 2 * 64 * 66 * 4  # 20 columns
+    assert listed_runs_bytes(1, 8, 8, 128, 1 << 20, 1) > 8 * 64 * 64 * 130 * 4
+    assert pk.pkv_attention_multi_workspace_bytes(1, 8, 8, 128, 1 << 20, 1) == listed_runs_bytes(
+        1, 8, 8, 128, 1 << 20, 1)  # the runs kernel's split is capped at 64
+    # enough pairs for the runs kernel; the short runs still cut their 2048-token contexts
+    assert pk.pkv_attention_multi_workspace_bytes(64, 32, 32, 128, 2048, 4) == listed_runs_bytes(
+        64, 32, 32, 128, 2048, 4) > 0
     assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 32768, 17) == 0  # 68 rows: no split
     assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 500, 4) == 0  # too short to split
     assert pk.pkv_attention_multi_workspace_bytes(8, 30, 8, 128, 32768, 4) == 0  # H_q % H_kv != 0

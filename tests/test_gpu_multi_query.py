@@ -429,6 +429,113 @@ def test_repeated_calls_and_graph_replays_are_bitwise_stable():
 
 
 
+LISTED_GRID = [(dt, d, G, B) for dt in ("f32", "bf16") for d in (64, 128) for G in (1, 2, 4, 8) for B in (16, 32)]
+
+
+@pytest.mark.parametrize("dt,d,G,B", LISTED_GRID)
+def test_short_runs_on_the_decode_kernel(dt, d, G, B, monkeypatch):
+    """Runs of at most 16 / G queries with a workspace take the decode kernel's listed path, the queries of a run
+    as further matrix-core columns: every shape against the oracle, over contexts that are cut into 512-token
+    partitions and between workgroups (runs of one query up to 16 / G, contexts from 1 to 3000 tokens), and the
+    same rows from the runs kernel (PKV_MULTI_PATH=runs)."""
+    import paged_kv_cache_physical_amd as pk
+    k = 16 // G
+    rng = wl.rng_for(500 + G * 10 + d + B, 2)
+    lens = [int(x) for x in rng.integers(1, 3000, size=20)] + [1, 2, 513, 3000]
+    runs = [min(n, int(x)) for n, x in zip(lens, rng.integers(1, k + 1, size=len(lens)))]
+    runs[-1] = min(k, lens[-1])
+    Hkv = 2
+    say(f"case {dt} d={d} G={G} B={B}: k={k} runs={runs}")
+    b = Batch(lens, G * Hkv, Hkv, d, B, dt, seed=G + d + B + 7)
+    q = wl.draw_values(wl.rng_for(61, wl.STREAM_Q, G, d), (sum(runs), G * Hkv, d), dt)
+    assert pk.pkv_attention_multi_workspace_bytes(len(lens), G * Hkv, Hkv, d, max(lens), max(runs)) > 0
+    out, t, l, starts = b.multi(runs, q, split=True)
+    ref = b.oracle(q, t, l, starts)
+    check_close(out, ref, dt, "decode kernel")
+    monkeypatch.setenv("PKV_MULTI_PATH", "runs")
+    other, *_ = b.multi(runs, q, split=True)
+    check_close(other, ref, dt, "runs kernel")
+
+
+def test_short_runs_on_the_decode_kernel_edges():
+    """The runs kernel's contract on the decode kernel's path: an empty run writes nothing, a run longer than its
+    context or than max_query_len gives NaN on the rows the call covers and leaves the rest alone, a run outside
+    the rows is left alone, and a bad block id poisons only its own sequence (cut or whole)."""
+    import paged_kv_cache_physical_amd as pk
+    b = Batch([1400, 33, 20, 640, 9, 2100], 8, 2, 64, 16, "f32", seed=13)  # G = 4: up to 4 queries per run
+    t, l = b.tables()
+    runs = [3, 0, 21, 2, 9, 4]
+    T = sum(runs)
+    q = wl.draw_values(wl.rng_for(14, wl.STREAM_Q), (T, 8, 64), "f32")
+    starts = np.concatenate([[0], np.cumsum(runs)]).astype(np.int32)
+    sentinel = torch.full((T, 8, 64), 7.0, dtype=torch.float32, device="cuda")
+    out, *_ = b.multi(runs, q, tables=t, lens=l, query_start=starts, max_query_len=4, out=sentinel, split=True)
+    ref0 = b.oracle(q[:3], t[:1], l[:1], starts[:2])
+    check_close(out[:3], ref0, "f32", "sequence 0")
+    assert np.all(np.isnan(out[3:3 + 4])) and np.all(out[3 + 4:24] == 7.0)  # 21 > max_query_len and > n
+    ref3 = b.oracle(q[24:26], t[3:4], l[3:4], np.array([0, 2], np.int32))
+    check_close(out[24:26], ref3, "f32", "sequence 3")
+    assert np.all(np.isnan(out[26:26 + 4])) and np.all(out[26 + 4:35] == 7.0)  # 9 > max_query_len
+    ref5 = b.oracle(q[35:39], t[5:6], l[5:6], np.array([0, 4], np.int32))
+    check_close(out[35:39], ref5, "f32", "sequence 5")
+    # bad block ids in a long (cut) sequence and a short one; a run outside [0, T) is left alone
+    t2 = t.copy()
+    t2[0, 40] = b.nb + 5
+    t2[3, 1] = b.nb + 6
+    starts2 = np.array([0, 3, 3, 3, 5, T + 4, T + 6], np.int32)
+    runs2 = [3, 0, 0, 2, 1, 2]
+    sentinel.fill_(7.0)
+    out, *_ = b.multi(runs2, q, tables=t2, lens=l, query_start=starts2, max_query_len=4, out=sentinel, split=True)
+    assert np.all(np.isnan(out[:5])) and np.all(out[5:] == 7.0)
+    # a workspace too small for the split is refused before any work
+    assert pk.pkv_attention_multi_workspace_bytes(6, 8, 2, 64, int(l.max()), 4) > 4096
+    with pytest.raises(pk.PkvError):
+        pk.pkv_paged_attention_multi(sentinel, to_dev(q, "f32"), *b.caches, torch.from_numpy(t).cuda(),
+                                     torch.from_numpy(l).cuda(), torch.from_numpy(starts).cuda(), int(l.max()), 4,
+                                     0.125, workspace=torch.empty(4096, dtype=torch.uint8, device="cuda"))
+
+
+def test_short_runs_on_the_decode_kernel_full_size_and_stable():
+    """Verification of 4 drafted tokens at the Llama-7B decode shape through the decode kernel's path: every row
+    against the oracle; repeated calls and graph replays give the same bits."""
+    import paged_kv_cache_physical_amd as pk
+    w = wl.named("llama7b_bf16", seed=0)
+    s = w.spec
+    runs = [4] * w.num_seqs
+    lens = [int(n) for n in w.context_lens]
+    b = Batch(lens, s.num_q_heads, s.num_kv_heads, s.head_dim, s.block_size, s.kv_dtype, seed=0, spare=64)
+    q = wl.draw_values(wl.rng_for(17, wl.STREAM_Q), (sum(runs), s.num_q_heads, s.head_dim), s.kv_dtype)
+    out, t, l, starts = b.multi(runs, q, split=True)
+    check_close(out, b.oracle(q, t, l, starts), s.kv_dtype, f"all {len(runs)} runs")
+    nbytes = pk.pkv_attention_multi_workspace_bytes(len(lens), s.num_q_heads, s.num_kv_heads, s.head_dim,
+                                                   int(l.max()), 4)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    qd = to_dev(q, s.kv_dtype)
+    bt, cl, st = torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(), torch.from_numpy(starts).cuda()
+    o = torch.empty((sum(runs), s.num_q_heads, s.head_dim), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    call = lambda: pk.pkv_paged_attention_multi(o, qd, *b.caches, bt, cl, st, int(l.max()), 4,
+                                                1.0 / np.sqrt(s.head_dim), stream=stream, workspace=ws)
+    with torch.cuda.stream(stream):
+        call()
+        torch.cuda.synchronize()
+        first = o.clone()
+        assert np.array_equal(first.cpu().numpy(), out)
+        for i in range(3):
+            o.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+            assert torch.equal(o, first), i
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            call()
+        for i in range(3):
+            o.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, first), i
+
+
 SPLIT_GRID = [(dt, G, B) for dt in ("f32", "bf16") for G in (1, 4, 8) for B in (16, 32)]
 
 
