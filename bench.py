@@ -456,11 +456,12 @@ def copy_probe(stream, nbytes=1 << 30):
 
 
 def decode_kernel_flags(kernel_name: str):
-    """(LIST, WRITE, FUSED) template flags of a paged_decode_kernel name, or None for another kernel."""
+    """(LIST, WRITE, FUSED) template flags of a paged_decode_kernel name (arguments DT, D, G, B, LIST, WRITE,
+    FUSED, queries per item), or None for another kernel."""
     if "paged_decode_kernel<" not in kernel_name:
         return None
     args = [x.strip() for x in kernel_name.split("paged_decode_kernel<", 1)[1].split(">", 1)[0].split(",")]
-    return tuple(x == "true" for x in args[-3:])
+    return tuple(x == "true" for x in args[4:7])
 
 
 def is_step_kernel(kernel_name: str) -> bool:
@@ -500,6 +501,37 @@ def traffic_summary(pmc_dirs, workload: str, nbytes=1 << 30):
     return out
 
 
+def kernel_counters(pmc_dirs, nbytes=1 << 30):
+    """Per-kernel medians of every counter in rocprofv3 --pmc CSVs (rows: kernel and grid size, dispatches,
+    counters).
+    FETCH_SIZE / WRITE_SIZE also as bytes per dispatch, scaled by their readings on the copy probe when the
+    inputs hold it (the probe's three 1 GiB copies)."""
+    import csv
+    import glob
+    vals = {}
+    for d in pmc_dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                key = (r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0))  # one row per kernel and launch size
+                vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    scale = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        # the probe: of the copy kernels' three largest readings, the largest median (the runtime's copy of nbytes)
+        top = [float(np.median(sorted(c[ctr])[-3:])) for (name, _), c in vals.items()
+               if "copy" in name.lower() and ctr in c and len(c[ctr]) >= 3]
+        if top:
+            scale[ctr] = nbytes / (max(top) * 1024.0)
+    rows = []
+    for (name, grid), ctrs in sorted(vals.items()):
+        rec = {"kernel": name, "grid_size": grid, "dispatches": max(len(v) for v in ctrs.values())}
+        for ctr, v in sorted(ctrs.items()):
+            rec[ctr] = float(np.median(v))
+            if ctr in scale:
+                rec[ctr.lower() + "_bytes"] = rec[ctr] * 1024.0 * scale[ctr]
+        rows.append(rec)
+    return {"scale": scale, "kernels": rows}
+
+
 def traffic_from_profiles(workload: str):
     path = os.path.join(ROOT, "profiles", f"paged_decode_{workload}_traffic.json")
     if not os.path.exists(path):
@@ -531,10 +563,16 @@ def main():
     ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated extra workloads")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (the reference dispatch for rocprofv3 byte counters)")
+    ap.add_argument("--kernel-counters", nargs="+", metavar="DIR",
+                    help="print per-kernel medians of the counters in rocprofv3 --pmc output dirs (bytes scaled by "
+                         "the copy probe when present) and exit")
     ap.add_argument("--traffic-from", nargs="+", metavar="DIR",
                     help="write profiles/paged_decode_<workload>_traffic.json from rocprofv3 --pmc output dirs "
                          "(FETCH_SIZE and WRITE_SIZE runs of this script with --copy-probe) and exit")
     args = ap.parse_args()
+    if args.kernel_counters:
+        print(json.dumps(kernel_counters(args.kernel_counters), indent=1))
+        return
     if args.traffic_from:
         rec = traffic_summary(args.traffic_from, args.workload)
         path = os.path.join(ROOT, "profiles", f"paged_decode_{args.workload}_traffic.json")

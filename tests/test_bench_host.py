@@ -5,9 +5,11 @@ import os
 
 import bench
 
-PASS = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, false, false>(pkv::AttnArgs)"
-FUSED = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, false, true>(pkv::AttnArgs)"
-STEP = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, true, true, true>(pkv::AttnArgs)"
+K = "void pkv::(anonymous namespace)::paged_decode_kernel<pkv::BF16, 128, 1, 16, {}>(pkv::AttnArgs)"
+PASS = K.format("true, false, false, 1")
+FUSED = K.format("true, false, true, 1")
+STEP = K.format("true, true, true, 1")
+RUNS = K.format("true, false, true, 16")  # runs of 16 queries: listed and fused, no token write
 COPY = "void pkv::(anonymous namespace)::copy_probe_kernel(uint4 const*, uint4*, long)"
 
 
@@ -22,8 +24,9 @@ def write_csv(path, rows):
 
 def test_step_kernel_name():
     assert bench.is_step_kernel(STEP)
-    assert not bench.is_step_kernel(PASS) and not bench.is_step_kernel(FUSED)
+    assert not bench.is_step_kernel(PASS) and not bench.is_step_kernel(FUSED) and not bench.is_step_kernel(RUNS)
     assert bench.decode_kernel_flags(PASS) == (True, False, False)
+    assert bench.decode_kernel_flags(RUNS) == (True, False, True)
     assert bench.decode_kernel_flags(PASS.replace("true, false, false", "false, false, false")) == (False, False, False)
     assert bench.decode_kernel_flags("void pkv::(anonymous namespace)::lse_reduce_kernel<128>(pkv::AttnArgs)") is None
 
