@@ -773,7 +773,12 @@ void paged_decode_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;
     const bool has_next = live(nxt.k);
 
-    for (int i0 = 0; i0 < cur.npad; i0 += NBUF) {
+    // npad >= NBUF: a loop that visibly runs at least once lets the compiler
+    // count the ring's refills between the next query's prefetch and its use
+    // at the item change (a zero-trip path would make it wait there for all
+    // but the merge's stores, draining the ring at every item boundary).
+    int i0 = 0;
+    do {
 #pragma unroll
       for (int s = 0; s < NBUF; ++s) {
         const int i = i0 + s;
@@ -942,7 +947,8 @@ void paged_decode_kernel(AttnArgs a) {
         load_values(vb[s], T);  // the slot's values are consumed: refill
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
+      i0 += NBUF;
+    } while (i0 < cur.npad);
 
     // ---- merge the waves' partial results ------------------------------------
     // Each wave parks (acc, max, sum) in this item's LDS buffer; after one
