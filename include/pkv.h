@@ -407,9 +407,12 @@ pkv_status pkv_paged_attention_decode(float* out, const void* q, const void* k_c
  * pkv_paged_attention_decode with the remaining arguments (k_cache and v_cache
  * serve both); the output and the caches are bit for bit those of the two
  * calls.  With up to 4096 sequences the write happens inside the attention
- * kernel: the workgroup that reads a sequence's last token writes it first
- * ([P2] key technical point 1: the kernel fetches blocks through the table;
- * [P2] core idea: each step appends one token per sequence).
+ * kernel: the tokens are stored at the start of the launch, and the
+ * workgroup that reads a sequence's last token takes that token's key and
+ * value from k_new and v_new, so no read waits for the stores (bf16 with
+ * B = 32: each workgroup stores the tokens it reads first and waits for
+ * them) ([P2] key technical point 1: the kernel fetches blocks through the
+ * table; [P2] core idea: each step appends one token per sequence).
  * Errors: as pkv_paged_attention_decode, and INVALID_ARG for a missing or
  * misaligned k_new / v_new. */
 pkv_status pkv_decode_step(const void* k_new, const void* v_new, float* out, const void* q, const void* k_cache,

@@ -244,16 +244,18 @@ struct Item {
   int flags;  // kDirect | kSplitSeq | kSpecial | kBad
   int n;      // the sequence's length
   int q0, nq; // its query rows (see run_rows)
+  int new_id; // kNew: the block id of the slot of token n - 1
 };
 constexpr int kDirect = 1;    // the segment covers the whole sequence: write the output rows
 constexpr int kSplitSeq = 2;  // the sequence has several partitions
 constexpr int kSpecial = 4;   // empty or invalid sequence: no groups, fill the rows
 constexpr int kBad = 8;       // invalid length: fill with NaN
+constexpr int kNew = 16;      // decode step: the segment holds the new token (n - 1), taken from the inputs
 
 // C: matrix-core columns in use, a (query, head) pair each (decode: the G
 // heads).  Up to 8 columns the items alternate between two merge buffers (one
 // barrier per item); 16 columns take one buffer and a second barrier.
-template <int C, int D, bool LIST>
+template <int C, int D, bool LIST, int NEWW>
 struct Shared {
   struct Merge {
     alignas(16) float region[kWaves][C][D + 4];  // per-wave partial output (padded rows)
@@ -263,6 +265,10 @@ struct Shared {
   uint32_t csum[LIST ? kMaxListedSeqs + 1 : 1];  // prefix sums of sequence costs
   int chain_first;  // combine: the first run holding a segment of the owner's sequence
   int chain_ok;     // combine: every segment arrived and belongs to the sequence
+  // decode step (NEWW > 0): the new token's key and value rows (NEWW dwords
+  // each) of the current item, in two entries that alternate between items
+  alignas(16) uint32_t knew[NEWW > 0 ? 2 : 1][NEWW > 0 ? NEWW : 1];
+  uint32_t vnew[NEWW > 0 ? 2 : 1][NEWW > 0 ? NEWW : 1];
 };
 
 // Cost of a partition in the work split: its groups plus a fixed charge for
@@ -369,7 +375,13 @@ __device__ __forceinline__ void combine_runs(const AttnArgs& a, int seq, int kvh
 // segment).  Otherwise every partition is an item: numbered part-major over
 // max_parts, dealt round-robin to the lanes, the empty ones (partition past
 // the sequence's end) skipped.  WRITE (LIST only): the decode step's variant,
-// which also stores each sequence's new token before reading.
+// which also stores each sequence's new token (position n - 1): the segment
+// that ends with it puts the token's key and value from the call's inputs
+// into the ring registers in place of the cache slot's bytes (the same bits
+// the cache holds once written, so the result equals the two-call path's),
+// and the workgroups store the tokens into the caches at their start with no
+// ordering against the reads; bf16 with 32-token blocks (no registers to
+// spare) instead stores the tokens of its own run first and waits for them.
 // FUSED (LIST only): the workgroup whose run starts with the last segment of a
 // sequence cut between runs (its owner) combines that sequence's segments at
 // the end of its run, once the earlier runs have handed their records over;
@@ -388,8 +400,14 @@ void paged_decode_kernel(AttnArgs a) {
   constexpr int NBUF = Gm::NBUF, R = Gm::R, TILE = Gm::TILE;
   constexpr bool kBF16 = Gm::kBF16;
   constexpr int NCOL = QR * G;  // columns in use
+  // WRITE: how the new token enters.  Late: the segment that ends with it
+  // takes its key and value from the inputs and stores them at its end.
+  // First: every run stores its sequences' tokens before reading (bf16 with
+  // 32-token blocks, whose ring leaves no registers for the late form).
+  constexpr bool kTokenFirst = WRITE && kBF16 && B == 32;
+  constexpr bool kTokenLate = WRITE && !kTokenFirst;
   static_assert(NCOL <= 16 && (QR == 1 || (LIST && FUSED && !WRITE)), "runs: 16 columns, listed and fused");
-  __shared__ Shared<NCOL, D, LIST> sh;
+  __shared__ Shared<NCOL, D, LIST, kTokenLate ? Gm::R / 4 : 0> sh;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = uni(tid / kWave);
@@ -410,6 +428,32 @@ void paged_decode_kernel(AttnArgs a) {
       const int np = seq_state<QR>(a, s, n, &special, &bad);
       const int last = special ? 0 : n - (np - 1) * P;  // tokens of the last partition
       sh.csum[s + 1] = static_cast<uint32_t>(np - 1) * full_cost + (last + GT - 1) / GT + kItemCharge;
+    }
+    if constexpr (kTokenLate) {
+      // The new tokens into the caches, once the lengths are read: workgroup
+      // (lane, KV head) stores the tokens of sequences lane, lane + lanes, ...
+      // of its head, through L2, while it works out its run; it waits for the
+      // stores before its first read.  No ordering with the reads of other workgroups is
+      // needed, as the reading segment takes the token from the inputs.
+      using TT = typename std::conditional<kBF16, uint16_t, uint32_t>::type;
+      constexpr int E = 16 / static_cast<int>(sizeof(TT));
+      for (int s = lane_b + lanes * wave; s < S; s += lanes * kWaves) {
+        const int n = ld_const(a.context_lens, s);
+        bool bad;
+        seq_parts(a, n, &bad);
+        if (bad || n == 0) continue;
+        const int id = ld_const(a.block_tables, static_cast<size_t>(s) * a.max_blocks + (n - 1) / B);
+        if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) continue;
+        const size_t row = (static_cast<size_t>(s) * Hkv + kvh_b) * D;
+        const TT* krow = static_cast<const TT*>(a.k_new) + row;
+        const TT* vrow = static_cast<const TT*>(a.v_new) + row;
+        const uint4 kv = *reinterpret_cast<const uint4*>(krow + (lane < D / E ? lane : 0) * E);
+        const TT v0 = vrow[lane];
+        const TT v1 = D > 64 ? vrow[64 + lane] : TT(0);
+        store_token_rows<TT, kStoreThrough>(const_cast<char*>(static_cast<const char*>(a.k_cache)),
+                                            const_cast<char*>(static_cast<const char*>(a.v_cache)),
+                                            static_cast<int64_t>(id) * Hkv + kvh_b, (n - 1) % B, B, D, lane, kv, v0, v1);
+      }
     }
     __syncthreads();
     if (wave == 0) {  // scan of the costs: a chunk per lane, then a wave-wide scan of the chunk sums
@@ -565,6 +609,13 @@ void paged_decode_kernel(AttnArgs a) {
     it.part = slot_of(it.tok_begin);
     it.part_next = it.tok_end == n ? nparts : slot_of(it.tok_end);
     it.flags = (whole ? kDirect : 0) | (nparts > 1 ? kSplitSeq : 0) | (special ? kSpecial : 0) | (bad ? kBad : 0);
+    it.new_id = 0;
+    if constexpr (kTokenLate) {
+      if (!special && it.tok_end == n) {
+        it.flags |= kNew;
+        it.new_id = ld_const(a.block_tables, static_cast<size_t>(it.seq) * a.max_blocks + (n - 1) / B);
+      }
+    }
     const int ngroups = (it.tok_end - it.tok_begin + GT - 1) / GT;
     it.nk = wave < ngroups ? (ngroups - wave + kWaves - 1) / kWaves : 0;
     it.npad = it.nk <= NBUF ? NBUF : (it.nk + NBUF - 1) & ~(NBUF - 1);
@@ -613,7 +664,7 @@ void paged_decode_kernel(AttnArgs a) {
     }
   }
   if (k_first >= k_end) return;
-  if constexpr (LIST && WRITE) {
+  if constexpr (LIST && kTokenFirst) {
     // The decode step's new tokens.  The run holds the last token of every
     // sequence in [k_first, run_end.seq) (a sequence cut at run_end goes on in
     // the next run), and only this workgroup reads that token for its head, so
@@ -749,9 +800,80 @@ void paged_decode_kernel(AttnArgs a) {
   load_query(q_cur, cur);
   if constexpr (kPrefetchQ) load_query(q_nxt, live(nxt.k) ? nxt : cur);
 
+  // Late token: the next item's key and value rows, dword j of a row in lane
+  // j % 64 (register j / 64), loaded one item ahead like the query.  When an
+  // item starts, every wave copies them into the item's entry of sh.knew and
+  // sh.vnew (the same bytes from each wave, so a wave reads back its own
+  // writes with no barrier; two entries alternate, and the merge barrier
+  // between items keeps a wave from overwriting an entry another still
+  // reads); the load is a whole item old by then, so the wait for it is exact.
+  constexpr int NW = kTokenLate ? (R / 4 + kWave - 1) / kWave : 1;
+  uint32_t kn_nxt[NW], vn_nxt[NW];
+  int ord = 0;  // the current item's position in this workgroup's walk
+  auto park_new = [&](int e) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      if (lane + kWave * j < R / 4) {
+        sh.knew[e][lane + kWave * j] = kn_nxt[j];
+        sh.vnew[e][lane + kWave * j] = vn_nxt[j];
+      }
+    }
+  };
+  auto load_new = [&](uint32_t (&kn)[NW], uint32_t (&vn)[NW], const Item& it, bool use)
+                      __attribute__((always_inline)) {
+    const bool has = use && (it.flags & kNew);
+    const size_t row = (static_cast<size_t>(it.seq) * Hkv + it.kvh) * R;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(a.k_new) + row, has ? R : 0);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(a.v_new) + row, has ? R : 0);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      kn[j] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * (lane + kWave * j), 0, 0);
+      vn[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, 4 * (lane + kWave * j), 0, 0);
+    }
+  };
+  if constexpr (kTokenLate) load_new(kn_nxt, vn_nxt, cur, true);  // parked once the ring's first loads are out
+  // Token r of a group in the ring slot's operand registers: the key row in
+  // the lanes of token row r % 16 of QK tile r / 16 (the 16 bytes at 64 st +
+  // 16 kq of the row), the value of dim 16 dt + m16 in the lanes whose tokens
+  // include r.  The rows go through the wave's own LDS copy (written and read
+  // by the same wave, in order), so each lane reads its operand bytes at a
+  // constant offset from one address.
+  auto patch_keys = [&](uint4 (&kbs)[NT][KS], int r) __attribute__((always_inline)) {
+    if (m16 == (r & 15)) {
+      const char* row = reinterpret_cast<const char*>(sh.knew[ord & 1]) + 16 * kq;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (t == (r >> 4))
+#pragma unroll
+          for (int st = 0; st < KS; ++st) kbs[t][st] = *reinterpret_cast<const uint4*>(row + 64 * st);
+    }
+  };
+  auto patch_values = [&](uint32_t (&vbs)[NDT][VW], int r) __attribute__((always_inline)) {
+    constexpr int TPL = (kBF16 ? 2 : 1) * VW;  // tokens per lane and d-tile
+    const int e = r % TPL;
+    if (kq == r / TPL) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        if constexpr (kBF16) {
+          const uint32_t v16 = reinterpret_cast<const uint16_t*>(sh.vnew[ord & 1])[16 * dt + m16];
+#pragma unroll
+          for (int w = 0; w < VW; ++w)
+            if (w == (e >> 1))
+              vbs[dt][w] = (e & 1) ? ((vbs[dt][w] & 0x0000ffffu) | (v16 << 16)) : ((vbs[dt][w] & 0xffff0000u) | v16);
+        } else {
+          const uint32_t x = sh.vnew[ord & 1][16 * dt + m16];
+#pragma unroll
+          for (int w = 0; w < VW; ++w)
+            if (w == e) vbs[dt][w] = x;
+        }
+      }
+    }
+  };
+
   uint4 kb[NBUF][NT][KS];
   uint32_t vb[NBUF][NDT][VW];
   bool pois_cur = false, pois_nxt = false;
+  if constexpr (kTokenLate) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this workgroup's token stores are done
   // The ring starts with positions 0 .. NBUF-1 of the first item.
 #pragma unroll
   for (int s = 0; s < NBUF; ++s) {
@@ -763,6 +885,10 @@ void paged_decode_kernel(AttnArgs a) {
   }
   // The block id of the next refill target is fetched one step ahead.
   int pend_id = table_entry(where(NBUF, live(nxt.k)));
+  if constexpr (kTokenLate) {
+    park_new(0);
+    load_new(kn_nxt, vn_nxt, nxt, live(nxt.k));
+  }
 
   const float c = a.c;
   int parity = 0;  // LDS merge buffer of the current item
@@ -784,6 +910,12 @@ void paged_decode_kernel(AttnArgs a) {
         const int i = i0 + s;
         const bool valid = i < cur.nk;
         const int t_first = cur.tok_begin + GT * (wave + kWaves * i);
+        // late token: the group holds it (then it is a valid group of the item)
+        const int r_new = cur.n - 1 - t_first;
+        const bool patch = kTokenLate && (cur.flags & kNew) && static_cast<unsigned>(r_new) < static_cast<unsigned>(GT);
+        if constexpr (kTokenLate) {
+          if (patch) patch_keys(kb[s], r_new);
+        }
 
         // Refill target of this slot: ring position i + NBUF.
         const int ti = i + NBUF;
@@ -817,6 +949,9 @@ void paged_decode_kernel(AttnArgs a) {
         load_keys(kb[s], T);  // the slot's keys are consumed: refill
         __builtin_amdgcn_sched_barrier(0);
 
+        if constexpr (kTokenLate) {
+          if (patch) patch_values(vb[s], r_new);
+        }
         if (valid) {
           // Scaled logits u = c (q . k).
 #pragma unroll
@@ -1068,6 +1203,11 @@ void paged_decode_kernel(AttnArgs a) {
       nxt.k = kn;
     }
     if constexpr (kPrefetchQ) load_query(q_nxt, live(nxt.k) ? nxt : cur);
+    if constexpr (kTokenLate) {
+      ++ord;
+      park_new(ord & 1);
+      load_new(kn_nxt, vn_nxt, nxt, live(nxt.k));
+    }
     // Ring position NBUF of the new item: when the item has only NBUF
     // positions it is the following item's first group, which the old item's
     // look-ahead could not know.
