@@ -461,8 +461,9 @@ pkv_status pkv_decode_step_static(const void* k_new, const void* v_new, float* o
  *     the order in which their work starts (longest first evens out the end
  *     of a ragged batch), or NULL for 0, 1, 2, ...  It changes scheduling
  *     only, never the results.  An entry outside [0, num_seqs) is skipped;
- *     a sequence the order leaves out is not computed (its rows are left as
- *     they were, or unspecified when the call splits contexts).
+ *     on the runs kernel (see Paths), a sequence the order leaves out is not
+ *     computed (its rows are left as they were, or unspecified when the call
+ *     splits contexts); the decode kernel's pass ignores the order.
  *   max_query_len: a bound on every q_s (it sizes the launch).
  *   workspace: device memory of workspace_bytes >= the value of
  *     pkv_attention_multi_workspace_bytes(...) for these sizes, 16-byte
@@ -481,9 +482,14 @@ pkv_status pkv_decode_step_static(const void* k_new, const void* v_new, float* o
  * kernel's listed pass, the queries of a run as further matrix-core columns of
  * one persistent, cost-balanced pass over 512-token partitions; that path
  * needs the workspace when a context exceeds 512 tokens, and without one the
- * call uses the runs kernel, unsplit.  Other batches use the runs kernel.  The
+ * call uses the runs kernel, unsplit.  Other batches use the runs kernel,
+ * except a batch with max_query_len > 16 / G and num_query_rows <
+ * num_seqs * max_query_len (some runs are shorter than the longest: prompt
+ * chunks beside decodes in one step), which takes two launches on the
+ * stream: the runs of at most 16 / G queries on the decode kernel's pass
+ * (when it fits, as above), then the longer ones on the runs kernel.  The
  * environment variable PKV_MULTI_PATH set to "runs" (read at each call) keeps
- * every batch on the runs kernel.  Both paths meet the same contract and
+ * every run on the runs kernel.  Both paths meet the same contract and
  * tolerances; their rows differ in rounding.
  * Tuning: where a pair has more than 64 rows, a workgroup serves 128 rows
  * (two row tiles per wave) when the batch's rows fill the GPU, else 64; the
@@ -502,7 +508,7 @@ pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_ca
 
 /* Bytes of workspace pkv_paged_attention_multi uses to split long contexts (0
  * when it would not split them): the larger of the two paths' needs.  The
- * decode kernel's path (short runs, see there) cuts contexts into 512-token
+ * decode kernel's path (runs of at most 16 / G queries, see there) cuts contexts into 512-token
  * partitions and between workgroups, with records per workgroup.  On the runs
  * kernel a context is split when every run's rows (max_query_len * H_q / H_kv)
  * fit one 64-row block and the batch has too few (sequence, KV head) pairs to

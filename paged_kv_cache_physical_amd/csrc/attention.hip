@@ -91,6 +91,7 @@ struct AttnArgs {
   int32_t num_q_heads;
   int32_t num_query_rows;
   int32_t max_query_len;
+  int32_t skip_long;  // 1: a run longer than max_query_len belongs to another launch (nothing is written)
 };
 
 // Hand-over of a record between workgroups of one launch, with no contract on
@@ -164,7 +165,8 @@ __device__ __forceinline__ int32_t ld_const(const int32_t* p, size_t i) {
 // positions n - nq .. n - 1 of its context.  Decode: the sequence's own row.
 // A run can also be (as the runs kernel takes it): outside the rows (nothing
 // is written), or impossible (longer than its context or than the batch's
-// longest run: NaN rows, at most max_query_len of them).
+// longest run: NaN rows, at most max_query_len of them).  With skip_long, a
+// run longer than max_query_len is left to the runs kernel (nothing written).
 struct RunRows {
   int q0, nq;
   bool bad;
@@ -176,7 +178,8 @@ __device__ __forceinline__ RunRows run_rows(const AttnArgs& a, int s, int n) {
   } else {
     const int q0 = ld_const(a.query_start, s);
     const int qs = ld_const(a.query_start, s + 1) - q0;
-    const bool rows = q0 >= 0 && qs > 0 && static_cast<int64_t>(q0) + qs <= a.num_query_rows;
+    const bool rows = q0 >= 0 && qs > 0 && static_cast<int64_t>(q0) + qs <= a.num_query_rows &&
+                      !(a.skip_long && qs > a.max_query_len);
     return RunRows{q0, rows ? min(qs, a.max_query_len) : 0, rows && (qs > n || qs > a.max_query_len)};
   }
 }
@@ -1658,7 +1661,8 @@ void* scratch_address() {
 // checked; PKV_ERR_UNSUPPORTED when the batch does not fit this path (too
 // many sequences, runs too long, or no workspace where the split needs one),
 // and the caller then uses the runs kernel; PKV_ERR_WORKSPACE for a workspace
-// too small.
+// too small.  With skip_long, max_query_len is the longest run this launch
+// takes, and the runs kernel takes the longer ones of the batch.
 constexpr int32_t kRunsPartition = 512;
 
 bool runs_listed_fits(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -1681,8 +1685,8 @@ pkv_status runs_listed(float* out, const void* q, const void* k_cache, const voi
                        const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
                        int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks, int32_t max_blocks, int32_t max_context_len,
-                       int32_t max_query_len, float scale, void* workspace, size_t workspace_bytes, int32_t kv_dtype,
-                       hipStream_t stream) {
+                       int32_t max_query_len, bool skip_long, float scale, void* workspace, size_t workspace_bytes,
+                       int32_t kv_dtype, hipStream_t stream) {
   if (!runs_listed_fits(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len))
     return PKV_ERR_UNSUPPORTED;
   const int G = num_q_heads / num_kv_heads;
@@ -1722,6 +1726,7 @@ pkv_status runs_listed(float* out, const void* q, const void* k_cache, const voi
   a.num_q_heads = num_q_heads;
   a.num_query_rows = num_query_rows;
   a.max_query_len = max_query_len;
+  a.skip_long = skip_long ? 1 : 0;
   const hipError_t err = kv_dtype == PKV_BF16 ? launch_runs<BF16>(a, head_dim, G, stream)
                                               : launch_runs<F32>(a, head_dim, G, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;

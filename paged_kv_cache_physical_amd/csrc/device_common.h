@@ -127,12 +127,14 @@ hipError_t launch_write_last_token(const void* k_new, const void* v_new, void* k
 
 // Runs of at most 16 / G queries per sequence on the decode kernel
 // (attention.hip); PKV_ERR_UNSUPPORTED when the batch does not fit that path.
+// skip_long: runs longer than max_query_len are left alone (another launch
+// takes them) instead of being filled with NaN.
 pkv_status runs_listed(float* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                        const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
                        int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks, int32_t max_blocks, int32_t max_context_len,
-                       int32_t max_query_len, float scale, void* workspace, size_t workspace_bytes, int32_t kv_dtype,
-                       hipStream_t stream);
+                       int32_t max_query_len, bool skip_long, float scale, void* workspace, size_t workspace_bytes,
+                       int32_t kv_dtype, hipStream_t stream);
 size_t runs_listed_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_context_len, int32_t max_query_len);
 

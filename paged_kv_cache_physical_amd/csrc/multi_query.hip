@@ -79,6 +79,7 @@ struct MultiArgs {
   int max_blocks;
   int max_context_len;
   int max_query_len;
+  int skip_upto;   // runs of at most this many queries belong to another launch (0: none)
   int wg_per_seq;  // row blocks per (sequence, KV head)
   int num_pairs;   // (sequence, KV head) pairs
   int pair_slots;  // with several row blocks per pair: ceil(num_pairs / 8), the pairs per XCD
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
 
   const int q0 = mq_ld(a.query_start, s);
   const int qs = mq_ld(a.query_start, s + 1) - q0;
-  if (q0 < 0 || qs <= 0 || static_cast<int64_t>(q0) + qs > a.num_query_rows) return;  // nothing it may write
+  if (q0 < 0 || qs <= a.skip_upto || static_cast<int64_t>(q0) + qs > a.num_query_rows) return;  // nothing to write
   const int n = mq_ld(a.context_lens, s);
   const bool bad = n > a.max_context_len || static_cast<int64_t>(n) > static_cast<int64_t>(a.max_blocks) * a.block_size ||
                    qs > n || qs > a.max_query_len;
@@ -640,7 +641,8 @@ __global__ __launch_bounds__(kWave* kMqWaves, (mq_min_blocks<DT, D>(T))) void pa
 // weighs nothing.  One workgroup per (pair, row of the longest run): wave 0 turns the
 // splits' maxima and sums into weights (one split per lane), then every
 // thread sums a share of the splits for four dims and LDS adds the shares.
-// Runs the attention kernel did not write, or wrote as NaN, are skipped.
+// Runs the attention kernel did not write, or wrote as NaN, are skipped, and
+// so are those it left to another launch.
 constexpr int kMqMaxSplits = 64;  // one split per lane of the weighting wave
 template <int D, int G>
 __global__ __launch_bounds__(256) void multi_combine_kernel(const MultiArgs a) {
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(256) void multi_combine_kernel(const MultiArgs a) {
   const int s = sg / a.num_kv_heads, g = sg % a.num_kv_heads;
   const int q0 = mq_ld(a.query_start, s);
   const int qs = mq_ld(a.query_start, s + 1) - q0;
-  if (q0 < 0 || qs <= 0 || static_cast<int64_t>(q0) + qs > a.num_query_rows) return;
+  if (q0 < 0 || qs <= a.skip_upto || static_cast<int64_t>(q0) + qs > a.num_query_rows) return;
   const int n = mq_ld(a.context_lens, s);
   if (n > a.max_context_len || static_cast<int64_t>(n) > static_cast<int64_t>(a.max_blocks) * a.block_size ||
       qs > n || qs > a.max_query_len || rr >= qs * G)  // the same for the whole workgroup
@@ -814,18 +816,32 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
     if (need > 0 && (workspace_bytes < need || !aligned16(workspace))) return PKV_ERR_WORKSPACE;
   }
 
-  // Runs of at most 16 / G queries (verification of drafted tokens) go to the
-  // decode kernel's listed path, where the queries of a run are further
-  // matrix-core columns of one persistent, cost-balanced pass (seq_order does
-  // not apply there); PKV_MULTI_PATH=runs (read at each call) keeps them here.
+  // Runs of at most 16 / G queries (verification of drafted tokens, decodes)
+  // go to the decode kernel's listed path, where the queries of a run are
+  // further matrix-core columns of one persistent, cost-balanced pass
+  // (seq_order does not apply there).  A batch whose longest run is longer
+  // and whose rows say that some runs are shorter (a mixed step: prompt chunks
+  // beside decodes) takes two launches: the short runs there, then the longer
+  // ones here.  PKV_MULTI_PATH=runs (read at each call) keeps every run here.
+  int skip_upto = 0;
   {
     const char* path = std::getenv("PKV_MULTI_PATH");
     if (!(path && std::strcmp(path, "runs") == 0)) {
-      const pkv_status st = runs_listed(out, q, k_cache, v_cache, block_tables, context_lens, query_start, num_seqs,
-                                        num_query_rows, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                                        max_blocks, max_context_len, max_query_len, scale, workspace, workspace_bytes,
-                                        kv_dtype, stream);
-      if (st != PKV_ERR_UNSUPPORTED) return st;
+      const int short_len = 16 / G;
+      if (max_query_len <= short_len) {
+        const pkv_status st = runs_listed(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                                          num_seqs, num_query_rows, num_q_heads, num_kv_heads, head_dim, block_size,
+                                          num_blocks, max_blocks, max_context_len, max_query_len, false, scale,
+                                          workspace, workspace_bytes, kv_dtype, stream);
+        if (st != PKV_ERR_UNSUPPORTED) return st;
+      } else if (static_cast<int64_t>(num_query_rows) < static_cast<int64_t>(num_seqs) * max_query_len) {
+        const pkv_status st = runs_listed(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                                          num_seqs, num_query_rows, num_q_heads, num_kv_heads, head_dim, block_size,
+                                          num_blocks, max_blocks, max_context_len, short_len, true, scale,
+                                          workspace, workspace_bytes, kv_dtype, stream);
+        if (st == PKV_OK) skip_upto = short_len;
+        else if (st != PKV_ERR_UNSUPPORTED) return st;
+      }
     }
   }
 
@@ -874,6 +890,7 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   a.max_blocks = max_blocks;
   a.max_context_len = max_context_len;
   a.max_query_len = max_query_len;
+  a.skip_upto = skip_upto;
   a.wg_per_seq = static_cast<int>(wg_per_seq);
   a.num_pairs = static_cast<int>(pairs);
   a.pair_slots = static_cast<int>(pair_slots);
@@ -904,7 +921,9 @@ extern "C" size_t pkv_attention_multi_workspace_bytes(int32_t num_seqs, int32_t 
     return 0;
   const size_t split = multi_plan(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim, max_context_len,
                                   max_query_len).bytes;
-  const size_t listed =
-      runs_listed_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len);
+  // the decode kernel takes the runs of at most 16 / G queries (all of them, or the short ones of a mixed step)
+  const int32_t short_len = 16 / (num_q_heads / num_kv_heads);
+  const size_t listed = runs_listed_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                                    max_query_len < short_len ? max_query_len : short_len);
   return split > listed ? split : listed;
 }

@@ -538,11 +538,9 @@ def test_duplicate_and_unknown_ids_in_one_append(libpkv):
 
 
 def listed_runs_bytes(S, Hq, Hkv, d, ctx, mq):
-    """The decode kernel's path for short runs (mq * G <= 16): records of 16 columns for two per workgroup of a
-    grid of at most 2048 (a multiple of H_kv), over 512-token partitions; 0 when no context is cut."""
-    G = Hq // Hkv
-    if mq * G > 16:
-        return 0
+    """The decode kernel's path for runs of at most 16 / G queries (all the runs when mq * G <= 16, else the short
+    runs of a mixed batch): records of 16 columns for two per workgroup of a grid of at most 2048 (a multiple of
+    H_kv), over 512-token partitions; 0 when no context is cut."""
     parts = -(-max(ctx, 1) // 512)
     if parts <= 1:
         return 0
@@ -569,7 +567,9 @@ def test_runs_of_queries_host_checks_and_split_plan(libpkv):
     # enough pairs for the runs kernel; the short runs still cut their 2048-token contexts
     assert pk.pkv_attention_multi_workspace_bytes(64, 32, 32, 128, 2048, 4) == listed_runs_bytes(
         64, 32, 32, 128, 2048, 4) > 0
-    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 32768, 17) == 0  # 68 rows: no split
+    # 68 rows: the runs kernel does not split, but the short runs of such a batch take the decode kernel's path
+    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 32768, 17) == listed_runs_bytes(
+        8, 32, 8, 128, 32768, 17) > 0
     assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 500, 4) == 0  # too short to split
     assert pk.pkv_attention_multi_workspace_bytes(8, 30, 8, 128, 32768, 4) == 0  # H_q % H_kv != 0
 

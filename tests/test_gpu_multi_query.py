@@ -372,10 +372,12 @@ def test_full_size_verification():
     check_close(out, b.oracle(q, t, l, starts), s.kv_dtype, f"all {len(runs)} runs")
 
 
-def test_full_size_mixed_step():
-    """One continuous-batching step at full size, launched as timed: 64 sequences with contexts uniform in
-    [640, 2048], 32/8 heads, d 128, bf16, B 16; 4 of them take a 512-query prompt chunk and 60 decode one token, in
-    longest-first order.  Every row (the four chunks and the 60 decodes) against the oracle."""
+def test_full_size_mixed_step(monkeypatch):
+    """One continuous-batching step at full size, launched as timed (with a workspace, longest-first order): 64
+    sequences with contexts uniform in [640, 2048], 32/8 heads, d 128, bf16, B 16; 4 of them take a 512-query
+    prompt chunk and 60 decode one token.  The decodes go to the decode kernel's pass, the chunks to the runs
+    kernel; every row (the four chunks and the 60 decodes) against the oracle, and again with every run on the
+    runs kernel (PKV_MULTI_PATH=runs)."""
     rng = wl.rng_for(31, 0)
     S, Hq, Hkv, d = 64, 32, 8, 128
     lens = [int(x) for x in rng.integers(640, 2048, size=S, endpoint=True)]
@@ -383,27 +385,98 @@ def test_full_size_mixed_step():
     b = Batch(lens, Hq, Hkv, d, 16, "bf16", seed=31)
     q = wl.draw_values(wl.rng_for(32, wl.STREAM_Q), (sum(runs), Hq, d), "bf16")
     order = np.argsort(-np.array(lens), kind="stable").astype(np.int32)
-    out, t, l, starts = b.multi(runs, q, order=order)
+    out, t, l, starts = b.multi(runs, q, order=order, split=True)
     ref = b.oracle(q, t, l, starts)
     check_close(out[:4 * 512], ref[:4 * 512], "bf16", "the four prompt chunks, all rows")
     check_close(out[4 * 512:], ref[4 * 512:], "bf16", "the 60 decodes")
+    monkeypatch.setenv("PKV_MULTI_PATH", "runs")
+    other, *_ = b.multi(runs, q, order=order, split=True)
+    check_close(other[:4 * 512], ref[:4 * 512], "bf16", "the four prompt chunks, runs kernel only")
+    check_close(other[4 * 512:], ref[4 * 512:], "bf16", "the 60 decodes, runs kernel only")
+    assert np.array_equal(other[:4 * 512], out[:4 * 512])  # the chunks come from the runs kernel either way
 
 
-def test_repeated_calls_and_graph_replays_are_bitwise_stable():
+MIXED_GRID = [("bf16", 128, 4, 16), ("f32", 64, 8, 32), ("bf16", 64, 1, 32), ("f32", 128, 2, 16),
+              ("bf16", 128, 8, 32)]
+
+
+@pytest.mark.parametrize("dt,d,G,B", MIXED_GRID)
+def test_mixed_step_two_launches(dt, d, G, B, monkeypatch):
+    """A batch whose longest run is longer than 16 / G queries while other runs are shorter (prompt chunks and a
+    whole prompt beside decodes and short verifications) takes two launches when given a workspace: the runs of
+    at most 16 / G queries on the decode kernel's pass, over contexts cut into 512-token partitions, the longer
+    ones on the runs kernel.  Every row against the oracle; the runs kernel alone (PKV_MULTI_PATH=runs) gives the
+    long runs' rows bit for bit and the short ones within the same bars."""
+    k = 16 // G
+    lens = [1800, 700, 2500, 64, 1200, 1, 900, 3000, 40, 513]
+    runs = [1, k, 200, 1, k + 1, 1, min(2, k), 1, 40, 1]
+    Hkv = 2
+    say(f"case {dt} d={d} G={G} B={B}: k={k} runs={runs}")
+    b = Batch(lens, G * Hkv, Hkv, d, B, dt, seed=G + d + B + 91)
+    q = wl.draw_values(wl.rng_for(92, wl.STREAM_Q, G, d), (sum(runs), G * Hkv, d), dt)
+    out, t, l, starts = b.multi(runs, q, split=True)
+    ref = b.oracle(q, t, l, starts)
+    check_close(out, ref, dt, "two launches")
+    monkeypatch.setenv("PKV_MULTI_PATH", "runs")
+    other, *_ = b.multi(runs, q, split=True)
+    check_close(other, ref, dt, "runs kernel only")
+    long_rows = np.concatenate([np.arange(starts[i], starts[i + 1]) for i, r in enumerate(runs) if r > k])
+    assert np.array_equal(other[long_rows], out[long_rows])
+
+
+def test_mixed_step_two_launches_edges():
+    """The runs kernel's contract holds across the two launches (G = 4: runs of up to 4 queries on the decode
+    kernel's pass, max_query_len 12): an empty run writes nothing; a run longer than its context gives NaN rows,
+    on either launch; a run longer than max_query_len gives NaN on its first max_query_len rows and leaves the
+    rest alone; a bad block id poisons only its own sequence, short (cut) or long."""
+    lens = [1400, 33, 20, 640, 9, 2100, 700, 2]
+    runs = [3, 0, 21, 2, 9, 4, 1, 3]
+    b = Batch(lens, 8, 2, 64, 16, "f32", seed=93)
+    t, l = b.tables()
+    T = sum(runs)
+    q = wl.draw_values(wl.rng_for(94, wl.STREAM_Q), (T, 8, 64), "f32")
+    starts = np.concatenate([[0], np.cumsum(runs)]).astype(np.int32)
+    rows = lambda i: slice(int(starts[i]), int(starts[i + 1]))
+    sentinel = torch.full((T, 8, 64), 7.0, dtype=torch.float32, device="cuda")
+    out, *_ = b.multi(runs, q, tables=t, lens=l, query_start=starts, max_query_len=12, out=sentinel, split=True)
+    refs = {}
+    for i in (0, 3, 4, 5, 6):
+        refs[i] = b.oracle(q[rows(i)], t[i:i + 1], l[i:i + 1], np.array([0, runs[i]], np.int32))
+        check_close(out[rows(i)], refs[i], "f32", f"sequence {i}")
+    s2 = int(starts[2])
+    assert np.all(np.isnan(out[s2:s2 + 12])) and np.all(out[s2 + 12:s2 + 21] == 7.0)  # 21 > 12 and > n: runs kernel
+    assert np.all(np.isnan(out[rows(7)]))  # 3 > its 2-token context: decode kernel's pass
+    t2 = t.copy()
+    t2[0, 40] = b.nb + 5  # a cut short-run sequence
+    t2[4, 0] = b.nb + 6   # the whole 9-token prompt
+    sentinel.fill_(7.0)
+    out, *_ = b.multi(runs, q, tables=t2, lens=l, query_start=starts, max_query_len=12, out=sentinel, split=True)
+    assert np.all(np.isnan(out[rows(0)])) and np.all(np.isnan(out[rows(4)]))
+    for i in (3, 5, 6):
+        check_close(out[rows(i)], refs[i], "f32", f"sequence {i} beside bad ids")
+
+
+@pytest.mark.parametrize("with_ws", [False, True])
+def test_repeated_calls_and_graph_replays_are_bitwise_stable(with_ws):
     """Runs of queries give the same bits on every call, and as a captured HIP graph on every replay, with eager
-    work and synchronisations between the replays."""
+    work and synchronisations between the replays; with a workspace the call takes two launches (the decode and
+    the 3-query verification on the decode kernel's pass, the rest on the runs kernel)."""
     import paged_kv_cache_physical_amd as pk
-    lens = [900, 1500, 37, 2048, 640]
-    runs = [300, 7, 37, 512, 1]
+    lens = [900, 1500, 37, 2048, 640, 1300]
+    runs = [300, 7, 37, 512, 1, 3]
     b = Batch(lens, 32, 8, 128, 16, "bf16", seed=29)
     t, l = b.tables()
     q = to_dev(wl.draw_values(wl.rng_for(30, wl.STREAM_Q), (sum(runs), 32, 128), "bf16"), "bf16")
     starts = torch.from_numpy(np.concatenate([[0], np.cumsum(runs)]).astype(np.int32)).cuda()
     bt, cl = torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda()
     out = torch.empty((sum(runs), 32, 128), dtype=torch.float32, device="cuda")
+    ws = None
+    if with_ws:
+        nbytes = pk.pkv_attention_multi_workspace_bytes(len(lens), 32, 8, 128, int(l.max()), max(runs))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
     call = lambda: pk.pkv_paged_attention_multi(out, q, *b.caches, bt, cl, starts, int(l.max()), max(runs),
-                                                1.0 / np.sqrt(128), stream=s)
+                                                1.0 / np.sqrt(128), stream=s, workspace=ws)
     with torch.cuda.stream(s):
         call()
         torch.cuda.synchronize()
