@@ -846,20 +846,31 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   }
 
   // Two row tiles per wave when a pair has more rows than one workgroup of
-  // one-tile waves holds, and the batch's rows (num_query_rows * G in all, the
-  // host's only measure of the work) make at least one full round of
-  // two-tile workgroups (two fit a CU); otherwise one tile per wave gives
-  // twice the workgroups to spread a few long prompts over.
-  // PKV_MULTI_TILES=1 or 2 (read at each call) forces the choice; both kernels
-  // give the same rows.
+  // one-tile waves holds and there is work enough for the coarser workgroups
+  // (two fit a CU, against three of one tile; a two-tile workgroup reads each
+  // chunk once for twice the rows).  The host's measures of the work are the
+  // row counts: the batch's rows, num_query_rows * G, make at least one full
+  // round of two-tile workgroups; or, with every run of this launch a long
+  // one (the short runs taken by the decode kernel, or all runs of the longest
+  // length) and contexts of at least twice the longest run (runs at the end of
+  // longer contexts, as chunked prompts are, so that the row blocks of a pair
+  // cost about the same), the rows of all pairs, num_query_rows * H_q, do.
+  // Otherwise one tile per wave gives more, smaller workgroups to spread a
+  // few causal prompts, or short runs, over.  PKV_MULTI_TILES=1 or 2 (read at
+  // each call) forces the choice; both kernels give the same rows.
   int T = 1;
   if (static_cast<int64_t>(max_query_len) * G > kMqRows) {
     const char* force = std::getenv("PKV_MULTI_TILES");
     if (force && (force[0] == '1' || force[0] == '2') && force[1] == 0) {
       T = force[0] - '0';
     } else {
-      const int64_t blocks2 = (static_cast<int64_t>(num_query_rows) * G + 2 * kMqRows - 1) / (2 * kMqRows);
-      if (blocks2 >= 2 * static_cast<int64_t>(device_cus())) T = 2;
+      const int64_t round2 = 2 * static_cast<int64_t>(device_cus()) * 2 * kMqRows;  // rows of one full round
+      const bool long_only = skip_upto > 0 || static_cast<int64_t>(num_query_rows) ==
+                                                  static_cast<int64_t>(num_seqs) * max_query_len;
+      const bool tails = long_only && max_context_len >= 2 * static_cast<int64_t>(max_query_len);
+      if (static_cast<int64_t>(num_query_rows) * G >= round2 ||
+          (tails && static_cast<int64_t>(num_query_rows) * num_q_heads >= round2))
+        T = 2;
     }
   }
   const int64_t rows_per_wg = static_cast<int64_t>(kMqRows) * T;
