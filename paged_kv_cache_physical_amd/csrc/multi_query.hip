@@ -821,9 +821,9 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
   // further matrix-core columns of one persistent, cost-balanced pass
   // (seq_order does not apply there).  A batch whose longest run is longer
   // and whose rows say that some runs are shorter (a mixed step: prompt chunks
-  // beside decodes) takes two launches: the runs of one query there, on the
-  // decode instantiation (G columns), then the longer ones here.
-  // PKV_MULTI_PATH=runs (read at each call) keeps every run here.
+  // beside decodes) takes two launches: the short runs there, then the
+  // longer ones here.  PKV_MULTI_PATH=runs (read at each call) keeps every
+  // run here.
   int skip_upto = 0;
   {
     const char* path = std::getenv("PKV_MULTI_PATH");
@@ -838,9 +838,9 @@ extern "C" pkv_status pkv_paged_attention_multi(float* out, const void* q, const
       } else if (static_cast<int64_t>(num_query_rows) < static_cast<int64_t>(num_seqs) * max_query_len) {
         const pkv_status st = runs_listed(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
                                           num_seqs, num_query_rows, num_q_heads, num_kv_heads, head_dim, block_size,
-                                          num_blocks, max_blocks, max_context_len, 1, true, scale, workspace,
-                                          workspace_bytes, kv_dtype, stream);
-        if (st == PKV_OK) skip_upto = 1;
+                                          num_blocks, max_blocks, max_context_len, short_len, true, scale,
+                                          workspace, workspace_bytes, kv_dtype, stream);
+        if (st == PKV_OK) skip_upto = short_len;
         else if (st != PKV_ERR_UNSUPPORTED) return st;
       }
     }

@@ -404,9 +404,9 @@ MIXED_GRID = [("bf16", 128, 4, 16), ("f32", 64, 8, 32), ("bf16", 64, 1, 32), ("f
 def test_mixed_step_two_launches(dt, d, G, B, monkeypatch):
     """A batch whose longest run is longer than 16 / G queries while other runs are shorter (prompt chunks and a
     whole prompt beside decodes and short verifications) takes two launches when given a workspace: the runs of
-    one query on the decode kernel's pass, over contexts cut into 512-token partitions, the longer ones on the
-    runs kernel.  Every row against the oracle; the runs kernel alone (PKV_MULTI_PATH=runs) gives the rows of
-    the runs longer than one query bit for bit and the decodes within the same bars."""
+    at most 16 / G queries on the decode kernel's pass, over contexts cut into 512-token partitions, the longer
+    ones on the runs kernel.  Every row against the oracle; the runs kernel alone (PKV_MULTI_PATH=runs) gives the
+    long runs' rows bit for bit and the short ones within the same bars."""
     k = 16 // G
     lens = [1800, 700, 2500, 64, 1200, 1, 900, 3000, 40, 513]
     runs = [1, k, 200, 1, k + 1, 1, min(2, k), 1, 40, 1]
@@ -420,18 +420,18 @@ def test_mixed_step_two_launches(dt, d, G, B, monkeypatch):
     monkeypatch.setenv("PKV_MULTI_PATH", "runs")
     other, *_ = b.multi(runs, q, split=True)
     check_close(other, ref, dt, "runs kernel only")
-    long_rows = np.concatenate([np.arange(starts[i], starts[i + 1]) for i, r in enumerate(runs) if r > 1])
+    long_rows = np.concatenate([np.arange(starts[i], starts[i + 1]) for i, r in enumerate(runs) if r > k])
     assert np.array_equal(other[long_rows], out[long_rows])
 
 
 def test_mixed_step_two_launches_edges():
-    """The runs kernel's contract holds across the two launches (G = 4, max_query_len 12: runs of one query on the
-    decode kernel's pass, longer ones on the runs kernel): an empty run writes nothing; a run longer than its
-    context gives NaN rows, on either launch; a run longer than max_query_len gives NaN on its first
-    max_query_len rows and leaves the rest alone; a bad block id poisons only its own sequence, a decode over a
-    cut context or a prompt."""
-    lens = [1400, 33, 20, 640, 9, 2100, 700, 2, 0]
-    runs = [1, 0, 21, 2, 9, 4, 1, 3, 1]
+    """The runs kernel's contract holds across the two launches (G = 4, max_query_len 12: runs of up to 4 queries
+    on the decode kernel's pass, longer ones on the runs kernel): an empty run writes nothing; a run longer than
+    its context gives NaN rows, on either launch; a run longer than max_query_len gives NaN on its first
+    max_query_len rows and leaves the rest alone; a bad block id poisons only its own sequence, a short run over
+    a cut context or a prompt."""
+    lens = [1400, 33, 20, 640, 9, 2100, 700, 2, 0, 3]
+    runs = [3, 0, 21, 2, 9, 4, 1, 3, 1, 5]
     b = Batch(lens, 8, 2, 64, 16, "f32", seed=93)
     t, l = b.tables()
     T = sum(runs)
@@ -446,10 +446,11 @@ def test_mixed_step_two_launches_edges():
         check_close(out[rows(i)], refs[i], "f32", f"sequence {i}")
     s2 = int(starts[2])
     assert np.all(np.isnan(out[s2:s2 + 12])) and np.all(out[s2 + 12:s2 + 21] == 7.0)  # 21 > 12 and > n: runs kernel
-    assert np.all(np.isnan(out[rows(7)]))  # 3 > its 2-token context: runs kernel
+    assert np.all(np.isnan(out[rows(7)]))  # 3 > its 2-token context: decode kernel's pass
     assert np.all(np.isnan(out[rows(8)]))  # a decode with no context: decode kernel's pass
+    assert np.all(np.isnan(out[rows(9)]))  # 5 > its 3-token context: runs kernel
     t2 = t.copy()
-    t2[0, 40] = b.nb + 5  # a decode over a cut context
+    t2[0, 40] = b.nb + 5  # a short run over a cut context
     t2[4, 0] = b.nb + 6   # the whole 9-token prompt
     sentinel.fill_(7.0)
     out, *_ = b.multi(runs, q, tables=t2, lens=l, query_start=starts, max_query_len=12, out=sentinel, split=True)
@@ -461,11 +462,11 @@ def test_mixed_step_two_launches_edges():
 @pytest.mark.parametrize("with_ws", [False, True])
 def test_repeated_calls_and_graph_replays_are_bitwise_stable(with_ws):
     """Runs of queries give the same bits on every call, and as a captured HIP graph on every replay, with eager
-    work and synchronisations between the replays; with a workspace the call takes two launches (the decodes on
-    the decode kernel's pass, the rest on the runs kernel)."""
+    work and synchronisations between the replays; with a workspace the call takes two launches (the decode and
+    the 3-query verification on the decode kernel's pass, the rest on the runs kernel)."""
     import paged_kv_cache_physical_amd as pk
     lens = [900, 1500, 37, 2048, 640, 1300]
-    runs = [300, 7, 37, 512, 1, 1]
+    runs = [300, 7, 37, 512, 1, 3]
     b = Batch(lens, 32, 8, 128, 16, "bf16", seed=29)
     t, l = b.tables()
     q = to_dev(wl.draw_values(wl.rng_for(30, wl.STREAM_Q), (sum(runs), 32, 128), "bf16"), "bf16")
