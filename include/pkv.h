@@ -487,9 +487,7 @@ pkv_status pkv_decode_step_static(const void* k_new, const void* v_new, float* o
  * num_seqs * max_query_len (some runs are shorter than the longest: prompt
  * chunks beside decodes in one step), which takes two launches on the
  * stream: the runs of at most 16 / G queries on the decode kernel's pass
- * (when it fits, as above), then the longer ones on the runs kernel.  A batch
- * whose runs all have one query (max_query_len 1) takes the decode kernel's
- * own form (G columns, rows placed by query_start).  The
+ * (when it fits, as above), then the longer ones on the runs kernel.  The
  * environment variable PKV_MULTI_PATH set to "runs" (read at each call) keeps
  * every run on the runs kernel.  Both paths meet the same contract and
  * tolerances; their rows differ in rounding.

@@ -162,20 +162,19 @@ __device__ __forceinline__ int32_t ld_const(const int32_t* p, size_t i) {
 }
 
 // A sequence's query rows (its run): rows q0 .. q0 + nq - 1 of q and out, at
-// positions n - nq .. n - 1 of its context.  Decode (no query_start): the
+// positions n - nq .. n - 1 of its context.  Decode (QR = 1): the
 // sequence's own row.  A run can also be (as the runs kernel takes it):
 // outside the rows (nothing is written), or impossible (longer than its
 // context or than the batch's longest run: NaN rows, at most max_query_len of
 // them).  With skip_long, a run longer than max_query_len is left to the runs
-// kernel (nothing written).  QR = 1 with query_start takes runs of one query
-// (max_query_len 1).
+// kernel (nothing written).
 struct RunRows {
   int q0, nq;
   bool bad;
 };
 template <int QR>
 __device__ __forceinline__ RunRows run_rows(const AttnArgs& a, int s, int n) {
-  if (QR == 1 && a.query_start == nullptr) return RunRows{s, 1, false};
+  if constexpr (QR == 1) return RunRows{s, 1, false};
   const int q0 = ld_const(a.query_start, s);
   const int qs = ld_const(a.query_start, s + 1) - q0;
   const bool rows = q0 >= 0 && qs > 0 && static_cast<int64_t>(q0) + qs <= a.num_query_rows &&
@@ -187,7 +186,7 @@ __device__ __forceinline__ RunRows run_rows(const AttnArgs& a, int s, int n) {
 template <int QR>
 __device__ __forceinline__ int seq_state(const AttnArgs& a, int s, int n, bool* special, bool* bad) {
   const int np = seq_parts(a, n, bad);
-  if (QR == 1 && a.query_start == nullptr) {
+  if constexpr (QR == 1) {
     *special = *bad || n == 0;
     return np;
   }
@@ -1123,7 +1122,7 @@ void paged_decode_kernel(AttnArgs a) {
       // the item's output rows: decode, the G heads of its KV head; runs, those
       // of each query of the run, Hq rows apart
       const size_t head0 = static_cast<size_t>(cur.q0) * Hkv * G + static_cast<size_t>(cur.kvh) * G;
-      const int out_rows = cur.nq > 0 ? (cur.nq - 1) * Hkv * G + G : 0;
+      const int out_rows = QR == 1 ? G : (cur.nq > 0 ? (cur.nq - 1) * Hkv * G + G : 0);
       // The partials' slot: LIST, record 0 of an owner's first item or record 1
       // of a run's last item; otherwise the segment's partition slot.
       const int rec = 2 * static_cast<int>(blockIdx.x) + ((owner && cur.k == k_first) ? 0 : 1);
@@ -1500,10 +1499,6 @@ hipError_t launch_op(const AttnArgs& a, int D, int G, bool list, Op op, hipStrea
 // Runs of queries: the listed, fused kernel with 16 / G queries per item.
 template <class DT, int D, int G>
 hipError_t launch_runs_g(const AttnArgs& a, hipStream_t stream) {
-  // runs of one query: the decode instantiation (G columns), with query_start
-  if (a.max_query_len == 1)
-    return a.block_size == 16 ? launch_kernel<DT, D, G, 16, true, false, true, 1>(a, stream)
-                              : launch_kernel<DT, D, G, 32, true, false, true, 1>(a, stream);
   return a.block_size == 16 ? launch_kernel<DT, D, G, 16, true, false, true, 16 / G>(a, stream)
                             : launch_kernel<DT, D, G, 32, true, false, true, 16 / G>(a, stream);
 }

@@ -537,11 +537,11 @@ ONE_QUERY_GRID = [("bf16", 128, 4, 16), ("f32", 64, 1, 32), ("bf16", 64, 8, 32),
 
 
 @pytest.mark.parametrize("dt,d,G,B", ONE_QUERY_GRID)
-def test_one_query_runs_on_the_decode_instantiation(dt, d, G, B):
-    """Runs of one query each (max_query_len 1: decodes given as runs) take the decode kernel's own instantiation
-    with the rows placed by query_start: every row against the oracle over contexts cut into 512-token partitions,
-    with empty runs between them; a run over an empty context is NaN; a bad block id poisons only its sequence;
-    a run outside the rows is left alone."""
+def test_one_query_runs_on_the_decode_kernel(dt, d, G, B):
+    """Runs of one query each (max_query_len 1: decodes given as runs) on the decode kernel's listed pass, with
+    the rows placed by query_start: every row against the oracle over contexts cut into 512-token partitions, with
+    empty runs between them; a run over an empty context is NaN; a bad block id poisons only its sequence; a run
+    outside the rows is left alone."""
     lens = [1800, 700, 2500, 64, 1200, 1, 900, 3000, 40, 513, 0]
     runs = [1, 1, 0, 1, 1, 1, 0, 1, 1, 1, 1]
     Hkv = 2
