@@ -1497,10 +1497,19 @@ hipError_t launch_op(const AttnArgs& a, int D, int G, bool list, Op op, hipStrea
 }
 
 // Runs of queries: the listed, fused kernel with 16 / G queries per item.
+template <class DT, int D, int G, int QR>
+hipError_t launch_runs_q(const AttnArgs& a, hipStream_t stream) {
+  return a.block_size == 16 ? launch_kernel<DT, D, G, 16, true, false, true, QR>(a, stream)
+                            : launch_kernel<DT, D, G, 32, true, false, true, QR>(a, stream);
+}
+// Queries per item: 16 / G (the whole column tile), or 4 for runs of at most
+// 4 queries at G <= 2 (4 or 8 columns: smaller merge and partial records).
 template <class DT, int D, int G>
 hipError_t launch_runs_g(const AttnArgs& a, hipStream_t stream) {
-  return a.block_size == 16 ? launch_kernel<DT, D, G, 16, true, false, true, 16 / G>(a, stream)
-                            : launch_kernel<DT, D, G, 32, true, false, true, 16 / G>(a, stream);
+  if constexpr (G <= 2) {
+    if (a.max_query_len <= 4) return launch_runs_q<DT, D, G, 4>(a, stream);
+  }
+  return launch_runs_q<DT, D, G, 16 / G>(a, stream);
 }
 template <class DT, int D>
 hipError_t launch_runs_d(const AttnArgs& a, int G, hipStream_t stream) {

@@ -533,6 +533,30 @@ def test_short_runs_on_the_decode_kernel(dt, d, G, B, monkeypatch):
     check_close(other, ref, dt, "runs kernel")
 
 
+FOUR_GRID = [(dt, d, G, B) for dt in ("f32", "bf16") for d in (64, 128) for G in (1, 2) for B in (16, 32)]
+
+
+@pytest.mark.parametrize("dt,d,G,B", FOUR_GRID)
+def test_runs_of_up_to_four_queries_at_one_or_two_heads_per_kv_head(dt, d, G, B, monkeypatch):
+    """With G <= 2 and runs of at most 4 queries the decode kernel's pass takes 4 queries per item (4 or 8
+    matrix-core columns instead of the whole 16-column tile): every shape against the oracle over contexts cut
+    into 512-token partitions and between workgroups, and against the runs kernel (PKV_MULTI_PATH=runs)."""
+    rng = wl.rng_for(700 + G * 10 + d + B, 3)
+    lens = [int(x) for x in rng.integers(1, 3000, size=20)] + [1, 3, 513, 3000]
+    runs = [min(n, int(x)) for n, x in zip(lens, rng.integers(1, 5, size=len(lens)))]
+    runs[-1] = 4
+    Hkv = 2
+    say(f"case {dt} d={d} G={G} B={B}: runs={runs}")
+    b = Batch(lens, G * Hkv, Hkv, d, B, dt, seed=G + d + B + 17)
+    q = wl.draw_values(wl.rng_for(71, wl.STREAM_Q, G, d), (sum(runs), G * Hkv, d), dt)
+    out, t, l, starts = b.multi(runs, q, split=True)
+    ref = b.oracle(q, t, l, starts)
+    check_close(out, ref, dt, "decode kernel, 4 queries per item")
+    monkeypatch.setenv("PKV_MULTI_PATH", "runs")
+    other, *_ = b.multi(runs, q, split=True)
+    check_close(other, ref, dt, "runs kernel")
+
+
 ONE_QUERY_GRID = [("bf16", 128, 4, 16), ("f32", 64, 1, 32), ("bf16", 64, 8, 32), ("f32", 128, 2, 16)]
 
 
