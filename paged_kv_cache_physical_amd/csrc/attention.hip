@@ -39,6 +39,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -1663,20 +1664,32 @@ void* scratch_address() {
 // Runs of at most 16 / G queries per sequence (the verification of drafted
 // tokens) on the decode kernel: its persistent, cost-balanced item list with
 // the queries of a run as further matrix-core columns.  The partition size is
-// 512 tokens.  Arguments as pkv_paged_attention_multi takes them, already
+// 512 tokens, or 256 for a small batch (see runs_partition).  Arguments as pkv_paged_attention_multi takes them, already
 // checked; PKV_ERR_UNSUPPORTED when the batch does not fit this path (too
 // many sequences, runs too long, or no workspace where the split needs one),
 // and the caller then uses the runs kernel; PKV_ERR_WORKSPACE for a workspace
 // too small.  With skip_long, max_query_len is the longest run this launch
 // takes, and the runs kernel takes the longer ones of the batch.
 constexpr int32_t kRunsPartition = 512;
+// The item list cuts its lanes' runs at single groups only when the batch's
+// cost holds four partitions per lane, else at partition starts, which leaves
+// lanes up to half a partition apart.  A batch whose cost, counted at its
+// longest context, stays under six partitions of 512 per lane (about 512
+// workgroups fill the GPU, H_kv per lane) takes 256-token partitions instead,
+// whose cuts are then fine.  The count is an upper bound, hence the margin.
+int32_t runs_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  const int64_t lanes = std::max<int64_t>(1, 512 / std::max<int32_t>(num_kv_heads, 1));
+  const int64_t groups = static_cast<int64_t>(num_seqs) * ((static_cast<int64_t>(max_context_len) + 15) / 16);
+  return groups < 6 * lanes * (kRunsPartition / 16 + kItemCharge) ? kRunsPartition / 2 : kRunsPartition;
+}
 
 bool runs_listed_fits(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t max_context_len, int32_t max_query_len) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return false;
   const int G = num_q_heads / num_kv_heads;
   if (max_query_len < 1 || static_cast<int64_t>(max_query_len) * G > 16) return false;
-  const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, 16, max_context_len, kRunsPartition, 16);
+  const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, 16, max_context_len,
+                              runs_partition(num_seqs, num_kv_heads, max_context_len), 16);
   // the output offsets of one run stay within 32 bits
   return plan.list && static_cast<int64_t>(max_query_len) * num_q_heads * head_dim * 4 < (int64_t{1} << 31);
 }
@@ -1684,7 +1697,9 @@ bool runs_listed_fits(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
 size_t runs_listed_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_context_len, int32_t max_query_len) {
   if (!runs_listed_fits(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_query_len)) return 0;
-  return make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, 16, max_context_len, kRunsPartition, 16).bytes;
+  return make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, 16, max_context_len,
+                   runs_partition(num_seqs, num_kv_heads, max_context_len), 16)
+      .bytes;
 }
 
 pkv_status runs_listed(float* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -1697,7 +1712,8 @@ pkv_status runs_listed(float* out, const void* q, const void* k_cache, const voi
     return PKV_ERR_UNSUPPORTED;
   const int G = num_q_heads / num_kv_heads;
   const Plan plan =
-      make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len, kRunsPartition, 16);
+      make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                runs_partition(num_seqs, num_kv_heads, max_context_len), 16);
   const int64_t items = static_cast<int64_t>(plan.max_parts) * num_seqs * num_kv_heads;
   if (items > INT32_MAX / 2) return PKV_ERR_UNSUPPORTED;
   AttnArgs a{};

@@ -540,8 +540,11 @@ def test_duplicate_and_unknown_ids_in_one_append(libpkv):
 def listed_runs_bytes(S, Hq, Hkv, d, ctx, mq):
     """The decode kernel's path for runs of at most 16 / G queries (all the runs when mq * G <= 16, else the short
     runs of a mixed batch): records of 16 columns for two per workgroup of a grid of at most 2048 (a multiple of
-    H_kv), over 512-token partitions; 0 when no context is cut."""
-    parts = -(-max(ctx, 1) // 512)
+    H_kv), over 512-token partitions (256 when the batch's groups at its longest context stay under six 34-unit
+    partitions per lane of 512 / H_kv workgroups); 0 when no context is cut."""
+    lanes = max(1, 512 // Hkv)
+    P = 256 if S * (-(-ctx // 16)) < 6 * lanes * 34 else 512
+    parts = -(-max(ctx, 1) // P)
     if parts <= 1:
         return 0
     items = parts * S * Hkv
@@ -570,7 +573,10 @@ def test_runs_of_queries_host_checks_and_split_plan(libpkv):
     # 68 rows: the runs kernel does not split, but the short runs of such a batch take the decode kernel's path
     assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 32768, 17) == listed_runs_bytes(
         8, 32, 8, 128, 32768, 17) > 0
-    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 500, 4) == 0  # too short to split
+    # a small batch's short runs take 256-token partitions: 500-token contexts are cut, 256-token ones are not
+    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 500, 4) == listed_runs_bytes(
+        8, 32, 8, 128, 500, 4) > 0
+    assert pk.pkv_attention_multi_workspace_bytes(8, 32, 8, 128, 256, 4) == 0  # too short to split
     assert pk.pkv_attention_multi_workspace_bytes(8, 30, 8, 128, 32768, 4) == 0  # H_q % H_kv != 0
 
     def call(out=None, q=None, k=None, v=None, bt=None, cl=None, qs=None, order=None, S=2, T=8, Hq=8, Hkv=8, d=128,
