@@ -273,8 +273,10 @@ struct Shared {
 };
 
 // Cost of a partition in the work split: its groups plus a fixed charge for
-// an item's start-up and merge.
-constexpr int kItemCharge = 2;
+// an item's start-up and merge, worth eight groups (a boundary drains and
+// refills a wave's ring and meets the other waves twice; charges of 2 to 8
+// were measured, 8 the fastest on the GQA and Llama-7B decode batches).
+constexpr int kItemCharge = 8;
 
 // Log-sum-exp combination of one sequence's segments for one KV head: the
 // segments sit in record 1 of runs first .. last - 1 and record 0 of run last,

@@ -540,10 +540,10 @@ def test_duplicate_and_unknown_ids_in_one_append(libpkv):
 def listed_runs_bytes(S, Hq, Hkv, d, ctx, mq):
     """The decode kernel's path for runs of at most 16 / G queries (all the runs when mq * G <= 16, else the short
     runs of a mixed batch): records of 16 columns for two per workgroup of a grid of at most 2048 (a multiple of
-    H_kv), over 512-token partitions (256 when the batch's groups at its longest context stay under six 34-unit
+    H_kv), over 512-token partitions (256 when the batch's groups at its longest context stay under six 40-unit
     partitions per lane of 512 / H_kv workgroups); 0 when no context is cut."""
     lanes = max(1, 512 // Hkv)
-    P = 256 if S * (-(-ctx // 16)) < 6 * lanes * 34 else 512
+    P = 256 if S * (-(-ctx // 16)) < 6 * lanes * 40 else 512
     parts = -(-max(ctx, 1) // P)
     if parts <= 1:
         return 0
