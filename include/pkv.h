@@ -480,9 +480,10 @@ pkv_status pkv_decode_step_static(const void* k_new, const void* v_new, float* o
  * Paths: runs of at most 16 / G queries (max_query_len * H_q / H_kv <= 16;
  * speculative verification) with at most 4096 sequences go to the decode
  * kernel's listed pass, the queries of a run as further matrix-core columns of
- * one persistent, cost-balanced pass over 512-token partitions; that path
- * needs the workspace when a context exceeds 512 tokens, and without one the
- * call uses the runs kernel, unsplit.  Other batches use the runs kernel,
+ * one persistent, cost-balanced pass over 512-token partitions (256 for a
+ * small batch: num_seqs * ceil(max_context_len / 16) under 6 * (512 / H_kv)
+ * * 40); that path needs the workspace when a context exceeds a partition,
+ * and without one the call uses the runs kernel, unsplit.  Other batches use the runs kernel,
  * except a batch with max_query_len > 16 / G and num_query_rows <
  * num_seqs * max_query_len (some runs are shorter than the longest: prompt
  * chunks beside decodes in one step), which takes two launches on the
@@ -508,8 +509,9 @@ pkv_status pkv_paged_attention_multi(float* out, const void* q, const void* k_ca
 
 /* Bytes of workspace pkv_paged_attention_multi uses to split long contexts (0
  * when it would not split them): the larger of the two paths' needs.  The
- * decode kernel's path (runs of at most 16 / G queries, see there) cuts contexts into 512-token
- * partitions and between workgroups, with records per workgroup.  On the runs
+ * decode kernel's path (runs of at most 16 / G queries, see there) cuts
+ * contexts into 512- or 256-token partitions and between workgroups, with
+ * records per workgroup.  On the runs
  * kernel a context is split when every run's rows (max_query_len * H_q / H_kv)
  * fit one 64-row block and the batch has too few (sequence, KV head) pairs to
  * fill the GPU: each pair's context is cut into splits of at least 256 tokens,

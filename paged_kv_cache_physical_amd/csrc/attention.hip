@@ -1499,7 +1499,7 @@ hipError_t launch_op(const AttnArgs& a, int D, int G, bool list, Op op, hipStrea
   return hipErrorInvalidValue;
 }
 
-// Runs of queries: the listed, fused kernel with 16 / G queries per item.
+// Runs of queries: the listed, fused kernel with QR queries per item.
 template <class DT, int D, int G, int QR>
 hipError_t launch_runs_q(const AttnArgs& a, hipStream_t stream) {
   return a.block_size == 16 ? launch_kernel<DT, D, G, 16, true, false, true, QR>(a, stream)
@@ -1666,8 +1666,9 @@ void* scratch_address() {
 // Runs of at most 16 / G queries per sequence (the verification of drafted
 // tokens) on the decode kernel: its persistent, cost-balanced item list with
 // the queries of a run as further matrix-core columns.  The partition size is
-// 512 tokens, or 256 for a small batch (see runs_partition).  Arguments as pkv_paged_attention_multi takes them, already
-// checked; PKV_ERR_UNSUPPORTED when the batch does not fit this path (too
+// 512 tokens, or 256 for a small batch (see runs_partition).  Arguments as
+// pkv_paged_attention_multi takes them, already checked;
+// PKV_ERR_UNSUPPORTED when the batch does not fit this path (too
 // many sequences, runs too long, or no workspace where the split needs one),
 // and the caller then uses the runs kernel; PKV_ERR_WORKSPACE for a workspace
 // too small.  With skip_long, max_query_len is the longest run this launch
